@@ -1,0 +1,282 @@
+"""CSA2 decode-path oracle -- test infrastructure only.
+
+A plain, slow CPU statement of the CSA2 decode hot path, used by ``tests/``,
+``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg, and by
+nothing else.  The per-element arithmetic lives in ``csa2_oracle.c`` (plain C,
+binary64 where the result is a real number, exact where it is discrete); this
+module loads it with ctypes and composes the per-call steps the way the pages
+describe the modes:
+
+* Full    -- score every visible position, keep the top-k and build the
+  block-max candidate pool ("DeepSeek-V4.1-Flash: Pushing the Limits of KV
+  Cache Compression", "Hierarchical Sparse Indexer", Figure 5).
+* Reindex -- score only the pool's positions with the layer's own indexer
+  query, keep the top-k (same page; "Inside DeepSeek V4.1 Flash",
+  "Hierarchical indexing bounds later searches").
+* Reuse   -- no scoring; the latest top-k indices are used as they are
+  ("CSA2: share cache, refresh selection only when needed", mode table).
+* Attention over the selected dequantized FP4 entries together with the
+  128-token FP8 window ("Inside DeepSeek V4.1 Flash", "CSA2: reuse memory and
+  reuse selection independently"; knowledge note, "FP4 main KV").
+
+Nothing here shares code with the HIP path; pages of the caches are gathered
+with plain numpy indexing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa2_oracle.c")
+_LIB = os.path.join(_HERE, "libcsa2_oracle.so")
+
+D = 512            # main-KV channels
+DI = 128           # indexer-key channels
+PAGE = 64          # entries per page
+ENTRY_CODES = 256  # bytes of E2M1 codes per entry
+NGROUPS = 32       # E4M3 scales per entry
+ENTRY_BYTES = ENTRY_CODES + NGROUPS  # 288
+PAGE_BYTES = PAGE * ENTRY_BYTES      # 18,432
+BLOCK = 8
+SWA = 128
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, u32, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_double
+        L.csa2o_e4m3_decode.restype = dbl
+        L.csa2o_e4m3_decode.argtypes = [u32]
+        L.csa2o_e2m1_decode.restype = dbl
+        L.csa2o_e2m1_decode.argtypes = [u32]
+        L.csa2o_e4m3_nearest.restype = u32
+        L.csa2o_e4m3_nearest.argtypes = [dbl]
+        L.csa2o_e4m3_nearest_sixth.restype = u32
+        L.csa2o_e4m3_nearest_sixth.argtypes = [dbl]
+        L.csa2o_e2m1_nearest.restype = u32
+        L.csa2o_e2m1_nearest.argtypes = [dbl, dbl]
+        L.csa2o_quantize_row.argtypes = [P, P, P]
+        L.csa2o_quantize_kv.argtypes = [P, i64, P, P, i64]
+        L.csa2o_dequant_entry.argtypes = [P, P, P]
+        L.csa2o_index_scores.argtypes = [P, P, ctypes.c_int, P, i64, P]
+        L.csa2o_topk.argtypes = [P, P, i64, i32, P]
+        L.csa2o_pool.argtypes = [P, i64, i32, P, P]
+        L.csa2o_attention.argtypes = [P, ctypes.c_int, dbl, P, i64, P, P]
+        L.csa2o_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(lib().csa2o_num_threads())
+
+
+# ---------------------------------------------------------------- formats
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 codes (uint8 array) -> binary64 values (NaN for S.1111.111)."""
+    table = np.array([lib().csa2o_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    table = np.array([lib().csa2o_e2m1_decode(c) for c in range(16)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def e4m3_nearest(x: float) -> int:
+    return int(lib().csa2o_e4m3_nearest(float(x)))
+
+
+def e4m3_nearest_sixth(num: float) -> int:
+    return int(lib().csa2o_e4m3_nearest_sixth(float(num)))
+
+
+def e2m1_nearest(a: float, s: float) -> int:
+    return int(lib().csa2o_e2m1_nearest(float(a), float(s)))
+
+
+def bf16_to_f64(u16) -> np.ndarray:
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- a1: cache write
+def quantize_rows(x_bf16: np.ndarray):
+    """x_bf16: uint16 [R, 512] -> (codes uint8 [R, 256], scales uint8 [R, 32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, D)
+    R = x.shape[0]
+    codes = np.zeros((R, ENTRY_CODES), np.uint8)
+    scales = np.zeros((R, NGROUPS), np.uint8)
+    L = lib()
+    for r in range(R):
+        L.csa2o_quantize_row(_p(x[r]), _p(codes[r]), _p(scales[r]))
+    return codes, scales
+
+
+def quantize_kv(x_bf16: np.ndarray, dst_slot: np.ndarray, pool: np.ndarray) -> np.ndarray:
+    """Write rows into the paged pool (uint8 [n_pages, 18432]) in place."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, D)
+    slot = np.ascontiguousarray(dst_slot, dtype=np.int64)
+    assert pool.dtype == np.uint8 and pool.flags["C_CONTIGUOUS"]
+    n_pages = pool.shape[0]
+    lib().csa2o_quantize_kv(_p(x), x.shape[0], _p(slot), _p(pool), n_pages)
+    return pool
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, ENTRY_CODES)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, NGROUPS)
+    out = np.zeros((codes.shape[0], D), np.float64)
+    L = lib()
+    for r in range(codes.shape[0]):
+        L.csa2o_dequant_entry(_p(codes[r]), _p(scales[r]), _p(out[r]))
+    return out
+
+
+def pool_entry(kv_pool: np.ndarray, page: int, off: int):
+    """(codes, scales) of one entry of a paged main-KV pool."""
+    base = kv_pool[page]
+    return (base[off * ENTRY_CODES:(off + 1) * ENTRY_CODES],
+            base[PAGE * ENTRY_CODES + off * NGROUPS:PAGE * ENTRY_CODES + (off + 1) * NGROUPS])
+
+
+# ---------------------------------------------------------------- a2..a6: indexer
+def index_scores(q_codes: np.ndarray, w: np.ndarray, key_codes: np.ndarray) -> np.ndarray:
+    """q_codes uint8 [H,128], w float32 [H], key_codes uint8 [n,128] -> float32 [n]."""
+    q = np.ascontiguousarray(q_codes, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    k = np.ascontiguousarray(key_codes, dtype=np.uint8).reshape(-1, DI)
+    s = np.zeros(k.shape[0], np.float32)
+    lib().csa2o_index_scores(_p(q), _p(w), q.shape[0], _p(k), k.shape[0], _p(s))
+    return s
+
+
+def topk(s: np.ndarray, k: int, idx: np.ndarray | None = None) -> np.ndarray:
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.zeros(k, np.int32)
+    if idx is not None:
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        lib().csa2o_topk(_p(s), _p(idx), s.shape[0], k, _p(out))
+    else:
+        lib().csa2o_topk(_p(s), None, s.shape[0], k, _p(out))
+    return out
+
+
+def pool(s: np.ndarray, pool_blocks: int):
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.zeros(pool_blocks, np.int32)
+    n = ctypes.c_int32(0)
+    lib().csa2o_pool(_p(s), s.shape[0], pool_blocks, _p(out), ctypes.byref(n))
+    return out, int(n.value)
+
+
+def gather_keys(kidx_pool: np.ndarray, page_table_row: np.ndarray, n: int) -> np.ndarray:
+    """Logical indexer keys [n,128] of one sequence from the paged pool [P,64,128]."""
+    j = np.arange(n)
+    return kidx_pool[page_table_row[j // PAGE], j % PAGE]
+
+
+def pool_positions(pool_blocks_row: np.ndarray, n_blocks: int, n: int) -> np.ndarray:
+    """Positions covered by the first n_blocks pool blocks, ascending."""
+    pos = []
+    for b in pool_blocks_row[:n_blocks]:
+        pos.extend(range(8 * int(b), min(8 * int(b) + 8, n)))
+    return np.array(pos, dtype=np.int32)
+
+
+def index_full(q_idx, w, kidx_pool, page_table, n_entries, topk_k, pool_blocks):
+    """Full mode for a batch: returns (topk [B,T,k], pool [B,T,pool_blocks], pool_n [B,T])."""
+    B, T, HI, _ = q_idx.shape
+    out_topk = np.zeros((B, T, topk_k), np.int32)
+    out_pool = np.zeros((B, T, pool_blocks), np.int32)
+    out_n = np.zeros((B, T), np.int32)
+    for b in range(B):
+        n = int(n_entries[b])
+        keys = gather_keys(kidx_pool, page_table[b], n)
+        for t in range(T):
+            s = index_scores(q_idx[b, t], w[b, t], keys)
+            out_topk[b, t] = topk(s, topk_k)
+            out_pool[b, t], out_n[b, t] = pool(s, pool_blocks)
+    return out_topk, out_pool, out_n
+
+
+def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool_, pool_n, topk_k):
+    """Reindex mode: score only the pool's positions; returns topk [B,T,k]."""
+    B, T, HI, _ = q_idx.shape
+    out = np.zeros((B, T, topk_k), np.int32)
+    for b in range(B):
+        n = int(n_entries[b])
+        for t in range(T):
+            pos = pool_positions(pool_[b, t], int(pool_n[b, t]), n)
+            pt = page_table[b]
+            keys = kidx_pool[pt[pos // PAGE], pos % PAGE] if len(pos) else np.zeros((0, DI), np.uint8)
+            s = index_scores(q_idx[b, t], w[b, t], keys)
+            out[b, t] = topk(s, topk_k, pos)
+    return out
+
+
+# ---------------------------------------------------------------- a7: attention
+def attention(q: np.ndarray, sm_scale: float, rows: np.ndarray):
+    """q float64 [H,512], rows float64 [nr,512] -> (out [H,512], lse [H])."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.float64).reshape(-1, D)
+    H = q.shape[0]
+    out = np.zeros((H, D), np.float64)
+    lse = np.zeros(H, np.float64)
+    lib().csa2o_attention(_p(q), H, float(sm_scale), _p(rows), rows.shape[0], _p(out), _p(lse))
+    return out, lse
+
+
+def selected_rows(kv_pool, page_table_row, idx_row):
+    """Dequantized main-KV rows of the valid (>= 0) selected positions."""
+    sel = [int(j) for j in idx_row if j >= 0]
+    if not sel:
+        return np.zeros((0, D), np.float64)
+    codes = np.stack([pool_entry(kv_pool, int(page_table_row[j // PAGE]), j % PAGE)[0] for j in sel])
+    scales = np.stack([pool_entry(kv_pool, int(page_table_row[j // PAGE]), j % PAGE)[1] for j in sel])
+    return dequant(codes, scales)
+
+
+def sparse_attn(q_bf16, sm_scale, kv_pool, page_table, topk_idx, swa, batches=None, tokens=None):
+    """Attention for each (b, t): softmax over the selected entries plus SWA rows t..t+127.
+
+    q_bf16 uint16 [B,T,H,512]; kv_pool uint8 [P,18432]; topk_idx int32 [B,T,k];
+    swa uint8 [B,127+T,512] (E4M3).  Returns (out float64 [B,T,H,512], lse [B,T,H]);
+    only the (b, t) pairs listed in ``batches``/``tokens`` are computed (others NaN).
+    """
+    B, T, H, _ = q_bf16.shape
+    out = np.full((B, T, H, D), np.nan)
+    lse = np.full((B, T, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        for t in (range(T) if tokens is None else tokens):
+            rows = selected_rows(kv_pool, page_table[b], topk_idx[b, t])
+            win = e4m3_decode(swa[b, t:t + SWA])
+            allrows = np.concatenate([rows, win], axis=0)
+            out[b, t], lse[b, t] = attention(bf16_to_f64(q_bf16[b, t]), sm_scale, allrows)
+    return out, lse
