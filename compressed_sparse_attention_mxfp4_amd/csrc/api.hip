@@ -1,0 +1,36 @@
+// C ABI entry points that are not tied to one kernel family.
+#include "common.h"
+
+extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_n,
+                                      int32_t pool_blocks);
+extern "C" size_t csa2_attn_ws_bytes(int32_t B, int32_t T, int32_t H, int32_t topk);
+
+extern "C" size_t csa2_workspace_bytes(int op, int32_t B, int32_t T, int32_t heads,
+                                       int32_t max_n_entries, int32_t topk) {
+  if (B <= 0 || T <= 0 || heads <= 0) return 0;
+  switch (op) {
+    case CSA2_OP_INDEX_FULL:
+      if (max_n_entries <= 0) return 0;
+      return csa2_index_ws_bytes(op, B, T, max_n_entries, CSA2_MAX_POOL_BLOCKS);
+    case CSA2_OP_INDEX_REINDEX:
+      return csa2_index_ws_bytes(op, B, T, 0, CSA2_MAX_POOL_BLOCKS);
+    case CSA2_OP_SPARSE_ATTN:
+      if (topk <= 0) return 0;
+      return csa2_attn_ws_bytes(B, T, heads, topk);
+    default:
+      return 0;
+  }
+}
+
+extern "C" const char* csa2_status_str(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported size or shape";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int csa2_abi_version(void) { return 100; }

@@ -1,0 +1,116 @@
+// FP4 main-KV cache write (knowledge note "DeepSeek-V4.1-Flash: Pushing the
+// Limits of KV Cache Compression", section "FP4 main KV: trade precision for
+// bytes"; "Inside DeepSeek V4.1 Flash", section "Reconstructing the 890-byte
+// cache budget": 512 x 4/8 + 512/16 = 288 B per entry).
+//
+// One thread per 16-channel group: 32 threads cover one 1 KiB bf16 row with
+// two 16 B loads each (a wave reads 2 KiB contiguous), write 8 B of E2M1
+// nibbles each (256 B contiguous per row) and one E4M3 scale byte, gathered
+// four at a time into a dword store.  HBM-bound: 1,024 B read + 288 B
+// written per row.
+#include "common.h"
+
+namespace csa2 {
+
+// E4M3 code (positive, saturating at 448 = 0x7E) nearest to t, ties to even.
+// t >= 0 is a correctly rounded binary32 quotient amax / 6; rounding that
+// quotient to binary32 cannot move it onto or across an E4M3 midpoint
+// (amax has 8 significant bits, so amax / 6 is either exact or at least
+// 2^-10 relative away from every midpoint), so this equals the E4M3
+// rounding of the exact quotient.
+__device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
+  if (t >= 448.0f) return 0x7Eu;
+  if (t < 0.015625f) {  // below the smallest normal 2^-6: steps of 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);  // 0..8 (8 is the normal 2^-6)
+  }
+  uint32_t u = f2u(t);
+  uint32_t lsb = (u >> 20) & 1u;
+  u += 0x7FFFFu + lsb;                 // round the 23-bit mantissa to 3 bits
+  uint32_t e = (u >> 23) - 120u;       // E4M3 exponent field (bias 7)
+  uint32_t code = (e << 3) | ((u >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Value of a positive E4M3 code as binary32 (exact).
+__device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  return e ? u2f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+__global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t rows,
+                                                          const int64_t* __restrict__ slot,
+                                                          uint8_t* __restrict__ pool,
+                                                          int64_t n_pages) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = gid >> 5;      // row
+  const int g = (int)(gid & 31);   // 16-channel group
+  const bool live = r < rows;
+  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t s = -1;
+  if (live) {
+    const v4u* src = reinterpret_cast<const v4u*>(x + r * kD + g * 16);
+    v4u a = __builtin_nontemporal_load(src);
+    v4u b = __builtin_nontemporal_load(src + 1);
+    h[0] = a.x; h[1] = a.y; h[2] = a.z; h[3] = a.w;
+    h[4] = b.x; h[5] = b.y; h[6] = b.z; h[7] = b.w;
+    s = slot[r];
+  }
+  // amax over 16 bf16 magnitudes: non-negative bf16 bit patterns order like values
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = h[i] & 0x7FFFu, hi = (h[i] >> 16) & 0x7FFFu;
+    amax_bits = max(amax_bits, max(lo, hi));
+  }
+  const float amax = u2f(amax_bits << 16);
+  const uint32_t sc = e4m3_rne_pos(__fdiv_rn(amax, 6.0f));
+  const float sv = e4m3_value_pos(sc);
+  // E2M1 magnitude by counting midpoints passed; a tie at 0.25/1.25/2.5/5
+  // goes down to the even code, at 0.75/1.75/3.5 up to the even code.
+  const float m025 = 0.25f * sv, m075 = 0.75f * sv, m125 = 1.25f * sv, m175 = 1.75f * sv;
+  const float m250 = 2.5f * sv, m350 = 3.5f * sv, m500 = 5.0f * sv;
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t bits = (h[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+    float a = u2f((bits & 0x7FFFu) << 16);
+    uint32_t m = (uint32_t)(a > m025) + (uint32_t)(a >= m075) + (uint32_t)(a > m125) +
+                 (uint32_t)(a >= m175) + (uint32_t)(a > m250) + (uint32_t)(a >= m350) +
+                 (uint32_t)(a > m500);
+    m = (sv > 0.0f) ? m : 0u;
+    uint32_t code = ((bits >> 15) << 3) | m;
+    if (i < 8) w0 |= code << (4 * i);
+    else w1 |= code << (4 * (i - 8));
+  }
+  // four neighbouring groups' scale bytes -> one dword store
+  const uint32_t s1 = __shfl_down(sc, 1, 4), s2 = __shfl_down(sc, 2, 4), s3 = __shfl_down(sc, 3, 4);
+  const bool ok = live && s >= 0 && s < n_pages * kPage;
+  if (ok) {
+    const int64_t page = s >> 6, off = s & 63;
+    uint8_t* base = pool + page * kPageBytes;
+    v2u cw = {w0, w1};
+    __builtin_nontemporal_store(cw, reinterpret_cast<v2u*>(base + off * kEntryCodes + g * 8));
+    if ((g & 3) == 0) {
+      uint32_t sw = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+      __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t*>(base + kPage * kEntryCodes +
+                                                                  off * kEntryScales + g));
+    }
+  }
+}
+
+}  // namespace csa2
+
+extern "C" int csa2_quantize_kv(const uint16_t* kv_bf16, int64_t rows, const int64_t* dst_slot,
+                                uint8_t* kv_pool, int64_t n_pages, csa2_stream_t stream) {
+  if (rows < 0 || n_pages < 0) return CSA2_ERR_INVALID_ARG;
+  if (rows == 0) return CSA2_OK;
+  if (!kv_bf16 || !dst_slot || !kv_pool) return CSA2_ERR_INVALID_ARG;
+  if (n_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
+  const int64_t threads = rows * 32;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(csa2::quantize_kv_kernel, dim3((uint32_t)blocks), dim3(256), 0,
+                     (hipStream_t)stream, kv_bf16, rows, dst_slot, kv_pool, n_pages);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
+}

@@ -1,0 +1,182 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path on MI355X (gfx950).
+ *
+ * Four compute calls follow the pages' statement of one CSA2 decode layer
+ * ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+ * sections "CSA2: share cache, refresh selection only when needed" (mode
+ * table), "Hierarchical Sparse Indexer" (Figure 5), "FP4 main KV: trade
+ * precision for bytes"; "Inside DeepSeek V4.1 Flash: CED, CSA2 and the
+ * 890-Byte KV Cache", sections "CSA2: reuse memory and reuse selection
+ * independently", "Hierarchical indexing bounds later searches, not every
+ * search", "Reconstructing the 890-byte cache budget"):
+ *
+ *   csa2_quantize_kv    -- FP4 main-KV cache write (E2M1 + E4M3 per 16 ch)
+ *   csa2_index_full     -- Full mode: score every visible entry, top-k, and
+ *                          the block-max candidate pool (<= 2,048 blocks of 8)
+ *   csa2_index_reindex  -- Reindex mode: score only the pool, top-k
+ *   csa2_sparse_attn    -- gather + dequantize the selected entries and run
+ *                          one softmax over them and the 128-row FP8 window.
+ *                          Reuse mode is this call with a previous layer's
+ *                          top-k buffer passed in unchanged.
+ *
+ * Conventions (all calls):
+ *  - Every pointer argument except `stream` is a DEVICE pointer (HBM) owned
+ *    by the caller; the library never allocates, frees or synchronizes.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the null stream).  Inputs are read-only; outputs are fully written.
+ *  - Return value: CSA2_OK, or a negative status detected on the host before
+ *    any launch (argument and size checks), or CSA2_ERR_LAUNCH if the launch
+ *    itself failed.  On an error return nothing has been enqueued.
+ *  - Fixed dimensions: main KV 512 channels, indexer key 128 channels,
+ *    64 entries per page, pool blocks of 8 entries, window of 128 rows.
+ *  - Formats: bf16 = IEEE bfloat16 bits; FP8 = OCP E4M3 (E4M3FN, max 448,
+ *    codes 0x7F/0xFF are NaN); FP4 = OCP E2M1 nibbles.
+ *  - Preconditions not checked on the device: inputs finite, no FP8 NaN
+ *    codes, indexer weights w finite with |w| = 0 or 2^-100 <= |w| <= 2^100,
+ *    top-k indices distinct.  Page ids outside [0, n_pages) and positions
+ *    outside [0, n_entries[b]) are treated as not visible (never read).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_D 512                 /* main-KV channels */
+#define CSA2_DI 128                /* indexer-key channels */
+#define CSA2_PAGE 64               /* entries per page */
+#define CSA2_ENTRY_CODE_BYTES 256  /* 512 E2M1 nibbles */
+#define CSA2_ENTRY_SCALE_BYTES 32  /* one E4M3 scale per 16 channels */
+#define CSA2_ENTRY_BYTES 288       /* 256 + 32 */
+#define CSA2_PAGE_BYTES 18432      /* 64 x 288: 64 x 256 B codes, then 64 x 32 B scales */
+#define CSA2_KIDX_PAGE_BYTES 8192  /* 64 x 128 B FP8 indexer keys */
+#define CSA2_BLOCK 8               /* positions per pool block */
+#define CSA2_SWA 128               /* sliding-window rows per query token */
+#define CSA2_MAX_TOPK 2048
+#define CSA2_MAX_POOL_BLOCKS 2048
+#define CSA2_MAX_ENTRIES 262144    /* per sequence: 1M tokens at 4:1 */
+#define CSA2_MAX_INDEX_HEADS 64    /* indexer heads HI */
+#define CSA2_MAX_T 4               /* decode query tokens per sequence */
+
+enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, k > limit */
+  CSA2_ERR_UNSUPPORTED = -2, /* a size outside what the kernels are built for */
+  CSA2_ERR_WORKSPACE = -3,   /* ws NULL or ws_bytes below csa2_workspace_bytes */
+  CSA2_ERR_LAUNCH = -4       /* the HIP launch reported an error */
+};
+
+enum csa2_op {
+  CSA2_OP_INDEX_FULL = 1,
+  CSA2_OP_INDEX_REINDEX = 2,
+  CSA2_OP_SPARSE_ATTN = 3
+};
+
+typedef void *csa2_stream_t; /* hipStream_t */
+
+/*
+ * FP4 main-KV cache write.  Knowledge note, "FP4 main KV": E2M1 elements,
+ * one E4M3 scale per 16 channels, no second-level scale, applied after RoPE;
+ * "Inside DeepSeek V4.1 Flash", "Reconstructing the 890-byte cache budget":
+ * 288 B per 512-channel entry.
+ *   kv_bf16   [rows][512] bf16, post-RoPE rows to store.
+ *   dst_slot  [rows] int64: physical page * 64 + offset of each row; rows
+ *             whose slot is outside [0, n_pages * 64) are skipped.
+ *   kv_pool   [n_pages][18432] bytes.  Page layout: entry e's 256 code bytes
+ *             at e * 256 (channel 2i in the low nibble of byte i, nibble =
+ *             sign << 3 | magnitude code), then entry e's 32 scale bytes at
+ *             16384 + e * 32.
+ * Per 16-channel group: scale = E4M3 nearest to amax / 6 (ties to even,
+ * saturating at 448); element = E2M1 nearest to |x| / scale (ties to even,
+ * saturating at 6), sign copied from x; a zero scale gives zero magnitudes.
+ */
+int csa2_quantize_kv(const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_slot,
+                     uint8_t *kv_pool, int64_t n_pages, csa2_stream_t stream);
+
+/*
+ * Full mode of the hierarchical indexer.  Knowledge note, "Hierarchical
+ * Sparse Indexer" (Figure 5): the Full layer scores all visible positions,
+ * ranks blocks of 8 positions by their maximum score and keeps up to 2,048
+ * blocks as the candidate pool; it also keeps its own top-k.
+ *   q_idx      [B][T][HI][128] FP8 indexer queries.
+ *   w          [B][T][HI] float head weights.
+ *   kidx_pool  [n_pages][64][128] FP8 indexer keys (shared by later layers).
+ *   page_table [B][max_pages] int32 physical page of each logical page.
+ *   n_entries  [B] int32 visible entries per sequence (device).
+ *   max_n_entries  host upper bound of n_entries (sizes the grid).
+ * Score of entry j for token t (exact per-head dot rounded once to fp32,
+ * ReLU, then a binary32 fold in ascending head order):
+ *   s(j) = (..((+0 + fl(w_0 r_0)) + fl(w_1 r_1)) ..) + fl(w_{HI-1} r_{HI-1}),
+ *   r_h = max(fl(sum_c q[h][c] k_j[c]), +0).
+ * Outputs, per (b, t):
+ *   out_topk   [B][T][topk]: the topk best entries by (score desc, index asc),
+ *              written in ascending index order, -1 padded when n < topk.
+ *   out_pool   [B][T][pool_blocks]: the pool_blocks best blocks (block b =
+ *              entries [8b, 8b+8) clipped to n) by (max score desc, block
+ *              asc), ascending, -1 padded; out_pool_n [B][T] their count.
+ * Requires topk <= pool_blocks (then the top-k lies inside the pool),
+ * 1 <= HI <= 64, HI % 4 == 0, T <= 4, max_n_entries <= 262144.
+ */
+int csa2_index_full(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
+                    int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                    const int32_t *n_entries, int32_t max_n_entries, int32_t B, int32_t T,
+                    int32_t HI, int32_t topk, int32_t pool_blocks, int32_t *out_topk,
+                    int32_t *out_pool, int32_t *out_pool_n, void *ws, size_t ws_bytes,
+                    csa2_stream_t stream);
+
+/*
+ * Reindex mode.  Knowledge note, "Hierarchical Sparse Indexer": later
+ * Reindex layers score only the pool with their own indexer query and pick
+ * their own top-k inside it; the pool is query-specific.
+ *   pool [B][T][pool_blocks], pool_n [B][T]: as written by csa2_index_full.
+ * Same score, ranking and output format as csa2_index_full's out_topk,
+ * restricted to the positions of the first pool_n[b][t] pool blocks.
+ */
+int csa2_index_reindex(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
+                       int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                       const int32_t *n_entries, int32_t B, int32_t T, int32_t HI,
+                       const int32_t *pool, const int32_t *pool_n, int32_t pool_blocks,
+                       int32_t topk, int32_t *out_topk, void *ws, size_t ws_bytes,
+                       csa2_stream_t stream);
+
+/*
+ * Sparse attention over the selected FP4 entries merged with the FP8 window.
+ * "Inside DeepSeek V4.1 Flash", "CSA2: reuse memory and reuse selection
+ * independently": the main query attends to the selected global entries
+ * together with the local window; knowledge note, "FP4 main KV": entries are
+ * dequantized before attention, the window stays FP8.  Reuse mode passes the
+ * latest Full/Reindex top-k buffer as topk_idx.
+ *   q        [B][T][H][512] bf16 main queries.
+ *   topk_idx [B][T][topk] int32 entry positions, -1 = empty slot.
+ *   swa      [B][127 + T][512] FP8 window rows; token t uses rows t..t+127.
+ *   out      [B][T][H][512] float; out_lse [B][T][H] float (natural log) or NULL.
+ * For each (b, t, h) one softmax over J = {valid selected entries} U {window
+ * rows}: logits sm_scale * q . x_j, out = sum_j p_j x_j (each 512-channel
+ * row serves as key and value).  H must be 16, 32 or 64.
+ */
+int csa2_sparse_attn(const uint16_t *q, float sm_scale, const uint8_t *kv_pool, int64_t n_pages,
+                     const int32_t *page_table, int32_t max_pages, const int32_t *n_entries,
+                     const int32_t *topk_idx, int32_t topk, const uint8_t *swa, int32_t B,
+                     int32_t T, int32_t H, float *out, float *out_lse, void *ws, size_t ws_bytes,
+                     csa2_stream_t stream);
+
+/* Workspace bytes a call needs (op = enum csa2_op; `heads` = HI for the
+ * indexer calls, H for attention; `max_n_entries` unused for attention). */
+size_t csa2_workspace_bytes(int op, int32_t B, int32_t T, int32_t heads, int32_t max_n_entries,
+                            int32_t topk);
+
+/* Static description of a status code. */
+const char *csa2_status_str(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int csa2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -77,6 +77,8 @@ def lib():
         L.csa2o_e2m1_nearest.restype = u32
         L.csa2o_e2m1_nearest.argtypes = [dbl, dbl]
         L.csa2o_quantize_row.argtypes = [P, P, P]
+        L.csa2o_quantize_rows.argtypes = [P, i64, P, P]
+        L.csa2o_dequant_rows.argtypes = [P, P, i64, P]
         L.csa2o_quantize_kv.argtypes = [P, i64, P, P, i64]
         L.csa2o_dequant_entry.argtypes = [P, P, P]
         L.csa2o_index_scores.argtypes = [P, P, ctypes.c_int, P, i64, P]
@@ -133,9 +135,7 @@ def quantize_rows(x_bf16: np.ndarray):
     R = x.shape[0]
     codes = np.zeros((R, ENTRY_CODES), np.uint8)
     scales = np.zeros((R, NGROUPS), np.uint8)
-    L = lib()
-    for r in range(R):
-        L.csa2o_quantize_row(_p(x[r]), _p(codes[r]), _p(scales[r]))
+    lib().csa2o_quantize_rows(_p(x), R, _p(codes), _p(scales))
     return codes, scales
 
 
@@ -153,9 +153,7 @@ def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, ENTRY_CODES)
     scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, NGROUPS)
     out = np.zeros((codes.shape[0], D), np.float64)
-    L = lib()
-    for r in range(codes.shape[0]):
-        L.csa2o_dequant_entry(_p(codes[r]), _p(scales[r]), _p(out[r]))
+    lib().csa2o_dequant_rows(_p(codes), _p(scales), codes.shape[0], _p(out))
     return out
 
 
@@ -261,6 +259,20 @@ def selected_rows(kv_pool, page_table_row, idx_row):
     codes = np.stack([pool_entry(kv_pool, int(page_table_row[j // PAGE]), j % PAGE)[0] for j in sel])
     scales = np.stack([pool_entry(kv_pool, int(page_table_row[j // PAGE]), j % PAGE)[1] for j in sel])
     return dequant(codes, scales)
+
+
+def sparse_attn_from_rows(q_bf16_bt, sm_scale, sel_rows_bf16, swa_rows):
+    """Attention of one (b, t) given the bf16 source rows of its selected entries.
+
+    The oracle writes those rows to FP4 with its own cache-write statement,
+    dequantizes them, and attends over them plus the 128 FP8 window rows."""
+    if len(sel_rows_bf16):
+        codes, scales = quantize_rows(sel_rows_bf16)
+        rows = dequant(codes, scales)
+    else:
+        rows = np.zeros((0, D), np.float64)
+    allrows = np.concatenate([rows, e4m3_decode(swa_rows)], axis=0)
+    return attention(bf16_to_f64(q_bf16_bt), sm_scale, allrows)
 
 
 def sparse_attn(q_bf16, sm_scale, kv_pool, page_table, topk_idx, swa, batches=None, tokens=None):

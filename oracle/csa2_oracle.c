@@ -139,6 +139,13 @@ void csa2o_quantize_row(const uint16_t *x, uint8_t *codes, uint8_t *scales) {
   }
 }
 
+/* Many rows at once: the same per-row statement, rows in parallel. */
+void csa2o_quantize_rows(const uint16_t *x, int64_t rows, uint8_t *codes, uint8_t *scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    csa2o_quantize_row(x + r * D_MAIN, codes + r * ENTRY_CODES, scales + r * NGROUPS);
+}
+
 /* Paged cache write.  Reading of the page layout: a page holds 64 entries,
  * first their 64 x 256 B of codes, then their 64 x 32 B of scales; row r is
  * written to slot dst_slot[r] = page * 64 + offset.  Rows whose slot falls
@@ -163,6 +170,12 @@ void csa2o_dequant_entry(const uint8_t *codes, const uint8_t *scales, double *ou
     uint32_t nib = (ch & 1) ? (codes[ch / 2] >> 4) : (codes[ch / 2] & 0xF);
     out[ch] = csa2o_e2m1_decode(nib) * csa2o_e4m3_decode(scales[ch / GROUP]);
   }
+}
+
+void csa2o_dequant_rows(const uint8_t *codes, const uint8_t *scales, int64_t rows, double *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    csa2o_dequant_entry(codes + r * ENTRY_CODES, scales + r * NGROUPS, out + r * D_MAIN);
 }
 
 /* ---------------- O4: indexer score ----------------

@@ -1,0 +1,122 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_mxfp4_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+X = ctypes.c_void_p(0x1000)   # a non-null address; these calls fail before touching it
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(csa2.LIB_PATH):
+        from compressed_sparse_attention_mxfp4_amd import build
+        build.build()
+    return csa2.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(csa2_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
+               "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+    assert set(csa2.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings_and_version(L):
+    assert csa2.status_str(0) == "ok"
+    assert "workspace" in csa2.status_str(WORKSPACE)
+    assert csa2.status_str(12345) == "unknown status"
+    assert L.csa2_abi_version() == 100
+
+
+def test_workspace_sizes(L):
+    full = csa2.workspace_bytes(csa2.OP_INDEX_FULL, 4, 1, 64, 262144, 2048)
+    assert full >= 4 * 262144 * 4 + 4 * 32768 * 4
+    assert csa2.workspace_bytes(csa2.OP_INDEX_REINDEX, 8, 1, 64, 0, 2048) >= 8 * 16384 * 4
+    attn = csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, 4, 1, 64, 0, 2048)
+    n_splits = (2048 + 128 + 127) // 128
+    assert attn >= 4 * 4 * n_splits * 16 * 512 * 4
+    assert csa2.workspace_bytes(99, 1, 1, 1, 1, 1) == 0
+    assert csa2.workspace_bytes(csa2.OP_INDEX_FULL, 0, 1, 64, 100, 8) == 0
+
+
+def _full(L, q=X, w=X, k=X, n_pages=1, pt=X, max_pages=1, ne=X, max_n=64, B=1, T=1, HI=4, topk=8,
+          pool_blocks=16, ot=X, op=X, opn=X, ws=X, ws_bytes=1 << 30):
+    return L.csa2_index_full(q, w, k, n_pages, pt, max_pages, ne, max_n, B, T, HI, topk, pool_blocks,
+                             ot, op, opn, ws, ws_bytes, None)
+
+
+def test_index_full_argument_errors(L):
+    assert _full(L, q=None) == INVALID
+    assert _full(L, ot=None) == INVALID
+    assert _full(L, B=0) == INVALID
+    assert _full(L, topk=0) == INVALID
+    assert _full(L, topk=2049, pool_blocks=2048) == INVALID
+    assert _full(L, pool_blocks=4096) == INVALID
+    assert _full(L, HI=6) == UNSUPPORTED
+    assert _full(L, HI=68) == UNSUPPORTED
+    assert _full(L, T=3) == UNSUPPORTED
+    assert _full(L, topk=32, pool_blocks=16) == UNSUPPORTED
+    assert _full(L, max_n=262145) == UNSUPPORTED
+    assert _full(L, max_n=0) == INVALID
+    assert _full(L, ws=None) == WORKSPACE
+    assert _full(L, ws_bytes=16) == WORKSPACE
+
+
+def _reindex(L, q=X, pool=X, P=16, topk=8, HI=4, T=1, ws=X, ws_bytes=1 << 30):
+    return L.csa2_index_reindex(q, X, X, 1, X, 1, X, 1, T, HI, pool, X, P, topk, X, ws, ws_bytes, None)
+
+
+def test_index_reindex_argument_errors(L):
+    assert _reindex(L, q=None) == INVALID
+    assert _reindex(L, pool=None) == INVALID
+    assert _reindex(L, topk=17) == UNSUPPORTED
+    assert _reindex(L, HI=10) == UNSUPPORTED
+    assert _reindex(L, ws_bytes=0) == WORKSPACE
+
+
+def _attn(L, q=X, sm=1.0, topk=8, B=1, T=1, H=16, out=X, ws=X, ws_bytes=1 << 30):
+    return L.csa2_sparse_attn(q, sm, X, 1, X, 1, X, X, topk, X, B, T, H, out, None, ws, ws_bytes, None)
+
+
+def test_sparse_attn_argument_errors(L):
+    assert _attn(L, q=None) == INVALID
+    assert _attn(L, out=None) == INVALID
+    assert _attn(L, topk=0) == INVALID
+    assert _attn(L, topk=4096) == INVALID
+    assert _attn(L, H=48) == UNSUPPORTED
+    assert _attn(L, T=5) == UNSUPPORTED
+    assert _attn(L, sm=0.0) == INVALID
+    assert _attn(L, sm=float("nan")) == INVALID
+    assert _attn(L, ws=None) == WORKSPACE
+
+
+def test_quantize_argument_errors(L):
+    assert L.csa2_quantize_kv(None, 4, X, X, 1, None) == INVALID
+    assert L.csa2_quantize_kv(X, -1, X, X, 1, None) == INVALID
+    assert L.csa2_quantize_kv(X, 0, X, X, 1, None) == OK      # nothing to do, nothing launched
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        csa2._ptr(torch.zeros(4), torch.float32, "x")

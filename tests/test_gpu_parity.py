@@ -1,0 +1,301 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+FP4 codes, scales, top-k and pool index sets must match bit for bit; attention
+outputs within max-abs 2e-3 of the binary64 oracle given the same indices.
+Inputs come from the seeded generators only; the oracle never sees a value
+the HIP path produced except where noted (index sets fed to both sides after
+they have been shown equal).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_mxfp4_amd as csa2
+from compressed_sparse_attention_mxfp4_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bf16_dev(u16):
+    return dev(u16.view(np.int16), torch.bfloat16) if u16.dtype == np.uint16 else dev(u16)
+
+
+# ------------------------------------------------------------------ a1
+def gpu_quantize(x_u16, slots, n_pages, fill=0xAA):
+    pool = torch.full((n_pages, csa2.PAGE_BYTES), fill, dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(bf16_dev(x_u16), dev(slots.astype(np.int64)), pool)
+    return host(pool)
+
+
+def special_rows():
+    """Hand-picked groups: every E2M1 tie, scale ties, subnormal and zero scales, saturation, -0."""
+    vals = [
+        [6.0, -3.0, 1.0, 0.5, 0.25, 0.75, -0.0, 0.0, 2.5, 5.0, 4.0, 1.25, 1.75, 3.5, 0.30078125, 0.125],
+        [7.0, 1.0] + [0.0] * 14,
+        [6.375, -6.375] + [0.0] * 14,
+        [0.01171875, 0.0029296875] + [0.0] * 14,
+        [-0.005859375, 0.005859375] + [0.0] * 14,
+        [3072.0, 1000.0] + [0.0] * 14,
+        [-0.0] * 16,
+        [1e-30, -1e-30] + [0.0] * 14,
+        [60000.0, -1.0] + [0.0] * 14,
+    ]
+    rows = []
+    for v in vals:
+        row = np.tile(np.array(v, np.float32), 32)
+        rows.append(row)
+    return synth.bf16_bits(torch.tensor(np.stack(rows)))
+
+
+def test_quantize_parity_mixed(oracle):
+    say("quantize mixed 6000 rows")
+    x = np.concatenate([
+        synth.kv_rows(2000, 1),
+        synth.kv_rows(2000, 2, outlier_frac=0.05),
+        synth.kv_rows(2000, 3, channel_log10_range=(-2.0, 2.0)),
+        special_rows(),
+    ])
+    n_pages = (len(x) + 63) // 64 + 3
+    rng = np.random.default_rng(0)
+    slots = rng.permutation(n_pages * 64)[:len(x)].astype(np.int64)
+    slots[5] = -1
+    slots[6] = n_pages * 64 + 3
+    got = gpu_quantize(x, slots, n_pages)
+    ref = np.full((n_pages, oracle.PAGE_BYTES), 0xAA, np.uint8)
+    oracle.quantize_kv(x, slots, ref)
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_parity_full_cache_write(oracle):
+    say("quantize 1,048,576 rows, log-uniform channel scales, permuted pages")
+    x, slots, n_pages = synth.cache_write_rows()
+    got = gpu_quantize(x, slots, n_pages, fill=0)
+    codes, scales = oracle.quantize_rows(x)
+    page, off = slots // 64, slots % 64
+    gc = got[:, :64 * 256].reshape(n_pages, 64, 256)[page, off]
+    gs = got[:, 64 * 256:].reshape(n_pages, 64, 32)[page, off]
+    assert np.array_equal(gc, codes)
+    assert np.array_equal(gs, scales)
+
+
+# ------------------------------------------------------------------ a2..a6
+def gpu_index_full(wl, layer, topk=None, pool_blocks=None):
+    topk = topk or wl.topk
+    pool_blocks = pool_blocks or wl.pool_blocks
+    return csa2.index_full(dev(layer.q_idx), dev(layer.w), dev(wl.kidx_pool),
+                           dev(wl.paging.page_table), dev(wl.n_entries), wl.max_n, topk, pool_blocks)
+
+
+def oracle_index_full(oracle, wl, layer, topk=None, pool_blocks=None):
+    return oracle.index_full(layer.q_idx, layer.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries,
+                             topk or wl.topk, pool_blocks or wl.pool_blocks)
+
+
+def assert_index_equal(got, ref):
+    for g, r in zip(got, ref):
+        assert np.array_equal(host(g), r)
+
+
+def small_workload(n_entries, T=1, HI=8, H=16, topk=64, seed=0, key_codes=None, q_codes=None):
+    pg = synth.paging(n_entries, seed=seed + 3)
+    kidx = np.zeros((pg.n_pages, 64, 128), np.uint8)
+    total = int(np.sum(n_entries))
+    keys = synth.fp8_normal((total, 128), seed + 9) if key_codes is None else key_codes
+    kidx.reshape(-1, 128)[pg.all_slots()] = keys
+    L = synth.layer_inputs("full", len(n_entries), T, HI, H, seed)
+    if q_codes is not None:
+        L.q_idx = q_codes
+    kv = synth.kv_rows(total, seed + 12)
+    return synth.Workload("small", len(n_entries), T, H, HI, topk, 2048, 1 / math.sqrt(512),
+                          np.asarray(n_entries, np.int32), pg, kidx, kv, [L])
+
+
+def test_index_full_8k_b1(oracle):
+    say("index full 8K ctx B=1 HI=4 k=256")
+    wl = synth.workload("full_8k_b1")
+    got = gpu_index_full(wl, wl.layers[0])
+    assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
+
+
+@pytest.mark.parametrize("T,HI,topk", [(1, 8, 64), (2, 16, 512), (4, 4, 2048), (2, 64, 2048)])
+def test_index_full_ragged(oracle, T, HI, topk):
+    n = [1, 7, 8, 9, 100, 1023, 1025, 2047, 2048, 16389, 40000]
+    say(f"index full ragged n={n} T={T} HI={HI} k={topk}")
+    wl = small_workload(n, T=T, HI=HI, topk=topk, seed=T * 100 + HI)
+    got = gpu_index_full(wl, wl.layers[0])
+    assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
+
+
+def test_index_full_ties(oracle):
+    say("index full with tied scores (repeated keys)")
+    n = [5000, 700]
+    base = synth.fp8_normal((7, 128), 77)
+    rng = np.random.default_rng(3)
+    keys = base[rng.integers(0, 7, sum(n))]
+    wl = small_workload(n, T=2, HI=8, topk=256, seed=5, key_codes=keys)
+    got = gpu_index_full(wl, wl.layers[0])
+    assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
+
+
+def test_index_full_wide_exponent_range(oracle):
+    say("index full with every finite E4M3 code (general exact path)")
+    n = [3000, 999]
+    rng = np.random.default_rng(4)
+    finite = np.array([c for c in range(256) if c not in (127, 255)], np.uint8)
+    keys = rng.choice(finite, (sum(n), 128))
+    q = rng.choice(finite, (2, 1, 16, 128))
+    wl = small_workload(n, T=1, HI=16, topk=128, seed=6, key_codes=keys, q_codes=q)
+    got = gpu_index_full(wl, wl.layers[0])
+    assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
+
+
+def test_index_full_1m_b4(oracle):
+    say("index full 1M ctx B=4 HI=64 k=2048 (full size)")
+    wl = synth.workload("full_1m_b4")
+    got = gpu_index_full(wl, wl.layers[0])
+    ref = oracle_index_full(oracle, wl, wl.layers[0])
+    assert_index_equal(got, ref)
+    # the pool bounds: <= 2,048 blocks of 8 positions, and the top-k lies inside it
+    tk, pool_, pool_n = ref
+    assert (pool_n == 2048).all()
+    for b in range(wl.B):
+        pos = oracle.pool_positions(pool_[b, 0], int(pool_n[b, 0]), int(wl.n_entries[b]))
+        assert len(pos) <= 16384 and set(tk[b, 0]) <= set(pos)
+
+
+def test_index_deterministic():
+    say("index full twice, identical")
+    wl = small_workload([30000, 12345], T=2, HI=32, topk=1024, seed=9)
+    a = [host(x) for x in gpu_index_full(wl, wl.layers[0])]
+    b = [host(x) for x in gpu_index_full(wl, wl.layers[0])]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_group_128k_b8_full_reindex_reuse(oracle):
+    say("group 128K ctx B=8: Full -> Reindex -> Reuse")
+    wl = synth.workload("group_128k_b8")
+    full, reidx, reuse = wl.layers
+    tk, pool_, pool_n = gpu_index_full(wl, full)
+    ref_tk, ref_pool, ref_pool_n = oracle_index_full(oracle, wl, full)
+    assert np.array_equal(host(tk), ref_tk)
+    assert np.array_equal(host(pool_), ref_pool)
+    assert np.array_equal(host(pool_n), ref_pool_n)
+    rtk = csa2.index_reindex(dev(reidx.q_idx), dev(reidx.w), dev(wl.kidx_pool), dev(wl.paging.page_table),
+                             dev(wl.n_entries), pool_, pool_n, wl.topk)
+    ref_rtk = oracle.index_reindex(reidx.q_idx, reidx.w, wl.kidx_pool, wl.paging.page_table,
+                                   wl.n_entries, ref_pool, ref_pool_n, wl.topk)
+    assert np.array_equal(host(rtk), ref_rtk)
+    # Reindex stays inside the pool; Reuse takes the Reindex buffer unchanged
+    for b in range(wl.B):
+        pos = set(oracle.pool_positions(ref_pool[b, 0], int(ref_pool_n[b, 0]), int(wl.n_entries[b])))
+        assert set(ref_rtk[b, 0]) <= pos
+    kv_pool = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(bf16_dev(wl.kv_source), dev(wl.paging.all_slots()), kv_pool)
+    before = host(rtk).copy()
+    out = csa2.sparse_attn(bf16_dev(reuse.q), wl.sm_scale, kv_pool, dev(wl.paging.page_table),
+                           dev(wl.n_entries), rtk, dev(reuse.swa))
+    assert np.array_equal(host(rtk), before)
+    check_attention(oracle, wl, reuse, ref_rtk, host(out), batches=[0, 3, 7])
+
+
+# ------------------------------------------------------------------ a7
+def check_attention(oracle, wl, layer, idx, out, batches=None, tokens=None, lse=None):
+    offs = np.concatenate([[0], np.cumsum(wl.n_entries)[:-1]])
+    worst = 0.0
+    for b in (range(wl.B) if batches is None else batches):
+        for t in (range(wl.T) if tokens is None else tokens):
+            sel = [int(j) for j in idx[b, t] if j >= 0]
+            rows = wl.kv_source[offs[b] + np.array(sel, dtype=np.int64)] if sel else np.zeros((0, 512), np.uint16)
+            ref, ref_lse = oracle.sparse_attn_from_rows(layer.q[b, t], wl.sm_scale, rows,
+                                                        layer.swa[b, t:t + 128])
+            err = np.abs(out[b, t] - ref).max()
+            worst = max(worst, err)
+            assert err <= ATOL, (b, t, err)
+            if lse is not None:
+                assert np.abs(lse[b, t] - ref_lse).max() <= 1e-3
+    say(f"attention max-abs error {worst:.3g}")
+    return worst
+
+
+def gpu_attention(wl, layer, idx, with_lse=False):
+    kv_pool = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(bf16_dev(wl.kv_source), dev(wl.paging.all_slots()), kv_pool)
+    lse = torch.empty((wl.B, wl.T, wl.H), dtype=torch.float32, device="cuda") if with_lse else None
+    out = csa2.sparse_attn(bf16_dev(layer.q), wl.sm_scale, kv_pool, dev(wl.paging.page_table),
+                           dev(wl.n_entries), dev(idx) if isinstance(idx, np.ndarray) else idx,
+                           dev(layer.swa), out_lse=lse)
+    return host(out), (host(lse) if with_lse else None)
+
+
+def test_attention_8k_b1(oracle):
+    say("attention 8K ctx B=1 H=16 k=256 (indices from the Full layer)")
+    wl = synth.workload("full_8k_b1")
+    L = wl.layers[0]
+    ref_tk, _, _ = oracle_index_full(oracle, wl, L)
+    out, lse = gpu_attention(wl, L, ref_tk, with_lse=True)
+    check_attention(oracle, wl, L, ref_tk, out, lse=lse)
+
+
+@pytest.mark.parametrize("H,T,k,frac", [(16, 1, 256, 1.0), (32, 2, 512, 0.7), (64, 1, 2048, 0.5),
+                                        (64, 2, 2048, 1.0), (16, 4, 8, 1.0), (64, 1, 100, 0.0)])
+def test_attention_random_index_sets(oracle, H, T, k, frac):
+    say(f"attention random sets H={H} T={T} k={k} valid={frac}")
+    n = [5000, 300, 9999]
+    wl = small_workload(n, T=T, H=H, topk=k, seed=H + T + k)
+    L = synth.layer_inputs("reuse", wl.B, T, 0, H, 17, q_std=1.0)
+    idx = synth.random_topk(wl.B, T, k, wl.n_entries, seed=k, frac_valid=frac)
+    out, lse = gpu_attention(wl, L, idx, with_lse=True)
+    check_attention(oracle, wl, L, idx, out, lse=lse)
+
+
+def test_attention_outlier_heavy(oracle):
+    say("attention with 5% +-8 outliers and sharp logits")
+    n = [4096]
+    wl = small_workload(n, T=1, H=64, topk=2048, seed=31)
+    wl.kv_source = synth.kv_rows(4096, 32, outlier_frac=0.05)
+    wl.sm_scale = 1.0 / 8.0
+    L = synth.layer_inputs("reuse", 1, 1, 0, 64, 33, q_std=1.0)
+    idx = synth.random_topk(1, 1, 2048, wl.n_entries, seed=34)
+    out, _ = gpu_attention(wl, L, idx)
+    check_attention(oracle, wl, L, idx, out)
+
+
+def test_full_1m_b4_attention(oracle):
+    say("attention 1M ctx B=4 H=64 k=2048 (Full-layer indices, 1% outliers)")
+    wl = synth.workload("full_1m_b4")
+    L = wl.layers[0]
+    ref_tk, _, _ = oracle_index_full(oracle, wl, L)
+    out, lse = gpu_attention(wl, L, ref_tk, with_lse=True)
+    check_attention(oracle, wl, L, ref_tk, out, lse=lse)
