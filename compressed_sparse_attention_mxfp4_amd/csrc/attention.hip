@@ -47,7 +47,7 @@ __device__ __forceinline__ void fp4x8_to_f16(uint32_t x, _Float16 s256, half_t* 
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     // perm selector bytes [0x0C, k, 0x0C, 4+k]: [0, lo_n.byte k, 0, hi_n.byte k]
-    const uint32_t pick = 0x0C000C0Cu | ((uint32_t)k << 8) | ((uint32_t)(4 + k) << 24);
+    const uint32_t pick = 0x000C000Cu | ((uint32_t)k << 8) | ((uint32_t)(4 + k) << 24);
     const uint32_t sel = __builtin_amdgcn_perm(hi_n, lo_n, pick);
     uint32_t h2 = __builtin_amdgcn_perm(kE2M1HiHi, kE2M1HiLo, sel);
     h2 |= __builtin_amdgcn_perm(sgn1, sgn0, pick);
