@@ -32,8 +32,12 @@ OP_INDEX_FULL, OP_INDEX_REINDEX, OP_SPARSE_ATTN = 1, 2, 3
 
 EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-    "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version",
+    "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
 )
+
+# kernel ids for csa2_time_kernel
+K_QUANTIZE, K_SCORE_FULL, K_SELECT_FULL, K_SCORE_REINDEX, K_SELECT_REINDEX = 1, 2, 3, 4, 5
+K_ATTN_SPLIT, K_ATTN_COMBINE = 6, 7
 
 
 class Csa2Error(RuntimeError):
@@ -50,6 +54,10 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime (soname libamdhip64.so.7); importing it
+    # first makes libcsa2.so bind to that same runtime, so torch's streams,
+    # events and allocations are valid in the library.
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m compressed_sparse_attention_mxfp4_amd.build`")
@@ -67,6 +75,8 @@ def load(path: str = LIB_PATH):
     L.csa2_status_str.argtypes = [ctypes.c_int]
     L.csa2_status_str.restype = ctypes.c_char_p
     L.csa2_abi_version.restype = ctypes.c_int
+    L.csa2_time_kernel.argtypes = [ctypes.c_int, P, P]
+    L.csa2_time_kernel.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L

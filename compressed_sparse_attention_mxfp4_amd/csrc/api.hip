@@ -34,3 +34,19 @@ extern "C" const char* csa2_status_str(int status) {
 }
 
 extern "C" int csa2_abi_version(void) { return 100; }
+
+namespace csa2 {
+KernelEvents& kernel_events(int kernel) {
+  static KernelEvents table[CSA2_K_COUNT];
+  return table[(kernel > 0 && kernel < CSA2_K_COUNT) ? kernel : 0];
+}
+}  // namespace csa2
+
+extern "C" int csa2_time_kernel(int kernel, void* start_event, void* stop_event) {
+  if (kernel <= 0 || kernel >= CSA2_K_COUNT) return CSA2_ERR_INVALID_ARG;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return CSA2_ERR_INVALID_ARG;
+  csa2::KernelEvents& e = csa2::kernel_events(kernel);
+  e.start = reinterpret_cast<hipEvent_t>(start_event);
+  e.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return CSA2_OK;
+}

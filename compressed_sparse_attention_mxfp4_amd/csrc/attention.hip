@@ -365,8 +365,8 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   const size_t units = (size_t)B * T * (H / 16) * aa.n_splits;
   aa.part_o = reinterpret_cast<float*>(ws);
   aa.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(units * 16 * csa2::kD * 4));
-  hipLaunchKernelGGL(csa2::attn_split_kernel, dim3(aa.n_splits, H / 16, B * T),
-                     dim3(csa2::kAttnThreads), 0, (hipStream_t)stream, aa);
+  CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel, dim3(aa.n_splits, H / 16, B * T),
+              dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::CombineArgs ca{};
   ca.part_o = aa.part_o;
@@ -375,6 +375,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   ca.n_splits = aa.n_splits;
   ca.out = out;
   ca.out_lse = out_lse;
-  hipLaunchKernelGGL(csa2::attn_combine_kernel, dim3(B * T * H), dim3(256), 0, (hipStream_t)stream, ca);
+  CSA2_LAUNCH(CSA2_K_ATTN_COMBINE, csa2::attn_combine_kernel, dim3(B * T * H), dim3(256),
+              (hipStream_t)stream, ca);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

@@ -47,4 +47,22 @@ __device__ __forceinline__ int64_t phys_page(const int32_t* __restrict__ page_ta
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Events recorded around launches of each kernel (csa2_time_kernel).
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+KernelEvents& kernel_events(int kernel);
+
 }  // namespace csa2
+
+#include <hip/hip_ext.h>
+
+// Launch `kern` on `stream`, bracketed by the events registered for `kid`.
+#define CSA2_LAUNCH(kid, kern, grid, block, stream, ...)                                   \
+  do {                                                                                      \
+    const ::csa2::KernelEvents& ev_ = ::csa2::kernel_events(kid);                          \
+    if (ev_.start && ev_.stop)                                                              \
+      hipExtLaunchKernelGGL(kern, grid, block, 0, stream, ev_.start, ev_.stop, 0, __VA_ARGS__); \
+    else                                                                                    \
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, __VA_ARGS__);                        \
+  } while (0)

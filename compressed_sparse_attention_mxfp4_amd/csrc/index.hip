@@ -613,8 +613,8 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   sa.out_bm = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                        align256((size_t)B * T * max_n_entries * 4));
   const int gx = (max_n_entries + csa2::kEntriesPerWG - 1) / csa2::kEntriesPerWG;
-  hipLaunchKernelGGL(csa2::score_kernel<false>, dim3(gx, B), dim3(csa2::kScoreThreads), 0,
-                     (hipStream_t)stream, sa);
+  CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx, B), dim3(csa2::kScoreThreads),
+              (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -628,8 +628,8 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   se.out_topk = out_topk;
   se.out_pool = out_pool;
   se.out_pool_n = out_pool_n;
-  hipLaunchKernelGGL(csa2::select_kernel<true>, dim3(B * T), dim3(csa2::kSelThreads), 0,
-                     (hipStream_t)stream, se);
+  CSA2_LAUNCH(CSA2_K_SELECT_FULL, csa2::select_kernel<true>, dim3(B * T), dim3(csa2::kSelThreads),
+              (hipStream_t)stream, se);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }
 
@@ -662,8 +662,8 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   sa.pool_blocks = pool_blocks;
   sa.out_s = reinterpret_cast<float*>(ws);
   const int gx = (pool_blocks * csa2::kBlock + csa2::kEntriesPerWG - 1) / csa2::kEntriesPerWG;
-  hipLaunchKernelGGL(csa2::score_kernel<true>, dim3(gx, B * T), dim3(csa2::kScoreThreads), 0,
-                     (hipStream_t)stream, sa);
+  CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx, B * T),
+              dim3(csa2::kScoreThreads), (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -676,7 +676,7 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   se.pool_in = pool;
   se.pool_n_in = pool_n;
   se.out_topk = out_topk;
-  hipLaunchKernelGGL(csa2::select_kernel<false>, dim3(B * T), dim3(csa2::kSelThreads), 0,
-                     (hipStream_t)stream, se);
+  CSA2_LAUNCH(CSA2_K_SELECT_REINDEX, csa2::select_kernel<false>, dim3(B * T),
+              dim3(csa2::kSelThreads), (hipStream_t)stream, se);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

@@ -110,7 +110,7 @@ extern "C" int csa2_quantize_kv(const uint16_t* kv_bf16, int64_t rows, const int
   const int64_t threads = rows * 32;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(csa2::quantize_kv_kernel, dim3((uint32_t)blocks), dim3(256), 0,
-                     (hipStream_t)stream, kv_bf16, rows, dst_slot, kv_pool, n_pages);
+  CSA2_LAUNCH(CSA2_K_QUANTIZE, csa2::quantize_kv_kernel, dim3((uint32_t)blocks), dim3(256),
+              (hipStream_t)stream, kv_bf16, rows, dst_slot, kv_pool, n_pages);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

@@ -32,7 +32,7 @@
  *  - Formats: bf16 = IEEE bfloat16 bits; FP8 = OCP E4M3 (E4M3FN, max 448,
  *    codes 0x7F/0xFF are NaN); FP4 = OCP E2M1 nibbles.
  *  - Preconditions not checked on the device: inputs finite, no FP8 NaN
- *    codes, indexer weights w finite with |w| = 0 or 2^-100 <= |w| <= 2^100,
+ *    codes, indexer weights w finite with |w| = 0 or 2^-100 <= |w| <= 2^90,
  *    top-k indices distinct.  Page ids outside [0, n_pages) and positions
  *    outside [0, n_entries[b]) are treated as not visible (never read).
  */
@@ -119,7 +119,7 @@ int csa2_quantize_kv(const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_s
  *              entries [8b, 8b+8) clipped to n) by (max score desc, block
  *              asc), ascending, -1 padded; out_pool_n [B][T] their count.
  * Requires topk <= pool_blocks (then the top-k lies inside the pool),
- * 1 <= HI <= 64, HI % 4 == 0, T <= 4, max_n_entries <= 262144.
+ * 4 <= HI <= 64 with HI % 4 == 0, T in {1, 2, 4}, max_n_entries <= 262144.
  */
 int csa2_index_full(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
                     int64_t n_pages, const int32_t *page_table, int32_t max_pages,
@@ -163,6 +163,28 @@ int csa2_sparse_attn(const uint16_t *q, float sm_scale, const uint8_t *kv_pool, 
                      const int32_t *topk_idx, int32_t topk, const uint8_t *swa, int32_t B,
                      int32_t T, int32_t H, float *out, float *out_lse, void *ws, size_t ws_bytes,
                      csa2_stream_t stream);
+
+/* Kernels the library launches, for csa2_time_kernel. */
+enum csa2_kernel {
+  CSA2_K_QUANTIZE = 1,        /* cache write */
+  CSA2_K_SCORE_FULL = 2,      /* Full-mode score scan */
+  CSA2_K_SELECT_FULL = 3,     /* Full-mode pool + top-k selection */
+  CSA2_K_SCORE_REINDEX = 4,   /* Reindex-mode score scan over the pool */
+  CSA2_K_SELECT_REINDEX = 5,  /* Reindex-mode top-k selection */
+  CSA2_K_ATTN_SPLIT = 6,      /* attention over row splits */
+  CSA2_K_ATTN_COMBINE = 7,    /* merge of the splits */
+  CSA2_K_COUNT = 8
+};
+
+/*
+ * Measurement aid (not part of the method): from now on, record
+ * `start_event` immediately before and `stop_event` immediately after each
+ * launch of `kernel` on its launch stream (both are hipEvent_t created by
+ * the caller; NULL, NULL turns recording off).  Lets a benchmark time one
+ * kernel of a multi-kernel call with events on the right stream.  Process-
+ * wide setting; not thread-safe.  Returns CSA2_OK or CSA2_ERR_INVALID_ARG.
+ */
+int csa2_time_kernel(int kernel, void *start_event, void *stop_event);
 
 /* Workspace bytes a call needs (op = enum csa2_op; `heads` = HI for the
  * indexer calls, H for attention; `max_n_entries` unused for attention). */
