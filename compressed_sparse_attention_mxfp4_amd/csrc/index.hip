@@ -31,8 +31,7 @@ namespace csa2 {
 
 constexpr int kScoreThreads = 512;        // 8 waves
 constexpr int kWaves = kScoreThreads / 64;
-constexpr int kChunk = 32;                // entries folded together per wave
-constexpr int kEntriesPerWG = 1024;
+constexpr int kChunk = 32;                // entries folded together per wave (2 sub-tiles)
 constexpr int kMaxRT = 4;                 // row tiles of 16 heads (HI <= 64)
 constexpr int kFoldStride = kMaxRT * 16 + 4;
 
@@ -56,62 +55,66 @@ __device__ void build_lut(uint32_t* lut) {
   for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) lut[i] = limb_entry((uint32_t)(i >> 6));
 }
 
-struct Limbs {
-  v4i lo, mid, top;
-  uint32_t top_any;
-};
+__device__ __forceinline__ uint32_t lut_read(const uint8_t* lut_bytes, uint32_t lane4, uint32_t x, int k) {
+  const uint32_t addr = __builtin_amdgcn_perm(x, lane4, 0x0C0C0000u | ((4u + k) << 8));
+  return *reinterpret_cast<const uint32_t*>(lut_bytes + addr);
+}
 
-// 16 FP8 codes (one v4u) -> their three limb planes (16 int8 each).
-__device__ __forceinline__ void to_limbs(const uint8_t* lut_bytes, uint32_t lane4, v4u codes,
-                                         Limbs& out) {
-  uint32_t lo[4], mid[4], top[4];
-  uint32_t any = 0;
+// 16 FP8 codes -> lo and mid limb planes; `any` collects the top limbs
+// (nonzero iff some |value| >= 32).
+__device__ __forceinline__ void limbs2(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
+                                      v4i& mid, uint32_t& any) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    uint32_t x = codes[d];
-    uint32_t L[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t addr = __builtin_amdgcn_perm(x, lane4, 0x0C0C0000u | ((4u + k) << 8));
-      L[k] = *reinterpret_cast<const uint32_t*>(lut_bytes + addr);
-    }
-    uint32_t t01 = __builtin_amdgcn_perm(L[1], L[0], 0x05010400u);
-    uint32_t t23 = __builtin_amdgcn_perm(L[3], L[2], 0x05010400u);
-    lo[d] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-    mid[d] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
-    uint32_t u01 = __builtin_amdgcn_perm(L[1], L[0], 0x0C0C0602u);
-    uint32_t u23 = __builtin_amdgcn_perm(L[3], L[2], 0x0C0C0602u);
-    top[d] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
-    any |= top[d];
+    const uint32_t x = codes[d];
+    const uint32_t L0 = lut_read(lut_bytes, lane4, x, 0), L1 = lut_read(lut_bytes, lane4, x, 1);
+    const uint32_t L2 = lut_read(lut_bytes, lane4, x, 2), L3 = lut_read(lut_bytes, lane4, x, 3);
+    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x05010400u);  // [lo0 lo1 mid0 mid1]
+    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x05010400u);
+    lo[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
+    any |= L0 | L1 | L2 | L3;
   }
-  out.lo = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
-  out.mid = v4i{(int)mid[0], (int)mid[1], (int)mid[2], (int)mid[3]};
-  out.top = v4i{(int)top[0], (int)top[1], (int)top[2], (int)top[3]};
-  out.top_any = any;
+}
+
+// 16 FP8 codes -> all three limb planes (general path).
+__device__ __forceinline__ void limbs3(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
+                                      v4i& mid, v4i& top) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = codes[d];
+    const uint32_t L0 = lut_read(lut_bytes, lane4, x, 0), L1 = lut_read(lut_bytes, lane4, x, 1);
+    const uint32_t L2 = lut_read(lut_bytes, lane4, x, 2), L3 = lut_read(lut_bytes, lane4, x, 3);
+    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x05010400u);
+    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x05010400u);
+    lo[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
+    const uint32_t u01 = __builtin_amdgcn_perm(L1, L0, 0x0C0C0602u);
+    const uint32_t u23 = __builtin_amdgcn_perm(L3, L2, 0x0C0C0602u);
+    top[d] = (int)__builtin_amdgcn_perm(u23, u01, 0x05040100u);
+  }
 }
 
 __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Sum over 128 channels of |M| for the lane's 32 channels (both K-slices).
-__device__ __forceinline__ uint32_t abs_limb_sum(const Limbs& s0, const Limbs& s1) {
+__device__ __forceinline__ uint32_t abs8_sum(v4i v, uint32_t w) {
   uint32_t acc = 0;
-  const v4i* planes[6] = {&s0.lo, &s0.mid, &s0.top, &s1.lo, &s1.mid, &s1.top};
 #pragma unroll
-  for (int p = 0; p < 6; ++p) {
-    const uint32_t w = (p % 3 == 0) ? 1u : (p % 3 == 1) ? 128u : 16384u;
+  for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t x = (uint32_t)(*planes[p])[d];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        int v = (int)(int8_t)((x >> (8 * k)) & 0xFFu);
-        acc += (uint32_t)(v < 0 ? -v : v) * w;
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int b = (int)(int8_t)(((uint32_t)v[d] >> (8 * k)) & 0xFFu);
+      acc += (uint32_t)(b < 0 ? -b : b) * w;
     }
-  }
   return acc;
+}
+
+// Row stride of the block-maxima buffer: ceil(max_n / 8) rounded up to a
+// multiple of 4 so every row starts 16-byte aligned.
+__host__ __device__ __forceinline__ int bm_stride(int max_n) {
+  return ((max_n + kBlock - 1) / kBlock + 3) & ~3;
 }
 
 struct ScoreArgs {
@@ -130,16 +133,115 @@ struct ScoreArgs {
   int pool_blocks;
   float* out_s;           // full: [B][T][max_n]; pool: [B][T][pool_blocks*8]
   float* out_bm;          // full: [B][T][ceil(max_n/8)]
+  int rows;               // full: B; pool: B*T
+  int chunks_per_row;     // full: ceil(max_n/32); pool: pool_blocks/4
+  int chunks_per_wg;
 };
 
-// POOL = false: Full scan; blockIdx.y = b, the 8 waves split T tokens x
-//               entry slices of this workgroup's 1,024 positions.
-// POOL = true : Reindex scan; blockIdx.y = b * T + t, positions are the
-//               entries of the pool blocks of (b, t).
+// Keys of one 32-entry chunk for one wave: lane (g, col) holds entry
+// chunk + 16*st + col, channels [16g, 16g+16) and [64+16g, 64+16g+16).
+struct ChunkKeys {
+  v4u k[2][2];
+};
+
+// Row context of a wave: sequence b, token t, visible entries n, pool row.
+struct RowCtx {
+  int row = -1;
+  int b = 0, t = 0, n = 0, n_pos = 0;
+  const int32_t* pool_row = nullptr;
+};
+
+template <bool POOL>
+__device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full, RowCtx& r) {
+  r.row = row;
+  if (POOL) {
+    r.b = row / a.T;
+    r.t = row % a.T;
+  } else {
+    r.b = row;
+    r.t = t_full;
+  }
+  int n = a.n_entries[r.b];
+  n = min(n, a.max_n);
+  n = max(0, min(n, a.max_pages * kPage));
+  r.n = n;
+  if (POOL) {
+    r.pool_row = a.pool + (int64_t)row * a.pool_blocks;
+    const int pn = max(0, min(a.pool_n[row], a.pool_blocks));
+    r.n_pos = pn * kBlock;
+  } else {
+    r.n_pos = n;
+  }
+}
+
+// Position p of the row's list -> entry index j, or -1 when not visible.
+template <bool POOL>
+__device__ __forceinline__ int entry_of(const ScoreArgs& a, const RowCtx& r, int p) {
+  if (p >= r.n_pos) return -1;
+  int j = p;
+  if (POOL) {
+    const int blk = r.pool_row[p >> 3];
+    j = (blk >= 0 && blk < (r.n + kBlock - 1) / kBlock) ? blk * kBlock + (p & 7) : r.n;
+  }
+  if (j >= r.n) return -1;
+  return phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6) >= 0 ? j : -1;
+}
+
+template <bool POOL>
+__device__ __forceinline__ void load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g,
+                                           int col, ChunkKeys& ck) {
+  if (!POOL) {
+    // a 32-entry chunk lies inside one 64-entry page: one (scalar) page lookup
+    const int j0 = chunk * kChunk;
+    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j0 >> 6) : -1;
+    const uint8_t* base = a.kidx + (pg < 0 ? 0 : pg) * (kPage * kDI) + (j0 & 63) * kDI + 16 * g;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int j = j0 + st * 16 + col;
+      v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
+      if (pg >= 0 && j < r.n) {
+        const v4u* src = reinterpret_cast<const v4u*>(base + (st * 16 + col) * kDI);
+        k0 = __builtin_nontemporal_load(src);
+        k1 = __builtin_nontemporal_load(src + 4);
+      }
+      ck.k[st][0] = k0;
+      ck.k[st][1] = k1;
+    }
+    return;
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
+    v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
+    if (j >= 0) {
+      const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
+      const v4u* src = reinterpret_cast<const v4u*>(a.kidx + pg * (kPage * kDI) + (j & 63) * kDI + 16 * g);
+      k0 = __builtin_nontemporal_load(src);
+      k1 = __builtin_nontemporal_load(src + 4);
+    }
+    ck.k[st][0] = k0;
+    ck.k[st][1] = k1;
+  }
+}
+
+// Persistent scan.  POOL = false: Full mode, rows = sequences, the 8 waves
+// split T tokens x chunk slices.  POOL = true: Reindex mode, rows = (b, t),
+// positions are the entries of the row's pool blocks.  Each workgroup takes a
+// contiguous range of (row, 32-entry chunk) items; each wave prefetches its
+// next chunk's keys while it scores the current one.
 template <bool POOL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 64];
-  __shared__ __attribute__((aligned(16))) float fold[kWaves][kChunk * kFoldStride];
+  // The lookup table sits at LDS offset 0, so a lookup address is the
+  // perm result itself (code * 256 + lane * 4) with no base to add.
+  struct __attribute__((aligned(16))) Lds {
+    uint32_t lut[256 * 64];
+    float fold[kWaves][kChunk * kFoldStride];
+    float wsh[kWaves][kMaxRT * 16];  // w * 2^-18 per head
+  };
+  __shared__ Lds sm;
+  uint32_t* lut = sm.lut;
+  auto& fold = sm.fold;
+  auto& wsh = sm.wsh;
 
   build_lut(lut);
   __syncthreads();
@@ -150,160 +252,140 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4;   // 16-byte K slice within a 64-deep step
   const int col = lane & 15;
-
-  int b, t, slice, n_slices;
-  if (POOL) {
-    b = blockIdx.y / a.T;
-    t = blockIdx.y % a.T;
-    slice = wave;
-    n_slices = kWaves;
-  } else {
-    b = blockIdx.y;
-    t = wave % a.T;
-    slice = wave / a.T;
-    n_slices = kWaves / a.T;
-    if (t >= a.T || slice >= n_slices) return;  // idle waves when T does not divide 8
-  }
-  int n = a.n_entries[b];
-  n = min(n, a.max_n);
-  n = min(n, a.max_pages * kPage);
-  int n_pos;            // positions handled in this row
-  const int32_t* pool_row = nullptr;
-  if (POOL) {
-    pool_row = a.pool + ((int64_t)b * a.T + t) * a.pool_blocks;
-    int pn = a.pool_n[(int64_t)b * a.T + t];
-    pn = max(0, min(pn, a.pool_blocks));
-    n_pos = pn * kBlock;
-  } else {
-    n_pos = n;
-  }
-  const int wg_base = blockIdx.x * kEntriesPerWG;
-  if (wg_base >= n_pos && !POOL) return;
-
+  const int t_full = POOL ? 0 : wave % a.T;
+  const int slice = POOL ? wave : wave / a.T;
+  const int n_slices = POOL ? kWaves : kWaves / a.T;
   const int HI = a.HI;
   const int NRT = (HI + 15) >> 4;
 
-  // ---- query limbs (A operands) and head weights for token t
-  Limbs qa[kMaxRT][2];
-  float wq[kMaxRT][4];
-  uint32_t q_top = 0, q_abs_max = 0;
-  const int64_t qrow0 = ((int64_t)b * a.T + t) * HI;
-#pragma unroll
-  for (int rt = 0; rt < kMaxRT; ++rt) {
-    const int h = rt * 16 + col;
-    v4u c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
-    if (rt < NRT && h < HI) {
-      const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
-      c0 = src[0];
-      c1 = src[4];
-    }
-    to_limbs(lut_bytes, lane4, c0, qa[rt][0]);
-    to_limbs(lut_bytes, lane4, c1, qa[rt][1]);
-    q_top |= qa[rt][0].top_any | qa[rt][1].top_any;
-    uint32_t s = abs_limb_sum(qa[rt][0], qa[rt][1]);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    q_abs_max = max(q_abs_max, s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = rt * 16 + 4 * g + i;
-      // w * 2^-18 is exact for 2^-100 <= |w| (and w = 0), see csa2.h
-      wq[rt][i] = (rt < NRT && hh < HI) ? a.w[qrow0 + hh] * 0x1p-18f : 0.0f;
-    }
-  }
-  // q_abs_max = sum_c |Mq| of the lane's head; the fast path needs the
-  // wave maximum below 2^17 so that sum_c |Mq||Mk| < 2^17 * 2^14 = 2^31.
-  uint32_t qmax = q_abs_max;
-  for (int o = 1; o < 64; o <<= 1) qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, o));
-  const bool fast_q = (__ballot(q_top != 0) == 0) && (qmax < (1u << 17));
+  const int total = a.rows * a.chunks_per_row;
+  const int it0 = blockIdx.x * a.chunks_per_wg;
+  const int it1 = min(total, it0 + a.chunks_per_wg);
 
   float* my_fold = fold[wave];
-  float* out_s_row = a.out_s + ((int64_t)b * a.T + t) * (POOL ? (int64_t)a.pool_blocks * kBlock
-                                                                 : (int64_t)a.max_n);
-  const int n_chunks = (min(kEntriesPerWG, max(0, n_pos - wg_base)) + kChunk - 1) / kChunk;
-  for (int ch = slice; ch < n_chunks; ch += n_slices) {
-    const int chunk_base = wg_base + ch * kChunk;
+  float* my_w = wsh[wave];
+
+  int it = it0 + slice;
+  ChunkKeys cur, nxt;
+  if (it < it1) {
+    RowCtx r0;
+    row_ctx<POOL>(a, it / a.chunks_per_row, t_full, r0);
+    load_chunk<POOL>(a, r0, it % a.chunks_per_row, g, col, cur);
+  }
+  while (it < it1) {
+    // ---- a new row: query limbs (A operands) and head weights of token t
+    RowCtx rc;
+    const int row = it / a.chunks_per_row;
+    row_ctx<POOL>(a, row, t_full, rc);
+    const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+    v4i qlo[kMaxRT][2], qmid[kMaxRT][2];
+    uint32_t q_any = 0, q_abs = 0;
+#pragma unroll
+    for (int rt = 0; rt < kMaxRT; ++rt) {
+      const int h = rt * 16 + col;
+      v4u c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
+      if (rt < NRT && h < HI) {
+        const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
+        c0 = src[0];
+        c1 = src[4];
+      }
+      limbs2(lut_bytes, lane4, c0, qlo[rt][0], qmid[rt][0], q_any);
+      limbs2(lut_bytes, lane4, c1, qlo[rt][1], qmid[rt][1], q_any);
+      uint32_t sabs = abs8_sum(qlo[rt][0], 1) + abs8_sum(qlo[rt][1], 1) + abs8_sum(qmid[rt][0], 128) +
+                      abs8_sum(qmid[rt][1], 128);
+      sabs += __shfl_xor(sabs, 16);
+      sabs += __shfl_xor(sabs, 32);
+      q_abs = max(q_abs, sabs);
+    }
+    for (int o = 1; o < 64; o <<= 1) q_abs = max(q_abs, (uint32_t)__shfl_xor((int)q_abs, o));
+    // the fast path needs no top limb in q and sum_c |Mq| < 2^17, so that with
+    // |Mk| < 2^14 every partial and the total stay below 2^31
+    const bool fast_q = (__ballot((q_any & 0x00FF0000u) != 0) == 0) && (q_abs < (1u << 17));
+    // w * 2^-18 is exact for |w| >= 2^-100 (and w = 0)
+    my_w[lane] = lane < HI ? a.w[qrow0 + lane] * 0x1p-18f : 0.0f;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+
+    const int row_end = min(it1, (row + 1) * a.chunks_per_row);
+    for (; it < row_end; it += n_slices) {
+    const int chunk = it % a.chunks_per_row;
+    // prefetch the next chunk of this wave (possibly in the next row)
+    const int itn = it + n_slices;
+    if (itn < it1) {
+      RowCtx rn;
+      row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
+      load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, nxt);
+    }
+
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int p = chunk_base + st * 16 + col;   // position index in this row's list
-      int j = -1;
-      if (p < n_pos) {
-        if (POOL) {
-          const int blk = pool_row[p >> 3];
-          const bool blk_ok = blk >= 0 && blk < (n + kBlock - 1) / kBlock;
-          const int jj = blk_ok ? blk * kBlock + (p & 7) : n;
-          j = jj < n ? jj : -1;
-        } else {
-          j = p;
-        }
-      }
-      v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
-      if (j >= 0) {
-        const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, b, j >> 6);
-        if (pg >= 0) {
-          const v4u* src =
-              reinterpret_cast<const v4u*>(a.kidx + pg * (kPage * kDI) + (j & 63) * kDI + 16 * g);
-          k0 = src[0];
-          k1 = src[4];
-        }
-      }
-      Limbs kb0, kb1;
-      to_limbs(lut_bytes, lane4, k0, kb0);
-      to_limbs(lut_bytes, lane4, k1, kb1);
-      const bool fast = fast_q && (__ballot((kb0.top_any | kb1.top_any) != 0) == 0);
+      v4i klo0, kmid0, klo1, kmid1;
+      uint32_t k_any = 0;
+      limbs2(lut_bytes, lane4, cur.k[st][0], klo0, kmid0, k_any);
+      limbs2(lut_bytes, lane4, cur.k[st][1], klo1, kmid1, k_any);
+      const bool fast = fast_q && (__ballot((k_any & 0x00FF0000u) != 0) == 0);
+      // keep the sub-tiles and row tiles in sequence: interleaving them all
+      // needs more registers than two waves per SIMD have
+      __builtin_amdgcn_sched_barrier(0);
+      if (fast) {
 #pragma unroll
-      for (int rt = 0; rt < kMaxRT; ++rt) {
-        if (rt >= NRT) break;
-        float r4[4];
-        if (fast) {
-          v4i z = {0, 0, 0, 0};
-          v4i a0 = mfma8(qa[rt][0].lo, kb0.lo, z);
-          a0 = mfma8(qa[rt][1].lo, kb1.lo, a0);
-          v4i a1 = mfma8(qa[rt][0].lo, kb0.mid, z);
-          a1 = mfma8(qa[rt][0].mid, kb0.lo, a1);
-          a1 = mfma8(qa[rt][1].lo, kb1.mid, a1);
-          a1 = mfma8(qa[rt][1].mid, kb1.lo, a1);
-          v4i a2 = mfma8(qa[rt][0].mid, kb0.mid, z);
-          a2 = mfma8(qa[rt][1].mid, kb1.mid, a2);
+        for (int rt = 0; rt < kMaxRT; ++rt) {
+          if (rt >= NRT) break;
+          const v4i z = {0, 0, 0, 0};
+          v4i a0 = mfma8(qlo[rt][0], klo0, z);
+          a0 = mfma8(qlo[rt][1], klo1, a0);
+          v4i a1 = mfma8(qlo[rt][0], kmid0, z);
+          a1 = mfma8(qmid[rt][0], klo0, a1);
+          a1 = mfma8(qlo[rt][1], kmid1, a1);
+          a1 = mfma8(qmid[rt][1], klo1, a1);
+          v4i a2 = mfma8(qmid[rt][0], kmid0, z);
+          a2 = mfma8(qmid[rt][1], kmid1, a2);
+          const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
+          v4f pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // |each weighted term| <= sum |Mq||Mk| < 2^31: exact in wrapping int32
-            uint32_t D = (uint32_t)a0[i] + ((uint32_t)a1[i] << 7) + ((uint32_t)a2[i] << 14);
-            r4[i] = (float)(int32_t)D;
+            // each weighted term is bounded by sum |Mq||Mk| < 2^31: exact in int32
+            // |a1| < 2^22 and |a2| < 2^21 fit the signed 24-bit multiplier
+            const int32_t D = __mul24(a2[i], 16384) + __mul24(a1[i], 128) + a0[i];
+            const float r = (float)max(D, 0);
+            pv[i] = wv[i] * r;
           }
-        } else {
-          v4i z = {0, 0, 0, 0};
+          *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rt * 16 + 4 * g]) = pv;
+        }
+      } else {
+        // general path: three limb planes on both sides, exact binary64 recombination
+        for (int rt = 0; rt < NRT; ++rt) {
+          const int h = rt * 16 + col;
+          const v4i z = {0, 0, 0, 0};
           v4i acc[5] = {z, z, z, z, z};
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const Limbs& Q = qa[rt][s];
-            const Limbs& K = s ? kb1 : kb0;
-            acc[0] = mfma8(Q.lo, K.lo, acc[0]);
-            acc[1] = mfma8(Q.lo, K.mid, acc[1]);
-            acc[1] = mfma8(Q.mid, K.lo, acc[1]);
-            acc[2] = mfma8(Q.lo, K.top, acc[2]);
-            acc[2] = mfma8(Q.mid, K.mid, acc[2]);
-            acc[2] = mfma8(Q.top, K.lo, acc[2]);
-            acc[3] = mfma8(Q.mid, K.top, acc[3]);
-            acc[3] = mfma8(Q.top, K.mid, acc[3]);
-            acc[4] = mfma8(Q.top, K.top, acc[4]);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            v4u qc = {0, 0, 0, 0};
+            if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g)[4 * s2];
+            v4i ql, qm, qt, kl, km, kt;
+            limbs3(lut_bytes, lane4, qc, ql, qm, qt);
+            limbs3(lut_bytes, lane4, cur.k[st][s2], kl, km, kt);
+            acc[0] = mfma8(ql, kl, acc[0]);
+            acc[1] = mfma8(ql, km, acc[1]);
+            acc[1] = mfma8(qm, kl, acc[1]);
+            acc[2] = mfma8(ql, kt, acc[2]);
+            acc[2] = mfma8(qm, km, acc[2]);
+            acc[2] = mfma8(qt, kl, acc[2]);
+            acc[3] = mfma8(qm, kt, acc[3]);
+            acc[3] = mfma8(qt, km, acc[3]);
+            acc[4] = mfma8(qt, kt, acc[4]);
           }
+          const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
+          v4f pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // each term and the sum are integers below 2^53: exact, one rounding below
-            double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 +
-                       (double)acc[2][i] * 16384.0 + (double)acc[3][i] * 2097152.0 +
-                       (double)acc[4][i] * 268435456.0;
-            r4[i] = (float)D;
+            // every term and the sum are integers below 2^53: exact, one rounding
+            const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
+                             (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
+            const float f = (float)D;
+            pv[i] = wv[i] * (f > 0.0f ? f : 0.0f);
           }
+          *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rt * 16 + 4 * g]) = pv;
         }
-        v4f pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float r = r4[i] > 0.0f ? r4[i] : 0.0f;
-          pv[i] = wq[rt][i] * r;
-        }
-        *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rt * 16 + 4 * g]) = pv;
       }
     }
     // the fold reads what other lanes of this wave wrote
@@ -312,40 +394,41 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     // ---- sequential head fold: lane e < 32 folds entry e of this chunk
     float s = 0.0f;
     if (lane < kChunk) {
-      const float* row = &my_fold[lane * kFoldStride];
+      const float* frow = &my_fold[lane * kFoldStride];
       for (int h = 0; h < HI; h += 4) {
-        const v4f v = *reinterpret_cast<const v4f*>(row + h);
+        const v4f v = *reinterpret_cast<const v4f*>(frow + h);
         s = s + v[0];
-        if (h + 1 < HI) s = s + v[1];
-        if (h + 2 < HI) s = s + v[2];
-        if (h + 3 < HI) s = s + v[3];
+        s = s + v[1];
+        s = s + v[2];
+        s = s + v[3];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
-    // positions whose page is unusable are not visible: NaN marker (key 0)
-    const int p = chunk_base + lane;
-    bool valid = false;
-    if (lane < kChunk && p < n_pos) {
-      int jj = p;
-      if (POOL) {
-        const int blk = pool_row[p >> 3];
-        jj = (blk >= 0 && blk < (n + kBlock - 1) / kBlock) ? blk * kBlock + (p & 7) : n;
-      }
-      valid = jj < n && phys_page(a.page_table, a.max_pages, a.n_pages, b, jj >> 6) >= 0;
-      out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
+    const int p = chunk * kChunk + lane;
+    bool valid;
+    if (POOL) {
+      valid = lane < kChunk && entry_of<POOL>(a, rc, p) >= 0;
+    } else {
+      const int j0 = chunk * kChunk;
+      const bool page_ok = j0 < rc.n && phys_page(a.page_table, a.max_pages, a.n_pages, rc.b, j0 >> 6) >= 0;
+      valid = lane < kChunk && page_ok && p < rc.n;
     }
+    float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
+                                     (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)a.max_n);
+    if (lane < kChunk && p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);  // NaN: key 0
     if (!POOL) {
       // block maxima over the visible entries of blocks of 8
       float m = valid ? s : -__builtin_inff();
       m = fmaxf(m, __shfl_xor(m, 1));
       m = fmaxf(m, __shfl_xor(m, 2));
       m = fmaxf(m, __shfl_xor(m, 4));
-      if (lane < kChunk && (lane & 7) == 0 && p < n_pos) {
-        const int nb_row = (a.max_n + kBlock - 1) / kBlock;
-        a.out_bm[((int64_t)b * a.T + t) * nb_row + (p >> 3)] =
+      if (lane < kChunk && (lane & 7) == 0 && p < rc.n_pos) {
+        a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] =
             (m == -__builtin_inff()) ? u2f(0xFFFFFFFFu) : m;
       }
+    }
+    cur = nxt;
     }
   }
 }
@@ -353,10 +436,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------- selection
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;     // 2,048: 32 per lane of one wave
+constexpr int kHistCopies = 4;
 
 struct SelShared {
-  uint32_t hist[8][256];
+  uint32_t hist[kHistCopies][kBins];
   int wave_tot[kSelWaves];
+  uint32_t wave_min[kSelWaves], wave_max[kSelWaves];
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
@@ -368,86 +455,141 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
+    const int y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   if (lane == 63) sh.wave_tot[wave] = x;
   __syncthreads();
-  int before = 0, tot = 0;
-  for (int i = 0; i < kSelWaves; ++i) {
-    int wt = sh.wave_tot[i];
-    if (i < wave) before += wt;
-    tot += wt;
+  // lanes 0..15 hold the wave totals: one read, then an in-register scan
+  int wt = lane < kSelWaves ? sh.wave_tot[lane] : 0;
+#pragma unroll
+  for (int o = 1; o < kSelWaves; o <<= 1) {
+    const int y = __shfl_up(wt, o);
+    if (lane >= o) wt += y;
   }
+  const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
+  *total = __shfl(wt, kSelWaves - 1);
   __syncthreads();
-  *total = tot;
   return before + x - v;
 }
 
 // Top-K selection among keys held KPT per thread (thread i owns list
 // positions [i*KPT, i*KPT + KPT)), order (key desc, position asc); key 0
-// marks an empty slot.  Writes, in ascending position order, out(rank, pos)
-// for every selected position.  Returns the number selected.
+// marks an empty slot.  Calls emit(rank, pos) for every selected position,
+// in ascending position order, and returns the number selected.
+//
+// Radix select on the keys below their common leading bits (from the
+// block's min and max), 11-bit digits, LDS histograms in 4 copies to spread
+// atomics; then an order-preserving compaction that takes every key above
+// the threshold and the first (in position order) of the keys equal to it.
 template <int KPT, typename Emit>
 __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit emit) {
-  const int lane = lane_id();
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
   int valid = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) valid += key[r] != 0;
+  for (int r = 0; r < KPT; ++r) {
+    const uint32_t k = key[r];
+    valid += k != 0;
+    if (k != 0) {
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    sh.wave_min[wave] = kmin;
+    sh.wave_max[wave] = kmax;
+  }
   int n_valid;
-  (void)block_excl_scan(valid, sh, &n_valid);
-  uint32_t tau = 1;      // select all valid keys (key >= 1)
+  (void)block_excl_scan(valid, sh, &n_valid);  // its barriers also publish wave_min/max
+  {
+    uint32_t m0 = lane < kSelWaves ? sh.wave_min[lane] : 0xFFFFFFFFu;
+    uint32_t m1 = lane < kSelWaves ? sh.wave_max[lane] : 0u;
+#pragma unroll
+    for (int o = 1; o < kSelWaves; o <<= 1) {
+      m0 = min(m0, (uint32_t)__shfl_xor((int)m0, o));
+      m1 = max(m1, (uint32_t)__shfl_xor((int)m1, o));
+    }
+    // lanes 0..15 now hold the block's min and max; every lane takes lane 0's
+    kmin = (uint32_t)__shfl((int)m0, 0);
+    kmax = (uint32_t)__shfl((int)m1, 0);
+  }
+  uint32_t tau = 1;             // select all valid keys (every real key is >= 1)
   int need_eq = 0x7FFFFFFF;
   if (n_valid > K) {
-    uint32_t prefix = 0, mask = 0;
-    int rem = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < 8 * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
-      __syncthreads();
+    const uint32_t diff = kmin ^ kmax;
+    if (diff == 0) {
+      tau = kmin;
+      need_eq = K;
+    } else {
+      const int top = 31 - __builtin_clz(diff);           // highest bit where keys differ
+      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+      uint32_t prefix = kmin & mask;
+      int rem = K;
+      int shift = top + 1;
+      while (shift > 0) {
+        const int width = min(kDigitBits, shift);
+        shift -= width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
+          reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
+        __syncthreads();
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const uint32_t k = key[r];
-        if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 7][(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        // lane l owns bins 255-4l .. 252-4l (descending)
-        uint32_t c[4];
-        uint32_t sum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int bin = 255 - 4 * lane - q;
-          uint32_t v = 0;
-#pragma unroll
-          for (int cp = 0; cp < 8; ++cp) v += sh.hist[cp][bin];
-          c[q] = v;
-          sum += v;
+        for (int r = 0; r < KPT; ++r) {
+          const uint32_t k = key[r];
+          if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
         }
-        uint32_t incl = sum;
+        __syncthreads();
+        for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+          sh.hist[0][i] = sh.hist[0][i] + sh.hist[1][i] + sh.hist[2][i] + sh.hist[3][i];
+        __syncthreads();
+        if (threadIdx.x < 64) {
+          // lane l owns the 32 bins [2048 - 32(l+1), 2048 - 32l), read as 8 vectors
+          const v4u* hv = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
+          uint32_t sum = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          uint32_t y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
-        uint32_t above = incl - sum;   // count in bins above this lane's bins
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (above < (uint32_t)rem && (uint32_t)rem <= above + c[q]) {
-            sh.misc[0] = 255 - 4 * lane - q;
-            sh.misc[1] = (int)above;
+          for (int q = 0; q < 8; ++q) {
+            const v4u v = hv[q];
+            sum += v[0] + v[1] + v[2] + v[3];
           }
-          above += c[q];
+          uint32_t incl = sum;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+          }
+          uint32_t above = incl - sum;  // keys in the bins of lower lanes (higher digits)
+          if (above < (uint32_t)rem && (uint32_t)rem <= incl) {
+            // walk this lane's bins from the highest digit down
+            for (int q = 7; q >= 0; --q) {
+              const v4u v = hv[q];
+#pragma unroll
+              for (int e = 3; e >= 0; --e) {
+                const uint32_t c = v[e];
+                if ((uint32_t)rem > above && (uint32_t)rem <= above + c) {
+                  sh.misc[0] = kBins - 32 * (lane + 1) + 4 * q + e;
+                  sh.misc[1] = (int)above;
+                }
+                above += c;
+              }
+            }
+          }
         }
+        __syncthreads();
+        const uint32_t d = (uint32_t)sh.misc[0];
+        rem -= sh.misc[1];
+        prefix |= d << shift;
+        mask |= dmask << shift;
+        __syncthreads();
       }
-      __syncthreads();
-      const uint32_t d = (uint32_t)sh.misc[0];
-      rem -= sh.misc[1];
-      prefix |= d << shift;
-      mask |= 255u << shift;
-      __syncthreads();
+      tau = prefix;
+      need_eq = rem;
     }
-    tau = prefix;
-    need_eq = rem;
   }
   // compaction in position order
   int gt = 0, eq = 0;
@@ -507,14 +649,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   int pool_n;
   if (FULL) {
     const int nb = (n + kBlock - 1) / kBlock;
-    const int nb_row = (a.max_n + kBlock - 1) / kBlock;
-    const float* bm = a.bm + (int64_t)row * nb_row;
+    const float* bm = a.bm + (int64_t)row * bm_stride(a.max_n);
     constexpr int KPT = 32;  // 32,768 blocks = 262,144 entries
     uint32_t key[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int blk = threadIdx.x * KPT + r;
-      key[r] = blk < nb ? score_key(bm[blk]) : 0u;
+    for (int r4 = 0; r4 < KPT; r4 += 4) {
+      const int blk = threadIdx.x * KPT + r4;
+      v4f v = {0.f, 0.f, 0.f, 0.f};
+      if (blk + 3 < nb) v = *reinterpret_cast<const v4f*>(bm + blk);
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = blk + e < nb ? bm[blk + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[r4 + e] = blk + e < nb ? score_key(v[e]) : 0u;
     }
     for (int i = threadIdx.x; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
     __syncthreads();
@@ -560,6 +708,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// One resident workgroup per compute unit (the scan uses ~132 KB of LDS);
+// each takes a contiguous range of 32-entry chunks.  With T tokens sharing a
+// workgroup, every wave covers chunks_per_wg * T / 8 chunks.
+int persistent_grid(int total_chunks, int T, int* chunks_per_wg) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      n_cu = 256;
+  }
+  const int slices = csa2::kWaves / T;
+  int per = (total_chunks + n_cu - 1) / n_cu;
+  per = ((per + slices - 1) / slices) * slices;  // whole rounds of the waves
+  *chunks_per_wg = per;
+  return (total_chunks + per - 1) / per;
+}
+
 int check_index_common(const void* q_idx, const void* w, const void* kidx, int64_t n_pages,
                        const void* page_table, int32_t max_pages, const void* n_entries,
                        int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks) {
@@ -578,7 +744,7 @@ int check_index_common(const void* q_idx, const void* w, const void* kidx, int64
 extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_n,
                                       int32_t pool_blocks) {
   if (op == CSA2_OP_INDEX_FULL) {
-    const size_t nb = ((size_t)max_n + 7) / 8;
+    const size_t nb = (size_t)csa2::bm_stride(max_n);
     return align256((size_t)B * T * max_n * 4) + align256((size_t)B * T * nb * 4);
   }
   return align256((size_t)B * T * pool_blocks * 8 * 4);
@@ -612,8 +778,10 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   sa.out_s = reinterpret_cast<float*>(ws);
   sa.out_bm = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                        align256((size_t)B * T * max_n_entries * 4));
-  const int gx = (max_n_entries + csa2::kEntriesPerWG - 1) / csa2::kEntriesPerWG;
-  CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx, B), dim3(csa2::kScoreThreads),
+  sa.rows = B;
+  sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
+  const int gx = persistent_grid(sa.rows * sa.chunks_per_row, T, &sa.chunks_per_wg);
+  CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx), dim3(csa2::kScoreThreads),
               (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::SelectArgs se{};
@@ -661,9 +829,11 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   sa.pool_n = pool_n;
   sa.pool_blocks = pool_blocks;
   sa.out_s = reinterpret_cast<float*>(ws);
-  const int gx = (pool_blocks * csa2::kBlock + csa2::kEntriesPerWG - 1) / csa2::kEntriesPerWG;
-  CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx, B * T),
-              dim3(csa2::kScoreThreads), (hipStream_t)stream, sa);
+  sa.rows = B * T;
+  sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
+  const int gx = persistent_grid(sa.rows * sa.chunks_per_row, 1, &sa.chunks_per_wg);
+  CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads),
+              (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
