@@ -116,6 +116,9 @@ __device__ __forceinline__ uint32_t abs8_sum(v4i v, uint32_t w) {
 __host__ __device__ __forceinline__ int bm_stride(int max_n) {
   return ((max_n + kBlock - 1) / kBlock + 3) & ~3;
 }
+// Row stride of the Full-mode score buffer: max_n rounded up to a multiple
+// of 8, so each 8-entry block is 32-byte aligned.
+__host__ __device__ __forceinline__ int s_stride(int max_n) { return (max_n + 7) & ~7; }
 
 struct ScoreArgs {
   const uint8_t* q_idx;
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       valid = lane < kChunk && page_ok && p < rc.n;
     }
     float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
-                                     (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)a.max_n);
+                                     (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
     if (lane < kChunk && p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);  // NaN: key 0
     if (!POOL) {
       // block maxima over the visible entries of blocks of 8
@@ -440,8 +443,12 @@ constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;     // 2,048: 32 per lane of one wave
 constexpr int kHistCopies = 4;
 
+constexpr int kCandCap = 4096;            // candidates kept for the single-wave exact stage
+
 struct SelShared {
   uint32_t hist[kHistCopies][kBins];
+  uint32_t cand_key[kCandCap];
+  int cand_pos[kCandCap];
   int wave_tot[kSelWaves];
   uint32_t wave_min[kSelWaves], wave_max[kSelWaves];
   int misc[8];
@@ -473,15 +480,45 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   return before + x - v;
 }
 
+// Zero the 4-copy histogram (all threads), no barrier.
+__device__ __forceinline__ void hist_zero(SelShared& sh) {
+  for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
+    reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
+}
+
+// One wave: merge the 4 copies of the 32 bins lane l owns (bins
+// [2048 - 32(l+1), 2048 - 32l), lane 0 has the highest digits) into copy 0
+// and return their total.
+__device__ __forceinline__ uint32_t wave_merge_bins(SelShared& sh, int lane) {
+  uint32_t sum = 0;
+  v4u* h0 = reinterpret_cast<v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v4u v = h0[q];
+#pragma unroll
+    for (int cp = 1; cp < kHistCopies; ++cp)
+      v += reinterpret_cast<const v4u*>(&sh.hist[cp][kBins - 32 * (lane + 1)])[q];
+    h0[q] = v;
+    sum += v[0] + v[1] + v[2] + v[3];
+  }
+  return sum;
+}
+
 // Top-K selection among keys held KPT per thread (thread i owns list
 // positions [i*KPT, i*KPT + KPT)), order (key desc, position asc); key 0
 // marks an empty slot.  Calls emit(rank, pos) for every selected position,
 // in ascending position order, and returns the number selected.
 //
-// Radix select on the keys below their common leading bits (from the
-// block's min and max), 11-bit digits, LDS histograms in 4 copies to spread
-// atomics; then an order-preserving compaction that takes every key above
-// the threshold and the first (in position order) of the keys equal to it.
+// 1. Block min/max and valid count; digits are the 11 bits below the
+//    leading bits all keys share.
+// 2. A histogram of every 8th key brackets the digit range [d_lo, d_hi]
+//    that holds the K-th largest key.
+// 3. One pass counts the keys above the bracket and compacts the keys inside
+//    it (in position order) into LDS.  If the bracket does not hold the K-th
+//    key, or holds too many keys, a block-wide radix select runs instead.
+// 4. One wave finds the exact threshold among the candidates.
+// 5. Every key above the threshold is taken, and the first keys (in
+//    position order) equal to it up to K.
 template <int KPT, typename Emit>
 __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit emit) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -515,7 +552,6 @@ __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit
       m0 = min(m0, (uint32_t)__shfl_xor((int)m0, o));
       m1 = max(m1, (uint32_t)__shfl_xor((int)m1, o));
     }
-    // lanes 0..15 now hold the block's min and max; every lane takes lane 0's
     kmin = (uint32_t)__shfl((int)m0, 0);
     kmax = (uint32_t)__shfl((int)m1, 0);
   }
@@ -527,82 +563,218 @@ __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit
       tau = kmin;
       need_eq = K;
     } else {
-      const int top = 31 - __builtin_clz(diff);           // highest bit where keys differ
-      uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-      uint32_t prefix = kmin & mask;
-      int rem = K;
-      int shift = top + 1;
-      while (shift > 0) {
-        const int width = min(kDigitBits, shift);
-        shift -= width;
-        const uint32_t dmask = (1u << width) - 1u;
-        for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
-          reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
-        __syncthreads();
+      const int top = 31 - __builtin_clz(diff);  // highest bit where keys differ
+      const int shift1 = max(top + 1 - kDigitBits, 0);
+      // ---- 2. sample histogram
+      constexpr int kStride = KPT >= 16 ? 8 : 4;
+      hist_zero(sh);
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < KPT; r += kStride) {
+        const uint32_t k = key[r];
+        if (k != 0) atomicAdd(&sh.hist[lane & 3][(k >> shift1) & (kBins - 1)], 1u);
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const uint32_t sum = wave_merge_bins(sh, lane);
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        const float n_s = (float)__shfl((int)incl, 63);
+        const float ts = (float)K * n_s / (float)n_valid;          // expected sample rank
+        const float m = 3.0f * sqrtf(ts) + 8.0f;                   // margin, in samples
+        const float hi_cut = ts - m, lo_cut = ts + m;
+        // C(d) = samples with digit >= d; walk bins from high to low digits
+        uint32_t above = incl - sum;
+        int d_hi = -1, d_lo = -1;
+        const v4u* h0 = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
+        for (int q = 7; q >= 0; --q) {
+          const v4u v = h0[q];
+#pragma unroll
+          for (int e = 3; e >= 0; --e) {
+            const int bin = kBins - 32 * (lane + 1) + 4 * q + e;
+            const float c_prev = (float)above;   // samples with digit > bin
+            above += v[e];
+            const float c_here = (float)above;   // samples with digit >= bin
+            if (c_here >= hi_cut && c_prev < hi_cut) d_hi = bin;
+            if (c_here >= lo_cut && c_prev < lo_cut) d_lo = bin;
+          }
+        }
+        // the crossing bins are unique across lanes; unset means "not reached"
+        int dh = d_hi, dl = d_lo;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          dh = max(dh, __shfl_xor(dh, o));
+          dl = max(dl, __shfl_xor(dl, o));
+        }
+        if (lane == 0) {
+          sh.misc[0] = dh < 0 ? kBins - 1 : dh;  // hi_cut <= 0: everything above the top bin
+          sh.misc[1] = dl < 0 ? 0 : dl;          // lo_cut beyond all samples: down to digit 0
+        }
+      }
+      __syncthreads();
+      const uint32_t d_hi = (uint32_t)sh.misc[0];
+      const uint32_t d_lo = min((uint32_t)sh.misc[1], d_hi);
+      // ---- 3. exact counts around the bracket
+      int n_above = 0, n_cand = 0;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const uint32_t k = key[r];
+        const uint32_t d = (k >> shift1) & (kBins - 1);
+        n_above += k != 0 && d > d_hi;
+        n_cand += k != 0 && d <= d_hi && d >= d_lo;
+      }
+      int tot;
+      const int packed_off = block_excl_scan(n_above | (n_cand << 16), sh, &tot);
+      // both counts are at most 32,768, so the 16-bit halves never carry;
+      // the high half can reach bit 31, hence the unsigned decode
+      const int A = tot & 0xFFFF, C = (int)((uint32_t)tot >> 16);
+      const bool fast = A < K && K <= A + C && C <= kCandCap;
+      if (fast) {
+        int o = (int)((uint32_t)packed_off >> 16);
+        const int base = threadIdx.x * KPT;
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
           const uint32_t k = key[r];
-          if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
+          const uint32_t d = (k >> shift1) & (kBins - 1);
+          if (k != 0 && d <= d_hi && d >= d_lo) {
+            sh.cand_key[o] = k;
+            sh.cand_pos[o] = base + r;
+            ++o;
+          }
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < kBins; i += kSelThreads)
-          sh.hist[0][i] = sh.hist[0][i] + sh.hist[1][i] + sh.hist[2][i] + sh.hist[3][i];
-        __syncthreads();
+        // ---- 4. one wave: rank R = K - A among the C candidates
         if (threadIdx.x < 64) {
-          // lane l owns the 32 bins [2048 - 32(l+1), 2048 - 32l), read as 8 vectors
-          const v4u* hv = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
-          uint32_t sum = 0;
+          uint32_t prefix = 0, msk = 0;
+          int rem = K - A;
+          for (int sh8 = 24; sh8 >= 0; sh8 -= 8) {
+            // 256-bin histogram in copy 0, built by this wave only
+            for (int i = lane; i < 256; i += 64) sh.hist[0][i] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            for (int i = lane; i < C; i += 64) {
+              const uint32_t k = sh.cand_key[i];
+              if ((k & msk) == prefix) atomicAdd(&sh.hist[0][(k >> sh8) & 255u], 1u);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            // lane l owns bins 255-4l .. 252-4l
+            uint32_t cc[4], sum = 0;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const v4u v = hv[q];
-            sum += v[0] + v[1] + v[2] + v[3];
+            for (int e = 0; e < 4; ++e) {
+              cc[e] = sh.hist[0][255 - 4 * lane - e];
+              sum += cc[e];
+            }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int o2 = 1; o2 < 64; o2 <<= 1) {
+              const uint32_t y = __shfl_up(incl, o2);
+              if (lane >= o2) incl += y;
+            }
+            uint32_t above = incl - sum;
+            int dsel = -1, asel = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if ((uint32_t)rem > above && (uint32_t)rem <= above + cc[e]) {
+                dsel = 255 - 4 * lane - e;
+                asel = (int)above;
+              }
+              above += cc[e];
+            }
+            int dd = dsel, aa = asel;
+#pragma unroll
+            for (int o2 = 1; o2 < 64; o2 <<= 1) {
+              const int od = __shfl_xor(dd, o2), oa = __shfl_xor(aa, o2);
+              if (od > dd) {
+                dd = od;
+                aa = oa;
+              }
+            }
+            prefix |= (uint32_t)dd << sh8;
+            msk |= 255u << sh8;
+            rem -= aa;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            __builtin_amdgcn_wave_barrier();
           }
-          uint32_t incl = sum;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
+          if (lane == 0) {
+            sh.misc[2] = (int)prefix;
+            sh.misc[3] = rem;
           }
-          uint32_t above = incl - sum;  // keys in the bins of lower lanes (higher digits)
-          if (above < (uint32_t)rem && (uint32_t)rem <= incl) {
-            // walk this lane's bins from the highest digit down
-            for (int q = 7; q >= 0; --q) {
-              const v4u v = hv[q];
+        }
+        __syncthreads();
+        tau = (uint32_t)sh.misc[2];
+        need_eq = sh.misc[3];
+      } else {
+        // ---- fallback: block-wide radix select over all keys
+        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
+        uint32_t prefix = kmin & mask;
+        int rem = K;
+        int shift = top + 1;
+        while (shift > 0) {
+          const int width = min(kDigitBits, shift);
+          shift -= width;
+          const uint32_t dmask = (1u << width) - 1u;
+          hist_zero(sh);
+          __syncthreads();
 #pragma unroll
-              for (int e = 3; e >= 0; --e) {
-                const uint32_t c = v[e];
-                if ((uint32_t)rem > above && (uint32_t)rem <= above + c) {
-                  sh.misc[0] = kBins - 32 * (lane + 1) + 4 * q + e;
-                  sh.misc[1] = (int)above;
+          for (int r = 0; r < KPT; ++r) {
+            const uint32_t k = key[r];
+            if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
+          }
+          __syncthreads();
+          if (threadIdx.x < 64) {
+            const uint32_t sum = wave_merge_bins(sh, lane);
+            uint32_t incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const uint32_t y = __shfl_up(incl, o);
+              if (lane >= o) incl += y;
+            }
+            uint32_t above = incl - sum;
+            if (above < (uint32_t)rem && (uint32_t)rem <= incl) {
+              const v4u* h0 = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
+              for (int q = 7; q >= 0; --q) {
+                const v4u v = h0[q];
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                  if ((uint32_t)rem > above && (uint32_t)rem <= above + v[e]) {
+                    sh.misc[0] = kBins - 32 * (lane + 1) + 4 * q + e;
+                    sh.misc[1] = (int)above;
+                  }
+                  above += v[e];
                 }
-                above += c;
               }
             }
           }
+          __syncthreads();
+          const uint32_t d = (uint32_t)sh.misc[0];
+          rem -= sh.misc[1];
+          prefix |= d << shift;
+          mask |= dmask << shift;
+          __syncthreads();
         }
-        __syncthreads();
-        const uint32_t d = (uint32_t)sh.misc[0];
-        rem -= sh.misc[1];
-        prefix |= d << shift;
-        mask |= dmask << shift;
-        __syncthreads();
+        tau = prefix;
+        need_eq = rem;
       }
-      tau = prefix;
-      need_eq = rem;
     }
   }
-  // compaction in position order
+  // ---- 5. emit in position order: keys above tau, then the first need_eq equal to it
   int gt = 0, eq = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     gt += key[r] != 0 && key[r] > tau;
     eq += key[r] != 0 && key[r] == tau;
   }
-  int eq_tot;
-  const int eq_before = block_excl_scan(eq, sh, &eq_tot);
+  int tot2;
+  const int off2 = block_excl_scan(gt | (eq << 16), sh, &tot2);
+  const int gt_before = off2 & 0xFFFF, eq_before = (int)((uint32_t)off2 >> 16);
   const int take_eq = max(0, min(eq, need_eq - eq_before));
-  int sel_tot;
-  int off = block_excl_scan(gt + take_eq, sh, &sel_tot);
+  int off = gt_before + min(eq_before, need_eq);
+  const int sel_tot = (tot2 & 0xFFFF) + min((int)((uint32_t)tot2 >> 16), need_eq);
   int taken_eq = 0;
   const int base = threadIdx.x * KPT;
 #pragma unroll
@@ -680,20 +852,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // ---- top-k over the pool's positions (list position p = 8 * slot + i)
   constexpr int KPT2 = 16;  // 2 pool slots per thread, 16,384 positions
   uint32_t key2[KPT2];
-  const float* srow = FULL ? a.s + (int64_t)row * a.max_n : a.s + (int64_t)row * P * kBlock;
+  const float* srow = FULL ? a.s + (int64_t)row * s_stride(a.max_n) : a.s + (int64_t)row * P * kBlock;
 #pragma unroll
-  for (int r = 0; r < KPT2; ++r) {
-    const int p = threadIdx.x * KPT2 + r;
-    const int slot = p >> 3;
-    uint32_t k = 0;
-    if (slot < pool_n) {
-      const int blk = sh.pool_blk[slot];
-      if (blk >= 0 && blk < (n + kBlock - 1) / kBlock) {
-        const int j = blk * kBlock + (p & 7);
-        if (j < n) k = FULL ? score_key(srow[j]) : score_key(srow[p]);
-      }
+  for (int hs = 0; hs < 2; ++hs) {
+    const int slot = threadIdx.x * 2 + hs;
+    const int blk = slot < pool_n ? sh.pool_blk[slot] : -1;
+    const bool ok = blk >= 0 && blk < (n + kBlock - 1) / kBlock;
+    // the 8 scores of this slot: block blk's entries (Full) or the slot's
+    // pool-order scores (Reindex); both 32-byte aligned
+    v4f v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const v4f* src = reinterpret_cast<const v4f*>(srow + (FULL ? blk * kBlock : slot * kBlock));
+      v0 = src[0];
+      v1 = src[1];
     }
-    key2[r] = k;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = ok && blk * kBlock + e < n;
+      key2[hs * 8 + e] = in ? score_key(e < 4 ? v0[e] : v1[e - 4]) : 0u;
+    }
   }
   int32_t* out = a.out_topk + (int64_t)row * a.topk;
   const int got = block_topk<KPT2>(key2, a.topk, sh, [&](int rank, int p) {
@@ -745,7 +922,7 @@ extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_
                                       int32_t pool_blocks) {
   if (op == CSA2_OP_INDEX_FULL) {
     const size_t nb = (size_t)csa2::bm_stride(max_n);
-    return align256((size_t)B * T * max_n * 4) + align256((size_t)B * T * nb * 4);
+    return align256((size_t)B * T * csa2::s_stride(max_n) * 4) + align256((size_t)B * T * nb * 4);
   }
   return align256((size_t)B * T * pool_blocks * 8 * 4);
 }
@@ -777,7 +954,7 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   sa.HI = HI;
   sa.out_s = reinterpret_cast<float*>(ws);
   sa.out_bm = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                       align256((size_t)B * T * max_n_entries * 4));
+                                       align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4));
   sa.rows = B;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
   const int gx = persistent_grid(sa.rows * sa.chunks_per_row, T, &sa.chunks_per_wg);

@@ -168,6 +168,31 @@ def test_index_full_ties(oracle):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
+@pytest.mark.parametrize("distinct", [1, 3, 50])
+def test_index_full_max_entries_heavy_ties(oracle, distinct):
+    """262,144 entries (the maximum) drawn from a few distinct keys: thousands of
+    equal block maxima and scores, so both selections break ties by index over
+    the whole list (distinct=1: every score equal)."""
+    say(f"index full 262,144 entries from {distinct} distinct key(s)")
+    n = [262144, 131075]
+    base = synth.fp8_normal((distinct, 128), 70 + distinct)
+    rng = np.random.default_rng(distinct)
+    keys = base[rng.integers(0, distinct, sum(n))]
+    wl = small_workload(n, T=1, HI=4, topk=2048, seed=11, key_codes=keys)
+    got = gpu_index_full(wl, wl.layers[0])
+    assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
+
+
+def test_index_full_all_scores_zero(oracle):
+    say("index full with zero queries: every score is +0")
+    n = [262144, 9]
+    wl = small_workload(n, T=2, HI=4, topk=2048, seed=12, q_codes=np.zeros((2, 2, 4, 128), np.uint8))
+    got = gpu_index_full(wl, wl.layers[0])
+    ref = oracle_index_full(oracle, wl, wl.layers[0])
+    assert (ref[0][0, 0] == np.arange(2048)).all()  # ties go to the lowest indices
+    assert_index_equal(got, ref)
+
+
 def test_index_full_wide_exponent_range(oracle):
     say("index full with every finite E4M3 code (general exact path)")
     n = [3000, 999]
