@@ -31,9 +31,14 @@ namespace csa2 {
 
 constexpr int kScoreThreads = 512;        // 8 waves
 constexpr int kWaves = kScoreThreads / 64;
-constexpr int kChunk = 32;                // entries folded together per wave (2 sub-tiles)
+constexpr int kChunk = 32;                // entries scored together per wave (half a page)
+constexpr int kSub = kChunk / 16;         // 16-entry MFMA sub-tiles per chunk
 constexpr int kMaxRT = 4;                 // row tiles of 16 heads (HI <= 64)
-constexpr int kFoldStride = kMaxRT * 16 + 4;
+constexpr int kPassHeads = 64;            // heads folded per pass
+constexpr int kPassRT = kPassHeads / 16;  // row tiles per pass
+constexpr int kFoldStride = kPassHeads + 4;  // floats per entry row of the fold buffer
+constexpr int kMaxWaveChunks = 1024;      // chunks one wave may take in one launch
+constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
 // Lookup table: for every E4M3 code, its sign-magnitude 7-bit limbs of
 // M = value * 2^9 packed as int8 bytes [lo, mid, top, 0]; 64 copies so the
@@ -137,14 +142,14 @@ struct ScoreArgs {
   float* out_s;           // full: [B][T][max_n]; pool: [B][T][pool_blocks*8]
   float* out_bm;          // full: [B][T][ceil(max_n/8)]
   int rows;               // full: B; pool: B*T
-  int chunks_per_row;     // full: ceil(max_n/32); pool: pool_blocks/4
+  int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
   int chunks_per_wg;
 };
 
-// Keys of one 32-entry chunk for one wave: lane (g, col) holds entry
-// chunk + 16*st + col, channels [16g, 16g+16) and [64+16g, 64+16g+16).
+// Keys of one chunk for one wave: lane (g, col) holds entry 16*st + col of
+// the chunk, channels [16g, 16g+16) and [64+16g, 64+16g+16).
 struct ChunkKeys {
-  v4u k[2][2];
+  v4u k[kSub][2];
 };
 
 // Row context of a wave: sequence b, token t, visible entries n, pool row.
@@ -194,26 +199,32 @@ template <bool POOL>
 __device__ __forceinline__ void load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g,
                                            int col, ChunkKeys& ck) {
   if (!POOL) {
-    // a 32-entry chunk lies inside one 64-entry page: one (scalar) page lookup
+    // a Full-mode chunk lies inside one 64-entry page: one scalar page lookup
     const int j0 = chunk * kChunk;
-    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j0 >> 6) : -1;
-    const uint8_t* base = a.kidx + (pg < 0 ? 0 : pg) * (kPage * kDI) + (j0 & 63) * kDI + 16 * g;
+    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j0 / kPage) : -1;
+    // one buffer descriptor for the page (scalar registers) and a single
+    // 32-bit lane offset; the sub-tile and half offsets go in the scalar
+    // offset operand
+    const v4u z = {0, 0, 0, 0};
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int j = j0 + st * 16 + col;
-      v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
-      if (pg >= 0 && j < r.n) {
-        const v4u* src = reinterpret_cast<const v4u*>(base + (st * 16 + col) * kDI);
-        k0 = __builtin_nontemporal_load(src);
-        k1 = __builtin_nontemporal_load(src + 4);
+    for (int st = 0; st < kSub; ++st) ck.k[st][0] = ck.k[st][1] = z;
+    if (pg >= 0) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.kidx + pg * (kPage * kDI) + (j0 % kPage) * kDI), 0, kChunk * kDI, kBufferFlags);
+      const uint32_t lofs = (uint32_t)(col * kDI + 16 * g);
+      const int nv = r.n - j0;  // visible entries from the chunk start
+#pragma unroll
+      for (int st = 0; st < kSub; ++st) {
+        if (st * 16 + col < nv) {
+          ck.k[st][0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, st * 16 * kDI, 0);
+          ck.k[st][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, st * 16 * kDI + 64, 0);
+        }
       }
-      ck.k[st][0] = k0;
-      ck.k[st][1] = k1;
     }
     return;
   }
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
+  for (int st = 0; st < kSub; ++st) {
     const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
     v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
     if (j >= 0) {
@@ -227,11 +238,126 @@ __device__ __forceinline__ void load_chunk(const ScoreArgs& a, const RowCtx& r, 
   }
 }
 
+// Writes the chunk's scores (NaN, i.e. key 0, for positions that are not
+// visible) and, in Full mode, the maxima of its blocks of 8.
+template <bool POOL>
+__device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, float s) {
+  const int lane = lane_id();
+  const int p = chunk * kChunk + lane;
+  bool valid;
+  if (POOL) {
+    valid = lane < kChunk && entry_of<POOL>(a, rc, p) >= 0;
+  } else {
+    const bool page_ok = chunk * kChunk < rc.n &&
+                         phys_page(a.page_table, a.max_pages, a.n_pages, rc.b, chunk * kChunk / kPage) >= 0;
+    valid = lane < kChunk && page_ok && p < rc.n;
+  }
+  float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
+                                   (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
+  if (lane < kChunk && p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
+  if (!POOL) {
+    float m = valid ? s : -__builtin_inff();
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    if (lane < kChunk && (lane & 7) == 0 && p < rc.n_pos) {
+      a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] =
+          (m == -__builtin_inff()) ? u2f(0xFFFFFFFFu) : m;
+    }
+  }
+}
+
+// General exact path for one chunk (some |value| >= 32, or a query whose
+// limb sums could leave int32): three limb planes on both sides, five
+// partial sums per dot combined exactly in binary64 and rounded once.
+// Reads the chunk's codes again; returns this lane's entry score before
+// validity masking.
+template <bool POOL>
+__device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, int64_t qrow0,
+                                            const uint8_t* lut_bytes, float* my_fold, const float* my_w) {
+  const int lane = lane_id();
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  const int g = lane >> 4, col = lane & 15;
+  const int HI = a.HI;
+  const int NRT = (HI + 15) >> 4;
+  const int n_pass = (HI + kPassHeads - 1) / kPassHeads;
+  ChunkKeys raw;
+  load_chunk<POOL>(a, rc, chunk, g, col, raw);
+  // an offset the optimizer cannot see through: keeps the query decode
+  // below from being hoisted out of the chunk loop, where its 96 limb
+  // registers would stay live across the common path
+  int qoff = 16 * g;
+  asm volatile("" : "+v"(qoff));
+  float s = 0.0f;
+  for (int hh = 0; hh < n_pass; ++hh) {
+    for (int st = 0; st < kSub; ++st) {
+      for (int rl = 0; rl < kPassRT; ++rl) {
+        const int rt = kPassRT * hh + rl;
+        if (rt >= NRT) break;
+        const int h = rt * 16 + col;
+        const v4i z = {0, 0, 0, 0};
+        v4i acc[5] = {z, z, z, z, z};
+        for (int s2 = 0; s2 < 2; ++s2) {
+          v4u qc = {0, 0, 0, 0};
+          if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + qoff)[4 * s2];
+          v4i ql, qm, qt, kl, km, kt;
+          limbs3(lut_bytes, lane4, qc, ql, qm, qt);
+          limbs3(lut_bytes, lane4, raw.k[st][s2], kl, km, kt);
+          acc[0] = mfma8(ql, kl, acc[0]);
+          acc[1] = mfma8(ql, km, acc[1]);
+          acc[1] = mfma8(qm, kl, acc[1]);
+          acc[2] = mfma8(ql, kt, acc[2]);
+          acc[2] = mfma8(qm, km, acc[2]);
+          acc[2] = mfma8(qt, kl, acc[2]);
+          acc[3] = mfma8(qm, kt, acc[3]);
+          acc[3] = mfma8(qt, km, acc[3]);
+          acc[4] = mfma8(qt, kt, acc[4]);
+        }
+        const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
+        v4f pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // every term and the sum are integers below 2^53: exact, one rounding
+          const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
+                           (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
+          const float f = (float)D;
+          pv[i] = wv[i] * (f > 0.0f ? f : 0.0f);
+        }
+        *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rl * 16 + 4 * g]) = pv;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < kChunk) {
+      const float* frow = &my_fold[lane * kFoldStride];
+      const int nh = min(kPassHeads, HI - kPassHeads * hh);
+      for (int h = 0; h < nh; h += 4) {
+        const v4f v = *reinterpret_cast<const v4f*>(frow + h);
+        s = s + v[0];
+        s = s + v[1];
+        s = s + v[2];
+        s = s + v[3];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+  return s;
+}
+
 // Persistent scan.  POOL = false: Full mode, rows = sequences, the 8 waves
 // split T tokens x chunk slices.  POOL = true: Reindex mode, rows = (b, t),
 // positions are the entries of the row's pool blocks.  Each workgroup takes a
-// contiguous range of (row, 32-entry chunk) items; each wave prefetches its
-// next chunk's keys while it scores the current one.
+// contiguous range of (row, 32-entry chunk) items; each wave loads its next
+// chunk's keys while it scores the current one.
+//
+// Per chunk a wave decodes the 32 keys into limb planes once, runs the MFMAs
+// of its 2 sub-tiles x 4 row tiles, writes fl(w_h * relu(d_h)) to its LDS
+// fold buffer (entry-major), and lets lane e < 32 fold entry e's heads in
+// ascending order.  Chunks holding a code with a top limb (or rows whose
+// query could overflow int32) are only marked here and scored after the main
+// loop by the general path, so the main loop keeps the common path's
+// registers (no spills: a spill reload would wait for the prefetch).
 template <bool POOL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // The lookup table sits at LDS offset 0, so a lookup address is the
@@ -240,18 +366,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     uint32_t lut[256 * 64];
     float fold[kWaves][kChunk * kFoldStride];
     float wsh[kWaves][kMaxRT * 16];  // w * 2^-18 per head
+    uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
   };
   __shared__ Lds sm;
   uint32_t* lut = sm.lut;
-  auto& fold = sm.fold;
-  auto& wsh = sm.wsh;
 
   build_lut(lut);
+  for (int i = threadIdx.x; i < kWaves * kMaxWaveChunks / 32; i += blockDim.x) (&sm.defer[0][0])[i] = 0u;
   __syncthreads();
   const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut);
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4;   // 16-byte K slice within a 64-deep step
   const int col = lane & 15;
@@ -260,16 +386,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int n_slices = POOL ? kWaves : kWaves / a.T;
   const int HI = a.HI;
   const int NRT = (HI + 15) >> 4;
+  const int n_pass = (HI + kPassHeads - 1) / kPassHeads;
 
   const int total = a.rows * a.chunks_per_row;
   const int it0 = blockIdx.x * a.chunks_per_wg;
   const int it1 = min(total, it0 + a.chunks_per_wg);
 
-  float* my_fold = fold[wave];
-  float* my_w = wsh[wave];
+  float* my_fold = sm.fold[wave];
+  // this lane's fold-buffer slot for sub-tile 0, row tile 0 (the other
+  // tiles sit at constant offsets from it)
+  float* fold_w = my_fold + col * kFoldStride + 4 * g;
+  float* my_w = sm.wsh[wave];
+  uint32_t* my_defer = sm.defer[wave];
+  int k_seq = 0;  // index of the current chunk among this wave's chunks
 
   int it = it0 + slice;
-  ChunkKeys cur, nxt;
+  ChunkKeys cur;
   if (it < it1) {
     RowCtx r0;
     row_ctx<POOL>(a, it / a.chunks_per_row, t_full, r0);
@@ -311,128 +443,126 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
     const int row_end = min(it1, (row + 1) * a.chunks_per_row);
     for (; it < row_end; it += n_slices) {
-    const int chunk = it % a.chunks_per_row;
-    // prefetch the next chunk of this wave (possibly in the next row)
-    const int itn = it + n_slices;
-    if (itn < it1) {
-      RowCtx rn;
-      row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
-      load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, nxt);
-    }
-
+      const int chunk = it % a.chunks_per_row;
+      // ---- fast or general: a key code has a top limb iff |value| >= 32,
+      // i.e. its exponent field is >= 12 (bits 6 and 5 of the byte both set)
+      uint32_t hot = 0;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      v4i klo0, kmid0, klo1, kmid1;
-      uint32_t k_any = 0;
-      limbs2(lut_bytes, lane4, cur.k[st][0], klo0, kmid0, k_any);
-      limbs2(lut_bytes, lane4, cur.k[st][1], klo1, kmid1, k_any);
-      const bool fast = fast_q && (__ballot((k_any & 0x00FF0000u) != 0) == 0);
-      // keep the sub-tiles and row tiles in sequence: interleaving them all
-      // needs more registers than two waves per SIMD have
-      __builtin_amdgcn_sched_barrier(0);
-      if (fast) {
+      for (int st = 0; st < kSub; ++st)
 #pragma unroll
-        for (int rt = 0; rt < kMaxRT; ++rt) {
-          if (rt >= NRT) break;
-          const v4i z = {0, 0, 0, 0};
-          v4i a0 = mfma8(qlo[rt][0], klo0, z);
-          a0 = mfma8(qlo[rt][1], klo1, a0);
-          v4i a1 = mfma8(qlo[rt][0], kmid0, z);
-          a1 = mfma8(qmid[rt][0], klo0, a1);
-          a1 = mfma8(qlo[rt][1], kmid1, a1);
-          a1 = mfma8(qmid[rt][1], klo1, a1);
-          v4i a2 = mfma8(qmid[rt][0], kmid0, z);
-          a2 = mfma8(qmid[rt][1], kmid1, a2);
-          const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
-          v4f pv;
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // each weighted term is bounded by sum |Mq||Mk| < 2^31: exact in int32
-            // |a1| < 2^22 and |a2| < 2^21 fit the signed 24-bit multiplier
-            const int32_t D = __mul24(a2[i], 16384) + __mul24(a1[i], 128) + a0[i];
-            const float r = (float)max(D, 0);
-            pv[i] = wv[i] * r;
+          for (int d = 0; d < 4; ++d) hot |= cur.k[st][hs][d] & (cur.k[st][hs][d] << 1);
+      const bool fast = fast_q && (__ballot((hot & 0x40404040u) != 0) == 0);
+      const int itn = it + n_slices;
+      // sequential head fold of one half: lane e folds entry e of this chunk
+      float s = 0.0f;
+      auto fold_half = [&](int hh) {
+        // the fold reads what other lanes of this wave wrote
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < kChunk) {
+          const float* frow = &my_fold[lane * kFoldStride];
+          const int nh = min(kPassHeads, HI - kPassHeads * hh);
+          for (int h = 0; h < nh; h += 4) {
+            const v4f v = *reinterpret_cast<const v4f*>(frow + h);
+            s = s + v[0];
+            s = s + v[1];
+            s = s + v[2];
+            s = s + v[3];
           }
-          *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rt * 16 + 4 * g]) = pv;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+      };
+      if (fast) {
+        // ---- decode the chunk's keys into lo / mid limb planes
+        v4i klo[kSub][2], kmid[kSub][2];
+        uint32_t unused = 0;
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+          // one sub-tile at a time: issuing all 128 lookups at once would
+          // hold 128 address / result registers
+          __builtin_amdgcn_sched_barrier(0);
+          limbs2(lut_bytes, lane4, cur.k[st][0], klo[st][0], kmid[st][0], unused);
+          limbs2(lut_bytes, lane4, cur.k[st][1], klo[st][1], kmid[st][1], unused);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the next chunk of this wave (possibly in the next row) streams into
+        // the now free key registers while this one is scored
+        if (itn < it1) {
+          RowCtx rn;
+          row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
+          load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, cur);
+        }
+#pragma unroll
+        for (int hh = 0; hh < kMaxRT / kPassRT; ++hh) {
+          if (hh >= n_pass) break;
+#pragma unroll
+          for (int st = 0; st < kSub; ++st) {
+#pragma unroll
+            for (int rl = 0; rl < kPassRT; ++rl) {
+              const int rt = kPassRT * hh + rl;
+              if (rt >= NRT) break;
+              // keep the tiles in sequence: interleaving them needs more
+              // registers than two waves per SIMD have
+              __builtin_amdgcn_sched_barrier(0);
+              const v4i z = {0, 0, 0, 0};
+              v4i a0 = mfma8(qlo[rt][0], klo[st][0], z);
+              a0 = mfma8(qlo[rt][1], klo[st][1], a0);
+              v4i a1 = mfma8(qlo[rt][0], kmid[st][0], z);
+              a1 = mfma8(qmid[rt][0], klo[st][0], a1);
+              a1 = mfma8(qlo[rt][1], kmid[st][1], a1);
+              a1 = mfma8(qmid[rt][1], klo[st][1], a1);
+              v4i a2 = mfma8(qmid[rt][0], kmid[st][0], z);
+              a2 = mfma8(qmid[rt][1], kmid[st][1], a2);
+              const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
+              v4f pv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                // every weighted term is bounded by sum |Mq||Mk| < 2^31: exact in int32
+                const uint32_t t = (uint32_t)a1[i] + ((uint32_t)a2[i] << 7);
+                const int32_t D = (int32_t)((uint32_t)a0[i] + (t << 7));
+                const float r = (float)max(D, 0);
+                pv[i] = wv[i] * r;
+              }
+              *reinterpret_cast<v4f*>(fold_w + (st * 16 * kFoldStride + rl * 16)) = pv;
+            }
+          }
+          fold_half(hh);
         }
       } else {
-        // general path: three limb planes on both sides, exact binary64 recombination
-        for (int rt = 0; rt < NRT; ++rt) {
-          const int h = rt * 16 + col;
-          const v4i z = {0, 0, 0, 0};
-          v4i acc[5] = {z, z, z, z, z};
-          for (int s2 = 0; s2 < 2; ++s2) {
-            v4u qc = {0, 0, 0, 0};
-            if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g)[4 * s2];
-            v4i ql, qm, qt, kl, km, kt;
-            limbs3(lut_bytes, lane4, qc, ql, qm, qt);
-            limbs3(lut_bytes, lane4, cur.k[st][s2], kl, km, kt);
-            acc[0] = mfma8(ql, kl, acc[0]);
-            acc[1] = mfma8(ql, km, acc[1]);
-            acc[1] = mfma8(qm, kl, acc[1]);
-            acc[2] = mfma8(ql, kt, acc[2]);
-            acc[2] = mfma8(qm, km, acc[2]);
-            acc[2] = mfma8(qt, kl, acc[2]);
-            acc[3] = mfma8(qm, kt, acc[3]);
-            acc[3] = mfma8(qt, km, acc[3]);
-            acc[4] = mfma8(qt, kt, acc[4]);
-          }
-          const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
-          v4f pv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // every term and the sum are integers below 2^53: exact, one rounding
-            const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
-                             (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
-            const float f = (float)D;
-            pv[i] = wv[i] * (f > 0.0f ? f : 0.0f);
-          }
-          *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rt * 16 + 4 * g]) = pv;
+        // rare: scored after the main loop, out of this loop's registers
+        my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
+        if (itn < it1) {
+          RowCtx rn;
+          row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
+          load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, cur);
         }
       }
+
+      if (fast) emit_chunk<POOL>(a, rc, chunk, s);
+      ++k_seq;
     }
-    // the fold reads what other lanes of this wave wrote
+  }
+
+  // ---- deferred chunks: general exact path
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int k = 0; k < k_seq; ++k) {
+    if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
+    const int itk = it0 + slice + k * n_slices;
+    RowCtx rk;
+    row_ctx<POOL>(a, itk / a.chunks_per_row, t_full, rk);
+    const int64_t qrow_k = ((int64_t)rk.b * a.T + rk.t) * HI;
+    my_w[lane] = lane < HI ? a.w[qrow_k + lane] * 0x1p-18f : 0.0f;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
-    // ---- sequential head fold: lane e < 32 folds entry e of this chunk
-    float s = 0.0f;
-    if (lane < kChunk) {
-      const float* frow = &my_fold[lane * kFoldStride];
-      for (int h = 0; h < HI; h += 4) {
-        const v4f v = *reinterpret_cast<const v4f*>(frow + h);
-        s = s + v[0];
-        s = s + v[1];
-        s = s + v[2];
-        s = s + v[3];
-      }
-    }
+    const int chunk = itk % a.chunks_per_row;
+    const float s = general_chunk<POOL>(a, rk, chunk, qrow_k, lut_bytes, my_fold, my_w);
+    emit_chunk<POOL>(a, rk, chunk, s);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
-    const int p = chunk * kChunk + lane;
-    bool valid;
-    if (POOL) {
-      valid = lane < kChunk && entry_of<POOL>(a, rc, p) >= 0;
-    } else {
-      const int j0 = chunk * kChunk;
-      const bool page_ok = j0 < rc.n && phys_page(a.page_table, a.max_pages, a.n_pages, rc.b, j0 >> 6) >= 0;
-      valid = lane < kChunk && page_ok && p < rc.n;
-    }
-    float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
-                                     (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
-    if (lane < kChunk && p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);  // NaN: key 0
-    if (!POOL) {
-      // block maxima over the visible entries of blocks of 8
-      float m = valid ? s : -__builtin_inff();
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      if (lane < kChunk && (lane & 7) == 0 && p < rc.n_pos) {
-        a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] =
-            (m == -__builtin_inff()) ? u2f(0xFFFFFFFFu) : m;
-      }
-    }
-    cur = nxt;
-    }
   }
 }
 
@@ -899,6 +1029,8 @@ int persistent_grid(int total_chunks, int T, int* chunks_per_wg) {
   const int slices = csa2::kWaves / T;
   int per = (total_chunks + n_cu - 1) / n_cu;
   per = ((per + slices - 1) / slices) * slices;  // whole rounds of the waves
+  // each wave tracks at most kMaxWaveChunks chunks; beyond that, more workgroups
+  per = std::min(per, csa2::kMaxWaveChunks * slices);
   *chunks_per_wg = per;
   return (total_chunks + per - 1) / per;
 }
