@@ -567,53 +567,63 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------- selection
+//
+// One workgroup per (b, t) row.  Keys are order-preserving uint32 images of
+// the scores (key 0 = empty); thread t owns list positions t + 1024 r, so
+// every load instruction of a wave covers 64 consecutive positions and the
+// position order of a wave's keys for one r is the order of its lanes (ballot
+// masks give ranks).
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;     // 2,048: 32 per lane of one wave
 constexpr int kHistCopies = 4;
+constexpr int kCandCap = 2048;             // candidates of the one-wave exact stage (32 per lane)
+constexpr int kMaxKPT = 32;
 
-constexpr int kCandCap = 4096;            // candidates kept for the single-wave exact stage
-
+// hist, sub, cand and mask are contiguous (64 KB): between the two
+// selections of a Full-mode row they hold the 16,384 staged keys.
 struct SelShared {
-  uint32_t hist[kHistCopies][kBins];
-  uint32_t cand_key[kCandCap];
-  int cand_pos[kCandCap];
+  uint32_t hist[kHistCopies][kBins];  // level-1 sample histogram; radix fallback
+  uint32_t sub[2][kBins];             // level-2 histograms of the bracket's end bins; exact stage
+  uint32_t cand[kCandCap];
+  uint64_t mask[kMaxKPT * kSelWaves][2];  // per (r, wave): ballots of keys above / equal to tau
   int wave_tot[kSelWaves];
-  uint32_t wave_min[kSelWaves], wave_max[kSelWaves];
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
+static_assert(offsetof(SelShared, wave_tot) == 65536, "staging area layout");
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trip).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)v), 63);
+}
 
 // Exclusive prefix sum over the workgroup in thread order; returns the
 // thread's offset and writes the total to *total.
 __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) sh.wave_tot[wave] = x;
   __syncthreads();
-  // lanes 0..15 hold the wave totals: one read, then an in-register scan
-  int wt = lane < kSelWaves ? sh.wave_tot[lane] : 0;
-#pragma unroll
-  for (int o = 1; o < kSelWaves; o <<= 1) {
-    const int y = __shfl_up(wt, o);
-    if (lane >= o) wt += y;
-  }
-  const int before = wave > 0 ? __shfl(wt, wave - 1) : 0;
-  *total = __shfl(wt, kSelWaves - 1);
+  // lanes 0..15 hold the wave totals: one read, then a scan in registers
+  const int wt = (int)wave_incl_scan(lane < kSelWaves ? (uint32_t)sh.wave_tot[lane] : 0u);
+  const int before = wave > 0 ? __builtin_amdgcn_readlane(wt, wave - 1) : 0;
+  *total = __builtin_amdgcn_readlane(wt, kSelWaves - 1);
   __syncthreads();
   return before + x - v;
-}
-
-// Zero the 4-copy histogram (all threads), no barrier.
-__device__ __forceinline__ void hist_zero(SelShared& sh) {
-  for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
-    reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
 }
 
 // One wave: merge the 4 copies of the 32 bins lane l owns (bins
@@ -634,296 +644,308 @@ __device__ __forceinline__ uint32_t wave_merge_bins(SelShared& sh, int lane) {
   return sum;
 }
 
-// Top-K selection among keys held KPT per thread (thread i owns list
-// positions [i*KPT, i*KPT + KPT)), order (key desc, position asc); key 0
-// marks an empty slot.  Calls emit(rank, pos) for every selected position,
-// in ascending position order, and returns the number selected.
+// One wave, histogram h of 2,048 bins (lane l owns bins [2048 - 32(l+1),
+// 2048 - 32l)), `above` samples lie above all of them.  For the rank x
+// (counted from the top, 1-based, real-valued) returns the bin holding it
+// (-1 if x is beyond the last bin) and writes the count above that bin.
+__device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t sum, uint32_t above0, float x,
+                                             uint32_t* above_bin, int lane) {
+  const uint32_t incl = wave_incl_scan(sum);
+  uint32_t above = above0 + incl - sum;
+  int bin = -1;
+  uint32_t ab = 0;
+  const v4u* hv = reinterpret_cast<const v4u*>(h + kBins - 32 * (lane + 1));
+  for (int q = 7; q >= 0; --q) {
+    const v4u v = hv[q];
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      const float prev = (float)above;
+      above += v[e];
+      if ((float)above >= x && prev < x) {
+        bin = kBins - 32 * (lane + 1) + 4 * q + e;
+        ab = above - v[e];
+      }
+    }
+  }
+  // at most one lane found the crossing
+  const uint64_t who = __ballot(bin >= 0);
+  if (who == 0) {
+    *above_bin = 0;
+    return -1;
+  }
+  const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(who));
+  *above_bin = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+  return __builtin_amdgcn_readlane(bin, src);
+}
+
+// Top-K selection among the keys of the list (thread t holds positions
+// t + 1024 r), order (key desc, position asc); key 0 marks an empty slot.
+// Calls emit(rank, pos) for every selected position (rank = place in
+// ascending position order) and returns the number selected.
 //
-// 1. Block min/max and valid count; digits are the 11 bits below the
-//    leading bits all keys share.
-// 2. A histogram of every 8th key brackets the digit range [d_lo, d_hi]
-//    that holds the K-th largest key.
-// 3. One pass counts the keys above the bracket and compacts the keys inside
-//    it (in position order) into LDS.  If the bracket does not hold the K-th
-//    key, or holds too many keys, a block-wide radix select runs instead.
-// 4. One wave finds the exact threshold among the candidates.
-// 5. Every key above the threshold is taken, and the first keys (in
-//    position order) equal to it up to K.
+// 1. Valid count, and a histogram of a fixed 1/8 (KPT = 32) or 1/4 sample of
+//    the keys on their top 11 bits.
+// 2. The sample ranks K*n_s/n +- (3 sqrt + 8) give the two end bins of a
+//    bracket; a second sample histogram on the next 11 bits inside those bins
+//    narrows it to 22-bit key prefixes [lo_key, hi_key].
+// 3. One pass counts the keys above the bracket (A) and inside it (C) and
+//    compacts the inside keys into LDS.  If A < K <= A + C and C is small,
+//    one wave finds the exact threshold tau among them with an 8-bit radix
+//    select held in registers; otherwise a block-wide radix select over all
+//    keys runs (never needed for exactness, only as the fallback).
+// 4. Emission: every key above tau, and the first keys (in position order)
+//    equal to tau up to K; ranks come from ballot masks and a prefix over
+//    the (r, wave) words.
 template <int KPT, typename Emit>
 __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit emit) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  static_assert(KPT <= kMaxKPT, "keys per thread");
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  constexpr int kSampleEvery = KPT >= 32 ? 8 : 4;  // sample r with r % kSampleEvery == wave % kSampleEvery
+  const int rs = wave % kSampleEvery;
+
+  // ---- 1. valid count and level-1 sample histogram
+  for (int i = threadIdx.x; i < (kHistCopies + 2) * kBins / 4; i += kSelThreads)
+    reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};  // hist and sub are contiguous
+  __syncthreads();
   int valid = 0;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const uint32_t k = key[r];
     valid += k != 0;
-    if (k != 0) {
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
-    }
+    if ((r % kSampleEvery) == rs && k != 0) atomicAdd(&sh.hist[lane & 3][k >> 21], 1u);
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
-  if (lane == 0) {
-    sh.wave_min[wave] = kmin;
-    sh.wave_max[wave] = kmax;
-  }
-  int n_valid;
-  (void)block_excl_scan(valid, sh, &n_valid);  // its barriers also publish wave_min/max
-  {
-    uint32_t m0 = lane < kSelWaves ? sh.wave_min[lane] : 0xFFFFFFFFu;
-    uint32_t m1 = lane < kSelWaves ? sh.wave_max[lane] : 0u;
-#pragma unroll
-    for (int o = 1; o < kSelWaves; o <<= 1) {
-      m0 = min(m0, (uint32_t)__shfl_xor((int)m0, o));
-      m1 = max(m1, (uint32_t)__shfl_xor((int)m1, o));
-    }
-    kmin = (uint32_t)__shfl((int)m0, 0);
-    kmax = (uint32_t)__shfl((int)m1, 0);
-  }
-  uint32_t tau = 1;             // select all valid keys (every real key is >= 1)
-  int need_eq = 0x7FFFFFFF;
+  valid = wave_sum(valid);
+  if (lane == 0) sh.wave_tot[wave] = valid;
+  __syncthreads();
+  int n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
+
+  uint32_t tau = 0;   // with tau = 0 every valid key is selected
+  int need_eq = 0;
   if (n_valid > K) {
-    const uint32_t diff = kmin ^ kmax;
-    if (diff == 0) {
-      tau = kmin;
-      need_eq = K;
-    } else {
-      const int top = 31 - __builtin_clz(diff);  // highest bit where keys differ
-      const int shift1 = max(top + 1 - kDigitBits, 0);
-      // ---- 2. sample histogram
-      constexpr int kStride = KPT >= 16 ? 8 : 4;
-      hist_zero(sh);
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < KPT; r += kStride) {
-        const uint32_t k = key[r];
-        if (k != 0) atomicAdd(&sh.hist[lane & 3][(k >> shift1) & (kBins - 1)], 1u);
+    // ---- 2. bracket from the sample: level 1 (bits 31..21)
+    if (wave == 0) {
+      const uint32_t sum = wave_merge_bins(sh, lane);
+      const uint32_t n_s = (uint32_t)wave_sum((int)sum);
+      const float ts = (float)K * (float)n_s / (float)n_valid;  // expected sample rank of the K-th key
+      const float m = 3.0f * sqrtf(ts) + 8.0f;
+      const float x_hi = ts - m, x_lo = ts + m;
+      uint32_t ab_hi = 0, ab_lo = 0;
+      const int b_hi = x_hi <= 0.0f ? -2 : wave_crossing(sh.hist[0], sum, 0, x_hi, &ab_hi, lane);
+      const int b_lo = wave_crossing(sh.hist[0], sum, 0, x_lo, &ab_lo, lane);
+      if (lane == 0) {
+        sh.misc[0] = b_hi;  // < 0: no upper cut
+        sh.misc[1] = b_lo;  // < 0: the lower cut lies below every sample
+        sh.misc[2] = __float_as_int(x_hi - (float)ab_hi);
+        sh.misc[3] = __float_as_int(x_lo - (float)ab_lo);
       }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const uint32_t sum = wave_merge_bins(sh, lane);
-        uint32_t incl = sum;
+    }
+    __syncthreads();
+    const int b_hi = sh.misc[0], b_lo = sh.misc[1];
+    // ---- level 2: bits 20..10 of the samples inside the end bins
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
-        const float n_s = (float)__shfl((int)incl, 63);
-        const float ts = (float)K * n_s / (float)n_valid;          // expected sample rank
-        const float m = 3.0f * sqrtf(ts) + 8.0f;                   // margin, in samples
-        const float hi_cut = ts - m, lo_cut = ts + m;
-        // C(d) = samples with digit >= d; walk bins from high to low digits
-        uint32_t above = incl - sum;
-        int d_hi = -1, d_lo = -1;
-        const v4u* h0 = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
-        for (int q = 7; q >= 0; --q) {
-          const v4u v = h0[q];
+    for (int r = 0; r < KPT; ++r) {
+      const uint32_t k = key[r];
+      if ((r % kSampleEvery) != rs || k == 0) continue;
+      const int d1 = (int)(k >> 21);
+      const uint32_t d2 = (k >> 10) & (kBins - 1);
+      if (d1 == b_hi) atomicAdd(&sh.sub[0][d2], 1u);
+      else if (d1 == b_lo) atomicAdd(&sh.sub[1][d2], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t hi_key = 0xFFFFFFFFu, lo_key = 1u;
+      if (b_hi >= 0) {
+        uint32_t sum = 0;
+        const v4u* hv = reinterpret_cast<const v4u*>(&sh.sub[0][kBins - 32 * (lane + 1)]);
 #pragma unroll
-          for (int e = 3; e >= 0; --e) {
-            const int bin = kBins - 32 * (lane + 1) + 4 * q + e;
-            const float c_prev = (float)above;   // samples with digit > bin
-            above += v[e];
-            const float c_here = (float)above;   // samples with digit >= bin
-            if (c_here >= hi_cut && c_prev < hi_cut) d_hi = bin;
-            if (c_here >= lo_cut && c_prev < lo_cut) d_lo = bin;
-          }
-        }
-        // the crossing bins are unique across lanes; unset means "not reached"
-        int dh = d_hi, dl = d_lo;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          dh = max(dh, __shfl_xor(dh, o));
-          dl = max(dl, __shfl_xor(dl, o));
-        }
-        if (lane == 0) {
-          sh.misc[0] = dh < 0 ? kBins - 1 : dh;  // hi_cut <= 0: everything above the top bin
-          sh.misc[1] = dl < 0 ? 0 : dl;          // lo_cut beyond all samples: down to digit 0
-        }
+        for (int q = 0; q < 8; ++q) sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
+        uint32_t ab;
+        int s = wave_crossing(sh.sub[0], sum, 0, __int_as_float(sh.misc[2]), &ab, lane);
+        if (s < 0) s = kBins - 1;  // cannot happen (the bin holds the rank); keep the cut conservative
+        hi_key = ((uint32_t)b_hi << 21) | ((uint32_t)s << 10) | 0x3FFu;
       }
-      __syncthreads();
-      const uint32_t d_hi = (uint32_t)sh.misc[0];
-      const uint32_t d_lo = min((uint32_t)sh.misc[1], d_hi);
-      // ---- 3. exact counts around the bracket
-      int n_above = 0, n_cand = 0;
+      if (b_lo >= 0) {
+        const uint32_t* h = sh.sub[b_lo == b_hi ? 0 : 1];
+        uint32_t sum = 0;
+        const v4u* hv = reinterpret_cast<const v4u*>(h + kBins - 32 * (lane + 1));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
+        uint32_t ab;
+        int s = wave_crossing(h, sum, 0, __int_as_float(sh.misc[3]), &ab, lane);
+        if (s < 0) s = 0;  // cannot happen; keep the cut conservative
+        lo_key = max(((uint32_t)b_lo << 21) | ((uint32_t)s << 10), 1u);
+      }
+      if (lane == 0) {
+        sh.misc[4] = (int)hi_key;
+        sh.misc[5] = (int)lo_key;
+      }
+    }
+    __syncthreads();
+    const uint32_t hi_key = (uint32_t)sh.misc[4];
+    const uint32_t lo_key = min((uint32_t)sh.misc[5], hi_key);
+    // ---- 3. exact counts around the bracket and candidate compaction
+    int n_above = 0, n_in = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const uint32_t k = key[r];
+      n_above += k > hi_key;
+      n_in += k >= lo_key && k <= hi_key;  // lo_key >= 1 excludes empty slots
+    }
+    int tot;
+    const int packed_off = block_excl_scan(n_above | (n_in << 16), sh, &tot);
+    // both counts are at most 32,768: the halves never carry; decode unsigned
+    const int A = tot & 0xFFFF, C = (int)((uint32_t)tot >> 16);
+    if (A < K && K <= A + C && C <= kCandCap) {
+      int o = (int)((uint32_t)packed_off >> 16);
 #pragma unroll
       for (int r = 0; r < KPT; ++r) {
         const uint32_t k = key[r];
-        const uint32_t d = (k >> shift1) & (kBins - 1);
-        n_above += k != 0 && d > d_hi;
-        n_cand += k != 0 && d <= d_hi && d >= d_lo;
+        if (k >= lo_key && k <= hi_key) sh.cand[o++] = k;
       }
-      int tot;
-      const int packed_off = block_excl_scan(n_above | (n_cand << 16), sh, &tot);
-      // both counts are at most 32,768, so the 16-bit halves never carry;
-      // the high half can reach bit 31, hence the unsigned decode
-      const int A = tot & 0xFFFF, C = (int)((uint32_t)tot >> 16);
-      const bool fast = A < K && K <= A + C && C <= kCandCap;
-      if (fast) {
-        int o = (int)((uint32_t)packed_off >> 16);
-        const int base = threadIdx.x * KPT;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-          const uint32_t k = key[r];
-          const uint32_t d = (k >> shift1) & (kBins - 1);
-          if (k != 0 && d <= d_hi && d >= d_lo) {
-            sh.cand_key[o] = k;
-            sh.cand_pos[o] = base + r;
-            ++o;
-          }
-        }
-        __syncthreads();
-        // ---- 4. one wave: rank R = K - A among the C candidates
-        if (threadIdx.x < 64) {
-          uint32_t prefix = 0, msk = 0;
-          int rem = K - A;
-          for (int sh8 = 24; sh8 >= 0; sh8 -= 8) {
-            // 256-bin histogram in copy 0, built by this wave only
-            for (int i = lane; i < 256; i += 64) sh.hist[0][i] = 0;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            for (int i = lane; i < C; i += 64) {
-              const uint32_t k = sh.cand_key[i];
-              if ((k & msk) == prefix) atomicAdd(&sh.hist[0][(k >> sh8) & 255u], 1u);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            // lane l owns bins 255-4l .. 252-4l
-            uint32_t cc[4], sum = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              cc[e] = sh.hist[0][255 - 4 * lane - e];
-              sum += cc[e];
-            }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int o2 = 1; o2 < 64; o2 <<= 1) {
-              const uint32_t y = __shfl_up(incl, o2);
-              if (lane >= o2) incl += y;
-            }
-            uint32_t above = incl - sum;
-            int dsel = -1, asel = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if ((uint32_t)rem > above && (uint32_t)rem <= above + cc[e]) {
-                dsel = 255 - 4 * lane - e;
-                asel = (int)above;
-              }
-              above += cc[e];
-            }
-            int dd = dsel, aa = asel;
-#pragma unroll
-            for (int o2 = 1; o2 < 64; o2 <<= 1) {
-              const int od = __shfl_xor(dd, o2), oa = __shfl_xor(aa, o2);
-              if (od > dd) {
-                dd = od;
-                aa = oa;
-              }
-            }
-            prefix |= (uint32_t)dd << sh8;
-            msk |= 255u << sh8;
-            rem -= aa;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-          }
-          if (lane == 0) {
-            sh.misc[2] = (int)prefix;
-            sh.misc[3] = rem;
-          }
-        }
-        __syncthreads();
-        tau = (uint32_t)sh.misc[2];
-        need_eq = sh.misc[3];
-      } else {
-        // ---- fallback: block-wide radix select over all keys
-        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);
-        uint32_t prefix = kmin & mask;
-        int rem = K;
-        int shift = top + 1;
-        while (shift > 0) {
+      __syncthreads();
+      if (wave == 0) {
+        // ---- one wave: the (K - A)-th largest candidate, 8-bit digits below
+        // the common prefix of lo_key and hi_key
+        // candidates are re-read from LDS on every pass, 8 per lane at a time
+        constexpr int kCPL = kCandCap / 64;
+        constexpr int kGroup = 8;
+        const uint32_t diff = lo_key ^ hi_key;
+        const int top = diff == 0 ? -1 : 31 - __builtin_clz(diff);
+        uint32_t msk = top >= 31 ? 0u : ~((2u << top) - 1u);
+        if (top < 0) msk = 0xFFFFFFFFu;
+        uint32_t prefix = hi_key & msk;
+        int rem = K - A;
+        uint32_t* bins = sh.sub[0];
+        for (int shift = top + 1; shift > 0;) {
           const int width = min(kDigitBits, shift);
           shift -= width;
           const uint32_t dmask = (1u << width) - 1u;
-          hist_zero(sh);
-          __syncthreads();
+          v4u* mine = reinterpret_cast<v4u*>(bins + kBins - 32 * (lane + 1));
 #pragma unroll
-          for (int r = 0; r < KPT; ++r) {
-            const uint32_t k = key[r];
-            if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
-          }
-          __syncthreads();
-          if (threadIdx.x < 64) {
-            const uint32_t sum = wave_merge_bins(sh, lane);
-            uint32_t incl = sum;
+          for (int q = 0; q < 8; ++q) mine[q] = v4u{0u, 0u, 0u, 0u};
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          for (int j0 = 0; j0 < kCPL; j0 += kGroup) {
+            if (j0 * 64 >= C) break;
+            uint32_t c[kGroup];
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-              const uint32_t y = __shfl_up(incl, o);
-              if (lane >= o) incl += y;
+            for (int j = 0; j < kGroup; ++j) {
+              const int idx = (j0 + j) * 64 + lane;
+              c[j] = idx < C ? sh.cand[idx] : 0u;
             }
-            uint32_t above = incl - sum;
-            if (above < (uint32_t)rem && (uint32_t)rem <= incl) {
-              const v4u* h0 = reinterpret_cast<const v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
-              for (int q = 7; q >= 0; --q) {
-                const v4u v = h0[q];
 #pragma unroll
-                for (int e = 3; e >= 0; --e) {
-                  if ((uint32_t)rem > above && (uint32_t)rem <= above + v[e]) {
-                    sh.misc[0] = kBins - 32 * (lane + 1) + 4 * q + e;
-                    sh.misc[1] = (int)above;
-                  }
-                  above += v[e];
-                }
-              }
-            }
+            for (int j = 0; j < kGroup; ++j)
+              if (c[j] != 0u && (c[j] & msk) == prefix) atomicAdd(&bins[(c[j] >> shift) & dmask], 1u);
           }
-          __syncthreads();
-          const uint32_t d = (uint32_t)sh.misc[0];
-          rem -= sh.misc[1];
-          prefix |= d << shift;
-          mask |= dmask << shift;
-          __syncthreads();
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          uint32_t sum = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) sum += mine[q][0] + mine[q][1] + mine[q][2] + mine[q][3];
+          uint32_t ab;
+          // the rank lies in exactly one bin
+          const int d = wave_crossing(bins, sum, 0, (float)rem, &ab, lane);
+          prefix |= (uint32_t)d << shift;
+          msk |= dmask << shift;
+          rem -= (int)ab;
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          __builtin_amdgcn_wave_barrier();
         }
-        tau = prefix;
-        need_eq = rem;
+        if (lane == 0) {
+          sh.misc[6] = (int)prefix;
+          sh.misc[7] = rem;
+        }
       }
+      __syncthreads();
+      tau = (uint32_t)sh.misc[6];
+      need_eq = sh.misc[7];
+    } else {
+      // ---- fallback: block-wide radix select over all keys (32 = 11 + 11 + 10 bits)
+      uint32_t prefix = 0, mask = 0;
+      int rem = K;
+      int shift = 32;
+      while (shift > 0) {
+        const int width = min(kDigitBits, shift);
+        shift -= width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
+          reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+          const uint32_t k = key[r];
+          if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t sum = wave_merge_bins(sh, lane);
+          uint32_t ab;
+          const int d = wave_crossing(sh.hist[0], sum, 0, (float)rem, &ab, lane);
+          if (lane == 0) {
+            sh.misc[0] = d;
+            sh.misc[1] = (int)ab;
+          }
+        }
+        __syncthreads();
+        const uint32_t d = (uint32_t)sh.misc[0];
+        rem -= sh.misc[1];
+        prefix |= d << shift;
+        mask |= dmask << shift;
+        __syncthreads();
+      }
+      tau = prefix;
+      need_eq = rem;
     }
   }
-  // ---- 5. emit in position order: keys above tau, then the first need_eq equal to it
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    gt += key[r] != 0 && key[r] > tau;
-    eq += key[r] != 0 && key[r] == tau;
-  }
-  int tot2;
-  const int off2 = block_excl_scan(gt | (eq << 16), sh, &tot2);
-  const int gt_before = off2 & 0xFFFF, eq_before = (int)((uint32_t)off2 >> 16);
-  const int take_eq = max(0, min(eq, need_eq - eq_before));
-  int off = gt_before + min(eq_before, need_eq);
-  const int sel_tot = (tot2 & 0xFFFF) + min((int)((uint32_t)tot2 >> 16), need_eq);
-  int taken_eq = 0;
-  const int base = threadIdx.x * KPT;
+
+  // ---- 4. emit in position order.  Word i = (r, wave) covers positions
+  // [1024 r + 64 wave, +64); bit l of its masks is position + l.
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const uint32_t k = key[r];
-    bool sel = false;
-    if (k != 0 && k > tau) sel = true;
-    else if (k != 0 && k == tau && taken_eq < take_eq) {
-      sel = true;
-      ++taken_eq;
+    const uint64_t mg = __ballot(k > tau);
+    const uint64_t me = __ballot(k != 0 && k == tau);
+    if (lane == 0) {
+      sh.mask[r * kSelWaves + wave][0] = mg;
+      sh.mask[r * kSelWaves + wave][1] = me;
     }
-    if (sel) emit(off++, base + r);
   }
-  return sel_tot;
+  __syncthreads();
+  constexpr int kWords = KPT * kSelWaves;
+  const int i = (int)threadIdx.x;
+  uint64_t mg = 0, me = 0;
+  if (i < kWords) {
+    mg = sh.mask[i][0];
+    me = sh.mask[i][1];
+  }
+  int tot2;
+  const int pre = block_excl_scan(__builtin_popcountll(mg) | (__builtin_popcountll(me) << 16), sh, &tot2);
+  // both totals are at most 32,768: no carry between the halves; decode unsigned
+  const int gt_tot = tot2 & 0xFFFF, eq_tot = (int)((uint32_t)tot2 >> 16);
+  if (i < kWords) {
+    const int gt_before = pre & 0xFFFF, eq_before = (int)((uint32_t)pre >> 16);
+    // the first (need_eq - eq_before) keys equal to tau, in position order
+    int take = min(max(need_eq - eq_before, 0), __builtin_popcountll(me));
+    uint64_t sel = mg, m = me;
+    for (; take > 0; --take) {
+      const uint64_t low = m & (~m + 1);
+      sel |= low;
+      m ^= low;
+    }
+    int rank = gt_before + min(eq_before, need_eq);
+    const int p0 = (i / kSelWaves) * kSelThreads + (i % kSelWaves) * 64;
+    while (sel != 0) {
+      emit(rank++, p0 + __builtin_ctzll(sel));
+      sel &= sel - 1;
+    }
+  }
+  return gt_tot + min(eq_tot, need_eq);
 }
 
 struct SelectArgs {
-  const float* s;        // full: [B][T][max_n]; reindex: [B][T][pool_blocks*8] (pool order)
-  const float* bm;       // full: [B][T][ceil(max_n/8)]
+  const float* s;        // full: [B][T][s_stride(max_n)]; reindex: [B][T][pool_blocks*8] (pool order)
+  const float* bm;       // full: [B][T][bm_stride(max_n)]
   const int32_t* n_entries;
   int max_n;
   int max_pages;
@@ -947,31 +969,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int b = row / a.T;
   int n = min(a.n_entries[b], min(a.max_n, a.max_pages * kPage));
   n = max(n, 0);
+  const int nb = (n + kBlock - 1) / kBlock;
   const int P = a.pool_blocks;
   int pool_n;
   if (FULL) {
-    const int nb = (n + kBlock - 1) / kBlock;
     const float* bm = a.bm + (int64_t)row * bm_stride(a.max_n);
     constexpr int KPT = 32;  // 32,768 blocks = 262,144 entries
+    // reads past the row's nb blocks return 0 and are masked: no branch per load
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)bm, 0, nb * 4, kBufferFlags);
     uint32_t key[KPT];
 #pragma unroll
-    for (int r4 = 0; r4 < KPT; r4 += 4) {
-      const int blk = threadIdx.x * KPT + r4;
-      v4f v = {0.f, 0.f, 0.f, 0.f};
-      if (blk + 3 < nb) v = *reinterpret_cast<const v4f*>(bm + blk);
-      else {
+    for (int r = 0; r < KPT; ++r) {
+      const int blk = r * kSelThreads + (int)threadIdx.x;
+      key[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)blk * 4u, 0, 0);
+    }
+    // consumed unconditionally (after all loads are issued), so the compiler
+    // cannot move each load into a branch of its own
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = blk + e < nb ? bm[blk + e] : 0.f;
-      }
+    for (int r = 0; r < KPT; ++r) asm volatile("" : "+v"(key[r]));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[r4 + e] = blk + e < nb ? score_key(v[e]) : 0u;
+    for (int r = 0; r < KPT; ++r) {
+      const int blk = r * kSelThreads + (int)threadIdx.x;
+      key[r] = blk < nb ? score_key(__uint_as_float(key[r])) : 0u;
     }
     for (int i = threadIdx.x; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
-    __syncthreads();
     pool_n = block_topk<KPT>(key, P, sh, [&](int rank, int pos) { sh.pool_blk[rank] = pos; });
     __syncthreads();
-    for (int i = threadIdx.x; i < P; i += kSelThreads)
-      a.out_pool[(int64_t)row * P + i] = sh.pool_blk[i];
+    for (int i = threadIdx.x; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = sh.pool_blk[i];
     if (threadIdx.x == 0) a.out_pool_n[row] = pool_n;
   } else {
     pool_n = max(0, min(a.pool_n_in[row], P));
@@ -979,29 +1003,51 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       sh.pool_blk[i] = i < pool_n ? a.pool_in[(int64_t)row * P + i] : -1;
     __syncthreads();
   }
-  // ---- top-k over the pool's positions (list position p = 8 * slot + i)
-  constexpr int KPT2 = 16;  // 2 pool slots per thread, 16,384 positions
-  uint32_t key2[KPT2];
+  // ---- top-k over the pool's positions (list position p = 8 * slot + e).
+  // The pool's 8-entry blocks are gathered with 16-byte loads (two slots per
+  // thread) and staged in LDS as keys in position order, over the selection
+  // buffers (free between the two selections).
+  constexpr int KPT2 = 16;  // 16,384 positions
   const float* srow = FULL ? a.s + (int64_t)row * s_stride(a.max_n) : a.s + (int64_t)row * P * kBlock;
+  const uint32_t row_bytes = FULL ? (uint32_t)s_stride(a.max_n) * 4u : (uint32_t)P * kBlock * 4u;
+  const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, row_bytes, kBufferFlags);
+  uint32_t* staged = &sh.hist[0][0];
+  {
+    v4u g[2][2];
+    int blk[2];
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const int slot = threadIdx.x * 2 + hs;
-    const int blk = slot < pool_n ? sh.pool_blk[slot] : -1;
-    const bool ok = blk >= 0 && blk < (n + kBlock - 1) / kBlock;
-    // the 8 scores of this slot: block blk's entries (Full) or the slot's
-    // pool-order scores (Reindex); both 32-byte aligned
-    v4f v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      const v4f* src = reinterpret_cast<const v4f*>(srow + (FULL ? blk * kBlock : slot * kBlock));
-      v0 = src[0];
-      v1 = src[1];
+    for (int hs = 0; hs < 2; ++hs) {
+      const int slot = (int)threadIdx.x + hs * kSelThreads;
+      blk[hs] = slot < pool_n ? sh.pool_blk[slot] : -1;
+      const bool ok = blk[hs] >= 0 && blk[hs] < nb;
+      // an offset past the row reads zeros (masked below)
+      const uint32_t off = ok ? (uint32_t)(FULL ? blk[hs] : slot) * kBlock * 4u : row_bytes;
+      g[hs][0] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+      g[hs][1] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off + 16u, 0, 0);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool in = ok && blk * kBlock + e < n;
-      key2[hs * 8 + e] = in ? score_key(e < 4 ? v0[e] : v1[e - 4]) : 0u;
+    for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(g[hs][0]), "+v"(g[hs][1]));
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const int slot = (int)threadIdx.x + hs * kSelThreads;
+      const bool ok = blk[hs] >= 0 && blk[hs] < nb;
+      v4u k0, k1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = e < 4 ? g[hs][0][e] : g[hs][1][e - 4];
+        const uint32_t k = (ok && blk[hs] * kBlock + e < n) ? score_key(__uint_as_float(bits)) : 0u;
+        if (e < 4) k0[e] = k;
+        else k1[e - 4] = k;
+      }
+      reinterpret_cast<v4u*>(staged)[2 * slot] = k0;
+      reinterpret_cast<v4u*>(staged)[2 * slot + 1] = k1;
     }
   }
+  __syncthreads();
+  uint32_t key2[KPT2];
+#pragma unroll
+  for (int r = 0; r < KPT2; ++r) key2[r] = staged[r * kSelThreads + (int)threadIdx.x];
+  __syncthreads();  // the selection below reuses the staging area
   int32_t* out = a.out_topk + (int64_t)row * a.topk;
   const int got = block_topk<KPT2>(key2, a.topk, sh, [&](int rank, int p) {
     out[rank] = sh.pool_blk[p >> 3] * kBlock + (p & 7);
