@@ -112,6 +112,7 @@ def main():
     ap.add_argument("--workload", default="full_1m_b4")
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (> 512 MB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path has no multi-GPU leg (asked for --gpus {args.gpus}).",
@@ -161,50 +162,89 @@ def main():
     ws_i, ws_a = csa2.Workspace(), csa2.Workspace()
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, strm):
         c = i % args.copies
-        csa2.quantize_kv(new_rows, new_slots, kvp[c], stream=stream)
+        csa2.quantize_kv(new_rows, new_slots, kvp[c], stream=strm)
         csa2.index_full(q_idx, w, kidx[c], pt, ne, wl.max_n, wl.topk, wl.pool_blocks, out_topk=out_topk,
-                        out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=stream)
-        csa2.sparse_attn(q, wl.sm_scale, kvp[c], pt, ne, out_topk, swa, out=out, ws=ws_a, stream=stream)
+                        out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=strm)
+        csa2.sparse_attn(q, wl.sm_scale, kvp[c], pt, ne, out_topk, swa, out=out, ws=ws_a, stream=strm)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, stream)
     torch.cuda.synchronize()
-
     ev = HipEvents()
+    ev.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    K = args.steps
+
+    # ---- pass 1: per-kernel durations (eager launches, event pair around each launch)
     kernels = {"score_full": csa2.K_SCORE_FULL, "select_full": csa2.K_SELECT_FULL,
                "attn_split": csa2.K_ATTN_SPLIT, "attn_combine": csa2.K_ATTN_COMBINE,
                "quantize": csa2.K_QUANTIZE}
-    K = args.steps
     pairs = {name: (ev.create(K), ev.create(K)) for name in kernels}
-    whole = ev.create(2)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    ev.rt.hipEventRecord(whole[0], ctypes.c_void_p(stream.cuda_stream))
     for i in range(K):
         for name, kid in kernels.items():
             csa2.lib().csa2_time_kernel(kid, pairs[name][0][i], pairs[name][1][i])
-        step(args.warmup + i)
-    ev.rt.hipEventRecord(whole[1], ctypes.c_void_p(stream.cuda_stream))
+        step(args.warmup + i, stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     for kid in kernels.values():
         csa2.lib().csa2_time_kernel(kid, None, None)
-    total_ms = ev.elapsed_ms(whole[0], whole[1])
     kern_us = {name: 1000.0 * float(np.mean([ev.elapsed_ms(a, b) for a, b in zip(*pairs[name])]))
                for name in kernels}
     for a, b in pairs.values():
         ev.destroy(a)
         ev.destroy(b)
+    eager_ref = out_topk.clone(), out.clone()
+
+    # ---- pass 2: whole steps, timed with one event pair around K steps
+    graphs = None
+    if not args.eager:
+        # one captured step per cache copy; the library makes no allocation or memset
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(args.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(c, torch.cuda.current_stream())
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        # a replay reproduces the eager step (same copy as the last eager step)
+        last = (args.warmup + K - 1) % args.copies
+        graphs[last].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_topk, eager_ref[0]) and torch.equal(out, eager_ref[1]), \
+            "graph replay differs from the eager step"
+        for i in range(args.warmup):
+            graphs[i % args.copies].replay()
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if graphs is not None:
+            graphs[i % args.copies].replay()
+        else:
+            step(i, stream)
+
+    whole = ev.create(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.rt.hipEventRecord(whole[0], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    for i in range(K):
+        run_step(i)
+    ev.rt.hipEventRecord(whole[1], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.elapsed_ms(whole[0], whole[1])
 
     ms_per_step = total_ms / K
     value = 1000.0 / ms_per_step
     nbytes = algorithmic_bytes(wl)
     scan_gbs = nbytes["scan"] / (kern_us["score_full"] * 1e-6) / 1e9
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    log(f"{K} steps: {ms_per_step * 1000:.1f} us/step (wall {wall / K * 1e6:.1f} us/step); kernels us: "
+    log(f"{K} steps ({'eager' if graphs is None else 'graph replay'}): {ms_per_step * 1000:.1f} us/step "
+        f"(wall {wall / K * 1e6:.1f} us/step); kernels us: "
         + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
 
     result = {
@@ -223,7 +263,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "query_tokens": T,
                    "context_tokens": int(wl.max_n) * 4, "entries_per_seq": int(wl.max_n),
                    "indexer_heads": wl.HI, "heads": H, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
-                   "cache_copies_rotated": args.copies},
+                   "cache_copies_rotated": args.copies,
+                   "launch": "eager" if graphs is None else "hip_graph_replay"},
         "hbm_tb_s": round(step_gbs / 1000.0, 3),
         "hbm_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": nbytes["step"],
