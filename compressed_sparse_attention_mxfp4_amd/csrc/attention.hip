@@ -22,10 +22,20 @@ namespace csa2 {
 constexpr int kAttnThreads = 256;
 constexpr int kRowsPerSplit = 128;
 constexpr int kSub = 32;               // rows per sub-chunk
-constexpr int kKrStride = 128 + 8;     // halves per row-major row (136 -> 68 dwords)
-constexpr int kKtStride = kSub + 4;    // halves per channel-major row (36 -> 18 dwords)
+constexpr int kRowHalves = 128;        // a wave's 128-channel slice of one row (256 B, 16 chunks of 16 B)
+
+// LDS tile of 32 rows x 128 fp16 channels, row-major, with 16-byte chunk k of
+// row r stored at chunk k ^ bitrev4(r & 15).  This one layout serves three
+// access patterns without bank conflicts: the dequant stores (16 B), the
+// Q.K operand loads (16 B, one row per lane) and the transposing P.V operand
+// loads (8 B, 4 rows x 4 channels per 16 lanes).
+__device__ __forceinline__ int swz(int row) { return (int)(__builtin_bitreverse32((uint32_t)row & 15u) >> 28); }
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // in halves
+  return row * kRowHalves + 8 * (chunk ^ swz(row));
+}
 
 typedef _Float16 half_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma16(v8h a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -91,10 +101,19 @@ struct AttnArgs {
   float* part_ml;  // [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
 };
 
+// Source of one row of a split: an FP4 entry (page base, entry in page) or
+// a window row (byte offset of the row), or nothing.
+struct RowSrc {
+  int64_t base;  // FP4: page byte offset; window: row byte offset; -1: absent
+  int kind;      // 0 absent, 1 FP4 entry (entry index in page in `e`), 2 window row
+  int e;
+};
+
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kKrStride];
-  __shared__ __attribute__((aligned(16))) half_t kt[4][128 * kKtStride];
+  __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
   __shared__ __attribute__((aligned(16))) v4f ssum[4][2][64];
+  __shared__ int64_t rbase[kRowsPerSplit];
+  __shared__ int rkind[kRowsPerSplit];
 
   const int split = blockIdx.x;
   const int ht = blockIdx.y;
@@ -106,6 +125,36 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   const int NHT = a.H >> 4;
   int n = a.n_entries[b];
   n = min(n, a.max_pages * kPage);
+
+  const int n_rows = a.topk + kSwa;
+  const int row0 = split * kRowsPerSplit;
+  const int row1 = min(n_rows, row0 + kRowsPerSplit);
+  const int32_t* idx_row = a.topk_idx + (int64_t)bt * a.topk;
+
+  // ---- resolve the split's rows once: FP4 entry address (index, page
+  // lookup) or window row; threads 0..127 take one row each
+  if (threadIdx.x < kRowsPerSplit) {
+    const int row = row0 + (int)threadIdx.x;
+    int64_t base = -1;
+    int kind = 0;
+    if (row < row1) {
+      if (row < a.topk) {
+        const int j = idx_row[row];
+        if (j >= 0 && j < n) {
+          const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, b, j >> 6);
+          if (pg >= 0) {
+            base = pg * kPageBytes + (int64_t)(j & 63);  // page offset + entry (low 6 bits)
+            kind = 1;
+          }
+        }
+      } else {
+        base = ((int64_t)b * (kSwa - 1 + a.T) + t + (row - a.topk)) * kD;
+        kind = 2;
+      }
+    }
+    rbase[threadIdx.x] = base;
+    rkind[threadIdx.x] = kind;
+  }
 
   // ---- Q slice as the B operand: head ht*16+col, channels 128*wave + 32*s + 8*g .. +8
   v8h qb[4];
@@ -122,11 +171,36 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
       }
     }
   }
+  __syncthreads();
 
-  const int n_rows = a.topk + kSwa;
-  const int row0 = split * kRowsPerSplit;
-  const int row1 = min(n_rows, row0 + kRowsPerSplit);
-  const int32_t* idx_row = a.topk_idx + (int64_t)bt * a.topk;
+  // ---- issue every code load of the split up front.  Lane (rg, cg) of
+  // wave w dequantizes rows 4*rg .. 4*rg+3 of each 32-row sub-chunk,
+  // channels 128*w + 16*cg .. +16: per row 8 code bytes + 1 scale byte
+  // (FP4) or 16 bytes (window).
+  const int rg = lane >> 3, cg = lane & 7;
+  const int ch0 = 128 * wave + 16 * cg;
+  constexpr int kSubs = kRowsPerSplit / kSub;  // 4
+  // Two unconditional 8-byte loads per row (no branch, so no load waits on
+  // another's destination registers): FP4 row -> 16 code nibbles and the
+  // dword holding the scale byte; window row -> its 16 FP8 codes; absent row
+  // -> the pool's first bytes, discarded.
+  v2u lo8[kSubs][4], hi8[kSubs][4];
+#pragma unroll
+  for (int sc = 0; sc < kSubs; ++sc)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = sc * kSub + 4 * rg + i;
+      const int kind = rkind[rr];
+      const int64_t base = rbase[rr];
+      const int64_t pgo = base & ~(int64_t)63;
+      const int e = (int)(base & 63);
+      const uint8_t* p0 = kind == 1 ? a.kv_pool + pgo + e * kEntryCodes + ch0 / 2
+                          : kind == 2 ? a.swa + base + ch0 : a.kv_pool;
+      const uint8_t* p1 = kind == 1 ? a.kv_pool + pgo + kPage * kEntryCodes + e * kEntryScales + (ch0 / 16 & ~3)
+                          : kind == 2 ? a.swa + base + ch0 + 8 : a.kv_pool;
+      lo8[sc][i] = *reinterpret_cast<const v2u*>(p0);
+      hi8[sc][i] = *reinterpret_cast<const v2u*>(p1);
+    }
 
   float m_run = -__builtin_inff();  // running max (log2 units) of head `col`
   float l_run = 0.0f;               // running sum of head `col`
@@ -135,63 +209,45 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   for (int c = 0; c < 8; ++c) o_acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   half_t* my_kr = kr[wave];
-  half_t* my_kt = kt[wave];
 
-  for (int sub = row0; sub < row1; sub += kSub) {
-    // ---- dequantize rows sub .. sub+31, channels 128*wave + 64*hc .. +64
-    const int r = lane & 31, hc = lane >> 5;
-    const int row = sub + r;
-    const int cbase = 128 * wave + 64 * hc;
-    half_t vals[64];
-    bool valid = false;
-    if (row < row1) {
-      if (row < a.topk) {
-        const int j = idx_row[row];
-        if (j >= 0 && j < n) {
-          const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, b, j >> 6);
-          if (pg >= 0) {
-            valid = true;
-            const uint8_t* base = a.kv_pool + pg * kPageBytes;
-            const uint8_t* cp = base + (j & 63) * kEntryCodes + cbase / 2;
-            const v4u c0 = *reinterpret_cast<const v4u*>(cp);
-            const v4u c1 = *reinterpret_cast<const v4u*>(cp + 16);
-            const uint32_t sc = *reinterpret_cast<const uint32_t*>(
-                base + kPage * kEntryCodes + (j & 63) * kEntryScales + cbase / 16);
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-              const uint32_t x = d < 4 ? c0[d] : c1[d - 4];
-              const _Float16 s256 = e4m3_div256_f16((sc >> (8 * (d >> 1))) & 0xFFu);
-              fp4x8_to_f16(x, s256, vals + 8 * d);
-            }
-          }
-        }
+  for (int sc = 0; sc < kSubs; ++sc) {
+    const int sub = row0 + sc * kSub;
+    if (sub >= row1) break;
+    // ---- dequantize: 4 rows x 16 channels (chunks 2cg, 2cg+1) per lane into
+    // the swizzled row-major tile; odd channel groups store their two chunks
+    // in the other order (keeps each store instruction conflict-free)
+    v8h rv[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kind = rkind[sc * kSub + 4 * rg + i];
+      half_t tmp[16];
+      if (kind == 1) {
+        const uint32_t scode = (hi8[sc][i][0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
+        const _Float16 s256 = e4m3_div256_f16(scode);
+        fp4x8_to_f16(lo8[sc][i][0], s256, tmp);
+        fp4x8_to_f16(lo8[sc][i][1], s256, tmp + 8);
       } else {
-        valid = true;
-        const uint8_t* sp = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t + (row - a.topk)) * kD + cbase;
+        // window row (kind 2), or absent (kind 0: decode zeros)
+        const bool w = kind == 2;
+        const uint32_t c4[4] = {w ? lo8[sc][i][0] : 0u, w ? lo8[sc][i][1] : 0u, w ? hi8[sc][i][0] : 0u,
+                                w ? hi8[sc][i][1] : 0u};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const v4u c = *reinterpret_cast<const v4u*>(sp + 16 * d);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fp8x4_to_f16(c[e], vals + 16 * d + 4 * e);
-        }
+        for (int d = 0; d < 4; ++d) fp8x4_to_f16(c4[d], tmp + 4 * d);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rv[i][0][e] = tmp[e];
+        rv[i][1][e] = tmp[8 + e];
+      }
+      const int odd = cg & 1;
+      const v8h first = odd ? rv[i][1] : rv[i][0];
+      const v8h second = odd ? rv[i][0] : rv[i][1];
+      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]) = first;
+      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]) = second;
     }
-    if (!valid) {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) vals[i] = (_Float16)0.0f;
-    }
-    const uint64_t vmask_all = __ballot(valid);
-    const uint32_t vmask = (uint32_t)vmask_all;  // bit r: row sub+r is present
-    // row-major and channel-major copies of this wave's slice
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v8h v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = vals[8 * i + e];
-      *reinterpret_cast<v8h*>(&my_kr[r * kKrStride + 64 * hc + 8 * i]) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) my_kt[(64 * hc + i) * kKtStride + r] = vals[i];
+    // bit r: row sub+r is present
+    const uint32_t vmask = (uint32_t)__ballot(lane < kSub && rkind[sc * kSub + (lane & (kSub - 1))] != 0);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
 
@@ -202,7 +258,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
       sacc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const v8h ka = *reinterpret_cast<const v8h*>(&my_kr[(rt * 16 + col) * kKrStride + 32 * s + 8 * g]);
+        const v8h ka = *reinterpret_cast<const v8h*>(&my_kr[tile_off(rt * 16 + col, 4 * s + g)]);
         sacc[rt] = mfma16(ka, qb[s], sacc[rt]);
       }
       ssum[wave][rt][lane] = sacc[rt];
@@ -257,12 +313,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
 
     // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128)
-    // P's K slice for lane l is rows {4g..4g+3, 16+4g..16+4g+3}; V matches it.
+    // P's K slice for lane (g, col) is rows {4g..4g+3, 16+4g..16+4g+3}.  The
+    // matching V column (channel 16c + col over those rows) comes from the
+    // row-major tile through the transposing LDS load: within each 16-lane
+    // group, lane i receives element i % 4 of the 4 halves that lane
+    // 4j + i / 4 points at, for j = 0..3.  Lane (g, col) therefore points at
+    // row 4g + col / 4 (+16), channels 16c + 4 (col % 4) .. +3.
+    const int tr_row = 4 * g + (col >> 2);
+    const int tq = col & 3;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const half_t* vt = &my_kt[(c * 16 + col) * kKtStride];
-      const v4h v0 = *reinterpret_cast<const v4h*>(vt + 4 * g);
-      const v4h v1 = *reinterpret_cast<const v4h*>(vt + 16 + 4 * g);
+      const half_t* p0 = &my_kr[tile_off(tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)];
+      const half_t* p1 = &my_kr[tile_off(16 + tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)];
+      const v4h v0 = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p0)));
+      const v4h v1 = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p1)));
       const v8h vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       o_acc[c] = mfma16(pa, vb, o_acc[c]);
     }
@@ -292,31 +358,47 @@ struct CombineArgs {
   float* out_lse;
 };
 
-// One workgroup per (b, t, h): merge the splits' (max, sum, output).
-__global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
+// One workgroup per (b, t, h), 128 threads of 4 channels: merge the splits'
+// (max, sum, output).  The split weights are formed once (one wave, in
+// registers), then every thread issues its loads for all splits together.
+constexpr int kMaxSplits = (CSA2_MAX_TOPK + CSA2_SWA + kRowsPerSplit - 1) / kRowsPerSplit;
+
+__global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
+  __shared__ float wsplit[kMaxSplits];
+  __shared__ float inv_l;
   const int h = blockIdx.x % a.H;
   const int bt = blockIdx.x / a.H;
   const int NHT = a.H >> 4, ht = h >> 4, hh = h & 15;
   const int64_t base = ((int64_t)bt * NHT + ht) * a.n_splits;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[(base + s) * 32 + hh]);
-  float L = 0.0f;
-  float acc0 = 0.0f, acc1 = 0.0f;
-  const int c = threadIdx.x * 2;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ms = a.part_ml[(base + s) * 32 + hh];
+  const int lane = lane_id();
+  if (threadIdx.x < 64) {
+    const bool in = lane < a.n_splits;
+    const float ms = in ? a.part_ml[(base + lane) * 32 + hh] : -__builtin_inff();
+    const float ls = in ? a.part_ml[(base + lane) * 32 + 16 + hh] : 0.0f;
+    float M = ms;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float wgt = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - M);
-    L += wgt * a.part_ml[(base + s) * 32 + 16 + hh];
-    const float* po = a.part_o + ((base + s) * 16 + hh) * kD;
-    acc0 += wgt * po[c];
-    acc1 += wgt * po[c + 1];
+    float L = wgt * ls;
+    // fixed-order sum over the splits (lane order)
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    if (in) wsplit[lane] = wgt;
+    if (lane == 0) {
+      inv_l = 1.0f / L;
+      if (a.out_lse) a.out_lse[(int64_t)bt * a.H + h] = (M + log2f(L)) * 0.69314718055994530942f;
+    }
   }
-  const float inv = 1.0f / L;
-  float* o = a.out + ((int64_t)bt * a.H + h) * kD;
-  o[c] = acc0 * inv;
-  o[c + 1] = acc1 * inv;
-  if (a.out_lse && threadIdx.x == 0)
-    a.out_lse[(int64_t)bt * a.H + h] = (M + log2f(L)) * 0.69314718055994530942f;
+  __syncthreads();
+  const int c = threadIdx.x * 4;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s >= a.n_splits) break;
+    const v4f po = *reinterpret_cast<const v4f*>(a.part_o + ((base + s) * 16 + hh) * kD + c);
+    acc += wsplit[s] * po;
+  }
+  *reinterpret_cast<v4f*>(a.out + ((int64_t)bt * a.H + h) * kD + c) = acc * inv_l;
 }
 
 }  // namespace csa2
@@ -375,7 +457,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   ca.n_splits = aa.n_splits;
   ca.out = out;
   ca.out_lse = out_lse;
-  CSA2_LAUNCH(CSA2_K_ATTN_COMBINE, csa2::attn_combine_kernel, dim3(B * T * H), dim3(256),
+  CSA2_LAUNCH(CSA2_K_ATTN_COMBINE, csa2::attn_combine_kernel, dim3(B * T * H), dim3(128),
               (hipStream_t)stream, ca);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

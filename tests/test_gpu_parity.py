@@ -324,3 +324,62 @@ def test_full_1m_b4_attention(oracle):
     ref_tk, _, _ = oracle_index_full(oracle, wl, L)
     out, lse = gpu_attention(wl, L, ref_tk, with_lse=True)
     check_attention(oracle, wl, L, ref_tk, out, lse=lse)
+
+
+def test_layer_step_graph_replays_match_eager(oracle):
+    """A captured layer step (cache write, Full indexer, attention) replayed
+    several times, with eager work and synchronizations between replays,
+    gives the eager results on every replay; the eager result itself is
+    checked against the oracle."""
+    say("HIP graph of a layer step: 3 replays vs eager, n = [20000, 3001]")
+    n = [20000, 3001]
+    wl = small_workload(n, T=2, HI=16, H=16, topk=256, seed=21)
+    L = wl.layers[0]
+    B, T, H = wl.B, wl.T, wl.H
+    kidx = dev(wl.kidx_pool)
+    pt, ne = dev(wl.paging.page_table), dev(wl.n_entries)
+    q_idx, w = dev(L.q_idx), dev(L.w)
+    q = dev(L.q.view(np.int16), torch.bfloat16)
+    swa = dev(L.swa)
+    slots = wl.paging.all_slots()
+    kv_pool = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(dev(wl.kv_source.view(np.int16), torch.bfloat16), dev(slots), kv_pool)
+    last = np.cumsum(wl.n_entries) - 1
+    rows = dev(wl.kv_source[last].view(np.int16), torch.bfloat16)
+    rslots = dev(slots[last])
+    out_topk = torch.empty((B, T, wl.topk), dtype=torch.int32, device="cuda")
+    out_pool = torch.empty((B, T, wl.pool_blocks), dtype=torch.int32, device="cuda")
+    out_pool_n = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T, H, 512), dtype=torch.float32, device="cuda")
+    ws_i, ws_a = csa2.Workspace(), csa2.Workspace()
+
+    def step(strm):
+        csa2.quantize_kv(rows, rslots, kv_pool, stream=strm)
+        csa2.index_full(q_idx, w, kidx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks, out_topk=out_topk,
+                        out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=strm)
+        csa2.sparse_attn(q, wl.sm_scale, kv_pool, pt, ne, out_topk, swa, out=out, ws=ws_a, stream=strm)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [host(x).copy() for x in (out_topk, out_pool, out_pool_n, out)]
+    r_tk, r_pool, r_pn = oracle_index_full(oracle, wl, L)
+    assert np.array_equal(ref[0], r_tk) and np.array_equal(ref[1], r_pool) and np.array_equal(ref[2], r_pn)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # eager work in between: scribble over the outputs, then replay
+        out_topk.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(x) for x in (out_topk, out_pool, out_pool_n, out)]
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), f"replay {rep} differs from the eager step"
