@@ -9,12 +9,14 @@
 //
 // Work split: one workgroup per (b, t, 16-head tile, 128-row split of the
 // row list [top-k slots | 128 window rows]); its 4 waves own 128 channels
-// each.  Per 32-row sub-chunk a wave dequantizes its channel slice into LDS
-// (row-major for Q.K, channel-major for P.V; FP4 and FP8 values are exact in
-// fp16), computes partial logits over its channels with f16 MFMA, the four
-// partials are summed in fixed order through LDS, and every wave runs the
-// same online softmax and accumulates P.V for its channels.  Splits write
-// (max, sum, unnormalised output) and a combine kernel merges them.
+// each.  The split's rows are resolved once (index, page) and all their code
+// bytes are loaded up front.  Per 32-row sub-chunk a wave converts its
+// channel slice to fp16 (hardware FP4 / E4M3 conversion, exact) into a
+// swizzled row-major LDS tile, computes partial logits over its channels
+// with f16 MFMA; the four partials are summed in fixed order through LDS,
+// every wave runs the same online softmax and accumulates P.V for its
+// channels, reading V transposed from the same tile.  Splits write (max,
+// sum, unnormalised output) and a combine kernel merges them.
 #include "common.h"
 
 namespace csa2 {
@@ -36,51 +38,26 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {  // in halves
 
 typedef _Float16 half_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48): each
+// permlane swap of a register with itself leaves the two values of a lane
+// pair in the two results, in the same order on both lanes.
+__device__ __forceinline__ float rows4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ v4f mfma16(v8h a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// E2M1 magnitude codes 0..7 as the high byte of fp16(256 * value); the low
-// byte of every such fp16 is zero, and code 0 (value 0) selects 0x00.
-// 256 * {0, .5, 1, 1.5, 2, 3, 4, 6} = {0, 128, 256, 384, 512, 768, 1024, 1536}.
-constexpr uint32_t kE2M1HiLo = 0x5E5C5800u;  // bytes for codes 0..3
-constexpr uint32_t kE2M1HiHi = 0x66646260u;  // bytes for codes 4..7
-
-// 8 E2M1 nibbles (one dword, channel 2i in the low nibble of byte i) times
-// a scale given as fp16(scale / 256) -> 8 fp16 values, exactly.
-__device__ __forceinline__ void fp4x8_to_f16(uint32_t x, _Float16 s256, half_t* out) {
-  const uint32_t lo_n = x & 0x07070707u;
-  const uint32_t hi_n = (x >> 4) & 0x07070707u;
-  const uint32_t sgn0 = (x & 0x08080808u) << 4;  // channel 2i sign at bit 7 of byte i
-  const uint32_t sgn1 = x & 0x80808080u;         // channel 2i+1 sign at bit 7 of byte i
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // perm selector bytes [0x0C, k, 0x0C, 4+k]: [0, lo_n.byte k, 0, hi_n.byte k]
-    const uint32_t pick = 0x000C000Cu | ((uint32_t)k << 8) | ((uint32_t)(4 + k) << 24);
-    const uint32_t sel = __builtin_amdgcn_perm(hi_n, lo_n, pick);
-    uint32_t h2 = __builtin_amdgcn_perm(kE2M1HiHi, kE2M1HiLo, sel);
-    h2 |= __builtin_amdgcn_perm(sgn1, sgn0, pick);
-    _Float16 v0 = __builtin_bit_cast(_Float16, (uint16_t)(h2 & 0xFFFFu));
-    _Float16 v1 = __builtin_bit_cast(_Float16, (uint16_t)(h2 >> 16));
-    out[2 * k] = v0 * s256;
-    out[2 * k + 1] = v1 * s256;
-  }
-}
-
-// fp16 bits of (E4M3 value / 256) for a scale code (sign ignored: scales are >= 0).
-__device__ __forceinline__ _Float16 e4m3_div256_f16(uint32_t code) {
-  return __builtin_bit_cast(_Float16, (uint16_t)((code & 0x7Fu) << 7));
-}
-
-// 4 E4M3 codes -> 4 fp16 values, exactly (fp16 bits of value/256, times 256).
-__device__ __forceinline__ void fp8x4_to_f16(uint32_t x, half_t* out) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t c = (x >> (8 * k)) & 0xFFu;
-    const uint16_t hb = (uint16_t)(((c & 0x7Fu) << 7) | ((c & 0x80u) << 8));
-    out[k] = __builtin_bit_cast(_Float16, hb) * (_Float16)256.0f;
-  }
 }
 
 struct AttnArgs {
@@ -96,6 +73,7 @@ struct AttnArgs {
   const uint8_t* swa;
   int T;
   int H;
+  int BT;
   int n_splits;
   float* part_o;   // [B*T][H/16][n_splits][16][512]
   float* part_ml;  // [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
@@ -111,18 +89,28 @@ struct RowSrc {
 
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
-  __shared__ __attribute__((aligned(16))) v4f ssum[4][2][64];
-  __shared__ int64_t rbase[kRowsPerSplit];
+  __shared__ __attribute__((aligned(16))) v4f ssum[2][4][2][64];  // double-buffered by sub-chunk
+  __shared__ __attribute__((aligned(16))) float alph[4][16];       // per wave: rescale factor per head
+  __shared__ const uint8_t* rptr0[kRowsPerSplit];  // codes (FP4) or window row start
+  __shared__ const uint8_t* rptr1[kRowsPerSplit];  // scale row (FP4) or window row start + 8
   __shared__ int rkind[kRowsPerSplit];
 
-  const int split = blockIdx.x;
-  const int ht = blockIdx.y;
-  const int bt = blockIdx.z;
+  // XCD-aware order: workgroup id % 8 picks the XCD (and its L2).  The NHT
+  // head tiles of one (split, b, t) unit take ids 8 apart, so they share an
+  // XCD and its L2 copy of the unit's rows.
+  const int NHT = a.H >> 4;
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int rest = id >> 3;
+  const int ht = rest % NHT;
+  const int unit = (rest / NHT) * 8 + xcd;  // split + n_splits * (b*T + t)
+  if (unit >= a.n_splits * a.BT) return;
+  const int split = unit % a.n_splits;
+  const int bt = unit / a.n_splits;
   const int b = bt / a.T, t = bt % a.T;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int NHT = a.H >> 4;
   int n = a.n_entries[b];
   n = min(n, a.max_pages * kPage);
 
@@ -135,7 +123,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   // lookup) or window row; threads 0..127 take one row each
   if (threadIdx.x < kRowsPerSplit) {
     const int row = row0 + (int)threadIdx.x;
-    int64_t base = -1;
+    // absent rows point at the pool's first bytes (read and discarded)
+    const uint8_t* p0 = a.kv_pool;
+    const uint8_t* p1 = a.kv_pool;
     int kind = 0;
     if (row < row1) {
       if (row < a.topk) {
@@ -143,16 +133,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
         if (j >= 0 && j < n) {
           const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, b, j >> 6);
           if (pg >= 0) {
-            base = pg * kPageBytes + (int64_t)(j & 63);  // page offset + entry (low 6 bits)
+            const uint8_t* page = a.kv_pool + pg * kPageBytes;
+            p0 = page + (j & 63) * kEntryCodes;
+            p1 = page + kPage * kEntryCodes + (j & 63) * kEntryScales;
             kind = 1;
           }
         }
       } else {
-        base = ((int64_t)b * (kSwa - 1 + a.T) + t + (row - a.topk)) * kD;
+        p0 = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t + (row - a.topk)) * kD;
+        p1 = p0 + 8;
         kind = 2;
       }
     }
-    rbase[threadIdx.x] = base;
+    rptr0[threadIdx.x] = p0;
+    rptr1[threadIdx.x] = p1;
     rkind[threadIdx.x] = kind;
   }
 
@@ -184,22 +178,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   // another's destination registers): FP4 row -> 16 code nibbles and the
   // dword holding the scale byte; window row -> its 16 FP8 codes; absent row
   // -> the pool's first bytes, discarded.
+  // lane offsets from the row bases: FP4 codes at ch0/2, scale dword at
+  // (ch0/16) & ~3; window bytes at ch0 (both halves)
+  const int off_fp4_0 = ch0 / 2, off_fp4_1 = (ch0 / 16) & ~3;
   v2u lo8[kSubs][4], hi8[kSubs][4];
 #pragma unroll
   for (int sc = 0; sc < kSubs; ++sc)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = sc * kSub + 4 * rg + i;
-      const int kind = rkind[rr];
-      const int64_t base = rbase[rr];
-      const int64_t pgo = base & ~(int64_t)63;
-      const int e = (int)(base & 63);
-      const uint8_t* p0 = kind == 1 ? a.kv_pool + pgo + e * kEntryCodes + ch0 / 2
-                          : kind == 2 ? a.swa + base + ch0 : a.kv_pool;
-      const uint8_t* p1 = kind == 1 ? a.kv_pool + pgo + kPage * kEntryCodes + e * kEntryScales + (ch0 / 16 & ~3)
-                          : kind == 2 ? a.swa + base + ch0 + 8 : a.kv_pool;
-      lo8[sc][i] = *reinterpret_cast<const v2u*>(p0);
-      hi8[sc][i] = *reinterpret_cast<const v2u*>(p1);
+      const bool fp4 = rkind[rr] == 1;
+      lo8[sc][i] = *reinterpret_cast<const v2u*>(rptr0[rr] + (fp4 ? off_fp4_0 : ch0));
+      hi8[sc][i] = *reinterpret_cast<const v2u*>(rptr1[rr] + (fp4 ? off_fp4_1 : ch0));
     }
 
   float m_run = -__builtin_inff();  // running max (log2 units) of head `col`
@@ -221,24 +211,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kind = rkind[sc * kSub + 4 * rg + i];
-      half_t tmp[16];
+      // hardware conversions with unit scale are exact for every FP4 and
+      // E4M3 code (element 0 = low nibble / low byte); the E4M3 block scale
+      // is applied by one packed fp16 multiply per channel pair, exact since
+      // the product has at most 6 significant bits and lies in fp16 range
+      h2_t v[8];
       if (kind == 1) {
         const uint32_t scode = (hi8[sc][i][0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
-        const _Float16 s256 = e4m3_div256_f16(scode);
-        fp4x8_to_f16(lo8[sc][i][0], s256, tmp);
-        fp4x8_to_f16(lo8[sc][i][1], s256, tmp + 8);
+        const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scode | (scode << 8), 1.0f, false);
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 0) * s2;
+          v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 1) * s2;
+          v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 2) * s2;
+          v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 3) * s2;
+        }
       } else {
-        // window row (kind 2), or absent (kind 0: decode zeros)
+        // window row (kind 2): 16 E4M3 codes; absent row (kind 0): zeros
         const bool w = kind == 2;
         const uint32_t c4[4] = {w ? lo8[sc][i][0] : 0u, w ? lo8[sc][i][1] : 0u, w ? hi8[sc][i][0] : 0u,
                                 w ? hi8[sc][i][1] : 0u};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) fp8x4_to_f16(c4[d], tmp + 4 * d);
+        for (int d = 0; d < 4; ++d) {
+          v[2 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, false);
+          v[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, true);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        rv[i][0][e] = tmp[e];
-        rv[i][1][e] = tmp[8 + e];
+      for (int e = 0; e < 4; ++e) {
+        rv[i][0][2 * e] = v[e][0];
+        rv[i][0][2 * e + 1] = v[e][1];
+        rv[i][1][2 * e] = v[4 + e][0];
+        rv[i][1][2 * e + 1] = v[4 + e][1];
       }
       const int odd = cg & 1;
       const v8h first = odd ? rv[i][1] : rv[i][0];
@@ -261,18 +265,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
         const v8h ka = *reinterpret_cast<const v8h*>(&my_kr[tile_off(rt * 16 + col, 4 * s + g)]);
         sacc[rt] = mfma16(ka, qb[s], sacc[rt]);
       }
-      ssum[wave][rt][lane] = sacc[rt];
+      ssum[sc & 1][wave][rt][lane] = sacc[rt];
     }
+    // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
+    // and this buffer is rewritten only after the next sub-chunk's barrier
     __syncthreads();
     v4f st[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      st[rt] = ssum[0][rt][lane];
-      st[rt] = st[rt] + ssum[1][rt][lane];
-      st[rt] = st[rt] + ssum[2][rt][lane];
-      st[rt] = st[rt] + ssum[3][rt][lane];
+      st[rt] = ssum[sc & 1][0][rt][lane];
+      st[rt] = st[rt] + ssum[sc & 1][1][rt][lane];
+      st[rt] = st[rt] + ssum[sc & 1][2][rt][lane];
+      st[rt] = st[rt] + ssum[sc & 1][3][rt][lane];
     }
-    __syncthreads();
 
     // ---- online softmax for head `col` over rows 4g+i (+16)
     float lg[8];
@@ -287,8 +292,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
         lg[rt * 4 + i] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows4_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = (m_new == -__builtin_inff()) ? 1.0f : exp2f(m_run - m_new);
     float psum = 0.0f;
@@ -299,14 +303,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
       psum += p;
       pa[k] = (_Float16)p;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = rows4_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // rescale output rows (heads 4g+i) by their alpha
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+    // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
+    if (lane < 16) alph[wave][lane] = alpha;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -444,10 +449,13 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   aa.T = T;
   aa.H = H;
   aa.n_splits = n_splits_for(topk);
+  aa.BT = B * T;
   const size_t units = (size_t)B * T * (H / 16) * aa.n_splits;
   aa.part_o = reinterpret_cast<float*>(ws);
   aa.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(units * 16 * csa2::kD * 4));
-  CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel, dim3(aa.n_splits, H / 16, B * T),
+  const int n_units = aa.n_splits * B * T;
+  const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
+  CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel, dim3(grid),
               dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   csa2::CombineArgs ca{};
