@@ -123,7 +123,7 @@ def counters_driver(args):
     return 0
 
 
-def cpu_baseline(wl, min_seconds=8.0, max_reps=20):
+def cpu_baseline(wl, min_seconds=12.0, max_reps=40):
     """The oracle, as it stands, on the same layer step; all host cores it uses."""
     import oracle
     oracle.build(force=False)
