@@ -9,16 +9,16 @@
 //   s_j = binary32 fold over ascending h of fl(w_h * max(d_h, +0)).
 //
 // Exactness on MFMA.  Every E4M3 value is M * 2^-9 with M an integer,
-// |M| <= 229,376 < 2^18.  M is split into sign-magnitude 7-bit limbs
-// (lo, mid, top), each in [-127, 127], so q.k * 2^18 = sum over limb pairs
-// of 2^(7(a+b)) * (Q_a . K_b), and every Q_a . K_b is an exact int32 from
-// the int8 MFMA.  For the common case (all |q|, |k| < 32, i.e. no top limb,
-// and sum_c |Mq| < 2^17) the recombined integer fits int32 and is rounded
-// to binary32 by one conversion; otherwise the five weighted partial sums
-// are combined exactly in binary64 (at most 43 significant bits) and
-// rounded once.  The FP8 MFMA is not used: it aligns each group of 8
-// products to the group maximum and keeps about 13 bits, so it does not
-// return the exactly rounded dot.
+// |M| <= 229,376 < 2^18.  M is split into 7-bit limbs with a signed top,
+// each an int8, so q.k * 2^18 = sum over limb pairs of 2^(7(a+b)) (Q_a . K_b),
+// and every Q_a . K_b is an exact int32 from the int8 MFMA.  In the common
+// case (all |q|, |k| < 32, so M = lo + 2^7 mid with two limbs, and
+// sum_c |q_c| < 256) the recombined integer fits int32 and is rounded to
+// binary32 by one conversion; otherwise three limbs per side give five
+// weighted partial sums, combined exactly in binary64 (at most 43
+// significant bits) and rounded once.  The FP8 MFMA is not used: it aligns
+// each group of 8 products to the group maximum and keeps about 13 bits, so
+// it does not return the exactly rounded dot.
 //
 // Layout of v_mfma_i32_16x16x64_i8 used below: lane l holds row (l & 15) of
 // A and column (l & 15) of B, bytes 16*(l >> 4) .. +15 of the 64-deep slice;
@@ -29,35 +29,48 @@
 
 namespace csa2 {
 
-constexpr int kScoreThreads = 512;        // 8 waves
+constexpr int kScoreThreads = 512;           // 8 waves
 constexpr int kWaves = kScoreThreads / 64;
-constexpr int kChunk = 32;                // entries scored together per wave (half a page)
-constexpr int kSub = kChunk / 16;         // 16-entry MFMA sub-tiles per chunk
-constexpr int kMaxRT = 4;                 // row tiles of 16 heads (HI <= 64)
-constexpr int kPassHeads = 64;            // heads folded per pass
-constexpr int kPassRT = kPassHeads / 16;  // row tiles per pass
+constexpr int kChunk = 64;                   // entries scored together per wave: one page
+constexpr int kSub = kChunk / 16;            // 16-entry MFMA sub-tiles per chunk
+constexpr int kRT = 4;                       // row tiles of 16 heads (HI <= 64)
+constexpr int kPassRT = 2;                   // row tiles folded per pass
+constexpr int kPassHeads = kPassRT * 16;     // heads folded per pass
 constexpr int kFoldStride = kPassHeads + 4;  // floats per entry row of the fold buffer
-constexpr int kMaxWaveChunks = 1024;      // chunks one wave may take in one launch
-constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (32-bit data, no swizzle)
+constexpr int kMaxWaveChunks = 1024;         // chunks one wave may take in one launch
+constexpr int kBufferFlags = 0x00020000;     // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
-// Lookup table: for every E4M3 code, its sign-magnitude 7-bit limbs of
-// M = value * 2^9 packed as int8 bytes [lo, mid, top, 0]; 64 copies so the
-// 64 lanes of a wave read distinct banks (address = code * 256 + lane * 4).
+// Lookup table: for every E4M3 code, the limbs of M = value * 2^9 as bytes
+//   [lo | hot, mid_s, mid_u, top]
+// for two splits:
+//   fast     M = lo + 2^7 mid_s               (|M| < 2^14: lo in [0,127], mid_s signed)
+//   general  M = lo + 2^7 mid_u + 2^14 top    (lo, mid_u in [0,127], top signed)
+// A code with |value| >= 32 (|M| >= 2^14, exponent field >= 12) has no fast
+// split: its first byte is 0x80, a bit no fast lo byte has set, and its
+// second byte is 0.  Its true lo is 0 (M is then a multiple of 2^11), so the
+// general split reads lo as the first byte & 0x7F.  64 copies so the 64
+// lanes of a wave read distinct banks (address = code * 256 + lane * 4).
 __device__ __forceinline__ uint32_t limb_entry(uint32_t code) {
-  uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  uint32_t M = (e == 0) ? m : ((8u + m) << (e - 1));
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  int M = (e == 0) ? (int)m : (int)((8u + m) << (e - 1));
   if (e == 15 && m == 7) M = 0;  // NaN codes are a precondition violation; keep them inert
-  uint32_t lo = M & 127u, mid = (M >> 7) & 127u, top = M >> 14;
-  if (code & 0x80u) {
-    lo = (0u - lo) & 0xFFu;
-    mid = (0u - mid) & 0xFFu;
-    top = (0u - top) & 0xFFu;
-  }
-  return lo | (mid << 8) | (top << 16);
+  if (code & 0x80u) M = -M;
+  const bool hot = e >= 12;
+  const uint32_t b0 = hot ? 0x80u : ((uint32_t)M & 127u);
+  const uint32_t b1 = hot ? 0u : ((uint32_t)(M >> 7) & 0xFFu);
+  const uint32_t b2 = (uint32_t)(M >> 7) & 127u;
+  const uint32_t b3 = (uint32_t)(M >> 14) & 0xFFu;
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
+// Thread t of the 512 writes 32 of the 64 copies of code t / 2 (128 bytes).
 __device__ void build_lut(uint32_t* lut) {
-  for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) lut[i] = limb_entry((uint32_t)(i >> 6));
+  const int t = threadIdx.x;
+  const uint32_t v = limb_entry((uint32_t)(t >> 1));
+  const v4u q = {v, v, v, v};
+  v4u* dst = reinterpret_cast<v4u*>(lut + (t >> 1) * 64 + (t & 1) * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = q;
 }
 
 __device__ __forceinline__ uint32_t lut_read(const uint8_t* lut_bytes, uint32_t lane4, uint32_t x, int k) {
@@ -65,10 +78,10 @@ __device__ __forceinline__ uint32_t lut_read(const uint8_t* lut_bytes, uint32_t 
   return *reinterpret_cast<const uint32_t*>(lut_bytes + addr);
 }
 
-// 16 FP8 codes -> lo and mid limb planes; `any` collects the top limbs
-// (nonzero iff some |value| >= 32).
+// 16 FP8 codes -> fast lo and mid_s limb planes (byte order kept).  A lo
+// byte with bit 7 set marks a code without a fast split.
 __device__ __forceinline__ void limbs2(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
-                                      v4i& mid, uint32_t& any) {
+                                      v4i& mid) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t x = codes[d];
@@ -78,11 +91,10 @@ __device__ __forceinline__ void limbs2(const uint8_t* lut_bytes, uint32_t lane4,
     const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x05010400u);
     lo[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
     mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
-    any |= L0 | L1 | L2 | L3;
   }
 }
 
-// 16 FP8 codes -> all three limb planes (general path).
+// 16 FP8 codes -> general lo, mid_u and top limb planes.
 __device__ __forceinline__ void limbs3(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
                                       v4i& mid, v4i& top) {
 #pragma unroll
@@ -90,12 +102,12 @@ __device__ __forceinline__ void limbs3(const uint8_t* lut_bytes, uint32_t lane4,
     const uint32_t x = codes[d];
     const uint32_t L0 = lut_read(lut_bytes, lane4, x, 0), L1 = lut_read(lut_bytes, lane4, x, 1);
     const uint32_t L2 = lut_read(lut_bytes, lane4, x, 2), L3 = lut_read(lut_bytes, lane4, x, 3);
-    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x05010400u);
-    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x05010400u);
-    lo[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x06020400u);  // [lo0 lo1 midu0 midu1]
+    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x06020400u);
+    lo[d] = (int)(__builtin_amdgcn_perm(t23, t01, 0x05040100u) & 0x7F7F7F7Fu);
     mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
-    const uint32_t u01 = __builtin_amdgcn_perm(L1, L0, 0x0C0C0602u);
-    const uint32_t u23 = __builtin_amdgcn_perm(L3, L2, 0x0C0C0602u);
+    const uint32_t u01 = __builtin_amdgcn_perm(L1, L0, 0x0C0C0703u);  // [top0 top1 0 0]
+    const uint32_t u23 = __builtin_amdgcn_perm(L3, L2, 0x0C0C0703u);
     top[d] = (int)__builtin_amdgcn_perm(u23, u01, 0x05040100u);
   }
 }
@@ -104,16 +116,30 @@ __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t abs8_sum(v4i v, uint32_t w) {
-  uint32_t acc = 0;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int b = (int)(int8_t)(((uint32_t)v[d] >> (8 * k)) & 0xFFu);
-      acc += (uint32_t)(b < 0 ? -b : b) * w;
-    }
-  return acc;
+// a0 + 2^7 a1 + 2^14 a2 (mod 2^32) as two shift-adds.  The inner sum is
+// made opaque so the compiler cannot re-associate the expression into two
+// shifts and a three-way add; it stays ordinary code (not inline asm) so the
+// compiler still inserts the wait states a VALU read of an MFMA result needs.
+__device__ __forceinline__ uint32_t recombine(uint32_t a0, uint32_t a1, uint32_t a2) {
+  uint32_t t = (a2 << 7) + a1;
+  asm volatile("" : "+v"(t));
+  return (t << 7) + a0;
+}
+
+// Maximum over each aligned group of 8 lanes, in every lane of the group.
+__device__ __forceinline__ float group8_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  return m;
+}
+
+// Orders this lane's LDS accesses around a hand-off to other lanes of the
+// wave: the LDS executes one wave's instructions in order, so keeping the
+// compiler from moving memory accesses across this point is enough.
+__device__ __forceinline__ void wave_lds_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Row stride of the block-maxima buffer: ceil(max_n / 8) rounded up to a
@@ -139,11 +165,12 @@ struct ScoreArgs {
   const int32_t* pool;    // pool mode
   const int32_t* pool_n;  // pool mode
   int pool_blocks;
-  float* out_s;           // full: [B][T][max_n]; pool: [B][T][pool_blocks*8]
-  float* out_bm;          // full: [B][T][ceil(max_n/8)]
+  float* out_s;           // full: [B][T][s_stride(max_n)]; pool: [B][T][pool_blocks*8]
+  float* out_bm;          // full: [B][T][bm_stride(max_n)]
   int rows;               // full: B; pool: B*T
   int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
-  int chunks_per_wg;
+  int chunks_per_wg;      // chunks of one row per workgroup
+  int wg_per_row;         // workgroups per row
 };
 
 // Keys of one chunk for one wave: lane (g, col) holds entry 16*st + col of
@@ -154,14 +181,12 @@ struct ChunkKeys {
 
 // Row context of a wave: sequence b, token t, visible entries n, pool row.
 struct RowCtx {
-  int row = -1;
   int b = 0, t = 0, n = 0, n_pos = 0;
   const int32_t* pool_row = nullptr;
 };
 
 template <bool POOL>
 __device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full, RowCtx& r) {
-  r.row = row;
   if (POOL) {
     r.b = row / a.T;
     r.t = row % a.T;
@@ -195,33 +220,32 @@ __device__ __forceinline__ int entry_of(const ScoreArgs& a, const RowCtx& r, int
   return phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6) >= 0 ? j : -1;
 }
 
+// Loads one chunk's keys; not visible entries read as zero.  Full mode: the
+// chunk is logical page `chunk`, read through one buffer descriptor per
+// 16-entry sub-tile whose record count ends at the sub-tile's last visible
+// entry, so the loads need no predicate (the hardware returns zero past the
+// count) and share one lane offset.  Returns whether the page is usable
+// (Full mode; true in pool mode).
 template <bool POOL>
-__device__ __forceinline__ void load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g,
-                                           int col, ChunkKeys& ck) {
+__device__ __forceinline__ bool load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g, int col,
+                                           ChunkKeys& ck) {
   if (!POOL) {
-    // a Full-mode chunk lies inside one 64-entry page: one scalar page lookup
     const int j0 = chunk * kChunk;
-    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j0 / kPage) : -1;
-    // one buffer descriptor for the page (scalar registers) and a single
-    // 32-bit lane offset; the sub-tile and half offsets go in the scalar
-    // offset operand
-    const v4u z = {0, 0, 0, 0};
+    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, chunk) : -1;
+    const int nv = pg >= 0 ? min(r.n - j0, kChunk) : 0;
+    const uint8_t* base = a.kidx + (pg >= 0 ? pg * (kPage * kDI) : 0);
+    const uint32_t lofs = (uint32_t)(col * kDI + 16 * g);
 #pragma unroll
-    for (int st = 0; st < kSub; ++st) ck.k[st][0] = ck.k[st][1] = z;
-    if (pg >= 0) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.kidx + pg * (kPage * kDI) + (j0 % kPage) * kDI), 0, kChunk * kDI, kBufferFlags);
-      const uint32_t lofs = (uint32_t)(col * kDI + 16 * g);
-      const int nv = r.n - j0;  // visible entries from the chunk start
-#pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        if (st * 16 + col < nv) {
-          ck.k[st][0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, st * 16 * kDI, 0);
-          ck.k[st][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, st * 16 * kDI + 64, 0);
-        }
-      }
+    for (int st = 0; st < kSub; ++st) {
+      // readfirstlane: the clamp would otherwise become a vector med3 and the
+      // descriptor a per-lane value, loaded through a waterfall loop
+      const int nst = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * st, 0), 16));
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(base + st * 16 * kDI), 0, nst * kDI, kBufferFlags);
+      ck.k[st][0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, 0, 0);
+      ck.k[st][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs + 64, 0, 0);
     }
-    return;
+    return pg >= 0;
   }
 #pragma unroll
   for (int st = 0; st < kSub; ++st) {
@@ -236,31 +260,24 @@ __device__ __forceinline__ void load_chunk(const ScoreArgs& a, const RowCtx& r, 
     ck.k[st][0] = k0;
     ck.k[st][1] = k1;
   }
+  return true;
 }
 
-// Writes the chunk's scores (NaN, i.e. key 0, for positions that are not
-// visible) and, in Full mode, the maxima of its blocks of 8.
+// Writes the chunk's scores (lane e: entry e of the chunk; NaN, i.e. key 0,
+// for positions that are not visible) and, in Full mode, the maxima of its
+// blocks of 8.
 template <bool POOL>
-__device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, float s) {
+__device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, float s,
+                                           bool page_ok) {
   const int lane = lane_id();
   const int p = chunk * kChunk + lane;
-  bool valid;
-  if (POOL) {
-    valid = lane < kChunk && entry_of<POOL>(a, rc, p) >= 0;
-  } else {
-    const bool page_ok = chunk * kChunk < rc.n &&
-                         phys_page(a.page_table, a.max_pages, a.n_pages, rc.b, chunk * kChunk / kPage) >= 0;
-    valid = lane < kChunk && page_ok && p < rc.n;
-  }
+  const bool valid = POOL ? entry_of<POOL>(a, rc, p) >= 0 : (page_ok && p < rc.n);
   float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
                                    (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
-  if (lane < kChunk && p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
+  if (p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
   if (!POOL) {
-    float m = valid ? s : -__builtin_inff();
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    if (lane < kChunk && (lane & 7) == 0 && p < rc.n_pos) {
+    const float m = group8_max(valid ? s : -__builtin_inff());
+    if ((lane & 7) == 0 && p < rc.n_pos) {
       a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] =
           (m == -__builtin_inff()) ? u2f(0xFFFFFFFFu) : m;
     }
@@ -274,46 +291,52 @@ __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc,
 // validity masking.
 template <bool POOL>
 __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, int64_t qrow0,
-                                            const uint8_t* lut_bytes, float* my_fold, const float* my_w) {
+                                               const uint8_t* lut_bytes, float* my_fold, bool& page_ok) {
   const int lane = lane_id();
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4, col = lane & 15;
   const int HI = a.HI;
-  const int NRT = (HI + 15) >> 4;
-  const int n_pass = (HI + kPassHeads - 1) / kPassHeads;
   ChunkKeys raw;
-  load_chunk<POOL>(a, rc, chunk, g, col, raw);
+  page_ok = load_chunk<POOL>(a, rc, chunk, g, col, raw);
   // an offset the optimizer cannot see through: keeps the query decode
-  // below from being hoisted out of the chunk loop, where its 96 limb
-  // registers would stay live across the common path
+  // below inside this function's loop
   int qoff = 16 * g;
   asm volatile("" : "+v"(qoff));
+  float* fold_w = my_fold + col * kFoldStride + 4 * g;
+  const float* fold_r = my_fold + lane * kFoldStride;
   float s = 0.0f;
-  for (int hh = 0; hh < n_pass; ++hh) {
-    for (int st = 0; st < kSub; ++st) {
-      for (int rl = 0; rl < kPassRT; ++rl) {
-        const int rt = kPassRT * hh + rl;
-        if (rt >= NRT) break;
-        const int h = rt * 16 + col;
+  for (int hh = 0; hh < kRT / kPassRT; ++hh) {
+    for (int rl = 0; rl < kPassRT; ++rl) {
+      const int rt = kPassRT * hh + rl;
+      const int h = rt * 16 + col;
+      v4i ql[2], qm[2], qt[2];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        v4u qc = {0, 0, 0, 0};
+        if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + qoff)[4 * s2];
+        limbs3(lut_bytes, lane4, qc, ql[s2], qm[s2], qt[s2]);
+      }
+      v4f wv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = rt * 16 + 4 * g + i;
+        wv[i] = hw < HI ? a.w[qrow0 + hw] * 0x1p-18f : 0.0f;
+      }
+      for (int st = 0; st < kSub; ++st) {
         const v4i z = {0, 0, 0, 0};
         v4i acc[5] = {z, z, z, z, z};
         for (int s2 = 0; s2 < 2; ++s2) {
-          v4u qc = {0, 0, 0, 0};
-          if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + qoff)[4 * s2];
-          v4i ql, qm, qt, kl, km, kt;
-          limbs3(lut_bytes, lane4, qc, ql, qm, qt);
+          v4i kl, km, kt;
           limbs3(lut_bytes, lane4, raw.k[st][s2], kl, km, kt);
-          acc[0] = mfma8(ql, kl, acc[0]);
-          acc[1] = mfma8(ql, km, acc[1]);
-          acc[1] = mfma8(qm, kl, acc[1]);
-          acc[2] = mfma8(ql, kt, acc[2]);
-          acc[2] = mfma8(qm, km, acc[2]);
-          acc[2] = mfma8(qt, kl, acc[2]);
-          acc[3] = mfma8(qm, kt, acc[3]);
-          acc[3] = mfma8(qt, km, acc[3]);
-          acc[4] = mfma8(qt, kt, acc[4]);
+          acc[0] = mfma8(ql[s2], kl, acc[0]);
+          acc[1] = mfma8(ql[s2], km, acc[1]);
+          acc[1] = mfma8(qm[s2], kl, acc[1]);
+          acc[2] = mfma8(ql[s2], kt, acc[2]);
+          acc[2] = mfma8(qm[s2], km, acc[2]);
+          acc[2] = mfma8(qt[s2], kl, acc[2]);
+          acc[3] = mfma8(qm[s2], kt, acc[3]);
+          acc[3] = mfma8(qt[s2], km, acc[3]);
+          acc[4] = mfma8(qt[s2], kt, acc[4]);
         }
-        const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
         v4f pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -323,41 +346,35 @@ __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx&
           const float f = (float)D;
           pv[i] = wv[i] * (f > 0.0f ? f : 0.0f);
         }
-        *reinterpret_cast<v4f*>(&my_fold[(st * 16 + col) * kFoldStride + rl * 16 + 4 * g]) = pv;
+        *reinterpret_cast<v4f*>(fold_w + st * 16 * kFoldStride + rl * 16) = pv;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    if (lane < kChunk) {
-      const float* frow = &my_fold[lane * kFoldStride];
-      const int nh = min(kPassHeads, HI - kPassHeads * hh);
-      for (int h = 0; h < nh; h += 4) {
-        const v4f v = *reinterpret_cast<const v4f*>(frow + h);
-        s = s + v[0];
-        s = s + v[1];
-        s = s + v[2];
-        s = s + v[3];
-      }
+    wave_lds_order();
+    for (int h = 0; h < kPassHeads; h += 4) {
+      const v4f v = *reinterpret_cast<const v4f*>(fold_r + h);
+      s = s + v[0];
+      s = s + v[1];
+      s = s + v[2];
+      s = s + v[3];
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_order();
   }
   return s;
 }
 
-// Persistent scan.  POOL = false: Full mode, rows = sequences, the 8 waves
-// split T tokens x chunk slices.  POOL = true: Reindex mode, rows = (b, t),
-// positions are the entries of the row's pool blocks.  Each workgroup takes a
-// contiguous range of (row, 32-entry chunk) items; each wave loads its next
+// Scan.  POOL = false: Full mode, rows = sequences, the 8 waves split
+// T tokens x chunk slices.  POOL = true: Reindex mode, rows = (b, t),
+// positions are the entries of the row's pool blocks.  Each workgroup takes
+// a range of 64-entry chunks inside one row; each wave loads its next
 // chunk's keys while it scores the current one.
 //
-// Per chunk a wave decodes the 32 keys into limb planes once, runs the MFMAs
-// of its 2 sub-tiles x 4 row tiles, writes fl(w_h * relu(d_h)) to its LDS
-// fold buffer (entry-major), and lets lane e < 32 fold entry e's heads in
-// ascending order.  Chunks holding a code with a top limb (or rows whose
-// query could overflow int32) are only marked here and scored after the main
-// loop by the general path, so the main loop keeps the common path's
-// registers (no spills: a spill reload would wait for the prefetch).
+// Per chunk a wave decodes the 64 keys into fast limb planes once, then in
+// two passes of 32 heads runs the MFMAs of 4 sub-tiles x 2 row tiles, writes
+// fl(w_h * relu(d_h)) to its LDS fold buffer (entry-major), and lets lane e
+// fold entry e's heads in ascending order.  Chunks holding a code without a
+// fast split, and rows whose query could overflow int32, are only marked
+// here and scored after the main loop by the general path, which keeps the
+// main loop free of its registers.
 template <bool POOL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // The lookup table sits at LDS offset 0, so a lookup address is the
@@ -365,204 +382,171 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   struct __attribute__((aligned(16))) Lds {
     uint32_t lut[256 * 64];
     float fold[kWaves][kChunk * kFoldStride];
-    float wsh[kWaves][kMaxRT * 16];  // w * 2^-18 per head
+    float wsh[kWaves][kRT * 16];                  // w * 2^-18 per head
     uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
   };
   __shared__ Lds sm;
-  uint32_t* lut = sm.lut;
 
-  build_lut(lut);
+  build_lut(sm.lut);
   for (int i = threadIdx.x; i < kWaves * kMaxWaveChunks / 32; i += blockDim.x) (&sm.defer[0][0])[i] = 0u;
   __syncthreads();
-  const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut);
+  const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(sm.lut);
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4;   // 16-byte K slice within a 64-deep step
   const int col = lane & 15;
+  const int HI = a.HI;
   const int t_full = POOL ? 0 : wave % a.T;
   const int slice = POOL ? wave : wave / a.T;
   const int n_slices = POOL ? kWaves : kWaves / a.T;
-  const int HI = a.HI;
-  const int NRT = (HI + 15) >> 4;
-  const int n_pass = (HI + kPassHeads - 1) / kPassHeads;
+  const int row = blockIdx.x / a.wg_per_row;
+  const int c0 = (blockIdx.x % a.wg_per_row) * a.chunks_per_wg;
+  const int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
+  int chunk = c0 + slice;
+  if (row >= a.rows || chunk >= c1) return;  // no workgroup barrier follows
 
-  const int total = a.rows * a.chunks_per_row;
-  const int it0 = blockIdx.x * a.chunks_per_wg;
-  const int it1 = min(total, it0 + a.chunks_per_wg);
+  RowCtx rc;
+  row_ctx<POOL>(a, row, t_full, rc);
+  const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  ChunkKeys cur;
+  bool cur_ok = load_chunk<POOL>(a, rc, chunk, g, col, cur);
+
+  // ---- query of token t: fast limb planes (A operands), weights, and the
+  // fast-path conditions (no code without a fast split, sum_c |q_c| < 256
+  // for every head, i.e. sum_c |Mq| < 2^17)
+  v4i qlo[kRT][2], qmid[kRT][2];
+  uint32_t qflag = 0;
+  float qabs = 0.0f;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int h = rt * 16 + col;
+    v4u c[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (h < HI) {
+      const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
+      c[0] = src[0];
+      c[1] = src[4];
+    }
+    float sa = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      limbs2(lut_bytes, lane4, c[s2], qlo[rt][s2], qmid[rt][s2]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        qflag |= (uint32_t)qlo[rt][s2][d];
+        const v2f x0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[s2][d], 1.0f, false);
+        const v2f x1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[s2][d], 1.0f, true);
+        sa = sa + fabsf(x0[0]) + fabsf(x0[1]) + fabsf(x1[0]) + fabsf(x1[1]);
+      }
+    }
+    sa += __shfl_xor(sa, 16);
+    sa += __shfl_xor(sa, 32);
+    qabs = fmaxf(qabs, sa);
+  }
+  const bool fast_q = __ballot((qflag & 0x80808080u) != 0 || !(qabs < 256.0f)) == 0;
+  // w * 2^-18, exact for |w| >= 2^-100 and w = 0 (zero for heads >= HI)
+  float* my_w = sm.wsh[wave];
+  {
+    const float wl = a.w[qrow0 + min(lane, HI - 1)];
+    my_w[lane] = lane < HI ? wl * 0x1p-18f : 0.0f;
+  }
+  wave_lds_order();
 
   float* my_fold = sm.fold[wave];
-  // this lane's fold-buffer slot for sub-tile 0, row tile 0 (the other
-  // tiles sit at constant offsets from it)
-  float* fold_w = my_fold + col * kFoldStride + 4 * g;
-  float* my_w = sm.wsh[wave];
+  float* fold_w = my_fold + col * kFoldStride + 4 * g;  // this lane's slot for sub-tile 0, row tile 0
+  const float* fold_r = my_fold + lane * kFoldStride;   // entry `lane`'s row
   uint32_t* my_defer = sm.defer[wave];
   int k_seq = 0;  // index of the current chunk among this wave's chunks
 
-  int it = it0 + slice;
-  ChunkKeys cur;
-  if (it < it1) {
-    RowCtx r0;
-    row_ctx<POOL>(a, it / a.chunks_per_row, t_full, r0);
-    load_chunk<POOL>(a, r0, it % a.chunks_per_row, g, col, cur);
-  }
-  while (it < it1) {
-    // ---- a new row: query limbs (A operands) and head weights of token t
-    RowCtx rc;
-    const int row = it / a.chunks_per_row;
-    row_ctx<POOL>(a, row, t_full, rc);
-    const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
-    v4i qlo[kMaxRT][2], qmid[kMaxRT][2];
-    uint32_t q_any = 0, q_abs = 0;
-#pragma unroll
-    for (int rt = 0; rt < kMaxRT; ++rt) {
-      const int h = rt * 16 + col;
-      v4u c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
-      if (rt < NRT && h < HI) {
-        const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
-        c0 = src[0];
-        c1 = src[4];
-      }
-      limbs2(lut_bytes, lane4, c0, qlo[rt][0], qmid[rt][0], q_any);
-      limbs2(lut_bytes, lane4, c1, qlo[rt][1], qmid[rt][1], q_any);
-      uint32_t sabs = abs8_sum(qlo[rt][0], 1) + abs8_sum(qlo[rt][1], 1) + abs8_sum(qmid[rt][0], 128) +
-                      abs8_sum(qmid[rt][1], 128);
-      sabs += __shfl_xor(sabs, 16);
-      sabs += __shfl_xor(sabs, 32);
-      q_abs = max(q_abs, sabs);
+  for (; chunk < c1; chunk += n_slices, ++k_seq) {
+    const int next = chunk + n_slices;
+    if (!fast_q) {
+      my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
+      continue;
     }
-    for (int o = 1; o < 64; o <<= 1) q_abs = max(q_abs, (uint32_t)__shfl_xor((int)q_abs, o));
-    // the fast path needs no top limb in q and sum_c |Mq| < 2^17, so that with
-    // |Mk| < 2^14 every partial and the total stay below 2^31
-    const bool fast_q = (__ballot((q_any & 0x00FF0000u) != 0) == 0) && (q_abs < (1u << 17));
-    // w * 2^-18 is exact for |w| >= 2^-100 (and w = 0)
-    my_w[lane] = lane < HI ? a.w[qrow0 + lane] * 0x1p-18f : 0.0f;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    // ---- decode the chunk's keys into fast limb planes
+    v4i klo[kSub][2], kmid[kSub][2];
+    uint32_t kflag = 0;
+#pragma unroll
+    for (int st = 0; st < kSub; ++st) {
+      // one sub-tile at a time: issuing all lookups at once would hold
+      // 256 address / result registers
+      __builtin_amdgcn_sched_barrier(0);
+      limbs2(lut_bytes, lane4, cur.k[st][0], klo[st][0], kmid[st][0]);
+      limbs2(lut_bytes, lane4, cur.k[st][1], klo[st][1], kmid[st][1]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) kflag |= (uint32_t)klo[st][0][d] | (uint32_t)klo[st][1][d];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool page_ok = cur_ok;
+    // the next chunk streams into the now free key registers while this
+    // one is scored
+    if (next < c1) cur_ok = load_chunk<POOL>(a, rc, next, g, col, cur);
+    if (__ballot((kflag & 0x80808080u) != 0) != 0) {
+      // rare: scored after the main loop, out of this loop's registers
+      my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
+      continue;
+    }
 
-    const int row_end = min(it1, (row + 1) * a.chunks_per_row);
-    for (; it < row_end; it += n_slices) {
-      const int chunk = it % a.chunks_per_row;
-      // ---- fast or general: a key code has a top limb iff |value| >= 32,
-      // i.e. its exponent field is >= 12 (bits 6 and 5 of the byte both set)
-      uint32_t hot = 0;
+    float s = 0.0f;
 #pragma unroll
-      for (int st = 0; st < kSub; ++st)
+    for (int hh = 0; hh < kRT / kPassRT; ++hh) {
+      // 8 tiles (sub-tile st, row tile 2 hh + rl), each: 8 MFMAs, then the
+      // recombination.  Overlapping the MFMAs of one tile with the
+      // recombination of the previous needs more registers than two waves
+      // per SIMD have; the other wave of the SIMD fills that gap instead.
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) hot |= cur.k[st][hs][d] & (cur.k[st][hs][d] << 1);
-      const bool fast = fast_q && (__ballot((hot & 0x40404040u) != 0) == 0);
-      const int itn = it + n_slices;
-      // sequential head fold of one half: lane e folds entry e of this chunk
-      float s = 0.0f;
-      auto fold_half = [&](int hh) {
-        // the fold reads what other lanes of this wave wrote
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        if (lane < kChunk) {
-          const float* frow = &my_fold[lane * kFoldStride];
-          const int nh = min(kPassHeads, HI - kPassHeads * hh);
-          for (int h = 0; h < nh; h += 4) {
-            const v4f v = *reinterpret_cast<const v4f*>(frow + h);
-            s = s + v[0];
-            s = s + v[1];
-            s = s + v[2];
-            s = s + v[3];
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-      };
-      if (fast) {
-        // ---- decode the chunk's keys into lo / mid limb planes
-        v4i klo[kSub][2], kmid[kSub][2];
-        uint32_t unused = 0;
-#pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          // one sub-tile at a time: issuing all 128 lookups at once would
-          // hold 128 address / result registers
-          __builtin_amdgcn_sched_barrier(0);
-          limbs2(lut_bytes, lane4, cur.k[st][0], klo[st][0], kmid[st][0], unused);
-          limbs2(lut_bytes, lane4, cur.k[st][1], klo[st][1], kmid[st][1], unused);
-        }
+      for (int k = 0; k < kSub * kPassRT; ++k) {
+        const int st = k >> 1, rl = k & 1, rt = kPassRT * hh + rl;
         __builtin_amdgcn_sched_barrier(0);
-        // the next chunk of this wave (possibly in the next row) streams into
-        // the now free key registers while this one is scored
-        if (itn < it1) {
-          RowCtx rn;
-          row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
-          load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, cur);
+        const v4i z = {0, 0, 0, 0};
+        v4i c1 = mfma8(qlo[rt][0], kmid[st][0], z);
+        v4i c0 = mfma8(qlo[rt][0], klo[st][0], z);
+        v4i c2 = mfma8(qmid[rt][0], kmid[st][0], z);
+        c1 = mfma8(qmid[rt][0], klo[st][0], c1);
+        c0 = mfma8(qlo[rt][1], klo[st][1], c0);
+        c2 = mfma8(qmid[rt][1], kmid[st][1], c2);
+        c1 = mfma8(qlo[rt][1], kmid[st][1], c1);
+        c1 = mfma8(qmid[rt][1], klo[st][1], c1);
+        // lane (g, col) outputs heads 16 rt + 4 g + i
+        const v4f wv = *reinterpret_cast<const v4f*>(my_w + rt * 16 + 4 * g);
+        v4f pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // D = a0 + 2^7 a1 + 2^14 a2 = sum_c Mq Mk, exact in int32 since
+          // |D| <= sum_c |Mq| |Mk| < 2^17 * 2^14
+          const uint32_t D = recombine((uint32_t)c0[i], (uint32_t)c1[i], (uint32_t)c2[i]);
+          const float r = (float)(uint32_t)max((int)D, 0);
+          pv[i] = wv[i] * r;
         }
-#pragma unroll
-        for (int hh = 0; hh < kMaxRT / kPassRT; ++hh) {
-          if (hh >= n_pass) break;
-#pragma unroll
-          for (int st = 0; st < kSub; ++st) {
-#pragma unroll
-            for (int rl = 0; rl < kPassRT; ++rl) {
-              const int rt = kPassRT * hh + rl;
-              if (rt >= NRT) break;
-              // keep the tiles in sequence: interleaving them needs more
-              // registers than two waves per SIMD have
-              __builtin_amdgcn_sched_barrier(0);
-              const v4i z = {0, 0, 0, 0};
-              v4i a0 = mfma8(qlo[rt][0], klo[st][0], z);
-              a0 = mfma8(qlo[rt][1], klo[st][1], a0);
-              v4i a1 = mfma8(qlo[rt][0], kmid[st][0], z);
-              a1 = mfma8(qmid[rt][0], klo[st][0], a1);
-              a1 = mfma8(qlo[rt][1], kmid[st][1], a1);
-              a1 = mfma8(qmid[rt][1], klo[st][1], a1);
-              v4i a2 = mfma8(qmid[rt][0], kmid[st][0], z);
-              a2 = mfma8(qmid[rt][1], kmid[st][1], a2);
-              const v4f wv = *reinterpret_cast<const v4f*>(&my_w[rt * 16 + 4 * g]);
-              v4f pv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                // every weighted term is bounded by sum |Mq||Mk| < 2^31: exact in int32
-                const uint32_t t = (uint32_t)a1[i] + ((uint32_t)a2[i] << 7);
-                const int32_t D = (int32_t)((uint32_t)a0[i] + (t << 7));
-                const float r = (float)max(D, 0);
-                pv[i] = wv[i] * r;
-              }
-              *reinterpret_cast<v4f*>(fold_w + (st * 16 * kFoldStride + rl * 16)) = pv;
-            }
-          }
-          fold_half(hh);
-        }
-      } else {
-        // rare: scored after the main loop, out of this loop's registers
-        my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
-        if (itn < it1) {
-          RowCtx rn;
-          row_ctx<POOL>(a, itn / a.chunks_per_row, t_full, rn);
-          load_chunk<POOL>(a, rn, itn % a.chunks_per_row, g, col, cur);
-        }
+        *reinterpret_cast<v4f*>(fold_w + st * 16 * kFoldStride + rl * 16) = pv;
       }
-
-      if (fast) emit_chunk<POOL>(a, rc, chunk, s);
-      ++k_seq;
+      // sequential fold of this pass's heads: lane e folds entry e
+      wave_lds_order();
+      v4f f[kPassHeads / 4];
+#pragma unroll
+      for (int j = 0; j < kPassHeads / 4; ++j) f[j] = *reinterpret_cast<const v4f*>(fold_r + 4 * j);
+#pragma unroll
+      for (int j = 0; j < kPassHeads / 4; ++j) {
+        s = s + f[j][0];
+        s = s + f[j][1];
+        s = s + f[j][2];
+        s = s + f[j][3];
+      }
+      wave_lds_order();
     }
+    emit_chunk<POOL>(a, rc, chunk, s, page_ok);
   }
 
   // ---- deferred chunks: general exact path
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __builtin_amdgcn_wave_barrier();
+  wave_lds_order();
   for (int k = 0; k < k_seq; ++k) {
     if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
-    const int itk = it0 + slice + k * n_slices;
-    RowCtx rk;
-    row_ctx<POOL>(a, itk / a.chunks_per_row, t_full, rk);
-    const int64_t qrow_k = ((int64_t)rk.b * a.T + rk.t) * HI;
-    my_w[lane] = lane < HI ? a.w[qrow_k + lane] * 0x1p-18f : 0.0f;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    const int chunk = itk % a.chunks_per_row;
-    const float s = general_chunk<POOL>(a, rk, chunk, qrow_k, lut_bytes, my_fold, my_w);
-    emit_chunk<POOL>(a, rk, chunk, s);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    const int ck = c0 + slice + k * n_slices;
+    bool ok;
+    const float s = general_chunk<POOL>(a, rc, ck, qrow0, lut_bytes, my_fold, ok);
+    emit_chunk<POOL>(a, rc, ck, s, ok);
   }
 }
 
@@ -1061,10 +1045,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// One resident workgroup per compute unit (the scan uses ~132 KB of LDS);
-// each takes a contiguous range of 32-entry chunks.  With T tokens sharing a
-// workgroup, every wave covers chunks_per_wg * T / 8 chunks.
-int persistent_grid(int total_chunks, int T, int* chunks_per_wg) {
+// Workgroups of the scan: each takes a range of chunks inside one row, about
+// one workgroup per compute unit in total (the scan uses ~138 KB of LDS).
+// With T tokens sharing a workgroup, every wave covers chunks_per_wg * T / 8
+// chunks of the range.
+int score_grid(int rows, int chunks_per_row, int T, int* chunks_per_wg, int* wg_per_row) {
   static int n_cu = 0;
   if (n_cu == 0) {
     int dev = 0;
@@ -1073,12 +1058,14 @@ int persistent_grid(int total_chunks, int T, int* chunks_per_wg) {
       n_cu = 256;
   }
   const int slices = csa2::kWaves / T;
-  int per = (total_chunks + n_cu - 1) / n_cu;
+  const int want = std::max(1, n_cu / rows);
+  int per = (chunks_per_row + want - 1) / want;
   per = ((per + slices - 1) / slices) * slices;  // whole rounds of the waves
-  // each wave tracks at most kMaxWaveChunks chunks; beyond that, more workgroups
+  // each wave tracks at most kMaxWaveChunks chunks
   per = std::min(per, csa2::kMaxWaveChunks * slices);
   *chunks_per_wg = per;
-  return (total_chunks + per - 1) / per;
+  *wg_per_row = (chunks_per_row + per - 1) / per;
+  return rows * *wg_per_row;
 }
 
 int check_index_common(const void* q_idx, const void* w, const void* kidx, int64_t n_pages,
@@ -1135,7 +1122,7 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
                                        align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4));
   sa.rows = B;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
-  const int gx = persistent_grid(sa.rows * sa.chunks_per_row, T, &sa.chunks_per_wg);
+  const int gx = score_grid(sa.rows, sa.chunks_per_row, T, &sa.chunks_per_wg, &sa.wg_per_row);
   CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx), dim3(csa2::kScoreThreads),
               (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
@@ -1186,7 +1173,7 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   sa.out_s = reinterpret_cast<float*>(ws);
   sa.rows = B * T;
   sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
-  const int gx = persistent_grid(sa.rows * sa.chunks_per_row, 1, &sa.chunks_per_wg);
+  const int gx = score_grid(sa.rows, sa.chunks_per_row, 1, &sa.chunks_per_wg, &sa.wg_per_row);
   CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads),
               (hipStream_t)stream, sa);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
