@@ -38,6 +38,11 @@ constexpr int kPassRT = 2;                   // row tiles folded per pass
 constexpr int kPassHeads = kPassRT * 16;     // heads folded per pass
 constexpr int kFoldStride = kPassHeads + 4;  // floats per entry row of the fold buffer
 constexpr int kMaxWaveChunks = 1024;         // chunks one wave may take in one launch
+// A workgroup's chunks of one row: at most 1016 * 64 = 65,024 entries per
+// token, so its 16-bit histogram counters cannot overflow.
+constexpr int kMaxWgChunks = 1016;
+// Level-1 histogram of the selections: score keys by their top 10 bits.
+constexpr int kHistBins = 1024;
 constexpr int kBufferFlags = 0x00020000;     // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
 // Lookup table: for every E4M3 code, the limbs of M = value * 2^9 as bytes
@@ -171,7 +176,14 @@ struct ScoreArgs {
   int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
   int chunks_per_wg;      // chunks of one row per workgroup
   int wg_per_row;         // workgroups per row
+  uint32_t* hist;         // [B][T][2][kHistBins], zeroed before the launch: counts of the
+                          // visible entries' and the blocks' score keys by their top 10 bits
 };
+
+// Adds 1 to bin `bin` of a histogram of 16-bit counters packed two per word.
+__device__ __forceinline__ void hist_add16(uint32_t* h, uint32_t bin) {
+  atomicAdd(&h[bin >> 1], 1u << ((bin & 1u) << 4));
+}
 
 // Keys of one chunk for one wave: lane (g, col) holds entry 16*st + col of
 // the chunk, channels [16g, 16g+16) and [64+16g, 64+16g+16).
@@ -265,21 +277,24 @@ __device__ __forceinline__ bool load_chunk(const ScoreArgs& a, const RowCtx& r, 
 
 // Writes the chunk's scores (lane e: entry e of the chunk; NaN, i.e. key 0,
 // for positions that are not visible) and, in Full mode, the maxima of its
-// blocks of 8.
+// blocks of 8.  Counts the visible entries' keys in hist_s and the blocks'
+// in hist_bm (LDS, 16-bit counters).
 template <bool POOL>
 __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, float s,
-                                           bool page_ok) {
+                                           bool page_ok, uint32_t* hist_s, uint32_t* hist_bm) {
   const int lane = lane_id();
   const int p = chunk * kChunk + lane;
   const bool valid = POOL ? entry_of<POOL>(a, rc, p) >= 0 : (page_ok && p < rc.n);
   float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
                                    (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
   if (p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
+  if (valid) hist_add16(hist_s, score_key(s) >> 22);
   if (!POOL) {
     const float m = group8_max(valid ? s : -__builtin_inff());
     if ((lane & 7) == 0 && p < rc.n_pos) {
-      a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] =
-          (m == -__builtin_inff()) ? u2f(0xFFFFFFFFu) : m;
+      const bool any = m != -__builtin_inff();
+      a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] = any ? m : u2f(0xFFFFFFFFu);
+      if (any) hist_add16(hist_bm, score_key(m) >> 22);
     }
   }
 }
@@ -384,11 +399,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     float fold[kWaves][kChunk * kFoldStride];
     float wsh[kWaves][kRT * 16];                  // w * 2^-18 per head
     uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
+    // per token: level-1 histograms of entry scores and block maxima,
+    // 16-bit counters packed two per word
+    uint32_t hist[CSA2_MAX_T][2][kHistBins / 2];
   };
   __shared__ Lds sm;
 
   build_lut(sm.lut);
   for (int i = threadIdx.x; i < kWaves * kMaxWaveChunks / 32; i += blockDim.x) (&sm.defer[0][0])[i] = 0u;
+  for (int i = threadIdx.x; i < CSA2_MAX_T * kHistBins; i += blockDim.x) (&sm.hist[0][0][0])[i] = 0u;
   __syncthreads();
   const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(sm.lut);
 
@@ -405,8 +424,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int c0 = (blockIdx.x % a.wg_per_row) * a.chunks_per_wg;
   const int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
   int chunk = c0 + slice;
-  if (row >= a.rows || chunk >= c1) return;  // no workgroup barrier follows
-
+  uint32_t* hist_s = sm.hist[t_full][0];
+  uint32_t* hist_bm = sm.hist[t_full][1];
+  if (row < a.rows && chunk < c1) {
   RowCtx rc;
   row_ctx<POOL>(a, row, t_full, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
@@ -536,7 +556,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       }
       wave_lds_order();
     }
-    emit_chunk<POOL>(a, rc, chunk, s, page_ok);
+    emit_chunk<POOL>(a, rc, chunk, s, page_ok, hist_s, hist_bm);
   }
 
   // ---- deferred chunks: general exact path
@@ -546,8 +566,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int ck = c0 + slice + k * n_slices;
     bool ok;
     const float s = general_chunk<POOL>(a, rc, ck, qrow0, lut_bytes, my_fold, ok);
-    emit_chunk<POOL>(a, rc, ck, s, ok);
+    emit_chunk<POOL>(a, rc, ck, s, ok, hist_s, hist_bm);
   }
+  }  // this wave's chunks
+
+  // ---- the workgroup's histograms into the row's (global, 32-bit) ones
+  __syncthreads();
+  if (row < a.rows) {
+    const int n_tok = POOL ? 1 : a.T;
+    for (int i = threadIdx.x; i < n_tok * kHistBins; i += blockDim.x) {
+      const uint32_t v = (&sm.hist[0][0][0])[i];
+      if (v == 0u) continue;
+      const int t = i / kHistBins, h = (i / (kHistBins / 2)) & 1, wd = i % (kHistBins / 2);
+      const int64_t grow = POOL ? (int64_t)row : (int64_t)row * a.T + t;  // (b, t)
+      uint32_t* gh = a.hist + (grow * 2 + h) * kHistBins + 2 * wd;
+      if (v & 0xFFFFu) atomicAdd(gh, v & 0xFFFFu);
+      if (v >> 16) atomicAdd(gh + 1, v >> 16);
+    }
+  }
+}
+
+// Clears the level-1 histograms before a scan.
+__global__ void hist_zero_kernel(uint32_t* h, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) h[i] = 0u;
 }
 
 // ---------------------------------------------------------------- selection
@@ -561,22 +602,20 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;     // 2,048: 32 per lane of one wave
-constexpr int kHistCopies = 4;
-constexpr int kCandCap = 2048;             // candidates of the one-wave exact stage (32 per lane)
 constexpr int kMaxKPT = 32;
 
-// hist, sub, cand and mask are contiguous (64 KB): between the two
-// selections of a Full-mode row they hold the 16,384 staged keys.
 struct SelShared {
-  uint32_t hist[kHistCopies][kBins];  // level-1 sample histogram; radix fallback
-  uint32_t sub[2][kBins];             // level-2 histograms of the bracket's end bins; exact stage
-  uint32_t cand[kCandCap];
-  uint64_t mask[kMaxKPT * kSelWaves][2];  // per (r, wave): ballots of keys above / equal to tau
+  union {
+    uint32_t staged[16 * kSelThreads];  // the gathered pool keys (Full mode, top-k pass input)
+    struct {
+      uint32_t bins[kBins];                    // one radix level's histogram
+      uint64_t mask[kMaxKPT * kSelWaves][2];   // per (r, wave): ballots of keys above / equal to tau
+    } w;
+  } u;
   int wave_tot[kSelWaves];
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
-static_assert(offsetof(SelShared, wave_tot) == 65536, "staging area layout");
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS round trip).
@@ -608,24 +647,6 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   *total = __builtin_amdgcn_readlane(wt, kSelWaves - 1);
   __syncthreads();
   return before + x - v;
-}
-
-// One wave: merge the 4 copies of the 32 bins lane l owns (bins
-// [2048 - 32(l+1), 2048 - 32l), lane 0 has the highest digits) into copy 0
-// and return their total.
-__device__ __forceinline__ uint32_t wave_merge_bins(SelShared& sh, int lane) {
-  uint32_t sum = 0;
-  v4u* h0 = reinterpret_cast<v4u*>(&sh.hist[0][kBins - 32 * (lane + 1)]);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    v4u v = h0[q];
-#pragma unroll
-    for (int cp = 1; cp < kHistCopies; ++cp)
-      v += reinterpret_cast<const v4u*>(&sh.hist[cp][kBins - 32 * (lane + 1)])[q];
-    h0[q] = v;
-    sum += v[0] + v[1] + v[2] + v[3];
-  }
-  return sum;
 }
 
 // One wave, histogram h of 2,048 bins (lane l owns bins [2048 - 32(l+1),
@@ -667,223 +688,95 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t sum, ui
 // Calls emit(rank, pos) for every selected position (rank = place in
 // ascending position order) and returns the number selected.
 //
-// 1. Valid count, and a histogram of a fixed 1/8 (KPT = 32) or 1/4 sample of
-//    the keys on their top 11 bits.
-// 2. The sample ranks K*n_s/n +- (3 sqrt + 8) give the two end bins of a
-//    bracket; a second sample histogram on the next 11 bits inside those bins
-//    narrows it to 22-bit key prefixes [lo_key, hi_key].
-// 3. One pass counts the keys above the bracket (A) and inside it (C) and
-//    compacts the inside keys into LDS.  If A < K <= A + C and C is small,
-//    one wave finds the exact threshold tau among them with an 8-bit radix
-//    select held in registers; otherwise a block-wide radix select over all
-//    keys runs (never needed for exactness, only as the fallback).
-// 4. Emission: every key above tau, and the first keys (in position order)
+// 1. Valid count.
+// 2. With more than K valid keys: radix select of the K-th largest key tau
+//    over 10 + 11 + 11 bits.  The first level's histogram is `l1v` (thread t
+//    holds bin t, key bits 31..22), accumulated by the scan.  It may count
+//    more keys than the list holds, but only keys below the K-th: bins above
+//    the crossing then hold the same counts as the list's own keys, and the
+//    crossing bin is the same.  The next two levels count the list's keys
+//    that match the prefix found so far.
+// 3. Emission: every key above tau, and the first keys (in position order)
 //    equal to tau up to K; ranks come from ballot masks and a prefix over
 //    the (r, wave) words.
 template <int KPT, typename Emit>
-__device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit emit) {
+__device__ int block_topk(const uint32_t (&key)[KPT], int K, uint32_t l1v, SelShared& sh, Emit emit) {
   static_assert(KPT <= kMaxKPT, "keys per thread");
+  static_assert(kBins == 2 * kSelThreads, "two bins per thread");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  constexpr int kSampleEvery = KPT >= 32 ? 8 : 4;  // sample r with r % kSampleEvery == wave % kSampleEvery
-  const int rs = wave % kSampleEvery;
+  const int tid = (int)threadIdx.x;
+  uint32_t* bins = sh.u.w.bins;
 
-  // ---- 1. valid count and level-1 sample histogram
-  for (int i = threadIdx.x; i < (kHistCopies + 2) * kBins / 4; i += kSelThreads)
-    reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};  // hist and sub are contiguous
-  __syncthreads();
+  // ---- 1. valid count; the level-1 histogram goes to bins [0, 1024)
   int valid = 0;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const uint32_t k = key[r];
-    valid += k != 0;
-    if ((r % kSampleEvery) == rs && k != 0) atomicAdd(&sh.hist[lane & 3][k >> 21], 1u);
-  }
+  for (int r = 0; r < KPT; ++r) valid += key[r] != 0;
   valid = wave_sum(valid);
   if (lane == 0) sh.wave_tot[wave] = valid;
+  bins[tid] = l1v;
+  bins[tid + kSelThreads] = 0u;
   __syncthreads();
-  int n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
+  const int n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
 
-  uint32_t tau = 0;   // with tau = 0 every valid key is selected
+  uint32_t tau = 0;  // with tau = 0 every valid key is selected
   int need_eq = 0;
   if (n_valid > K) {
-    // ---- 2. bracket from the sample: level 1 (bits 31..21)
-    if (wave == 0) {
-      const uint32_t sum = wave_merge_bins(sh, lane);
-      const uint32_t n_s = (uint32_t)wave_sum((int)sum);
-      const float ts = (float)K * (float)n_s / (float)n_valid;  // expected sample rank of the K-th key
-      const float m = 3.0f * sqrtf(ts) + 8.0f;
-      const float x_hi = ts - m, x_lo = ts + m;
-      uint32_t ab_hi = 0, ab_lo = 0;
-      const int b_hi = x_hi <= 0.0f ? -2 : wave_crossing(sh.hist[0], sum, 0, x_hi, &ab_hi, lane);
-      const int b_lo = wave_crossing(sh.hist[0], sum, 0, x_lo, &ab_lo, lane);
-      if (lane == 0) {
-        sh.misc[0] = b_hi;  // < 0: no upper cut
-        sh.misc[1] = b_lo;  // < 0: the lower cut lies below every sample
-        sh.misc[2] = __float_as_int(x_hi - (float)ab_hi);
-        sh.misc[3] = __float_as_int(x_lo - (float)ab_lo);
-      }
-    }
-    __syncthreads();
-    const int b_hi = sh.misc[0], b_lo = sh.misc[1];
-    // ---- level 2: bits 20..10 of the samples inside the end bins
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const uint32_t k = key[r];
-      if ((r % kSampleEvery) != rs || k == 0) continue;
-      const int d1 = (int)(k >> 21);
-      const uint32_t d2 = (k >> 10) & (kBins - 1);
-      if (d1 == b_hi) atomicAdd(&sh.sub[0][d2], 1u);
-      else if (d1 == b_lo) atomicAdd(&sh.sub[1][d2], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t hi_key = 0xFFFFFFFFu, lo_key = 1u;
-      if (b_hi >= 0) {
+    // ---- 2. radix select
+    uint32_t prefix = 0, msk = 0;
+    int rem = K;
+    // one wave: the bin holding rank `rem` of the current histogram
+    auto cross = [&]() {
+      if (wave == 0) {
+        const v4u* mine = reinterpret_cast<const v4u*>(bins + kBins - 32 * (lane + 1));
         uint32_t sum = 0;
-        const v4u* hv = reinterpret_cast<const v4u*>(&sh.sub[0][kBins - 32 * (lane + 1)]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
+        for (int q = 0; q < 8; ++q) sum += mine[q][0] + mine[q][1] + mine[q][2] + mine[q][3];
         uint32_t ab;
-        int s = wave_crossing(sh.sub[0], sum, 0, __int_as_float(sh.misc[2]), &ab, lane);
-        if (s < 0) s = kBins - 1;  // cannot happen (the bin holds the rank); keep the cut conservative
-        hi_key = ((uint32_t)b_hi << 21) | ((uint32_t)s << 10) | 0x3FFu;
+        const int d = wave_crossing(bins, sum, 0, (float)rem, &ab, lane);
+        if (lane == 0) {
+          sh.misc[0] = d;
+          sh.misc[1] = (int)ab;
+        }
       }
-      if (b_lo >= 0) {
-        const uint32_t* h = sh.sub[b_lo == b_hi ? 0 : 1];
-        uint32_t sum = 0;
-        const v4u* hv = reinterpret_cast<const v4u*>(h + kBins - 32 * (lane + 1));
-#pragma unroll
-        for (int q = 0; q < 8; ++q) sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
-        uint32_t ab;
-        int s = wave_crossing(h, sum, 0, __int_as_float(sh.misc[3]), &ab, lane);
-        if (s < 0) s = 0;  // cannot happen; keep the cut conservative
-        lo_key = max(((uint32_t)b_lo << 21) | ((uint32_t)s << 10), 1u);
-      }
-      if (lane == 0) {
-        sh.misc[4] = (int)hi_key;
-        sh.misc[5] = (int)lo_key;
-      }
-    }
-    __syncthreads();
-    const uint32_t hi_key = (uint32_t)sh.misc[4];
-    const uint32_t lo_key = min((uint32_t)sh.misc[5], hi_key);
-    // ---- 3. exact counts around the bracket and candidate compaction
-    int n_above = 0, n_in = 0;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const uint32_t k = key[r];
-      n_above += k > hi_key;
-      n_in += k >= lo_key && k <= hi_key;  // lo_key >= 1 excludes empty slots
-    }
-    int tot;
-    const int packed_off = block_excl_scan(n_above | (n_in << 16), sh, &tot);
-    // both counts are at most 32,768: the halves never carry; decode unsigned
-    const int A = tot & 0xFFFF, C = (int)((uint32_t)tot >> 16);
-    if (A < K && K <= A + C && C <= kCandCap) {
-      int o = (int)((uint32_t)packed_off >> 16);
+      __syncthreads();
+      return sh.misc[0];
+    };
+    // histogram of digit (key >> shift) & dmask over the keys matching the prefix
+    auto build = [&](int shift, uint32_t dmask) {
+      bins[tid] = 0u;
+      bins[tid + kSelThreads] = 0u;
+      __syncthreads();
 #pragma unroll
       for (int r = 0; r < KPT; ++r) {
         const uint32_t k = key[r];
-        if (k >= lo_key && k <= hi_key) sh.cand[o++] = k;
+        if (k != 0u && (k & msk) == prefix) atomicAdd(&bins[(k >> shift) & dmask], 1u);
       }
       __syncthreads();
-      if (wave == 0) {
-        // ---- one wave: the (K - A)-th largest candidate, 8-bit digits below
-        // the common prefix of lo_key and hi_key
-        // candidates are re-read from LDS on every pass, 8 per lane at a time
-        constexpr int kCPL = kCandCap / 64;
-        constexpr int kGroup = 8;
-        const uint32_t diff = lo_key ^ hi_key;
-        const int top = diff == 0 ? -1 : 31 - __builtin_clz(diff);
-        uint32_t msk = top >= 31 ? 0u : ~((2u << top) - 1u);
-        if (top < 0) msk = 0xFFFFFFFFu;
-        uint32_t prefix = hi_key & msk;
-        int rem = K - A;
-        uint32_t* bins = sh.sub[0];
-        for (int shift = top + 1; shift > 0;) {
-          const int width = min(kDigitBits, shift);
-          shift -= width;
-          const uint32_t dmask = (1u << width) - 1u;
-          v4u* mine = reinterpret_cast<v4u*>(bins + kBins - 32 * (lane + 1));
-#pragma unroll
-          for (int q = 0; q < 8; ++q) mine[q] = v4u{0u, 0u, 0u, 0u};
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-          for (int j0 = 0; j0 < kCPL; j0 += kGroup) {
-            if (j0 * 64 >= C) break;
-            uint32_t c[kGroup];
-#pragma unroll
-            for (int j = 0; j < kGroup; ++j) {
-              const int idx = (j0 + j) * 64 + lane;
-              c[j] = idx < C ? sh.cand[idx] : 0u;
-            }
-#pragma unroll
-            for (int j = 0; j < kGroup; ++j)
-              if (c[j] != 0u && (c[j] & msk) == prefix) atomicAdd(&bins[(c[j] >> shift) & dmask], 1u);
-          }
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-          uint32_t sum = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) sum += mine[q][0] + mine[q][1] + mine[q][2] + mine[q][3];
-          uint32_t ab;
-          // the rank lies in exactly one bin
-          const int d = wave_crossing(bins, sum, 0, (float)rem, &ab, lane);
-          prefix |= (uint32_t)d << shift;
-          msk |= dmask << shift;
-          rem -= (int)ab;
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-        }
-        if (lane == 0) {
-          sh.misc[6] = (int)prefix;
-          sh.misc[7] = rem;
-        }
-      }
-      __syncthreads();
-      tau = (uint32_t)sh.misc[6];
-      need_eq = sh.misc[7];
-    } else {
-      // ---- fallback: block-wide radix select over all keys (32 = 11 + 11 + 10 bits)
-      uint32_t prefix = 0, mask = 0;
-      int rem = K;
-      int shift = 32;
-      while (shift > 0) {
-        const int width = min(kDigitBits, shift);
-        shift -= width;
-        const uint32_t dmask = (1u << width) - 1u;
-        for (int i = threadIdx.x; i < kHistCopies * kBins / 4; i += kSelThreads)
-          reinterpret_cast<v4u*>(&sh.hist[0][0])[i] = v4u{0u, 0u, 0u, 0u};
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-          const uint32_t k = key[r];
-          if (k != 0 && (k & mask) == prefix) atomicAdd(&sh.hist[lane & 3][(k >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-          const uint32_t sum = wave_merge_bins(sh, lane);
-          uint32_t ab;
-          const int d = wave_crossing(sh.hist[0], sum, 0, (float)rem, &ab, lane);
-          if (lane == 0) {
-            sh.misc[0] = d;
-            sh.misc[1] = (int)ab;
-          }
-        }
-        __syncthreads();
-        const uint32_t d = (uint32_t)sh.misc[0];
-        rem -= sh.misc[1];
-        prefix |= d << shift;
-        mask |= dmask << shift;
-        __syncthreads();
-      }
-      tau = prefix;
-      need_eq = rem;
+    };
+    int d = cross();
+    if (d < 0) {
+      // the scan's histogram holds fewer than K keys above the list's K-th:
+      // never for a consistent input; count the list's own keys instead
+      build(22, 1023u);
+      d = cross();
     }
+    prefix = (uint32_t)d << 22;
+    msk = 1023u << 22;
+    rem -= sh.misc[1];
+#pragma unroll
+    for (int shift = 11; shift >= 0; shift -= 11) {
+      build(shift, 2047u);
+      d = cross();
+      prefix |= (uint32_t)d << shift;
+      msk |= 2047u << shift;
+      rem -= sh.misc[1];
+    }
+    tau = prefix;
+    need_eq = rem;
   }
 
-  // ---- 4. emit in position order.  Word i = (r, wave) covers positions
+  // ---- 3. emit in position order.  Word i = (r, wave) covers positions
   // [1024 r + 64 wave, +64); bit l of its masks is position + l.
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
@@ -891,8 +784,8 @@ __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit
     const uint64_t mg = __ballot(k > tau);
     const uint64_t me = __ballot(k != 0 && k == tau);
     if (lane == 0) {
-      sh.mask[r * kSelWaves + wave][0] = mg;
-      sh.mask[r * kSelWaves + wave][1] = me;
+      sh.u.w.mask[r * kSelWaves + wave][0] = mg;
+      sh.u.w.mask[r * kSelWaves + wave][1] = me;
     }
   }
   __syncthreads();
@@ -900,8 +793,8 @@ __device__ int block_topk(const uint32_t (&key)[KPT], int K, SelShared& sh, Emit
   const int i = (int)threadIdx.x;
   uint64_t mg = 0, me = 0;
   if (i < kWords) {
-    mg = sh.mask[i][0];
-    me = sh.mask[i][1];
+    mg = sh.u.w.mask[i][0];
+    me = sh.u.w.mask[i][1];
   }
   int tot2;
   const int pre = block_excl_scan(__builtin_popcountll(mg) | (__builtin_popcountll(me) << 16), sh, &tot2);
@@ -941,6 +834,7 @@ struct SelectArgs {
   int32_t* out_topk;         // [B][T][topk]
   int32_t* out_pool;         // full: [B][T][pool_blocks]
   int32_t* out_pool_n;       // full: [B][T]
+  const uint32_t* hist;      // [B][T][2][1024]: level-1 counts of entry scores, block maxima
 };
 
 // One workgroup per (b, t).  FULL: select the pool from block maxima, then
@@ -955,6 +849,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   n = max(n, 0);
   const int nb = (n + kBlock - 1) / kBlock;
   const int P = a.pool_blocks;
+  // level-1 histograms the scan accumulated (thread t: bin t), loaded early
+  const uint32_t l1_s = a.hist[((int64_t)row * 2 + 0) * kHistBins + threadIdx.x];
+  const uint32_t l1_bm = FULL ? a.hist[((int64_t)row * 2 + 1) * kHistBins + threadIdx.x] : 0u;
   int pool_n;
   if (FULL) {
     const float* bm = a.bm + (int64_t)row * bm_stride(a.max_n);
@@ -977,7 +874,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       key[r] = blk < nb ? score_key(__uint_as_float(key[r])) : 0u;
     }
     for (int i = threadIdx.x; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
-    pool_n = block_topk<KPT>(key, P, sh, [&](int rank, int pos) { sh.pool_blk[rank] = pos; });
+    pool_n = block_topk<KPT>(key, P, l1_bm, sh, [&](int rank, int pos) { sh.pool_blk[rank] = pos; });
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = sh.pool_blk[i];
     if (threadIdx.x == 0) a.out_pool_n[row] = pool_n;
@@ -995,7 +892,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const float* srow = FULL ? a.s + (int64_t)row * s_stride(a.max_n) : a.s + (int64_t)row * P * kBlock;
   const uint32_t row_bytes = FULL ? (uint32_t)s_stride(a.max_n) * 4u : (uint32_t)P * kBlock * 4u;
   const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, row_bytes, kBufferFlags);
-  uint32_t* staged = &sh.hist[0][0];
+  uint32_t* staged = sh.u.staged;
   {
     v4u g[2][2];
     int blk[2];
@@ -1033,7 +930,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   for (int r = 0; r < KPT2; ++r) key2[r] = staged[r * kSelThreads + (int)threadIdx.x];
   __syncthreads();  // the selection below reuses the staging area
   int32_t* out = a.out_topk + (int64_t)row * a.topk;
-  const int got = block_topk<KPT2>(key2, a.topk, sh, [&](int rank, int p) {
+  // Full mode: the level-1 counts are those of every entry of the row; the
+  // top-k lies inside the pool, so entries outside it all rank below the
+  // k-th and the pool's own counts agree above the crossing bin
+  const int got = block_topk<KPT2>(key2, a.topk, l1_s, sh, [&](int rank, int p) {
     out[rank] = sh.pool_blk[p >> 3] * kBlock + (p & 7);
   });
   for (int i = got + threadIdx.x; i < a.topk; i += kSelThreads) out[i] = -1;
@@ -1061,8 +961,9 @@ int score_grid(int rows, int chunks_per_row, int T, int* chunks_per_wg, int* wg_
   const int want = std::max(1, n_cu / rows);
   int per = (chunks_per_row + want - 1) / want;
   per = ((per + slices - 1) / slices) * slices;  // whole rounds of the waves
-  // each wave tracks at most kMaxWaveChunks chunks
-  per = std::min(per, csa2::kMaxWaveChunks * slices);
+  // each wave tracks at most kMaxWaveChunks chunks; the workgroup's 16-bit
+  // histogram counters hold at most kMaxWgChunks chunks of one token
+  per = std::min(per, std::min(csa2::kMaxWaveChunks * slices, csa2::kMaxWgChunks));
   *chunks_per_wg = per;
   *wg_per_row = (chunks_per_row + per - 1) / per;
   return rows * *wg_per_row;
@@ -1083,13 +984,34 @@ int check_index_common(const void* q_idx, const void* w, const void* kidx, int64
 }
 }  // namespace
 
+// Workspace: scores, block maxima (Full mode), level-1 histograms.
+size_t hist_bytes(int32_t B, int32_t T) { return align256((size_t)B * T * 2 * csa2::kHistBins * 4); }
+
 extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_n,
                                       int32_t pool_blocks) {
   if (op == CSA2_OP_INDEX_FULL) {
     const size_t nb = (size_t)csa2::bm_stride(max_n);
-    return align256((size_t)B * T * csa2::s_stride(max_n) * 4) + align256((size_t)B * T * nb * 4);
+    return align256((size_t)B * T * csa2::s_stride(max_n) * 4) + align256((size_t)B * T * nb * 4) +
+           hist_bytes(B, T);
   }
-  return align256((size_t)B * T * pool_blocks * 8 * 4);
+  return align256((size_t)B * T * pool_blocks * 8 * 4) + hist_bytes(B, T);
+}
+
+// Launches the histogram clear, then the scan.
+int launch_scan(bool pool, const csa2::ScoreArgs& sa, int T_grid, int B, int T, hipStream_t stream) {
+  const int nh = B * T * 2 * csa2::kHistBins;
+  hipLaunchKernelGGL(csa2::hist_zero_kernel, dim3(std::min((nh + 1023) / 1024, 64)), dim3(1024), 0, stream,
+                     sa.hist, nh);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  csa2::ScoreArgs args = sa;
+  const int gx = score_grid(args.rows, args.chunks_per_row, T_grid, &args.chunks_per_wg, &args.wg_per_row);
+  if (pool)
+    CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads), stream,
+                args);
+  else
+    CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx), dim3(csa2::kScoreThreads), stream,
+                args);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }
 
 extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
@@ -1120,12 +1042,13 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   sa.out_s = reinterpret_cast<float*>(ws);
   sa.out_bm = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                        align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4));
+  sa.hist = reinterpret_cast<uint32_t*>(
+      reinterpret_cast<char*>(ws) + align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4) +
+      align256((size_t)B * T * csa2::bm_stride(max_n_entries) * 4));
   sa.rows = B;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
-  const int gx = score_grid(sa.rows, sa.chunks_per_row, T, &sa.chunks_per_wg, &sa.wg_per_row);
-  CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx), dim3(csa2::kScoreThreads),
-              (hipStream_t)stream, sa);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  st = launch_scan(false, sa, T, B, T, (hipStream_t)stream);
+  if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
   se.bm = sa.out_bm;
@@ -1138,6 +1061,7 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   se.out_topk = out_topk;
   se.out_pool = out_pool;
   se.out_pool_n = out_pool_n;
+  se.hist = sa.hist;
   CSA2_LAUNCH(CSA2_K_SELECT_FULL, csa2::select_kernel<true>, dim3(B * T), dim3(csa2::kSelThreads),
               (hipStream_t)stream, se);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
@@ -1171,12 +1095,12 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   sa.pool_n = pool_n;
   sa.pool_blocks = pool_blocks;
   sa.out_s = reinterpret_cast<float*>(ws);
+  sa.hist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) +
+                                        align256((size_t)B * T * pool_blocks * 8 * 4));
   sa.rows = B * T;
   sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
-  const int gx = score_grid(sa.rows, sa.chunks_per_row, 1, &sa.chunks_per_wg, &sa.wg_per_row);
-  CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads),
-              (hipStream_t)stream, sa);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  st = launch_scan(true, sa, 1, B, T, (hipStream_t)stream);
+  if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
   se.n_entries = n_entries;
@@ -1187,6 +1111,7 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   se.pool_blocks = pool_blocks;
   se.pool_in = pool;
   se.pool_n_in = pool_n;
+  se.hist = sa.hist;
   se.out_topk = out_topk;
   CSA2_LAUNCH(CSA2_K_SELECT_REINDEX, csa2::select_kernel<false>, dim3(B * T),
               dim3(csa2::kSelThreads), (hipStream_t)stream, se);
