@@ -605,17 +605,29 @@ constexpr int kBins = 1 << kDigitBits;     // 2,048: 32 per lane of one wave
 constexpr int kMaxKPT = 32;
 
 struct SelShared {
-  union {
-    uint32_t staged[16 * kSelThreads];  // the gathered pool keys (Full mode, top-k pass input)
-    struct {
-      uint32_t bins[kBins];                    // one radix level's histogram
-      uint64_t mask[kMaxKPT * kSelWaves][2];   // per (r, wave): ballots of keys above / equal to tau
-    } w;
-  } u;
+  uint32_t stage[kMaxKPT * kSelThreads];  // the block maxima, in transit to their threads
+  uint32_t bins[kBins];                   // one radix level's histogram
   int wave_tot[kSelWaves];
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Dword of SelShared::stage holding list position p: thread t = p / 32
+// reads its 32 positions as 8 16-byte pieces q = (p / 4) % 8, placed at
+// piece q ^ ((t / 2) % 8) of its row, so that both the coalesced writes and
+// the per-thread reads of 16 lanes cover all 64 banks.
+__device__ __forceinline__ int stage_addr(int p) {
+  const int t = p >> 5, q = (p >> 2) & 7;
+  return (t << 5) + ((q ^ ((t >> 1) & 7)) << 2) + (p & 3);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS round trip).
@@ -640,182 +652,186 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) sh.wave_tot[wave] = x;
-  __syncthreads();
+  lds_barrier();
   // lanes 0..15 hold the wave totals: one read, then a scan in registers
   const int wt = (int)wave_incl_scan(lane < kSelWaves ? (uint32_t)sh.wave_tot[lane] : 0u);
   const int before = wave > 0 ? __builtin_amdgcn_readlane(wt, wave - 1) : 0;
   *total = __builtin_amdgcn_readlane(wt, kSelWaves - 1);
-  __syncthreads();
+  lds_barrier();
   return before + x - v;
 }
 
 // One wave, histogram h of 2,048 bins (lane l owns bins [2048 - 32(l+1),
-// 2048 - 32l)), `above` samples lie above all of them.  For the rank x
-// (counted from the top, 1-based, real-valued) returns the bin holding it
-// (-1 if x is beyond the last bin) and writes the count above that bin.
-__device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t sum, uint32_t above0, float x,
-                                             uint32_t* above_bin, int lane) {
-  const uint32_t incl = wave_incl_scan(sum);
-  uint32_t above = above0 + incl - sum;
-  int bin = -1;
-  uint32_t ab = 0;
+// 2048 - 32l), lane 0 has the highest digits).  For the rank x >= 1 (counted
+// from the top) returns the bin holding it (-1 if the histogram holds fewer
+// than x keys) and writes the count above that bin.  The lane whose range
+// holds the rank is found by a scan of the lane totals; its 32 bins are then
+// scanned across lanes 0..31.
+__device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint32_t* above_bin, int lane) {
   const v4u* hv = reinterpret_cast<const v4u*>(h + kBins - 32 * (lane + 1));
-  for (int q = 7; q >= 0; --q) {
-    const v4u v = hv[q];
+  uint32_t sum = 0;
 #pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      const float prev = (float)above;
-      above += v[e];
-      if ((float)above >= x && prev < x) {
-        bin = kBins - 32 * (lane + 1) + 4 * q + e;
-        ab = above - v[e];
-      }
-    }
+  for (int q = 0; q < 8; ++q) {
+    const v4u v = hv[q];
+    sum += v[0] + v[1] + v[2] + v[3];
   }
-  // at most one lane found the crossing
-  const uint64_t who = __ballot(bin >= 0);
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint64_t who = __ballot(incl - sum < x && x <= incl);
   if (who == 0) {
     *above_bin = 0;
     return -1;
   }
   const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(who));
-  *above_bin = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
-  return __builtin_amdgcn_readlane(bin, src);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), src);
+  // lane j < 32 takes the j-th highest bin of lane src
+  const int top_bin = kBins - 32 * src - 1;
+  const uint32_t c = lane < 32 ? h[top_bin - lane] : 0u;
+  const uint32_t ci = wave_incl_scan(c);
+  const uint64_t hit = __ballot(lane < 32 && above + ci >= x);
+  const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  *above_bin = above + (uint32_t)__builtin_amdgcn_readlane((int)(ci - c), j);
+  return top_bin - j;
 }
 
-// Top-K selection among the keys of the list (thread t holds positions
-// t + 1024 r), order (key desc, position asc); key 0 marks an empty slot.
-// Calls emit(rank, pos) for every selected position (rank = place in
-// ascending position order) and returns the number selected.
+// Top-K selection among the keys of a list (thread t holds positions
+// KPT t + r), order (key desc, position asc); key 0 marks an empty slot.
+// Two steps, so that the first overlaps the loads of the keys:
 //
-// 1. Valid count.
-// 2. With more than K valid keys: radix select of the K-th largest key tau
-//    over 10 + 11 + 11 bits.  The first level's histogram is `l1v` (thread t
-//    holds bin t, key bits 31..22), accumulated by the scan.  It may count
-//    more keys than the list holds, but only keys below the K-th: bins above
-//    the crossing then hold the same counts as the list's own keys, and the
-//    crossing bin is the same.  The next two levels count the list's keys
-//    that match the prefix found so far.
-// 3. Emission: every key above tau, and the first keys (in position order)
-//    equal to tau up to K; ranks come from ballot masks and a prefix over
-//    the (r, wave) words.
-template <int KPT, typename Emit>
-__device__ int block_topk(const uint32_t (&key)[KPT], int K, uint32_t l1v, SelShared& sh, Emit emit) {
-  static_assert(KPT <= kMaxKPT, "keys per thread");
+// topk_level1: from `l1v`, the histogram the scan accumulated of the list's
+//    keys by their top 10 bits (thread t holds bin t), the number of valid
+//    keys and, with more than K, the first radix digit of the K-th largest
+//    key.  The histogram may count more keys than the list holds, but only
+//    keys below the K-th: bins above the crossing then hold the same counts
+//    as the list's own keys, the crossing bin is the same, and the list
+//    holds more than K valid keys exactly when the histogram does, or
+//    exactly K.
+// topk_finish: the next two digits (11 + 11 bits) from histograms of the
+//    list's keys that match the prefix so far, which gives the K-th largest
+//    key tau; then every key above tau, and the first keys (in position
+//    order) equal to tau up to K, are emitted: emit(rank, pos) with rank =
+//    place in ascending position order.  A thread's rank base is a prefix
+//    over the threads' counts, since its positions are contiguous.  Returns
+//    the number selected.
+struct TopkState {
+  int n_valid;
+  uint32_t prefix, msk;
+  int rem;
+  bool l1_ok;
+};
+
+// One wave finds the bin holding rank `rem` of sh.bins; all threads return it.
+__device__ __forceinline__ int bins_cross(SelShared& sh, int rem, int* above) {
+  const int lane = lane_id();
+  if (threadIdx.x < 64) {
+    uint32_t ab;
+    const int d = wave_crossing(sh.bins, (uint32_t)rem, &ab, lane);
+    if (lane == 0) {
+      sh.misc[0] = d;
+      sh.misc[1] = (int)ab;
+    }
+  }
+  lds_barrier();
+  *above = sh.misc[1];
+  return sh.misc[0];
+}
+
+__device__ TopkState topk_level1(uint32_t l1v, int K, SelShared& sh) {
   static_assert(kBins == 2 * kSelThreads, "two bins per thread");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tid = (int)threadIdx.x;
-  uint32_t* bins = sh.u.w.bins;
+  TopkState st{0, 0u, 0u, K, true};
+  // the level-1 digits occupy bins [0, 1024)
+  sh.bins[tid] = l1v;
+  sh.bins[tid + kSelThreads] = 0u;
+  const int wv = wave_sum((int)l1v);
+  if (lane == 0) sh.wave_tot[wave] = wv;
+  lds_barrier();
+  st.n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
+  if (st.n_valid > K) {
+    int ab;
+    const int d = bins_cross(sh, K, &ab);
+    if (d < 0) {
+      st.l1_ok = false;  // never for a consistent input (see topk_finish)
+    } else {
+      st.prefix = (uint32_t)d << 22;
+      st.msk = 1023u << 22;
+      st.rem = K - ab;
+    }
+  }
+  // sh.bins and sh.wave_tot are reused next: every thread has read them
+  lds_barrier();
+  return st;
+}
 
-  // ---- 1. valid count; the level-1 histogram goes to bins [0, 1024)
-  int valid = 0;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) valid += key[r] != 0;
-  valid = wave_sum(valid);
-  if (lane == 0) sh.wave_tot[wave] = valid;
-  bins[tid] = l1v;
-  bins[tid + kSelThreads] = 0u;
-  __syncthreads();
-  const int n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
-
+template <int KPT, typename Emit>
+__device__ int topk_finish(const uint32_t (&key)[KPT], int K, TopkState st, SelShared& sh, Emit emit) {
+  static_assert(KPT <= kMaxKPT, "keys per thread");
+  const int tid = (int)threadIdx.x;
+  uint32_t* bins = sh.bins;
   uint32_t tau = 0;  // with tau = 0 every valid key is selected
   int need_eq = 0;
-  if (n_valid > K) {
-    // ---- 2. radix select
-    uint32_t prefix = 0, msk = 0;
-    int rem = K;
-    // one wave: the bin holding rank `rem` of the current histogram
-    auto cross = [&]() {
-      if (wave == 0) {
-        const v4u* mine = reinterpret_cast<const v4u*>(bins + kBins - 32 * (lane + 1));
-        uint32_t sum = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) sum += mine[q][0] + mine[q][1] + mine[q][2] + mine[q][3];
-        uint32_t ab;
-        const int d = wave_crossing(bins, sum, 0, (float)rem, &ab, lane);
-        if (lane == 0) {
-          sh.misc[0] = d;
-          sh.misc[1] = (int)ab;
-        }
-      }
-      __syncthreads();
-      return sh.misc[0];
-    };
+  if (st.n_valid > K) {
+    uint32_t prefix = st.prefix, msk = st.msk;
+    int rem = st.rem;
     // histogram of digit (key >> shift) & dmask over the keys matching the prefix
     auto build = [&](int shift, uint32_t dmask) {
       bins[tid] = 0u;
       bins[tid + kSelThreads] = 0u;
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int r = 0; r < KPT; ++r) {
         const uint32_t k = key[r];
         if (k != 0u && (k & msk) == prefix) atomicAdd(&bins[(k >> shift) & dmask], 1u);
       }
-      __syncthreads();
+      lds_barrier();
     };
-    int d = cross();
-    if (d < 0) {
-      // the scan's histogram holds fewer than K keys above the list's K-th:
-      // never for a consistent input; count the list's own keys instead
+    int d, ab;
+    if (!st.l1_ok) {
+      // the scan's histogram holds fewer than K keys above the list's K-th
+      // (never for a consistent input): count the list's own keys instead
       build(22, 1023u);
-      d = cross();
+      d = bins_cross(sh, rem, &ab);
+      prefix = (uint32_t)d << 22;
+      msk = 1023u << 22;
+      rem -= ab;
     }
-    prefix = (uint32_t)d << 22;
-    msk = 1023u << 22;
-    rem -= sh.misc[1];
 #pragma unroll
     for (int shift = 11; shift >= 0; shift -= 11) {
       build(shift, 2047u);
-      d = cross();
+      d = bins_cross(sh, rem, &ab);
       prefix |= (uint32_t)d << shift;
       msk |= 2047u << shift;
-      rem -= sh.misc[1];
+      rem -= ab;
     }
     tau = prefix;
     need_eq = rem;
   }
 
-  // ---- 3. emit in position order.  Word i = (r, wave) covers positions
-  // [1024 r + 64 wave, +64); bit l of its masks is position + l.
+  // ---- 3. emit in position order
+  uint32_t gt_m = 0, eq_m = 0;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    const uint32_t k = key[r];
-    const uint64_t mg = __ballot(k > tau);
-    const uint64_t me = __ballot(k != 0 && k == tau);
-    if (lane == 0) {
-      sh.u.w.mask[r * kSelWaves + wave][0] = mg;
-      sh.u.w.mask[r * kSelWaves + wave][1] = me;
-    }
+    gt_m |= (key[r] > tau ? 1u : 0u) << r;
+    eq_m |= (key[r] != 0u && key[r] == tau ? 1u : 0u) << r;
   }
-  __syncthreads();
-  constexpr int kWords = KPT * kSelWaves;
-  const int i = (int)threadIdx.x;
-  uint64_t mg = 0, me = 0;
-  if (i < kWords) {
-    mg = sh.u.w.mask[i][0];
-    me = sh.u.w.mask[i][1];
+  const int ngt = __builtin_popcount(gt_m), neq = __builtin_popcount(eq_m);
+  int tot;
+  // both totals are at most 32,768: the 16-bit halves never carry
+  const int pre = block_excl_scan(ngt | (neq << 16), sh, &tot);
+  const int gt_tot = tot & 0xFFFF, eq_tot = (int)((uint32_t)tot >> 16);
+  const int gt_before = pre & 0xFFFF, eq_before = (int)((uint32_t)pre >> 16);
+  // this thread's keys equal to tau that are taken: the first ones in
+  // position order, up to need_eq over the whole list
+  uint32_t sel = gt_m, m = eq_m;
+  for (int take = min(max(need_eq - eq_before, 0), neq); take > 0; --take) {
+    sel |= m & (~m + 1u);
+    m &= m - 1u;
   }
-  int tot2;
-  const int pre = block_excl_scan(__builtin_popcountll(mg) | (__builtin_popcountll(me) << 16), sh, &tot2);
-  // both totals are at most 32,768: no carry between the halves; decode unsigned
-  const int gt_tot = tot2 & 0xFFFF, eq_tot = (int)((uint32_t)tot2 >> 16);
-  if (i < kWords) {
-    const int gt_before = pre & 0xFFFF, eq_before = (int)((uint32_t)pre >> 16);
-    // the first (need_eq - eq_before) keys equal to tau, in position order
-    int take = min(max(need_eq - eq_before, 0), __builtin_popcountll(me));
-    uint64_t sel = mg, m = me;
-    for (; take > 0; --take) {
-      const uint64_t low = m & (~m + 1);
-      sel |= low;
-      m ^= low;
-    }
-    int rank = gt_before + min(eq_before, need_eq);
-    const int p0 = (i / kSelWaves) * kSelThreads + (i % kSelWaves) * 64;
-    while (sel != 0) {
-      emit(rank++, p0 + __builtin_ctzll(sel));
-      sel &= sel - 1;
-    }
+  int rank = gt_before + min(eq_before, need_eq);
+  while (sel != 0u) {
+    emit(rank++, KPT * tid + __builtin_ctz(sel));
+    sel &= sel - 1u;
   }
   return gt_tot + min(eq_tot, need_eq);
 }
@@ -844,61 +860,68 @@ template <bool FULL>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   const int row = blockIdx.x;  // b * T + t
+  const int tid = (int)threadIdx.x;
   const int b = row / a.T;
   int n = min(a.n_entries[b], min(a.max_n, a.max_pages * kPage));
   n = max(n, 0);
   const int nb = (n + kBlock - 1) / kBlock;
   const int P = a.pool_blocks;
   // level-1 histograms the scan accumulated (thread t: bin t), loaded early
-  const uint32_t l1_s = a.hist[((int64_t)row * 2 + 0) * kHistBins + threadIdx.x];
-  const uint32_t l1_bm = FULL ? a.hist[((int64_t)row * 2 + 1) * kHistBins + threadIdx.x] : 0u;
+  const uint32_t l1_s = a.hist[((int64_t)row * 2 + 0) * kHistBins + tid];
+  const uint32_t l1_bm = FULL ? a.hist[((int64_t)row * 2 + 1) * kHistBins + tid] : 0u;
   int pool_n;
   if (FULL) {
-    const float* bm = a.bm + (int64_t)row * bm_stride(a.max_n);
+    // ---- the pool: thread t holds the maxima of blocks 32 t .. 32 t + 31,
+    // loaded coalesced (piece q of thread t: blocks 4096 q + 4 t .. + 3) and
+    // passed through LDS
     constexpr int KPT = 32;  // 32,768 blocks = 262,144 entries
-    // reads past the row's nb blocks return 0 and are masked: no branch per load
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)bm, 0, nb * 4, kBufferFlags);
+    static_assert(KPT <= kMaxKPT, "stage size");
+    const float* bm = a.bm + (int64_t)row * bm_stride(a.max_n);
+    // the whole row is read (reads past it return zero; no branch per load),
+    // so the loads need not wait for n; blocks >= nb are masked below
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)bm, 0, bm_stride(a.max_n) * 4, kBufferFlags);
+    v4u raw[KPT / 4];
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q)
+      raw[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(4 * kSelThreads * q + 4 * tid) * 4u, 0, 0);
+    for (int i = tid; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
+    // the first digit comes from the histogram while the loads are in flight
+    const TopkState st = topk_level1(l1_bm, P, sh);
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q)
+      *reinterpret_cast<v4u*>(&sh.stage[stage_addr(4 * kSelThreads * q + 4 * tid)]) = raw[q];
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) raw[q] = *reinterpret_cast<const v4u*>(&sh.stage[stage_addr(KPT * tid + 4 * q)]);
     uint32_t key[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int blk = r * kSelThreads + (int)threadIdx.x;
-      key[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)blk * 4u, 0, 0);
-    }
-    // consumed unconditionally (after all loads are issued), so the compiler
-    // cannot move each load into a branch of its own
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) asm volatile("" : "+v"(key[r]));
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int blk = r * kSelThreads + (int)threadIdx.x;
-      key[r] = blk < nb ? score_key(__uint_as_float(key[r])) : 0u;
-    }
-    for (int i = threadIdx.x; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
-    pool_n = block_topk<KPT>(key, P, l1_bm, sh, [&](int rank, int pos) { sh.pool_blk[rank] = pos; });
-    __syncthreads();
-    for (int i = threadIdx.x; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = sh.pool_blk[i];
-    if (threadIdx.x == 0) a.out_pool_n[row] = pool_n;
+    for (int r = 0; r < KPT; ++r)
+      key[r] = KPT * tid + r < nb ? score_key(__uint_as_float(raw[r / 4][r % 4])) : 0u;
+    pool_n = topk_finish<KPT>(key, P, st, sh, [&](int rank, int pos) { sh.pool_blk[rank] = pos; });
+    lds_barrier();
+    for (int i = tid; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = sh.pool_blk[i];
+    if (tid == 0) a.out_pool_n[row] = pool_n;
   } else {
     pool_n = max(0, min(a.pool_n_in[row], P));
-    for (int i = threadIdx.x; i < P; i += kSelThreads)
-      sh.pool_blk[i] = i < pool_n ? a.pool_in[(int64_t)row * P + i] : -1;
-    __syncthreads();
+    for (int i = tid; i < P; i += kSelThreads) sh.pool_blk[i] = i < pool_n ? a.pool_in[(int64_t)row * P + i] : -1;
+    lds_barrier();
   }
-  // ---- top-k over the pool's positions (list position p = 8 * slot + e).
-  // The pool's 8-entry blocks are gathered with 16-byte loads (two slots per
-  // thread) and staged in LDS as keys in position order, over the selection
-  // buffers (free between the two selections).
+  // ---- top-k over the pool's positions (list position p = 8 * slot + e):
+  // thread t gathers slots 2t and 2t + 1 (16 contiguous positions) with
+  // 16-byte loads straight into its keys
   constexpr int KPT2 = 16;  // 16,384 positions
   const float* srow = FULL ? a.s + (int64_t)row * s_stride(a.max_n) : a.s + (int64_t)row * P * kBlock;
   const uint32_t row_bytes = FULL ? (uint32_t)s_stride(a.max_n) * 4u : (uint32_t)P * kBlock * 4u;
   const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, row_bytes, kBufferFlags);
-  uint32_t* staged = sh.u.staged;
+  uint32_t key2[KPT2];
+  TopkState st2;
   {
     v4u g[2][2];
     int blk[2];
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
-      const int slot = (int)threadIdx.x + hs * kSelThreads;
+      const int slot = 2 * tid + hs;
       blk[hs] = slot < pool_n ? sh.pool_blk[slot] : -1;
       const bool ok = blk[hs] >= 0 && blk[hs] < nb;
       // an offset past the row reads zeros (masked below)
@@ -906,37 +929,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       g[hs][0] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
       g[hs][1] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off + 16u, 0, 0);
     }
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(g[hs][0]), "+v"(g[hs][1]));
+    // the first digit while the gathers are in flight
+    st2 = topk_level1(l1_s, a.topk, sh);
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
-      const int slot = (int)threadIdx.x + hs * kSelThreads;
       const bool ok = blk[hs] >= 0 && blk[hs] < nb;
-      v4u k0, k1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bits = e < 4 ? g[hs][0][e] : g[hs][1][e - 4];
-        const uint32_t k = (ok && blk[hs] * kBlock + e < n) ? score_key(__uint_as_float(bits)) : 0u;
-        if (e < 4) k0[e] = k;
-        else k1[e - 4] = k;
+        key2[8 * hs + e] = (ok && blk[hs] * kBlock + e < n) ? score_key(__uint_as_float(bits)) : 0u;
       }
-      reinterpret_cast<v4u*>(staged)[2 * slot] = k0;
-      reinterpret_cast<v4u*>(staged)[2 * slot + 1] = k1;
     }
   }
-  __syncthreads();
-  uint32_t key2[KPT2];
-#pragma unroll
-  for (int r = 0; r < KPT2; ++r) key2[r] = staged[r * kSelThreads + (int)threadIdx.x];
-  __syncthreads();  // the selection below reuses the staging area
   int32_t* out = a.out_topk + (int64_t)row * a.topk;
   // Full mode: the level-1 counts are those of every entry of the row; the
   // top-k lies inside the pool, so entries outside it all rank below the
   // k-th and the pool's own counts agree above the crossing bin
-  const int got = block_topk<KPT2>(key2, a.topk, l1_s, sh, [&](int rank, int p) {
+  const int got = topk_finish<KPT2>(key2, a.topk, st2, sh, [&](int rank, int p) {
     out[rank] = sh.pool_blk[p >> 3] * kBlock + (p & 7);
   });
-  for (int i = got + threadIdx.x; i < a.topk; i += kSelThreads) out[i] = -1;
+  for (int i = got + tid; i < a.topk; i += kSelThreads) out[i] = -1;
 }
 
 }  // namespace csa2
