@@ -170,6 +170,8 @@ def index_scores(q_codes: np.ndarray, w: np.ndarray, key_codes: np.ndarray) -> n
     q = np.ascontiguousarray(q_codes, dtype=np.uint8)
     w = np.ascontiguousarray(w, dtype=np.float32)
     k = np.ascontiguousarray(key_codes, dtype=np.uint8).reshape(-1, DI)
+    if q.shape[0] > 64:
+        raise ValueError("the score's head sum has 64 slots: at most 64 indexer heads")
     s = np.zeros(k.shape[0], np.float32)
     lib().csa2o_index_scores(_p(q), _p(w), q.shape[0], _p(k), k.shape[0], _p(s))
     return s

@@ -185,9 +185,13 @@ void csa2o_dequant_rows(const uint8_t *codes, const uint8_t *scales, int64_t row
  * indexer lineage named on [P1]): per indexer head h,
  *   d_h = sum_c q[h][c] * k[c]            (exact, then rounded once to fp32)
  *   r_h = d_h > 0 ? d_h : +0
- *   s   = (...((+0 + fl(w_0 r_0)) + fl(w_1 r_1)) + ...) + fl(w_{H-1} r_{H-1})
- * with every multiply and add a separate binary32 operation, heads in
- * ascending order.  Each product of two E4M3 values is a multiple of 2^-18
+ *   t_h = fl(w_h r_h) for h < H, t_h = +0 for H <= h < 64 (H <= 64)
+ *   s   = pairwise(t_0 .. t_63) + 0
+ * where pairwise() is the balanced binary tree over the 64 slots in
+ * ascending order: ((t_0 + t_1) + (t_2 + t_3)) + ..., every multiply and
+ * add a separate binary32 operation; the final + 0 turns -0 into +0.  The
+ * pages leave the order of the head sum open; a pairwise tree is the order
+ * a parallel reduction takes.  Each product of two E4M3 values is a multiple of 2^-18
  * below 2^18, so any sum of 128 of them fits in 43 bits and the binary64
  * accumulation below is exact; the cast to float is the single rounding.
  * q: [H][128] E4M3 codes; keys: [n][128] E4M3 codes; s: [n]. */
@@ -195,10 +199,9 @@ void csa2o_index_scores(const uint8_t *q, const float *w, int H,
                         const uint8_t *keys, int64_t n, float *s) {
   double qv[64 * D_IDX];
   double (*qd)[D_IDX] = (double (*)[D_IDX])qv;
-  double *qheap = NULL;
-  if (H > 64) {
-    qheap = (double *)malloc(sizeof(double) * (size_t)H * D_IDX);
-    qd = (double (*)[D_IDX])qheap;
+  if (H < 0 || H > 64) { /* the sum has 64 slots: more heads are not defined */
+    for (int64_t j = 0; j < n; ++j) s[j] = NAN;
+    return;
   }
   for (int h = 0; h < H; ++h)
     for (int c = 0; c < D_IDX; ++c) qd[h][c] = csa2o_e4m3_decode(q[h * D_IDX + c]);
@@ -206,18 +209,20 @@ void csa2o_index_scores(const uint8_t *q, const float *w, int H,
   for (int64_t j = 0; j < n; ++j) {
     double kd[D_IDX];
     for (int c = 0; c < D_IDX; ++c) kd[c] = csa2o_e4m3_decode(keys[j * D_IDX + c]);
-    float acc = 0.0f;
-    for (int h = 0; h < H; ++h) {
+    float t[64];
+    for (int h = 0; h < 64; ++h) {
+      t[h] = 0.0f;
+      if (h >= H) continue;
       double dot = 0.0;
       for (int c = 0; c < D_IDX; ++c) dot += qd[h][c] * kd[c];
       float d = (float)dot;
       float r = d > 0.0f ? d : 0.0f;
-      float p = w[h] * r;
-      acc = acc + p;
+      t[h] = w[h] * r;
     }
-    s[j] = acc;
+    for (int width = 32; width >= 1; width /= 2)
+      for (int i = 0; i < width; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    s[j] = t[0] + 0.0f;
   }
-  free(qheap);
 }
 
 /* ---------------- O5: top-k ----------------

@@ -190,16 +190,17 @@ def test_quantize_kv_paged_layout(oracle):
 
 # ------------------------------------------------------------------ a2 scores
 def _ref_scores_blas(oracle, q, w, keys):
-    """d_h by BLAS fp64 matmul (exact for FP8 inputs in any summation order), then the fold."""
+    """d_h by BLAS fp64 matmul (exact for FP8 inputs in any summation order), then the
+    pairwise head sum over 64 slots, written here as repeated halving of the slot array."""
     qd = oracle.e4m3_decode(q)
     kd = oracle.e4m3_decode(keys)
     d = (kd @ qd.T).astype(np.float32)                 # [n, H], single rounding
     r = np.where(d > 0, d, np.float32(0))
-    p = (r * w.astype(np.float32)[None, :]).astype(np.float32)
-    s = np.zeros(keys.shape[0], np.float32)
-    for h in range(q.shape[0]):
-        s = (s + p[:, h]).astype(np.float32)
-    return s
+    p = np.zeros((keys.shape[0], 64), np.float32)
+    p[:, :q.shape[0]] = (r * w.astype(np.float32)[None, :]).astype(np.float32)
+    while p.shape[1] > 1:
+        p = (p[:, 0::2] + p[:, 1::2]).astype(np.float32)
+    return (p[:, 0] + np.float32(0)).astype(np.float32)
 
 
 @pytest.mark.parametrize("dist", ["normal", "all_codes"])
@@ -252,6 +253,21 @@ def test_score_fold_order_golden(oracle):
             k[0, :3] = _e4m3(c["k_three"])
         s = oracle.index_scores(q, np.array(c["w"], np.float32), k)
         assert s[0] == np.float32(c["expect"]), c["name"]
+
+
+def test_score_rejects_more_than_64_heads(oracle):
+    with pytest.raises(ValueError):
+        oracle.index_scores(np.zeros((65, 128), np.uint8), np.ones(65, np.float32), np.zeros((1, 128), np.uint8))
+
+
+def test_score_never_negative_zero_all_64_heads(oracle):
+    # 64 heads with w < 0 and d < 0: every slot is -0, and so is the tree's root
+    q = np.zeros((64, 128), np.uint8)
+    q[:, 0] = _e4m3([1.0] * 64)
+    k = np.zeros((1, 128), np.uint8)
+    k[0, 0] = _e4m3([-2.0])[0]
+    s = oracle.index_scores(q, -np.ones(64, np.float32), k)
+    assert s[0] == 0 and not np.signbit(s[0])
 
 
 def test_score_never_negative_zero(oracle):
