@@ -27,6 +27,10 @@
 
 #include "common.h"
 
+// Every multiply and add of the score is its own binary32 operation: no
+// multiply-add contraction anywhere in this file.
+#pragma clang fp contract(off)
+
 namespace csa2 {
 
 constexpr int kScoreThreads = 512;           // 8 waves
@@ -34,9 +38,6 @@ constexpr int kWaves = kScoreThreads / 64;
 constexpr int kChunk = 64;                   // entries scored together per wave: one page
 constexpr int kSub = kChunk / 16;            // 16-entry MFMA sub-tiles per chunk
 constexpr int kRT = 4;                       // row tiles of 16 heads (HI <= 64)
-constexpr int kPassRT = 2;                   // row tiles folded per pass
-constexpr int kPassHeads = kPassRT * 16;     // heads folded per pass
-constexpr int kFoldStride = kPassHeads + 4;  // floats per entry row of the fold buffer
 constexpr int kMaxWaveChunks = 1024;         // chunks one wave may take in one launch
 // A workgroup's chunks of one row: at most 1016 * 64 = 65,024 entries per
 // token, so its 16-bit histogram counters cannot overflow.
@@ -68,14 +69,15 @@ __device__ __forceinline__ uint32_t limb_entry(uint32_t code) {
   return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
-// Thread t of the 512 writes 32 of the 64 copies of code t / 2 (128 bytes).
+// Item t < 512 writes 32 of the 64 copies of code t / 2 (128 bytes).
 __device__ void build_lut(uint32_t* lut) {
-  const int t = threadIdx.x;
-  const uint32_t v = limb_entry((uint32_t)(t >> 1));
-  const v4u q = {v, v, v, v};
-  v4u* dst = reinterpret_cast<v4u*>(lut + (t >> 1) * 64 + (t & 1) * 32);
+  for (int t = threadIdx.x; t < 512; t += blockDim.x) {
+    const uint32_t v = limb_entry((uint32_t)(t >> 1));
+    const v4u q = {v, v, v, v};
+    v4u* dst = reinterpret_cast<v4u*>(lut + (t >> 1) * 64 + (t & 1) * 32);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = q;
+    for (int i = 0; i < 8; ++i) dst[i] = q;
+  }
 }
 
 __device__ __forceinline__ uint32_t lut_read(const uint8_t* lut_bytes, uint32_t lane4, uint32_t x, int k) {
@@ -232,47 +234,54 @@ __device__ __forceinline__ int entry_of(const ScoreArgs& a, const RowCtx& r, int
   return phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6) >= 0 ? j : -1;
 }
 
-// Loads one chunk's keys; not visible entries read as zero.  Full mode: the
-// chunk is logical page `chunk`, read through one buffer descriptor per
-// 16-entry sub-tile whose record count ends at the sub-tile's last visible
-// entry, so the loads need no predicate (the hardware returns zero past the
-// count) and share one lane offset.  Returns whether the page is usable
-// (Full mode; true in pool mode).
+// Physical page of a Full-mode chunk (logical page `chunk`), or -1 when
+// none of its entries is visible or the page is not usable.
+__device__ __forceinline__ int64_t chunk_page(const ScoreArgs& a, const RowCtx& r, int chunk) {
+  return chunk * kChunk < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, chunk) : -1;
+}
+
+// Loads the keys of sub-tile st (entries 16 st .. 16 st + 15) of a chunk:
+// lane (g, col) gets entry 16 st + col, channels [16g, 16g+16) and
+// [64+16g, 64+16g+16); entries that are not visible read as zero.  Full
+// mode: `pg` is the chunk's page (chunk_page), read through a buffer
+// descriptor whose record count ends at the sub-tile's last visible entry,
+// so the loads need no predicate (the hardware returns zero past the count).
+template <bool POOL>
+__device__ __forceinline__ void load_sub(const ScoreArgs& a, const RowCtx& r, int chunk, int64_t pg, int st,
+                                         int g, int col, v4u (&k)[2]) {
+  if (!POOL) {
+    const int nv = pg >= 0 ? min(r.n - chunk * kChunk, kChunk) : 0;
+    const uint8_t* base = a.kidx + (pg >= 0 ? pg * (kPage * kDI) : 0) + st * 16 * kDI;
+    // readfirstlane: the clamp would otherwise become a vector med3 and the
+    // descriptor a per-lane value, loaded through a waterfall loop
+    const int nst = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * st, 0), 16));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nst * kDI, kBufferFlags);
+    const uint32_t lofs = (uint32_t)(col * kDI + 16 * g);
+    k[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, 0, 0);
+    k[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs + 64, 0, 0);
+    return;
+  }
+  const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
+  v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
+  if (j >= 0) {
+    const int64_t p = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
+    const v4u* src = reinterpret_cast<const v4u*>(a.kidx + p * (kPage * kDI) + (j & 63) * kDI + 16 * g);
+    k0 = __builtin_nontemporal_load(src);
+    k1 = __builtin_nontemporal_load(src + 4);
+  }
+  k[0] = k0;
+  k[1] = k1;
+}
+
+// Loads all sub-tiles of a chunk; returns whether the page is usable (Full
+// mode; true in pool mode).
 template <bool POOL>
 __device__ __forceinline__ bool load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g, int col,
                                            ChunkKeys& ck) {
-  if (!POOL) {
-    const int j0 = chunk * kChunk;
-    const int64_t pg = j0 < r.n ? phys_page(a.page_table, a.max_pages, a.n_pages, r.b, chunk) : -1;
-    const int nv = pg >= 0 ? min(r.n - j0, kChunk) : 0;
-    const uint8_t* base = a.kidx + (pg >= 0 ? pg * (kPage * kDI) : 0);
-    const uint32_t lofs = (uint32_t)(col * kDI + 16 * g);
+  const int64_t pg = POOL ? 0 : chunk_page(a, r, chunk);
 #pragma unroll
-    for (int st = 0; st < kSub; ++st) {
-      // readfirstlane: the clamp would otherwise become a vector med3 and the
-      // descriptor a per-lane value, loaded through a waterfall loop
-      const int nst = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * st, 0), 16));
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(base + st * 16 * kDI), 0, nst * kDI, kBufferFlags);
-      ck.k[st][0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs, 0, 0);
-      ck.k[st][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs + 64, 0, 0);
-    }
-    return pg >= 0;
-  }
-#pragma unroll
-  for (int st = 0; st < kSub; ++st) {
-    const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
-    v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
-    if (j >= 0) {
-      const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
-      const v4u* src = reinterpret_cast<const v4u*>(a.kidx + pg * (kPage * kDI) + (j & 63) * kDI + 16 * g);
-      k0 = __builtin_nontemporal_load(src);
-      k1 = __builtin_nontemporal_load(src + 4);
-    }
-    ck.k[st][0] = k0;
-    ck.k[st][1] = k1;
-  }
-  return true;
+  for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, r, chunk, pg, st, g, col, ck.k[st]);
+  return POOL || pg >= 0;
 }
 
 // Writes the chunk's scores (lane e: entry e of the chunk; NaN, i.e. key 0,
@@ -299,6 +308,32 @@ __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc,
   }
 }
 
+// Head of MFMA row r = 4 g + i of row tile rt: 16 g + 4 rt + i.  Lane
+// (g, col) then holds, for entry col of a sub-tile, the 16 consecutive heads
+// 16 g .. 16 g + 15 of the pairwise head sum (element i of tile rt).
+__device__ __forceinline__ int tile_head(int rt, int row) { return 16 * (row >> 2) + 4 * rt + (row & 3); }
+
+// Pairwise sum of the 64 head terms of entry col (lane (g, col) holds
+// p[rt][i] = term of head 16 g + 4 rt + i): levels 1..4 inside the lane,
+// 5 and 6 across the lanes l, l ^ 16, l ^ 32, then + 0 (no -0).  Every
+// lane (g, col) returns the sum of entry col.
+__device__ __forceinline__ float head_sum(const v4f (&p)[kRT]) {
+  float q4[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) q4[rt] = (p[rt][0] + p[rt][1]) + (p[rt][2] + p[rt][3]);
+  const float s16 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s16), __float_as_uint(s16), false, false);
+  const float s32 = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s32), __float_as_uint(s32), false, false);
+  return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;
+}
+
+// Lane e = 16 g + col keeps the sum of entry e: sub-tile g's sum (every
+// lane (g', col) holds the sum of entry 16 st + col of sub-tile st).
+__device__ __forceinline__ float keep_subtile(float mine, float sum, int st, int lane) {
+  return (lane >> 4) == st ? sum : mine;
+}
+
 // General exact path for one chunk (some |value| >= 32, or a query whose
 // limb sums could leave int32): three limb planes on both sides, five
 // partial sums per dot combined exactly in binary64 and rounded once.
@@ -306,7 +341,7 @@ __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc,
 // validity masking.
 template <bool POOL>
 __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, int64_t qrow0,
-                                               const uint8_t* lut_bytes, float* my_fold, bool& page_ok) {
+                                               const uint8_t* lut_bytes, const float* my_w, bool& page_ok) {
   const int lane = lane_id();
   const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4, col = lane & 15;
@@ -317,86 +352,70 @@ __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx&
   // below inside this function's loop
   int qoff = 16 * g;
   asm volatile("" : "+v"(qoff));
-  float* fold_w = my_fold + col * kFoldStride + 4 * g;
-  const float* fold_r = my_fold + lane * kFoldStride;
-  float s = 0.0f;
-  for (int hh = 0; hh < kRT / kPassRT; ++hh) {
-    for (int rl = 0; rl < kPassRT; ++rl) {
-      const int rt = kPassRT * hh + rl;
-      const int h = rt * 16 + col;
+  // unrolled: the per-tile arrays stay in registers
+  float s_mine = 0.0f;
+#pragma unroll
+  for (int st = 0; st < kSub; ++st) {
+    v4f p[kRT];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int hq = tile_head(rt, col);
       v4i ql[2], qm[2], qt[2];
+#pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         v4u qc = {0, 0, 0, 0};
-        if (h < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + qoff)[4 * s2];
+        if (hq < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + hq) * kDI + qoff)[4 * s2];
         limbs3(lut_bytes, lane4, qc, ql[s2], qm[s2], qt[s2]);
       }
-      v4f wv;
+      const v4i z = {0, 0, 0, 0};
+      v4i acc[5] = {z, z, z, z, z};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        v4i kl, km, kt;
+        limbs3(lut_bytes, lane4, raw.k[st][s2], kl, km, kt);
+        acc[0] = mfma8(ql[s2], kl, acc[0]);
+        acc[1] = mfma8(ql[s2], km, acc[1]);
+        acc[1] = mfma8(qm[s2], kl, acc[1]);
+        acc[2] = mfma8(ql[s2], kt, acc[2]);
+        acc[2] = mfma8(qm[s2], km, acc[2]);
+        acc[2] = mfma8(qt[s2], kl, acc[2]);
+        acc[3] = mfma8(qm[s2], kt, acc[3]);
+        acc[3] = mfma8(qt[s2], km, acc[3]);
+        acc[4] = mfma8(qt[s2], kt, acc[4]);
+      }
+      const v4f wv = *reinterpret_cast<const v4f*>(my_w + 16 * g + 4 * rt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int hw = rt * 16 + 4 * g + i;
-        wv[i] = hw < HI ? a.w[qrow0 + hw] * 0x1p-18f : 0.0f;
-      }
-      for (int st = 0; st < kSub; ++st) {
-        const v4i z = {0, 0, 0, 0};
-        v4i acc[5] = {z, z, z, z, z};
-        for (int s2 = 0; s2 < 2; ++s2) {
-          v4i kl, km, kt;
-          limbs3(lut_bytes, lane4, raw.k[st][s2], kl, km, kt);
-          acc[0] = mfma8(ql[s2], kl, acc[0]);
-          acc[1] = mfma8(ql[s2], km, acc[1]);
-          acc[1] = mfma8(qm[s2], kl, acc[1]);
-          acc[2] = mfma8(ql[s2], kt, acc[2]);
-          acc[2] = mfma8(qm[s2], km, acc[2]);
-          acc[2] = mfma8(qt[s2], kl, acc[2]);
-          acc[3] = mfma8(qm[s2], kt, acc[3]);
-          acc[3] = mfma8(qt[s2], km, acc[3]);
-          acc[4] = mfma8(qt[s2], kt, acc[4]);
-        }
-        v4f pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // every term and the sum are integers below 2^53: exact, one rounding
-          const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
-                           (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
-          const float f = (float)D;
-          pv[i] = wv[i] * (f > 0.0f ? f : 0.0f);
-        }
-        *reinterpret_cast<v4f*>(fold_w + st * 16 * kFoldStride + rl * 16) = pv;
+        // every term and the sum are integers below 2^53: exact, one rounding
+        const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
+                         (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
+        const float f = (float)D;
+        p[rt][i] = wv[i] * (f > 0.0f ? f : 0.0f);
       }
     }
-    wave_lds_order();
-    for (int h = 0; h < kPassHeads; h += 4) {
-      const v4f v = *reinterpret_cast<const v4f*>(fold_r + h);
-      s = s + v[0];
-      s = s + v[1];
-      s = s + v[2];
-      s = s + v[3];
-    }
-    wave_lds_order();
+    s_mine = keep_subtile(s_mine, head_sum(p), st, lane);
   }
-  return s;
+  return s_mine;
 }
 
-// Scan.  POOL = false: Full mode, rows = sequences, the 8 waves split
+// Scan.  POOL = false: Full mode, rows = sequences, the waves split
 // T tokens x chunk slices.  POOL = true: Reindex mode, rows = (b, t),
 // positions are the entries of the row's pool blocks.  Each workgroup takes
 // a range of 64-entry chunks inside one row; each wave loads its next
 // chunk's keys while it scores the current one.
 //
-// Per chunk a wave decodes the 64 keys into fast limb planes once, then in
-// two passes of 32 heads runs the MFMAs of 4 sub-tiles x 2 row tiles, writes
-// fl(w_h * relu(d_h)) to its LDS fold buffer (entry-major), and lets lane e
-// fold entry e's heads in ascending order.  Chunks holding a code without a
-// fast split, and rows whose query could overflow int32, are only marked
-// here and scored after the main loop by the general path, which keeps the
-// main loop free of its registers.
+// Per chunk a wave takes its 4 sub-tiles of 16 entries in turn: decode the
+// sub-tile's keys into fast limb planes, run the MFMAs of the 4 row tiles,
+// form fl(w_h * relu(d_h)) and the pairwise head sum in registers.  Chunks
+// holding a code without a fast split, and rows whose query could overflow
+// int32, are only marked here and scored after the main loop by the general
+// path, which keeps the main loop free of its registers.
 template <bool POOL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // The lookup table sits at LDS offset 0, so a lookup address is the
   // perm result itself (code * 256 + lane * 4) with no base to add.
   struct __attribute__((aligned(16))) Lds {
     uint32_t lut[256 * 64];
-    float fold[kWaves][kChunk * kFoldStride];
     float wsh[kWaves][kRT * 16];                  // w * 2^-18 per head
     uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
     // per token: level-1 histograms of entry scores and block maxima,
@@ -414,7 +433,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int g = lane >> 4;   // 16-byte K slice within a 64-deep step
+  const int g = lane >> 4;   // 16-byte K slice within a 64-deep step; head group of the outputs
   const int col = lane & 15;
   const int HI = a.HI;
   const int t_full = POOL ? 0 : wave % a.T;
@@ -433,15 +452,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   ChunkKeys cur;
   bool cur_ok = load_chunk<POOL>(a, rc, chunk, g, col, cur);
 
-  // ---- query of token t: fast limb planes (A operands), weights, and the
-  // fast-path conditions (no code without a fast split, sum_c |q_c| < 256
-  // for every head, i.e. sum_c |Mq| < 2^17)
+  // ---- query of token t: fast limb planes (A operands; row col of tile rt
+  // is head tile_head(rt, col)), weights, and the fast-path conditions (no
+  // code without a fast split, sum_c |q_c| < 256 for every head, i.e.
+  // sum_c |Mq| < 2^17)
   v4i qlo[kRT][2], qmid[kRT][2];
   uint32_t qflag = 0;
   float qabs = 0.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const int h = rt * 16 + col;
+    const int h = tile_head(rt, col);
     v4u c[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     if (h < HI) {
       const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
@@ -472,10 +492,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     my_w[lane] = lane < HI ? wl * 0x1p-18f : 0.0f;
   }
   wave_lds_order();
-
-  float* my_fold = sm.fold[wave];
-  float* fold_w = my_fold + col * kFoldStride + 4 * g;  // this lane's slot for sub-tile 0, row tile 0
-  const float* fold_r = my_fold + lane * kFoldStride;   // entry `lane`'s row
   uint32_t* my_defer = sm.defer[wave];
   int k_seq = 0;  // index of the current chunk among this wave's chunks
 
@@ -485,78 +501,53 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
       continue;
     }
-    // ---- decode the chunk's keys into fast limb planes
-    v4i klo[kSub][2], kmid[kSub][2];
+    const bool page_ok = cur_ok;
+    const int64_t next_pg = (POOL || next >= c1) ? 0 : chunk_page(a, rc, next);
+    if (next < c1) cur_ok = POOL || next_pg >= 0;
     uint32_t kflag = 0;
+    float s_mine = 0.0f;
 #pragma unroll
     for (int st = 0; st < kSub; ++st) {
-      // one sub-tile at a time: issuing all lookups at once would hold
-      // 256 address / result registers
+      // ---- the sub-tile's keys into fast limb planes
       __builtin_amdgcn_sched_barrier(0);
-      limbs2(lut_bytes, lane4, cur.k[st][0], klo[st][0], kmid[st][0]);
-      limbs2(lut_bytes, lane4, cur.k[st][1], klo[st][1], kmid[st][1]);
+      v4i klo[2], kmid[2];
+      limbs2(lut_bytes, lane4, cur.k[st][0], klo[0], kmid[0]);
+      limbs2(lut_bytes, lane4, cur.k[st][1], klo[1], kmid[1]);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) kflag |= (uint32_t)klo[st][0][d] | (uint32_t)klo[st][1][d];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const bool page_ok = cur_ok;
-    // the next chunk streams into the now free key registers while this
-    // one is scored
-    if (next < c1) cur_ok = load_chunk<POOL>(a, rc, next, g, col, cur);
-    if (__ballot((kflag & 0x80808080u) != 0) != 0) {
-      // rare: scored after the main loop, out of this loop's registers
-      my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
-      continue;
-    }
-
-    float s = 0.0f;
+      for (int d = 0; d < 4; ++d) kflag |= (uint32_t)klo[0][d] | (uint32_t)klo[1][d];
+      // the same sub-tile of the next chunk streams into the freed registers
+      if (next < c1) load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
+      v4f p[kRT];
 #pragma unroll
-    for (int hh = 0; hh < kRT / kPassRT; ++hh) {
-      // 8 tiles (sub-tile st, row tile 2 hh + rl), each: 8 MFMAs, then the
-      // recombination.  Overlapping the MFMAs of one tile with the
-      // recombination of the previous needs more registers than two waves
-      // per SIMD have; the other wave of the SIMD fills that gap instead.
-#pragma unroll
-      for (int k = 0; k < kSub * kPassRT; ++k) {
-        const int st = k >> 1, rl = k & 1, rt = kPassRT * hh + rl;
+      for (int rt = 0; rt < kRT; ++rt) {
         __builtin_amdgcn_sched_barrier(0);
         const v4i z = {0, 0, 0, 0};
-        v4i c1 = mfma8(qlo[rt][0], kmid[st][0], z);
-        v4i c0 = mfma8(qlo[rt][0], klo[st][0], z);
-        v4i c2 = mfma8(qmid[rt][0], kmid[st][0], z);
-        c1 = mfma8(qmid[rt][0], klo[st][0], c1);
-        c0 = mfma8(qlo[rt][1], klo[st][1], c0);
-        c2 = mfma8(qmid[rt][1], kmid[st][1], c2);
-        c1 = mfma8(qlo[rt][1], kmid[st][1], c1);
-        c1 = mfma8(qmid[rt][1], klo[st][1], c1);
-        // lane (g, col) outputs heads 16 rt + 4 g + i
-        const v4f wv = *reinterpret_cast<const v4f*>(my_w + rt * 16 + 4 * g);
-        v4f pv;
+        v4i c1v = mfma8(qlo[rt][0], kmid[0], z);
+        v4i c0v = mfma8(qlo[rt][0], klo[0], z);
+        v4i c2v = mfma8(qmid[rt][0], kmid[0], z);
+        c1v = mfma8(qmid[rt][0], klo[0], c1v);
+        c0v = mfma8(qlo[rt][1], klo[1], c0v);
+        c2v = mfma8(qmid[rt][1], kmid[1], c2v);
+        c1v = mfma8(qlo[rt][1], kmid[1], c1v);
+        c1v = mfma8(qmid[rt][1], klo[1], c1v);
+        const v4f wv = *reinterpret_cast<const v4f*>(my_w + 16 * g + 4 * rt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // D = a0 + 2^7 a1 + 2^14 a2 = sum_c Mq Mk, exact in int32 since
           // |D| <= sum_c |Mq| |Mk| < 2^17 * 2^14
-          const uint32_t D = recombine((uint32_t)c0[i], (uint32_t)c1[i], (uint32_t)c2[i]);
+          const uint32_t D = recombine((uint32_t)c0v[i], (uint32_t)c1v[i], (uint32_t)c2v[i]);
           const float r = (float)(uint32_t)max((int)D, 0);
-          pv[i] = wv[i] * r;
+          p[rt][i] = wv[i] * r;
         }
-        *reinterpret_cast<v4f*>(fold_w + st * 16 * kFoldStride + rl * 16) = pv;
       }
-      // sequential fold of this pass's heads: lane e folds entry e
-      wave_lds_order();
-      v4f f[kPassHeads / 4];
-#pragma unroll
-      for (int j = 0; j < kPassHeads / 4; ++j) f[j] = *reinterpret_cast<const v4f*>(fold_r + 4 * j);
-#pragma unroll
-      for (int j = 0; j < kPassHeads / 4; ++j) {
-        s = s + f[j][0];
-        s = s + f[j][1];
-        s = s + f[j][2];
-        s = s + f[j][3];
-      }
-      wave_lds_order();
+      s_mine = keep_subtile(s_mine, head_sum(p), st, lane);
     }
-    emit_chunk<POOL>(a, rc, chunk, s, page_ok, hist_s, hist_bm);
+    if (__ballot((kflag & 0x80808080u) != 0) != 0) {
+      // rare: scored after the main loop by the general path
+      my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
+      continue;
+    }
+    emit_chunk<POOL>(a, rc, chunk, s_mine, page_ok, hist_s, hist_bm);
   }
 
   // ---- deferred chunks: general exact path
@@ -565,7 +556,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
     const int ck = c0 + slice + k * n_slices;
     bool ok;
-    const float s = general_chunk<POOL>(a, rc, ck, qrow0, lut_bytes, my_fold, ok);
+    const float s = general_chunk<POOL>(a, rc, ck, qrow0, lut_bytes, my_w, ok);
     emit_chunk<POOL>(a, rc, ck, s, ok, hist_s, hist_bm);
   }
   }  // this wave's chunks

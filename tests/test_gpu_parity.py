@@ -148,6 +148,31 @@ def test_index_full_8k_b1(oracle):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
+@pytest.mark.parametrize("keys_kind", ["normal", "all_codes"])
+def test_index_full_scores_bitexact(oracle, keys_kind):
+    """The scan's scores, bit for bit: Full mode keeps them in the first region
+    of its workspace, [B][T][max_n rounded up to 8] float32 (NaN where not
+    visible).  "all_codes" keys run every finite E4M3 code (general path)."""
+    n = [3000, 1000, 777]
+    say(f"index full scores bit-exact n={n} T=2 HI=64 keys={keys_kind}")
+    key_codes = None
+    if keys_kind == "all_codes":
+        finite = np.array([c for c in range(256) if c not in (127, 255)], np.uint8)
+        key_codes = np.random.default_rng(11).choice(finite, (sum(n), 128))
+    wl = small_workload(n, T=2, HI=64, topk=256, seed=21, key_codes=key_codes)
+    L = wl.layers[0]
+    ws = csa2.Workspace()
+    csa2.index_full(dev(L.q_idx), dev(L.w), dev(wl.kidx_pool), dev(wl.paging.page_table),
+                    dev(wl.n_entries), wl.max_n, wl.topk, wl.pool_blocks, ws=ws)
+    stride = (wl.max_n + 7) & ~7
+    s_gpu = host(ws.buf)[: len(n) * 2 * stride * 4].view(np.float32).reshape(len(n), 2, stride)
+    for b, nb in enumerate(n):
+        keys = oracle.gather_keys(wl.kidx_pool, wl.paging.page_table[b], nb)
+        for t in range(2):
+            ref = oracle.index_scores(L.q_idx[b, t], L.w[b, t], keys)
+            assert np.array_equal(s_gpu[b, t, :nb].view(np.uint32), ref.view(np.uint32)), (b, t)
+
+
 @pytest.mark.parametrize("T,HI,topk", [(1, 8, 64), (2, 16, 512), (4, 4, 2048), (2, 64, 2048)])
 def test_index_full_ragged(oracle, T, HI, topk):
     n = [1, 7, 8, 9, 100, 1023, 1025, 2047, 2048, 16389, 40000]
