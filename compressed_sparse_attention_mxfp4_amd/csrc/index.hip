@@ -119,6 +119,15 @@ __device__ __forceinline__ void limbs3(const uint8_t* lut_bytes, uint32_t lane4,
   }
 }
 
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// Eight f16 ones (an MFMA operand whose rows all sum the other operand).
+__device__ __forceinline__ v8h ones8() {
+  const v8h o = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                 (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  return o;
+}
+
 __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
@@ -389,7 +398,7 @@ __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx&
         // every term and the sum are integers below 2^53: exact, one rounding
         const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
                          (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
-        const float f = (float)D;
+        const float f = (float)D * 0x1p-9f;  // fl(2^9 d): the weights hold w * 2^-9
         p[rt][i] = wv[i] * (f > 0.0f ? f : 0.0f);
       }
     }
@@ -452,13 +461,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   ChunkKeys cur;
   bool cur_ok = load_chunk<POOL>(a, rc, chunk, g, col, cur);
 
-  // ---- query of token t: fast limb planes (A operands; row col of tile rt
-  // is head tile_head(rt, col)), weights, and the fast-path conditions (no
-  // code without a fast split, sum_c |q_c| < 256 for every head, i.e.
-  // sum_c |Mq| < 2^17)
-  v4i qlo[kRT][2], qmid[kRT][2];
-  uint32_t qflag = 0;
-  float qabs = 0.0f;
+  // ---- query of token t: the f16 limbs ql = Mq mod 2^7 and qm = Mq >> 7 of
+  // M = q * 2^9 (A operands; row col of row tile rt is head tile_head(rt,
+  // col); slice s of lane group g covers channels 16 g + 8 s + e (s < 2) and
+  // 64 + 16 g + 8 (s - 2) + e, the keys' order), and the fast-path condition:
+  // every |q| < 32, so qm fits [-128, 127]
+  v8h ql[kRT][4], qm[kRT][4];
+  float qmax = 0.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int h = tile_head(rt, col);
@@ -468,28 +477,32 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       c[0] = src[0];
       c[1] = src[4];
     }
-    float sa = 0.0f;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      limbs2(lut_bytes, lane4, c[s2], qlo[rt][s2], qmid[rt][s2]);
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        qflag |= (uint32_t)qlo[rt][s2][d];
-        const v2f x0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[s2][d], 1.0f, false);
-        const v2f x1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[s2][d], 1.0f, true);
-        sa = sa + fabsf(x0[0]) + fabsf(x0[1]) + fabsf(x1[0]) + fabsf(x1[1]);
-      }
-    }
-    sa += __shfl_xor(sa, 16);
-    sa += __shfl_xor(sa, 32);
-    qabs = fmaxf(qabs, sa);
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int wsel = 0; wsel < 2; ++wsel) {
+          // M of two codes, exact in binary32
+          const v2f m2 = wsel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[hf][d], 512.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[hf][d], 512.0f, false);
+          const int slice = 2 * hf + (d >> 1), e = 4 * (d & 1) + 2 * wsel;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float hi = floorf(m2[j] * 0x1p-7f);
+            const float lo = m2[j] - hi * 128.0f;  // exact: both are small integers
+            ql[rt][slice][e + j] = (_Float16)lo;
+            qm[rt][slice][e + j] = (_Float16)hi;
+            qmax = fmaxf(qmax, fabsf(m2[j]));
+          }
+        }
   }
-  const bool fast_q = __ballot((qflag & 0x80808080u) != 0 || !(qabs < 256.0f)) == 0;
-  // w * 2^-18, exact for |w| >= 2^-100 and w = 0 (zero for heads >= HI)
+  const bool fast_q = __ballot(!(qmax < 16384.0f)) == 0;
+  // w * 2^-9, exact for |w| >= 2^-100 and w = 0 (zero for heads >= HI)
   float* my_w = sm.wsh[wave];
   {
     const float wl = a.w[qrow0 + min(lane, HI - 1)];
-    my_w[lane] = lane < HI ? wl * 0x1p-18f : 0.0f;
+    my_w[lane] = lane < HI ? wl * 0x1p-9f : 0.0f;
   }
   wave_lds_order();
   uint32_t* my_defer = sm.defer[wave];
@@ -504,45 +517,68 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const bool page_ok = cur_ok;
     const int64_t next_pg = (POOL || next >= c1) ? 0 : chunk_page(a, rc, next);
     if (next < c1) cur_ok = POOL || next_pg >= 0;
-    uint32_t kflag = 0;
+    bool exact_ok = true;
     float s_mine = 0.0f;
 #pragma unroll
     for (int st = 0; st < kSub; ++st) {
-      // ---- the sub-tile's keys into fast limb planes
+      // ---- the sub-tile's keys as f16 (exact for every E4M3 code), in the
+      // channel order of the query slices
       __builtin_amdgcn_sched_barrier(0);
-      v4i klo[2], kmid[2];
-      limbs2(lut_bytes, lane4, cur.k[st][0], klo[0], kmid[0]);
-      limbs2(lut_bytes, lane4, cur.k[st][1], klo[1], kmid[1]);
+      v8h kf[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) kflag |= (uint32_t)klo[0][d] | (uint32_t)klo[1][d];
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const h2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, false);
+          const h2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, true);
+          const int slice = 2 * hf + (d >> 1), e = 4 * (d & 1);
+          kf[slice][e + 0] = lo2[0];
+          kf[slice][e + 1] = lo2[1];
+          kf[slice][e + 2] = hi2[0];
+          kf[slice][e + 3] = hi2[1];
+        }
       // the same sub-tile of the next chunk streams into the freed registers
       if (next < c1) load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
+      __builtin_amdgcn_sched_barrier(0);
+      // sum_c |k_c| of each entry (every output row holds it): the fast path is
+      // exact when it is below 256, since then every partial sum of
+      // ql * k or qm * k (|ql|, |qm| <= 128) is a multiple of 2^-9 below 2^15
+      v4f kabs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const v8h ak = __builtin_bit_cast(v8h, __builtin_bit_cast(v4u, kf[sl]) & 0x7FFF7FFFu);
+        kabs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8(), ak, kabs, 0, 0, 0);
+      }
+      // all MFMAs of the sub-tile, then the four recombinations
+      v4f sl4[kRT], sm4[kRT];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f cl = z, cm = z;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[rt][sl], kf[sl], cl, 0, 0, 0);
+          cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(qm[rt][sl], kf[sl], cm, 0, 0, 0);
+        }
+        sl4[rt] = cl;
+        sm4[rt] = cm;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      exact_ok = exact_ok && kabs[0] < 256.0f;
       v4f p[kRT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        __builtin_amdgcn_sched_barrier(0);
-        const v4i z = {0, 0, 0, 0};
-        v4i c1v = mfma8(qlo[rt][0], kmid[0], z);
-        v4i c0v = mfma8(qlo[rt][0], klo[0], z);
-        v4i c2v = mfma8(qmid[rt][0], kmid[0], z);
-        c1v = mfma8(qmid[rt][0], klo[0], c1v);
-        c0v = mfma8(qlo[rt][1], klo[1], c0v);
-        c2v = mfma8(qmid[rt][1], kmid[1], c2v);
-        c1v = mfma8(qlo[rt][1], kmid[1], c1v);
-        c1v = mfma8(qmid[rt][1], klo[1], c1v);
         const v4f wv = *reinterpret_cast<const v4f*>(my_w + 16 * g + 4 * rt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // D = a0 + 2^7 a1 + 2^14 a2 = sum_c Mq Mk, exact in int32 since
-          // |D| <= sum_c |Mq| |Mk| < 2^17 * 2^14
-          const uint32_t D = recombine((uint32_t)c0v[i], (uint32_t)c1v[i], (uint32_t)c2v[i]);
-          const float r = (float)(uint32_t)max((int)D, 0);
-          p[rt][i] = wv[i] * r;
+          // fl(2^9 d) = fl(S_l + 2^7 S_m): both sums exact, one rounding
+          const float r = __builtin_fmaf(128.0f, sm4[rt][i], sl4[rt][i]);
+          p[rt][i] = wv[i] * (r > 0.0f ? r : 0.0f);
         }
       }
       s_mine = keep_subtile(s_mine, head_sum(p), st, lane);
     }
-    if (__ballot((kflag & 0x80808080u) != 0) != 0) {
+    if (__ballot(!exact_ok) != 0) {
       // rare: scored after the main loop by the general path
       my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
       continue;

@@ -148,18 +148,39 @@ def test_index_full_8k_b1(oracle):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
-@pytest.mark.parametrize("keys_kind", ["normal", "all_codes"])
+def _bounded_extreme_keys(rows, rng):
+    """Keys at the edge of the scan's fast path: sum_c |k_c| just below 256, one
+    channel holding most of it (up to 240) and the rest subnormal or tiny, with
+    random signs, so large and tiny products meet in one accumulation."""
+    keys = np.zeros((rows, 128), np.uint8)
+    big = np.array([0x77, 0x76, 0x74, 0x70, 0x6F, 0x6C, 0x68], np.uint8)  # 240, 224, 192, 128, 120, 96, 64
+    for j in range(rows):
+        keys[j] = rng.integers(0, 16, 128).astype(np.uint8) | (rng.integers(0, 2, 128).astype(np.uint8) << 7)
+        keys[j, rng.integers(0, 128)] = big[rng.integers(0, len(big))] | (np.uint8(rng.integers(0, 2)) << 7)
+    return keys
+
+
+@pytest.mark.parametrize("keys_kind", ["normal", "all_codes", "bounded_extreme"])
 def test_index_full_scores_bitexact(oracle, keys_kind):
     """The scan's scores, bit for bit: Full mode keeps them in the first region
     of its workspace, [B][T][max_n rounded up to 8] float32 (NaN where not
-    visible).  "all_codes" keys run every finite E4M3 code (general path)."""
+    visible).  "all_codes" keys run every finite E4M3 code (general path);
+    "bounded_extreme" keys and queries sit at the edge of the fast path's
+    exactness bound (sum |k| < 256, |q| < 32)."""
     n = [3000, 1000, 777]
     say(f"index full scores bit-exact n={n} T=2 HI=64 keys={keys_kind}")
-    key_codes = None
+    key_codes = q_codes = None
+    rng = np.random.default_rng(11)
     if keys_kind == "all_codes":
         finite = np.array([c for c in range(256) if c not in (127, 255)], np.uint8)
-        key_codes = np.random.default_rng(11).choice(finite, (sum(n), 128))
-    wl = small_workload(n, T=2, HI=64, topk=256, seed=21, key_codes=key_codes)
+        key_codes = rng.choice(finite, (sum(n), 128))
+    if keys_kind == "bounded_extreme":
+        key_codes = _bounded_extreme_keys(sum(n), rng)
+        # query codes with |q| <= 30 (exponent field <= 11), many near the top
+        qc = rng.integers(0, 0x5F, (len(n), 2, 64, 128)).astype(np.uint8)
+        qc[..., ::3] = 0x5E  # 28
+        q_codes = qc | (rng.integers(0, 2, qc.shape).astype(np.uint8) << 7)
+    wl = small_workload(n, T=2, HI=64, topk=256, seed=21, key_codes=key_codes, q_codes=q_codes)
     L = wl.layers[0]
     ws = csa2.Workspace()
     csa2.index_full(dev(L.q_idx), dev(L.w), dev(wl.kidx_pool), dev(wl.paging.page_table),
