@@ -458,8 +458,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   RowCtx rc;
   row_ctx<POOL>(a, row, t_full, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  // Full mode: the physical pages of this wave's chunks, lane k holding the
+  // page of its chunk number k0 + k (refilled every 64 chunks), so the loop
+  // reads them with readlane and issues no memory load of its own for them
+  // (a vector load there would wait for the key prefetch as well)
+  int wave_pages = -1;
+  auto fill_pages = [&](int k0) {
+    const int ck = c0 + slice + (k0 + lane) * n_slices;
+    wave_pages = (!POOL && ck < c1) ? (int)chunk_page(a, rc, ck) : -1;
+  };
+  auto page_of = [&](int k) -> int64_t {
+    return POOL ? 0 : (int64_t)__builtin_amdgcn_readlane(wave_pages, k & 63);
+  };
+  fill_pages(0);
   ChunkKeys cur;
-  bool cur_ok = load_chunk<POOL>(a, rc, chunk, g, col, cur);
+  bool cur_ok;
+  {
+    const int64_t pg0 = page_of(0);
+#pragma unroll
+    for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, rc, chunk, pg0, st, g, col, cur.k[st]);
+    cur_ok = POOL || pg0 >= 0;
+  }
 
   // ---- query of token t: the f16 limbs ql = Mq mod 2^7 and qm = Mq >> 7 of
   // M = q * 2^9 (A operands; row col of row tile rt is head tile_head(rt,
@@ -515,8 +534,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       continue;
     }
     const bool page_ok = cur_ok;
-    const int64_t next_pg = (POOL || next >= c1) ? 0 : chunk_page(a, rc, next);
-    if (next < c1) cur_ok = POOL || next_pg >= 0;
+    if (!POOL && ((k_seq + 1) & 63) == 0) fill_pages(k_seq + 1);
+    // past the range the prefetch reads nothing (Full mode: page -1, a
+    // zero record count) but is still issued: a conditional load would make
+    // the compiler merge old and new keys and wait for the loads at the loop
+    // edge
+    const int64_t next_pg = POOL ? 0 : (next < c1 ? page_of(k_seq + 1) : -1);
+    cur_ok = POOL || next_pg >= 0;
     bool exact_ok = true;
     float s_mine = 0.0f;
 #pragma unroll
@@ -538,7 +562,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
           kf[slice][e + 3] = hi2[1];
         }
       // the same sub-tile of the next chunk streams into the freed registers
-      if (next < c1) load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
+      // (after the conversions have read them)
+      __builtin_amdgcn_sched_barrier(0);
+      load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
       __builtin_amdgcn_sched_barrier(0);
       // sum_c |k_c| of each entry (every output row holds it): the fast path is
       // exact when it is below 256, since then every partial sum of
