@@ -9,20 +9,28 @@
 //   s_j = binary32 fold over ascending h of fl(w_h * max(d_h, +0)).
 //
 // Exactness on MFMA.  Every E4M3 value is M * 2^-9 with M an integer,
-// |M| <= 229,376 < 2^18.  M is split into 7-bit limbs with a signed top,
-// each an int8, so q.k * 2^18 = sum over limb pairs of 2^(7(a+b)) (Q_a . K_b),
-// and every Q_a . K_b is an exact int32 from the int8 MFMA.  In the common
-// case (all |q|, |k| < 32, so M = lo + 2^7 mid with two limbs, and
-// sum_c |q_c| < 256) the recombined integer fits int32 and is rounded to
-// binary32 by one conversion; otherwise three limbs per side give five
-// weighted partial sums, combined exactly in binary64 (at most 43
-// significant bits) and rounded once.  The FP8 MFMA is not used: it aligns
-// each group of 8 products to the group maximum and keeps about 13 bits, so
-// it does not return the exactly rounded dot.
+// |M| <= 229,376 < 2^18.
+//  - Fast path (f16 MFMA): keys are converted to f16 (exact for every code);
+//    the query, when every |q| < 32, is split as M = ql + 2^7 qm with ql in
+//    [0, 127] and qm in [-128, 127], both exact in f16.  S_l = ql . k and
+//    S_m = qm . k come from v_mfma_f32_16x16x32_f16; when the entry's
+//    sum_c k_c^2 < 500 (so sum_c |k_c| < 253), every partial sum of either
+//    is a multiple of 2^-9 below 2^15, exact in binary32 in any order, and
+//    fl(2^9 q.k) = fl(S_l + 2^7 S_m) is one fused multiply-add.
+//  - General path (int8 MFMA), for chunks with an entry over that bound or
+//    rows whose query has some |q| >= 32: three limbs per side,
+//    M = lo + 2^7 mid + 2^14 top (lo, mid in [0, 127], top signed), every
+//    limb-pair dot an exact int32 from v_mfma_i32_16x16x64_i8, five weighted
+//    partial sums combined exactly in binary64 (at most 43 significant
+//    bits) and rounded once.
+// The FP8 MFMA is not used: it aligns each group of 8 products to the group
+// maximum and keeps about 13 bits, so it does not return the exactly
+// rounded dot.
 //
-// Layout of v_mfma_i32_16x16x64_i8 used below: lane l holds row (l & 15) of
-// A and column (l & 15) of B, bytes 16*(l >> 4) .. +15 of the 64-deep slice;
-// the 4 outputs of lane l are rows 4*(l >> 4) + i, column l & 15.
+// MFMA lane layout (16x16 tiles): lane l holds row (l & 15) of A and column
+// (l & 15) of B, K elements 8*(l >> 4) .. +7 of a 32-deep f16 slice (16*(l >>
+// 4) .. +15 of a 64-deep int8 slice); the 4 outputs of lane l are rows
+// 4*(l >> 4) + i, column l & 15.
 #include <algorithm>
 
 #include "common.h"
@@ -46,76 +54,32 @@ constexpr int kMaxWgChunks = 1016;
 constexpr int kHistBins = 1024;
 constexpr int kBufferFlags = 0x00020000;     // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
-// Lookup table: for every E4M3 code, the limbs of M = value * 2^9 as bytes
-//   [lo | hot, mid_s, mid_u, top]
-// for two splits:
-//   fast     M = lo + 2^7 mid_s               (|M| < 2^14: lo in [0,127], mid_s signed)
-//   general  M = lo + 2^7 mid_u + 2^14 top    (lo, mid_u in [0,127], top signed)
-// A code with |value| >= 32 (|M| >= 2^14, exponent field >= 12) has no fast
-// split: its first byte is 0x80, a bit no fast lo byte has set, and its
-// second byte is 0.  Its true lo is 0 (M is then a multiple of 2^11), so the
-// general split reads lo as the first byte & 0x7F.  64 copies so the 64
-// lanes of a wave read distinct banks (address = code * 256 + lane * 4).
-__device__ __forceinline__ uint32_t limb_entry(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  int M = (e == 0) ? (int)m : (int)((8u + m) << (e - 1));
-  if (e == 15 && m == 7) M = 0;  // NaN codes are a precondition violation; keep them inert
-  if (code & 0x80u) M = -M;
-  const bool hot = e >= 12;
-  const uint32_t b0 = hot ? 0x80u : ((uint32_t)M & 127u);
-  const uint32_t b1 = hot ? 0u : ((uint32_t)(M >> 7) & 0xFFu);
-  const uint32_t b2 = (uint32_t)(M >> 7) & 127u;
-  const uint32_t b3 = (uint32_t)(M >> 14) & 0xFFu;
-  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-}
-
-// Item t < 512 writes 32 of the 64 copies of code t / 2 (128 bytes).
-__device__ void build_lut(uint32_t* lut) {
-  for (int t = threadIdx.x; t < 512; t += blockDim.x) {
-    const uint32_t v = limb_entry((uint32_t)(t >> 1));
-    const v4u q = {v, v, v, v};
-    v4u* dst = reinterpret_cast<v4u*>(lut + (t >> 1) * 64 + (t & 1) * 32);
+// General split of the 4 FP8 codes of one dword: M = value * 2^9 (exact
+// integer in binary32, |M| < 2^18) = lo + 2^7 mid + 2^14 top with lo, mid
+// in [0, 127] and top signed; byte i of each plane is code i's limb.
+__device__ __forceinline__ void limbs3_word(uint32_t x, uint32_t& lo, uint32_t& mid, uint32_t& top) {
+  const v2f a01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 512.0f, false);
+  const v2f a23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 512.0f, true);
+  const uint32_t M[4] = {(uint32_t)(int)a01[0], (uint32_t)(int)a01[1], (uint32_t)(int)a23[0],
+                         (uint32_t)(int)a23[1]};
+  lo = mid = top = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = q;
+  for (int i = 0; i < 4; ++i) {
+    lo |= (M[i] & 127u) << (8 * i);
+    mid |= ((M[i] >> 7) & 127u) << (8 * i);
+    top |= ((M[i] >> 14) & 255u) << (8 * i);  // low byte of the arithmetic shift
   }
 }
 
-__device__ __forceinline__ uint32_t lut_read(const uint8_t* lut_bytes, uint32_t lane4, uint32_t x, int k) {
-  const uint32_t addr = __builtin_amdgcn_perm(x, lane4, 0x0C0C0000u | ((4u + k) << 8));
-  return *reinterpret_cast<const uint32_t*>(lut_bytes + addr);
-}
-
-// 16 FP8 codes -> fast lo and mid_s limb planes (byte order kept).  A lo
-// byte with bit 7 set marks a code without a fast split.
-__device__ __forceinline__ void limbs2(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
-                                      v4i& mid) {
+// 16 FP8 codes -> general lo, mid and top limb planes.
+__device__ __forceinline__ void limbs3(v4u codes, v4i& lo, v4i& mid, v4i& top) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t x = codes[d];
-    const uint32_t L0 = lut_read(lut_bytes, lane4, x, 0), L1 = lut_read(lut_bytes, lane4, x, 1);
-    const uint32_t L2 = lut_read(lut_bytes, lane4, x, 2), L3 = lut_read(lut_bytes, lane4, x, 3);
-    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x05010400u);  // [lo0 lo1 mid0 mid1]
-    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x05010400u);
-    lo[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
-    mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
-  }
-}
-
-// 16 FP8 codes -> general lo, mid_u and top limb planes.
-__device__ __forceinline__ void limbs3(const uint8_t* lut_bytes, uint32_t lane4, v4u codes, v4i& lo,
-                                      v4i& mid, v4i& top) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t x = codes[d];
-    const uint32_t L0 = lut_read(lut_bytes, lane4, x, 0), L1 = lut_read(lut_bytes, lane4, x, 1);
-    const uint32_t L2 = lut_read(lut_bytes, lane4, x, 2), L3 = lut_read(lut_bytes, lane4, x, 3);
-    const uint32_t t01 = __builtin_amdgcn_perm(L1, L0, 0x06020400u);  // [lo0 lo1 midu0 midu1]
-    const uint32_t t23 = __builtin_amdgcn_perm(L3, L2, 0x06020400u);
-    lo[d] = (int)(__builtin_amdgcn_perm(t23, t01, 0x05040100u) & 0x7F7F7F7Fu);
-    mid[d] = (int)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
-    const uint32_t u01 = __builtin_amdgcn_perm(L1, L0, 0x0C0C0703u);  // [top0 top1 0 0]
-    const uint32_t u23 = __builtin_amdgcn_perm(L3, L2, 0x0C0C0703u);
-    top[d] = (int)__builtin_amdgcn_perm(u23, u01, 0x05040100u);
+    uint32_t l, m, t;
+    limbs3_word(codes[d], l, m, t);
+    lo[d] = (int)l;
+    mid[d] = (int)m;
+    top[d] = (int)t;
   }
 }
 
@@ -132,16 +96,6 @@ __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// a0 + 2^7 a1 + 2^14 a2 (mod 2^32) as two shift-adds.  The inner sum is
-// made opaque so the compiler cannot re-associate the expression into two
-// shifts and a three-way add; it stays ordinary code (not inline asm) so the
-// compiler still inserts the wait states a VALU read of an MFMA result needs.
-__device__ __forceinline__ uint32_t recombine(uint32_t a0, uint32_t a1, uint32_t a2) {
-  uint32_t t = (a2 << 7) + a1;
-  asm volatile("" : "+v"(t));
-  return (t << 7) + a0;
-}
-
 // Maximum over each aligned group of 8 lanes, in every lane of the group.
 __device__ __forceinline__ float group8_max(float m) {
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
@@ -156,6 +110,14 @@ __device__ __forceinline__ float group8_max(float m) {
 __device__ __forceinline__ void wave_lds_order() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Row stride of the block-maxima buffer: ceil(max_n / 8) rounded up to a
@@ -337,69 +299,86 @@ __device__ __forceinline__ float head_sum(const v4f (&p)[kRT]) {
   return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;
 }
 
+// The same from the in-lane sums q4[rt] = (p[rt][0] + p[rt][1]) +
+// (p[rt][2] + p[rt][3]) (levels 1 and 2).
+__device__ __forceinline__ float head_sum4(const float (&q4)[kRT]) {
+  const float s16 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s16), __float_as_uint(s16), false, false);
+  const float s32 = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s32), __float_as_uint(s32), false, false);
+  return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;
+}
+
 // Lane e = 16 g + col keeps the sum of entry e: sub-tile g's sum (every
 // lane (g', col) holds the sum of entry 16 st + col of sub-tile st).
 __device__ __forceinline__ float keep_subtile(float mine, float sum, int st, int lane) {
   return (lane >> 4) == st ? sum : mine;
 }
 
-// General exact path for one chunk (some |value| >= 32, or a query whose
-// limb sums could leave int32): three limb planes on both sides, five
+// Query of one token in the general split: for row tile rt and half s2,
+// the lo, mid and top planes of channels [64 s2 + 16 g, 64 s2 + 16 g + 16)
+// of head tile_head(rt, col), as lane (g, col) feeds them to the int8 MFMA.
+struct GenQuery {
+  v4i lo[kRT][2], mid[kRT][2], top[kRT][2];
+};
+
+__device__ __forceinline__ void general_query(const ScoreArgs& a, int64_t qrow0, GenQuery& gq) {
+  const int lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int h = tile_head(rt, col);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      v4u qc = {0, 0, 0, 0};
+      if (h < a.HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g)[4 * s2];
+      limbs3(qc, gq.lo[rt][s2], gq.mid[rt][s2], gq.top[rt][s2]);
+    }
+  }
+}
+
+// General exact path for one chunk: three limb planes on both sides, five
 // partial sums per dot combined exactly in binary64 and rounded once.
 // Reads the chunk's codes again; returns this lane's entry score before
-// validity masking.
+// validity masking.  wreg[rt][i] holds w * 2^-9 of head tile_head(rt, 4 g + i).
 template <bool POOL>
-__device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, int64_t qrow0,
-                                               const uint8_t* lut_bytes, const float* my_w, bool& page_ok) {
+__device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, const GenQuery& gq,
+                                               const v4f (&wreg)[kRT], bool& page_ok) {
   const int lane = lane_id();
-  const uint32_t lane4 = (uint32_t)lane * 4u;
   const int g = lane >> 4, col = lane & 15;
-  const int HI = a.HI;
   ChunkKeys raw;
   page_ok = load_chunk<POOL>(a, rc, chunk, g, col, raw);
-  // an offset the optimizer cannot see through: keeps the query decode
-  // below inside this function's loop
-  int qoff = 16 * g;
-  asm volatile("" : "+v"(qoff));
-  // unrolled: the per-tile arrays stay in registers
   float s_mine = 0.0f;
 #pragma unroll
   for (int st = 0; st < kSub; ++st) {
+    v4i kl[2], km[2], kt[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) limbs3(raw.k[st][s2], kl[s2], km[s2], kt[s2]);
     v4f p[kRT];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      const int hq = tile_head(rt, col);
-      v4i ql[2], qm[2], qt[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        v4u qc = {0, 0, 0, 0};
-        if (hq < HI) qc = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + hq) * kDI + qoff)[4 * s2];
-        limbs3(lut_bytes, lane4, qc, ql[s2], qm[s2], qt[s2]);
-      }
       const v4i z = {0, 0, 0, 0};
       v4i acc[5] = {z, z, z, z, z};
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        v4i kl, km, kt;
-        limbs3(lut_bytes, lane4, raw.k[st][s2], kl, km, kt);
-        acc[0] = mfma8(ql[s2], kl, acc[0]);
-        acc[1] = mfma8(ql[s2], km, acc[1]);
-        acc[1] = mfma8(qm[s2], kl, acc[1]);
-        acc[2] = mfma8(ql[s2], kt, acc[2]);
-        acc[2] = mfma8(qm[s2], km, acc[2]);
-        acc[2] = mfma8(qt[s2], kl, acc[2]);
-        acc[3] = mfma8(qm[s2], kt, acc[3]);
-        acc[3] = mfma8(qt[s2], km, acc[3]);
-        acc[4] = mfma8(qt[s2], kt, acc[4]);
+        const v4i ql = gq.lo[rt][s2], qm = gq.mid[rt][s2], qt = gq.top[rt][s2];
+        acc[0] = mfma8(ql, kl[s2], acc[0]);
+        acc[1] = mfma8(ql, km[s2], acc[1]);
+        acc[1] = mfma8(qm, kl[s2], acc[1]);
+        acc[2] = mfma8(ql, kt[s2], acc[2]);
+        acc[2] = mfma8(qm, km[s2], acc[2]);
+        acc[2] = mfma8(qt, kl[s2], acc[2]);
+        acc[3] = mfma8(qm, kt[s2], acc[3]);
+        acc[3] = mfma8(qt, km[s2], acc[3]);
+        acc[4] = mfma8(qt, kt[s2], acc[4]);
       }
-      const v4f wv = *reinterpret_cast<const v4f*>(my_w + 16 * g + 4 * rt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // every term and the sum are integers below 2^53: exact, one rounding
         const double D = (double)acc[0][i] + (double)acc[1][i] * 128.0 + (double)acc[2][i] * 16384.0 +
                          (double)acc[3][i] * 2097152.0 + (double)acc[4][i] * 268435456.0;
         const float f = (float)D * 0x1p-9f;  // fl(2^9 d): the weights hold w * 2^-9
-        p[rt][i] = wv[i] * (f > 0.0f ? f : 0.0f);
+        p[rt][i] = wreg[rt][i] * (f > 0.0f ? f : 0.0f);
       }
     }
     s_mine = keep_subtile(s_mine, head_sum(p), st, lane);
@@ -413,19 +392,22 @@ __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx&
 // a range of 64-entry chunks inside one row; each wave loads its next
 // chunk's keys while it scores the current one.
 //
-// Per chunk a wave takes its 4 sub-tiles of 16 entries in turn: decode the
-// sub-tile's keys into fast limb planes, run the MFMAs of the 4 row tiles,
-// form fl(w_h * relu(d_h)) and the pairwise head sum in registers.  Chunks
-// holding a code without a fast split, and rows whose query could overflow
-// int32, are only marked here and scored after the main loop by the general
-// path, which keeps the main loop free of its registers.
+// The workgroup first splits its tokens' queries into f16 limbs once, in
+// LDS, while every wave's first keys are in flight; each wave then copies
+// its token's limbs into registers.  Per chunk a wave takes its 4 sub-tiles
+// of 16 entries in turn: convert the keys to f16, run the MFMAs of the 4 row
+// tiles and the sub-tile's Gram matrix, form fl(w_h * relu(d_h)) and the
+// pairwise head sum in registers.  Chunks with an entry over the fast
+// path's bound, and rows whose query has some |q| >= 32, are only marked
+// here and scored after the main loop by the general path.
 template <bool POOL>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
-  // The lookup table sits at LDS offset 0, so a lookup address is the
-  // perm result itself (code * 256 + lane * 4) with no base to add.
   struct __attribute__((aligned(16))) Lds {
-    uint32_t lut[256 * 64];
-    float wsh[kWaves][kRT * 16];                  // w * 2^-18 per head
+    // per token: the f16 limbs ql, qm of the query, in the order the waves
+    // hold them: [row tile][slice][limb][lane]
+    v8h qlimb[CSA2_MAX_T][kRT][4][2][64];
+    float wsh[CSA2_MAX_T][kRT * 16];              // w * 2^-9 per head, 0 past HI
+    uint32_t qbad[CSA2_MAX_T];                    // nonzero: some |q| >= 32
     uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
     // per token: level-1 histograms of entry scores and block maxima,
     // 16-bit counters packed two per word
@@ -433,16 +415,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   };
   __shared__ Lds sm;
 
-  build_lut(sm.lut);
   for (int i = threadIdx.x; i < kWaves * kMaxWaveChunks / 32; i += blockDim.x) (&sm.defer[0][0])[i] = 0u;
   for (int i = threadIdx.x; i < CSA2_MAX_T * kHistBins; i += blockDim.x) (&sm.hist[0][0][0])[i] = 0u;
-  __syncthreads();
-  const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(sm.lut);
+  if (threadIdx.x < CSA2_MAX_T) sm.qbad[threadIdx.x] = 0u;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const uint32_t lane4 = (uint32_t)lane * 4u;
-  const int g = lane >> 4;   // 16-byte K slice within a 64-deep step; head group of the outputs
+  const int g = lane >> 4;   // K slice group of the MFMA operands; head group of the outputs
   const int col = lane & 15;
   const int HI = a.HI;
   const int t_full = POOL ? 0 : wave % a.T;
@@ -451,13 +430,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int row = blockIdx.x / a.wg_per_row;
   const int c0 = (blockIdx.x % a.wg_per_row) * a.chunks_per_wg;
   const int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
+  const bool have_row = row < a.rows;
   int chunk = c0 + slice;
+  const bool active = have_row && chunk < c1;
   uint32_t* hist_s = sm.hist[t_full][0];
   uint32_t* hist_bm = sm.hist[t_full][1];
-  if (row < a.rows && chunk < c1) {
   RowCtx rc;
-  row_ctx<POOL>(a, row, t_full, rc);
+  if (have_row) row_ctx<POOL>(a, row, t_full, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  lds_barrier();
+
   // Full mode: the physical pages of this wave's chunks, lane k holding the
   // page of its chunk number k0 + k (refilled every 64 chunks), so the loop
   // reads them with readlane and issues no memory load of its own for them
@@ -470,60 +452,81 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   auto page_of = [&](int k) -> int64_t {
     return POOL ? 0 : (int64_t)__builtin_amdgcn_readlane(wave_pages, k & 63);
   };
-  fill_pages(0);
   ChunkKeys cur;
-  bool cur_ok;
-  {
+  bool cur_ok = false;
+  if (active) {
+    fill_pages(0);
     const int64_t pg0 = page_of(0);
 #pragma unroll
     for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, rc, chunk, pg0, st, g, col, cur.k[st]);
     cur_ok = POOL || pg0 >= 0;
   }
 
-  // ---- query of token t: the f16 limbs ql = Mq mod 2^7 and qm = Mq >> 7 of
-  // M = q * 2^9 (A operands; row col of row tile rt is head tile_head(rt,
-  // col); slice s of lane group g covers channels 16 g + 8 s + e (s < 2) and
-  // 64 + 16 g + 8 (s - 2) + e, the keys' order), and the fast-path condition:
-  // every |q| < 32, so qm fits [-128, 127]
-  v8h ql[kRT][4], qm[kRT][4];
-  float qmax = 0.0f;
+  // ---- the workgroup's queries in f16 limbs: ql = Mq mod 2^7 and qm =
+  // floor(Mq / 2^7) of M = q * 2^9 (exact small integers).  Item (token,
+  // row tile rt, slice s, lane L): head tile_head(rt, L & 15), channels
+  // 16 gL + 8 s + e (s < 2) or 64 + 16 gL + 8 (s - 2) + e (e < 8, gL = L >> 4),
+  // the keys' order in the slices.
+  if (have_row) {
+    const int n_tok = POOL ? 1 : a.T;
+    const int b = rc.b;
+    for (int it = threadIdx.x; it < n_tok * kRT * 4 * 64; it += blockDim.x) {
+      const int L = it & 63, sl = (it >> 6) & 3, rt = (it >> 8) & 3, tk = it >> 10;
+      const int t = POOL ? rc.t : tk;
+      const int h = tile_head(rt, L & 15), gL = L >> 4;
+      const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
+      uint32_t c[2] = {0u, 0u};
+      if (h < HI) {
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(a.q_idx + (((int64_t)b * a.T + t) * HI + h) * kDI + ch);
+        c[0] = src[0];
+        c[1] = src[1];
+      }
+      v8h ql, qm;
+      bool bad = false;
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    const int h = tile_head(rt, col);
-    v4u c[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (h < HI) {
-      const v4u* src = reinterpret_cast<const v4u*>(a.q_idx + (qrow0 + h) * kDI + 16 * g);
-      c[0] = src[0];
-      c[1] = src[4];
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int wd = 0; wd < 2; ++wd)
 #pragma unroll
         for (int wsel = 0; wsel < 2; ++wsel) {
-          // M of two codes, exact in binary32
-          const v2f m2 = wsel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[hf][d], 512.0f, true)
-                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[hf][d], 512.0f, false);
-          const int slice = 2 * hf + (d >> 1), e = 4 * (d & 1) + 2 * wsel;
+          const v2f m2 = wsel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[wd], 512.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[wd], 512.0f, false);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
+            const int e = 4 * wd + 2 * wsel + j;
             const float hi = floorf(m2[j] * 0x1p-7f);
             const float lo = m2[j] - hi * 128.0f;  // exact: both are small integers
-            ql[rt][slice][e + j] = (_Float16)lo;
-            qm[rt][slice][e + j] = (_Float16)hi;
-            qmax = fmaxf(qmax, fabsf(m2[j]));
+            ql[e] = (_Float16)lo;
+            qm[e] = (_Float16)hi;
+            bad = bad || !(fabsf(m2[j]) < 16384.0f);
           }
         }
+      sm.qlimb[tk][rt][sl][0][L] = ql;
+      sm.qlimb[tk][rt][sl][1][L] = qm;
+      if (bad) atomicOr(&sm.qbad[tk], 1u);
+    }
+    for (int i = threadIdx.x; i < n_tok * 64; i += blockDim.x) {
+      const int tk = i >> 6, h = i & 63;
+      const int t = POOL ? rc.t : tk;
+      sm.wsh[tk][h] = h < HI ? a.w[((int64_t)b * a.T + t) * HI + h] * 0x1p-9f : 0.0f;
+    }
   }
-  const bool fast_q = __ballot(!(qmax < 16384.0f)) == 0;
-  // w * 2^-9, exact for |w| >= 2^-100 and w = 0 (zero for heads >= HI)
-  float* my_w = sm.wsh[wave];
-  {
-    const float wl = a.w[qrow0 + min(lane, HI - 1)];
-    my_w[lane] = lane < HI ? wl * 0x1p-9f : 0.0f;
+  lds_barrier();
+
+  if (active) {
+  // this wave's token: limbs (A operands, row col of row tile rt is head
+  // tile_head(rt, col)), weights of its output heads, fast-path condition
+  v8h ql[kRT][4], qm[kRT][4];
+  v4f wreg[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      ql[rt][sl] = sm.qlimb[t_full][rt][sl][0][lane];
+      qm[rt][sl] = sm.qlimb[t_full][rt][sl][1][lane];
+    }
+    wreg[rt] = *reinterpret_cast<const v4f*>(&sm.wsh[t_full][16 * g + 4 * rt]);
   }
-  wave_lds_order();
+  const bool fast_q = sm.qbad[t_full] == 0u;
   uint32_t* my_defer = sm.defer[wave];
   int k_seq = 0;  // index of the current chunk among this wave's chunks
 
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     // edge
     const int64_t next_pg = POOL ? 0 : (next < c1 ? page_of(k_seq + 1) : -1);
     cur_ok = POOL || next_pg >= 0;
-    bool exact_ok = true;
+    float gmax = 0.0f;
     float s_mine = 0.0f;
 #pragma unroll
     for (int st = 0; st < kSub; ++st) {
@@ -566,16 +569,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
       __builtin_amdgcn_sched_barrier(0);
-      // sum_c |k_c| of each entry (every output row holds it): the fast path is
-      // exact when it is below 256, since then every partial sum of
-      // ql * k or qm * k (|ql|, |qm| <= 128) is a multiple of 2^-9 below 2^15
-      v4f kabs = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const v8h ak = __builtin_bit_cast(v8h, __builtin_bit_cast(v4u, kf[sl]) & 0x7FFF7FFFu);
-        kabs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8(), ak, kabs, 0, 0, 0);
-      }
-      // all MFMAs of the sub-tile, then the four recombinations
+      // the 8 MFMAs of each row tile, then the sub-tile's Gram matrix
       v4f sl4[kRT], sm4[kRT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
@@ -589,21 +583,34 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
         sl4[rt] = cl;
         sm4[rt] = cm;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      exact_ok = exact_ok && kabs[0] < 256.0f;
-      v4f p[kRT];
+      // K K^T over the 128 channels: its diagonal holds sum_c k_c^2 of each
+      // entry, and no other element exceeds the largest diagonal one
+      // (Cauchy-Schwarz), so the maximum over all outputs is the largest
+      // sum of squares of the sub-tile
+      v4f gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], kf[sl], gram, 0, 0, 0);
+      float q4[kRT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const v4f wv = *reinterpret_cast<const v4f*>(my_w + 16 * g + 4 * rt);
+        const v4f wv = wreg[rt];
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // fl(2^9 d) = fl(S_l + 2^7 S_m): both sums exact, one rounding
           const float r = __builtin_fmaf(128.0f, sm4[rt][i], sl4[rt][i]);
-          p[rt][i] = wv[i] * (r > 0.0f ? r : 0.0f);
+          p[i] = wv[i] * (r > 0.0f ? r : 0.0f);
         }
+        q4[rt] = (p[0] + p[1]) + (p[2] + p[3]);
       }
-      s_mine = keep_subtile(s_mine, head_sum(p), st, lane);
+      gmax = fmaxf(gmax, fmaxf(fmaxf(gram[0], gram[1]), fmaxf(gram[2], gram[3])));
+      s_mine = keep_subtile(s_mine, head_sum4(q4), st, lane);
     }
+    // every entry of the chunk has sum_c k_c^2 < 500, hence (Cauchy-Schwarz
+    // over 128 channels) sum_c |k_c| < sqrt(128 * 500) < 253: the fast path
+    // is exact, since every partial sum of ql * k or qm * k (|ql|, |qm| <=
+    // 128) is then a multiple of 2^-9 below 2^15
+    const bool exact_ok = gmax < 500.0f;
     if (__ballot(!exact_ok) != 0) {
       // rare: scored after the main loop by the general path
       my_defer[k_seq >> 5] |= 1u << (k_seq & 31);
@@ -614,12 +621,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
   // ---- deferred chunks: general exact path
   wave_lds_order();
-  for (int k = 0; k < k_seq; ++k) {
-    if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
-    const int ck = c0 + slice + k * n_slices;
-    bool ok;
-    const float s = general_chunk<POOL>(a, rc, ck, qrow0, lut_bytes, my_w, ok);
-    emit_chunk<POOL>(a, rc, ck, s, ok, hist_s, hist_bm);
+  bool any_deferred = false;
+  for (int k = 0; k < (k_seq + 31) / 32; ++k) any_deferred = any_deferred || my_defer[k] != 0u;
+  if (any_deferred) {
+    GenQuery gq;
+    general_query(a, qrow0, gq);
+    for (int k = 0; k < k_seq; ++k) {
+      if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
+      const int ck = c0 + slice + k * n_slices;
+      bool ok;
+      const float s = general_chunk<POOL>(a, rc, ck, gq, wreg, ok);
+      emit_chunk<POOL>(a, rc, ck, s, ok, hist_s, hist_bm);
+    }
   }
   }  // this wave's chunks
 
@@ -664,14 +677,6 @@ struct SelShared {
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
-
-// Workgroup barrier that orders LDS accesses only: global loads in flight
-// stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Dword of SelShared::stage holding list position p: thread t = p / 32
 // reads its 32 positions as 8 16-byte pieces q = (p / 4) % 8, placed at

@@ -148,15 +148,37 @@ def test_index_full_8k_b1(oracle):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
+def _e4m3_value(codes):
+    c = codes.astype(np.int64)
+    e, m = (c >> 3) & 15, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8 * 2.0**-6, (1 + m / 8) * 2.0 ** (e - 7))
+    return np.where(c & 0x80, -mag, mag)
+
+
 def _bounded_extreme_keys(rows, rng):
-    """Keys at the edge of the scan's fast path: sum_c |k_c| just below 256, one
-    channel holding most of it (up to 240) and the rest subnormal or tiny, with
-    random signs, so large and tiny products meet in one accumulation."""
+    """Keys at the edge of the scan's fast path (sum_c k_c^2 < 500), random signs:
+    mode 0: one channel of 22, 20, 18 or 16 over subnormal and tiny channels,
+            so large and tiny products meet in one accumulation;
+    mode 1: 112..128 channels of 1.75 or 1.875 (sum |k| up to 240, so the
+            partial sums reach 128 * 240) and the rest subnormal;
+    mode 2: every channel 2.0 (sum k^2 = 512): just past the bound, left to
+            the general path."""
     keys = np.zeros((rows, 128), np.uint8)
-    big = np.array([0x77, 0x76, 0x74, 0x70, 0x6F, 0x6C, 0x68], np.uint8)  # 240, 224, 192, 128, 120, 96, 64
     for j in range(rows):
-        keys[j] = rng.integers(0, 16, 128).astype(np.uint8) | (rng.integers(0, 2, 128).astype(np.uint8) << 7)
-        keys[j, rng.integers(0, 128)] = big[rng.integers(0, len(big))] | (np.uint8(rng.integers(0, 2)) << 7)
+        mode = j % 3
+        tiny = rng.integers(0, 16, 128).astype(np.uint8)
+        if mode == 0:
+            row = tiny
+            row[rng.integers(0, 128)] = rng.choice(np.array([0x5B, 0x5A, 0x59, 0x58], np.uint8))
+        elif mode == 1:
+            row = rng.choice(np.array([0x3E, 0x3F], np.uint8), 128)
+            n_small = rng.integers(0, 17)
+            row[rng.permutation(128)[:n_small]] = tiny[:n_small] & 7
+        else:
+            row = np.full(128, 0x40, np.uint8)
+        keys[j] = row | (rng.integers(0, 2, 128).astype(np.uint8) << 7)
+    sq = (_e4m3_value(keys) ** 2).sum(axis=1)
+    assert (sq[0::3] < 500).all() and (sq[1::3] < 500).all() and (sq[2::3] >= 500).all()
     return keys
 
 
@@ -166,7 +188,7 @@ def test_index_full_scores_bitexact(oracle, keys_kind):
     of its workspace, [B][T][max_n rounded up to 8] float32 (NaN where not
     visible).  "all_codes" keys run every finite E4M3 code (general path);
     "bounded_extreme" keys and queries sit at the edge of the fast path's
-    exactness bound (sum |k| < 256, |q| < 32)."""
+    exactness bound (sum k^2 < 500, |q| < 32)."""
     n = [3000, 1000, 777]
     say(f"index full scores bit-exact n={n} T=2 HI=64 keys={keys_kind}")
     key_codes = q_codes = None
