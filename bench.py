@@ -306,7 +306,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8/fp4 storage; int8-MFMA exact scores; f16-MFMA attention; fp32 softmax",
+        "dtype": "fp8/fp4 storage; f16-MFMA exact scores (int8-MFMA general path); f16-MFMA attention; fp32 softmax",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "query_tokens": T,
                    "context_tokens": int(wl.max_n) * 4, "entries_per_seq": int(wl.max_n),
