@@ -96,11 +96,12 @@ __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Maximum over each aligned group of 8 lanes, in every lane of the group.
-__device__ __forceinline__ float group8_max(float m) {
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+// Maximum over each aligned group of 8 lanes, in every lane of the group
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror).
+__device__ __forceinline__ uint32_t group8_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
   return m;
 }
 
@@ -267,14 +268,15 @@ __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc,
   const bool valid = POOL ? entry_of<POOL>(a, rc, p) >= 0 : (page_ok && p < rc.n);
   float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
                                    (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
-  if (p < rc.n_pos) out_s_row[p] = valid ? s : u2f(0xFFFFFFFFu);
-  if (valid) hist_add16(hist_s, score_key(s) >> 22);
+  // order-preserving key of the score; 0 (stored as NaN) when not visible
+  const uint32_t key = valid ? score_key(s) : 0u;
+  if (p < rc.n_pos) out_s_row[p] = key_score(key);
+  if (valid) hist_add16(hist_s, key >> 22);
   if (!POOL) {
-    const float m = group8_max(valid ? s : -__builtin_inff());
+    const uint32_t m = group8_max(key);
     if ((lane & 7) == 0 && p < rc.n_pos) {
-      const bool any = m != -__builtin_inff();
-      a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] = any ? m : u2f(0xFFFFFFFFu);
-      if (any) hist_add16(hist_bm, score_key(m) >> 22);
+      a.out_bm[((int64_t)rc.b * a.T + rc.t) * bm_stride(a.max_n) + (p >> 3)] = key_score(m);
+      if (m != 0u) hist_add16(hist_bm, m >> 22);
     }
   }
 }
