@@ -99,7 +99,9 @@ def measured_traffic():
 
 def counters_driver(args):
     """Launch sequence for rocprofv3 counter runs: a plain 256 MiB device copy
-    (calibrates FETCH_SIZE / WRITE_SIZE), then the Full indexer of the workload."""
+    (calibrates FETCH_SIZE / WRITE_SIZE), then 3 times each: the Full indexer
+    of the workload, its sparse attention over the indexer's top-k, and the
+    cache write of all of the workload's rows (1,048,576 at 1M context)."""
     import torch
     import compressed_sparse_attention_mxfp4_amd as csa2
     from compressed_sparse_attention_mxfp4_amd import synth
@@ -117,7 +119,18 @@ def counters_driver(args):
     q, w, kidx, pt, ne = d(L.q_idx), d(L.w), d(wl.kidx_pool), d(wl.paging.page_table), d(wl.n_entries)
     ws = csa2.Workspace()
     for _ in range(3):
-        csa2.index_full(q, w, kidx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks, ws=ws)
+        topk = csa2.index_full(q, w, kidx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks, ws=ws)[0]
+    torch.cuda.synchronize()
+    kv_src = d(wl.kv_source.view(np.int16)).view(torch.bfloat16)
+    slots = d(wl.paging.all_slots())
+    kv = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    qa, swa = d(L.q.view(np.int16)).view(torch.bfloat16), d(L.swa)
+    ws_a = csa2.Workspace()
+    for _ in range(3):
+        csa2.quantize_kv(kv_src, slots, kv)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        csa2.sparse_attn(qa, wl.sm_scale, kv, pt, ne, topk, swa, ws=ws_a)
     torch.cuda.synchronize()
     log("counters driver done")
     return 0
