@@ -6,8 +6,15 @@
 // One thread per 16-channel group: 32 threads cover one 1 KiB bf16 row with
 // two 16 B loads each (a wave reads 2 KiB contiguous), write 8 B of E2M1
 // nibbles each (256 B contiguous per row) and one E4M3 scale byte, gathered
-// four at a time into a dword store.  HBM-bound: 1,024 B read + 288 B
-// written per row.
+// four at a time into a dword store.  1,024 B read + 288 B written per row.
+//
+// The elements are rounded in pairs on packed 16-bit integers: a non-negative
+// bf16 bit pattern orders like its value, and every E2M1 decision boundary
+// mid * scale (mid in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}, scale an E4M3
+// value) has at most 7 significant bits, so it is itself a bf16 value and
+// "|x| >= boundary" is an exact integer comparison of bit patterns (a strict
+// boundary compares against the next pattern up).  Three such comparisons
+// per element, a binary search over the 8 magnitudes, give the code.
 #include "common.h"
 
 namespace csa2 {
@@ -18,6 +25,22 @@ namespace csa2 {
 // (amax has 8 significant bits, so amax / 6 is either exact or at least
 // 2^-10 relative away from every midpoint), so this equals the E4M3
 // rounding of the exact quotient.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+// Per 16-bit half: all ones where a < t, else zero (a, t below 2^15: the
+// sign of the 16-bit difference, spread by an arithmetic shift).
+// Written as two packed instructions: the compiler would otherwise turn the
+// sign test into a compare and a select per half.
+__device__ __forceinline__ uint32_t below_mask(uint32_t a, uint32_t t) {
+  uint32_t d, m;
+  asm("v_pk_sub_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(t));
+  asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(m) : "v"(0x000F000Fu), "v"(d));  // shift 15 in both halves
+  return m;
+}
+// Bits of x where m is set, of y elsewhere.
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t x, uint32_t y) { return (m & x) | (~m & y); }
+
 __device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
   if (t >= 448.0f) return 0x7Eu;
   if (t < 0.015625f) {  // below the smallest normal 2^-6: steps of 2^-9
@@ -56,33 +79,43 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
     h[4] = b.x; h[5] = b.y; h[6] = b.z; h[7] = b.w;
     s = slot[r];
   }
-  // amax over 16 bf16 magnitudes: non-negative bf16 bit patterns order like values
-  uint32_t amax_bits = 0;
+  // amax over 16 bf16 magnitudes (pairs of bit patterns)
+  u16x2 mag[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t lo = h[i] & 0x7FFFu, hi = (h[i] >> 16) & 0x7FFFu;
-    amax_bits = max(amax_bits, max(lo, hi));
-  }
+  for (int i = 0; i < 8; ++i) mag[i] = as_u16x2(h[i] & 0x7FFF7FFFu);
+  u16x2 mx2 = mag[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx2 = max(mx2, mag[i]);
+  const uint32_t amax_bits = max((uint32_t)mx2.x, (uint32_t)mx2.y);
   const float amax = u2f(amax_bits << 16);
   const uint32_t sc = e4m3_rne_pos(__fdiv_rn(amax, 6.0f));
   const float sv = e4m3_value_pos(sc);
-  // E2M1 magnitude by counting midpoints passed; a tie at 0.25/1.25/2.5/5
-  // goes down to the even code, at 0.75/1.75/3.5 up to the even code.
-  const float m025 = 0.25f * sv, m075 = 0.75f * sv, m125 = 1.25f * sv, m175 = 1.75f * sv;
-  const float m250 = 2.5f * sv, m350 = 3.5f * sv, m500 = 5.0f * sv;
-  uint32_t w0 = 0, w1 = 0;
+  // decision boundaries as bf16 bit patterns: |x| >= t (ties at 0.75, 1.75,
+  // 3.5 go up to the even code) or |x| > t, i.e. >= t + 1 (ties at 0.25,
+  // 1.25, 2.5, 5 go down to the even code); a zero scale takes no boundary
+  auto bnd = [&](float mid, uint32_t strict) -> uint32_t {
+    return sc != 0u ? (f2u(mid * sv) >> 16) + strict : 0x7FFFu;
+  };
+  const uint32_t t0 = bnd(0.25f, 1u), t1 = bnd(0.75f, 0u), t2 = bnd(1.25f, 1u), t3 = bnd(1.75f, 0u);
+  const uint32_t t4 = bnd(2.5f, 1u), t5 = bnd(3.5f, 0u), t6 = bnd(5.0f, 1u);
+  // binary search, with masks M = all ones where |x| is below the boundary:
+  //   level 1: 1.75; level 2: 3.5 or 0.75; level 3: 5, 2.5, 1.25 or 0.25;
+  //   magnitude = 7 - (4 [M1] + 2 [M2] + [M3])
+  const uint32_t T3 = t3 * 0x10001u, T1 = t1 * 0x10001u, T5 = t5 * 0x10001u;
+  const uint32_t T0 = t0 * 0x10001u, T2 = t2 * 0x10001u, T4 = t4 * 0x10001u, T6 = t6 * 0x10001u;
+  uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t bits = (h[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-    float a = u2f((bits & 0x7FFFu) << 16);
-    uint32_t m = (uint32_t)(a > m025) + (uint32_t)(a >= m075) + (uint32_t)(a > m125) +
-                 (uint32_t)(a >= m175) + (uint32_t)(a > m250) + (uint32_t)(a >= m350) +
-                 (uint32_t)(a > m500);
-    m = (sv > 0.0f) ? m : 0u;
-    uint32_t code = ((bits >> 15) << 3) | m;
-    if (i < 8) w0 |= code << (4 * i);
-    else w1 |= code << (4 * (i - 8));
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t a = h[j] & 0x7FFF7FFFu;
+    const uint32_t m1 = below_mask(a, T3);
+    const uint32_t m2 = below_mask(a, bitsel(m1, T1, T5));
+    const uint32_t m3 = below_mask(a, bitsel(m1, bitsel(m2, T0, T2), bitsel(m2, T4, T6)));
+    const uint32_t nb = bitsel(0x00040004u, m1, bitsel(0x00020002u, m2, m3)) & 0x00070007u;
+    // codes of elements 2j (low half) and 2j + 1: sign << 3 | magnitude
+    const uint32_t c = (nb ^ 0x00070007u) | ((h[j] >> 12) & 0x00080008u);
+    w[j >> 2] |= ((c | (c >> 12)) & 0xFFu) << (8 * (j & 3));
   }
+  const uint32_t w0 = w[0], w1 = w[1];
   // four neighbouring groups' scale bytes -> one dword store
   const uint32_t s1 = __shfl_down(sc, 1, 4), s2 = __shfl_down(sc, 2, 4), s3 = __shfl_down(sc, 3, 4);
   const bool ok = live && s >= 0 && s < n_pages * kPage;

@@ -70,6 +70,11 @@ def special_rows():
         [-0.0] * 16,
         [1e-30, -1e-30] + [0.0] * 14,
         [60000.0, -1.0] + [0.0] * 14,
+        # scale 1.125 (amax 6.75) and 1.875 (amax 11.25): every E2M1 tie times the scale
+        [6.75, 0.28125, 0.84375, 1.40625, 1.96875, 2.8125, 3.9375, 5.625,
+         -0.28125, -0.84375, -1.40625, -1.96875, -2.8125, -3.9375, -5.625, 0.0],
+        [11.25, 0.46875, 1.40625, 2.34375, 3.28125, 4.6875, 6.5625, 9.375,
+         -0.46875, -1.40625, -2.34375, -3.28125, -4.6875, -6.5625, -9.375, -0.0],
     ]
     rows = []
     for v in vals:
