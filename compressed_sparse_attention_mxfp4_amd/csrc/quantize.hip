@@ -28,18 +28,20 @@ namespace csa2 {
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
 __device__ __forceinline__ uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-// Per 16-bit half: all ones where a < t, else zero (a, t below 2^15: the
-// sign of the 16-bit difference, spread by an arithmetic shift).
-// Written as two packed instructions: the compiler would otherwise turn the
-// sign test into a compare and a select per half.
-__device__ __forceinline__ uint32_t below_mask(uint32_t a, uint32_t t) {
-  uint32_t d, m;
-  asm("v_pk_sub_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(t));
-  asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(m) : "v"(0x000F000Fu), "v"(d));  // shift 15 in both halves
-  return m;
+// Per 16-bit half: all ones where a > t1, else zero (a, t1 below 2^15: the
+// sign of the 16-bit difference t1 - a, spread by an arithmetic shift).
+// `sh15` holds 15 in both halves, as a value the compiler cannot see: with a
+// constant shift it turns the sign test into a compare and a select per half.
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t reach_mask(uint32_t a, uint32_t t1, i16x2 sh15) {
+  const i16x2 d = __builtin_bit_cast(i16x2, as_u32(as_u16x2(t1) - as_u16x2(a)));
+  return __builtin_bit_cast(uint32_t, (i16x2)(d >> sh15));
 }
+// Logical shift right by 12 of each 16-bit half.
+__device__ __forceinline__ uint32_t pk_shr12(uint32_t x) { return as_u32(as_u16x2(x) >> (u16x2){12, 12}); }
 // Bits of x where m is set, of y elsewhere.
 __device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t x, uint32_t y) { return (m & x) | (~m & y); }
+
 
 __device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
   if (t >= 448.0f) return 0x7Eu;
@@ -90,32 +92,50 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
   const float amax = u2f(amax_bits << 16);
   const uint32_t sc = e4m3_rne_pos(__fdiv_rn(amax, 6.0f));
   const float sv = e4m3_value_pos(sc);
-  // decision boundaries as bf16 bit patterns: |x| >= t (ties at 0.75, 1.75,
-  // 3.5 go up to the even code) or |x| > t, i.e. >= t + 1 (ties at 0.25,
-  // 1.25, 2.5, 5 go down to the even code); a zero scale takes no boundary
+  // decision boundaries as bf16 bit patterns in both halves: |x| >= t (ties
+  // at 0.75, 1.75, 3.5 go up to the even code) or |x| > t, i.e. >= t + 1
+  // (ties at 0.25, 1.25, 2.5, 5 go down to the even code).  A zero scale
+  // (every |x| < 0.006) takes the scale 2^100 instead: every boundary lies
+  // above every |x|, and the magnitudes are 0.
+  const float svb = sc != 0u ? sv : 0x1p100f;
+  // (each boundary is kept minus one: "|x| >= t" is "t - 1 - |x| < 0")
   auto bnd = [&](float mid, uint32_t strict) -> uint32_t {
-    return sc != 0u ? (f2u(mid * sv) >> 16) + strict : 0x7FFFu;
+    const uint32_t p = f2u(mid * svb);
+    return __builtin_amdgcn_perm(p, p, 0x03020302u) + strict * 0x10001u - 0x10001u;  // high half, twice
   };
-  const uint32_t t0 = bnd(0.25f, 1u), t1 = bnd(0.75f, 0u), t2 = bnd(1.25f, 1u), t3 = bnd(1.75f, 0u);
-  const uint32_t t4 = bnd(2.5f, 1u), t5 = bnd(3.5f, 0u), t6 = bnd(5.0f, 1u);
-  // binary search, with masks M = all ones where |x| is below the boundary:
+  const uint32_t T0 = bnd(0.25f, 1u), T1 = bnd(0.75f, 0u), T2 = bnd(1.25f, 1u), T3 = bnd(1.75f, 0u);
+  const uint32_t T4 = bnd(2.5f, 1u), T5 = bnd(3.5f, 0u), T6 = bnd(5.0f, 1u);
+  // binary search, with masks G = all ones where |x| reaches the boundary:
   //   level 1: 1.75; level 2: 3.5 or 0.75; level 3: 5, 2.5, 1.25 or 0.25;
-  //   magnitude = 7 - (4 [M1] + 2 [M2] + [M3])
-  const uint32_t T3 = t3 * 0x10001u, T1 = t1 * 0x10001u, T5 = t5 * 0x10001u;
-  const uint32_t T0 = t0 * 0x10001u, T2 = t2 * 0x10001u, T4 = t4 * 0x10001u, T6 = t6 * 0x10001u;
-  uint32_t w[2] = {0u, 0u};
+  //   magnitude = 4 [G1] + 2 [G2] + [G3].  Codes of elements 2j (low half)
+  //   and 2j + 1 (high half): sign << 3 | magnitude.
+  // constants as values the compiler cannot see, so that each select stays
+  // one v_bfi_b32 and each shift one packed shift
+  i16x2 sh15 = {15, 15};
+  uint32_t K4 = 0x00040004u, K2 = 0x00020002u, K7 = 0x00070007u;
+  asm("" : "+v"(sh15), "+v"(K4), "+v"(K2), "+v"(K7));
+  uint32_t c[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t a = h[j] & 0x7FFF7FFFu;
-    const uint32_t m1 = below_mask(a, T3);
-    const uint32_t m2 = below_mask(a, bitsel(m1, T1, T5));
-    const uint32_t m3 = below_mask(a, bitsel(m1, bitsel(m2, T0, T2), bitsel(m2, T4, T6)));
-    const uint32_t nb = bitsel(0x00040004u, m1, bitsel(0x00020002u, m2, m3)) & 0x00070007u;
-    // codes of elements 2j (low half) and 2j + 1: sign << 3 | magnitude
-    const uint32_t c = (nb ^ 0x00070007u) | ((h[j] >> 12) & 0x00080008u);
-    w[j >> 2] |= ((c | (c >> 12)) & 0xFFu) << (8 * (j & 3));
+    const uint32_t g1 = reach_mask(a, T3, sh15);
+    const uint32_t g2 = reach_mask(a, bitsel(g1, T5, T1), sh15);
+    const uint32_t g3 = reach_mask(a, bitsel(g2, bitsel(g1, T6, T2), bitsel(g1, T4, T0)), sh15);
+    // magnitude bit 2 from G1, bit 1 from G2, bit 0 from G3; bit 3 is the
+    // sign: h >> 12 per half is sign << 3 | three exponent bits
+    const uint32_t mag = bitsel(K4, g1, bitsel(K2, g2, g3));
+    c[j] = bitsel(K7, mag, pk_shr12(h[j]));
   }
-  const uint32_t w0 = w[0], w1 = w[1];
+  // nibble packing: perm gathers the low bytes of the halves of two pairs,
+  // x | x >> 4 puts each odd byte's code in the high nibble below it, and a
+  // final perm keeps bytes 0 and 2 of two such words
+  auto pack4 = [&](int j0) -> uint32_t {
+    const uint32_t x01 = __builtin_amdgcn_perm(c[j0 + 1], c[j0], 0x06040200u);  // c0.b0 c0.b2 c1.b0 c1.b2
+    const uint32_t x23 = __builtin_amdgcn_perm(c[j0 + 3], c[j0 + 2], 0x06040200u);
+    const uint32_t y01 = x01 | (x01 >> 4), y23 = x23 | (x23 >> 4);
+    return __builtin_amdgcn_perm(y23, y01, 0x06040200u);
+  };
+  const uint32_t w0 = pack4(0), w1 = pack4(4);
   // four neighbouring groups' scale bytes -> one dword store
   const uint32_t s1 = __shfl_down(sc, 1, 4), s2 = __shfl_down(sc, 2, 4), s3 = __shfl_down(sc, 3, 4);
   const bool ok = live && s >= 0 && s < n_pages * kPage;
