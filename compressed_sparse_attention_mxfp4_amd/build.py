@@ -23,7 +23,12 @@ def hipcc() -> str:
 def flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-munsafe-fp-atomics", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+            "-munsafe-fp-atomics",
+            # MFMA results in ordinary VGPRs: without it the attention kernel
+            # keeps its accumulators in AGPRs and copies them around every
+            # rescale and every partial-logit store
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
 def build(verbose: bool = False) -> str:

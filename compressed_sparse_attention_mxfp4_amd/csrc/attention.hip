@@ -206,7 +206,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     if (sub >= row1) break;
     // ---- dequantize: 4 rows x 16 channels (chunks 2cg, 2cg+1) per lane into
     // the swizzled row-major tile; odd channel groups store their two chunks
-    // in the other order (keeps each store instruction conflict-free)
+    // in the other order (keeps each store instruction conflict-free), so
+    // they convert their two 8-channel halves in the other order too
+    const int odd = cg & 1;
+    // wave-uniform: does this sub-chunk hold a window row?  If not, absent
+    // rows take a zero scale and every lane runs the FP4 conversion alone
+    const int kind_l = rkind[sc * kSub + (lane & (kSub - 1))];
+    const bool fp4_only = __ballot(lane < kSub && kind_l == 2) == 0;
     v8h rv[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -216,21 +222,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
       // is applied by one packed fp16 multiply per channel pair, exact since
       // the product has at most 6 significant bits and lies in fp16 range
       h2_t v[8];
-      if (kind == 1) {
+      if (fp4_only || kind == 1) {
         const uint32_t scode = (hi8[sc][i][0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
-        const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scode | (scode << 8), 1.0f, false);
+        // absent row (only reached when fp4_only): zero scale, zero row
+        const uint32_t spair = kind == 1 ? scode | (scode << 8) : 0u;
+        const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, false);
+        const uint32_t half[2] = {odd ? lo8[sc][i][1] : lo8[sc][i][0], odd ? lo8[sc][i][0] : lo8[sc][i][1]};
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 0) * s2;
-          v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 1) * s2;
-          v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 2) * s2;
-          v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo8[sc][i][d], 1.0f, 3) * s2;
+          v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 0) * s2;
+          v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 1) * s2;
+          v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 2) * s2;
+          v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 3) * s2;
         }
       } else {
         // window row (kind 2): 16 E4M3 codes; absent row (kind 0): zeros
         const bool w = kind == 2;
-        const uint32_t c4[4] = {w ? lo8[sc][i][0] : 0u, w ? lo8[sc][i][1] : 0u, w ? hi8[sc][i][0] : 0u,
-                                w ? hi8[sc][i][1] : 0u};
+        const v2u lo = odd ? hi8[sc][i] : lo8[sc][i], hi = odd ? lo8[sc][i] : hi8[sc][i];
+        const uint32_t c4[4] = {w ? lo[0] : 0u, w ? lo[1] : 0u, w ? hi[0] : 0u, w ? hi[1] : 0u};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           v[2 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, false);
@@ -244,14 +253,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
         rv[i][1][2 * e] = v[4 + e][0];
         rv[i][1][2 * e + 1] = v[4 + e][1];
       }
-      const int odd = cg & 1;
-      const v8h first = odd ? rv[i][1] : rv[i][0];
-      const v8h second = odd ? rv[i][0] : rv[i][1];
-      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]) = first;
-      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]) = second;
+      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]) = rv[i][0];
+      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]) = rv[i][1];
     }
     // bit r: row sub+r is present
-    const uint32_t vmask = (uint32_t)__ballot(lane < kSub && rkind[sc * kSub + (lane & (kSub - 1))] != 0);
+    const uint32_t vmask = (uint32_t)__ballot(lane < kSub && kind_l != 0);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
 
@@ -293,29 +299,45 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
         mx = fmaxf(mx, v);
       }
     mx = rows4_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : exp2f(m_run - m_new);
+    // Lazy reference: the running reference m_run moves only when a logit
+    // exceeds it by more than 8 (log2 units), so weights p stay <= 2^8 (exact
+    // range for the fp16 P operand and far from fp32 overflow) and the
+    // accumulator rescale is skipped while no head's reference moves.  The
+    // result is the same softmax: sums and outputs share the reference.
+    const bool grow = mx > m_run + 8.0f;  // m_run = -inf: any valid row grows it
+    const float m_new = grow ? mx : m_run;
+    // v_exp_f32 directly: its arguments are <= 8 or -inf (exp2(-inf) = 0), and
+    // results below the smallest normal (weights under 2^-126 of the
+    // reference) flush to 0.  While no row of head `col` has been valid, m_new
+    // is -inf; subtracting 0 instead keeps p = 0 and alpha = 0 (it scales
+    // only zeros then) rather than forming -inf - -inf.
+    const float m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
     float psum = 0.0f;
     v8h pa;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float p = (lg[k] == -__builtin_inff()) ? 0.0f : exp2f(lg[k] - m_new);
+      const float p = __builtin_amdgcn_exp2f(lg[k] - m_sub);
       psum += p;
       pa[k] = (_Float16)p;
     }
     psum = rows4_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // rescale output rows (heads 4g+i) by their alpha
+    // rescale output rows (heads 4g+i) by their alpha, only when some head
+    // with a nonzero accumulator moved its reference (wave-uniform test;
+    // every wave of the workgroup takes the same decision)
     // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
-    if (lane < 16) alph[wave][lane] = alpha;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+    if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
+      if (lane < 16) alph[wave][lane] = alpha;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
+        for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
+    }
 
     // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128)
     // P's K slice for lane (g, col) is rows {4g..4g+3, 16+4g..16+4g+3}.  The
