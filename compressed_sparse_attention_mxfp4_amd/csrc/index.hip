@@ -6,7 +6,9 @@
 //
 // Score of entry j for one query token (per indexer head h):
 //   d_h = exact sum_c q[h][c] k_j[c], rounded once to binary32
-//   s_j = binary32 fold over ascending h of fl(w_h * max(d_h, +0)).
+//   t_h = fl(w_h * max(d_h, +0)) for h < HI, +0 for HI <= h < 64
+//   s_j = balanced binary tree of binary32 adds over t_0 .. t_63 in
+//         ascending order, ((t_0 + t_1) + (t_2 + t_3)) + ..., then + 0.
 //
 // Exactness on MFMA.  Every E4M3 value is M * 2^-9 with M an integer,
 // |M| <= 229,376 < 2^18.

@@ -109,9 +109,10 @@ int csa2_quantize_kv(const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_s
  *   n_entries  [B] int32 visible entries per sequence (device).
  *   max_n_entries  host upper bound of n_entries (sizes the grid).
  * Score of entry j for token t (exact per-head dot rounded once to fp32,
- * ReLU, then a binary32 fold in ascending head order):
- *   s(j) = (..((+0 + fl(w_0 r_0)) + fl(w_1 r_1)) ..) + fl(w_{HI-1} r_{HI-1}),
- *   r_h = max(fl(sum_c q[h][c] k_j[c]), +0).
+ * ReLU, weighted, then a balanced binary tree of binary32 adds over 64 head
+ * slots in ascending head order, slots HI..63 holding +0):
+ *   r_h = max(fl(sum_c q[h][c] k_j[c]), +0),  t_h = fl(w_h r_h) (h < HI),
+ *   s(j) = (((t_0 + t_1) + (t_2 + t_3)) + ... + (t_62 + t_63)) + 0.
  * Outputs, per (b, t):
  *   out_topk   [B][T][topk]: the topk best entries by (score desc, index asc),
  *              written in ascending index order, -1 padded when n < topk.

@@ -3,7 +3,7 @@
 Formats against torch's own FP8 casts and an independent significand-rounding
 derivation; the cache write against hand-worked groups and the round-trip
 bound; scores against BLAS fp64 matmul (exact for FP8 inputs) and hand-worked
-fold cases; top-k and the pool against numpy lexsort brute force and the set
+head-sum order cases; top-k and the pool against numpy lexsort brute force and the set
 relations the pages fix; attention against torch's fp64 scaled-dot-product
 attention and closed-form special cases.
 """
@@ -238,7 +238,7 @@ def _e4m3(v):
     return synth.fp8_bits(torch.tensor(v, dtype=torch.float32))
 
 
-def test_score_fold_order_golden(oracle):
+def test_score_head_sum_order_golden(oracle):
     for c in gold("score_order.json")["cases"]:
         if "q_channel0" in c:
             H = len(c["q_channel0"])
