@@ -39,6 +39,10 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {  // in halves
 typedef _Float16 half_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+template <int M>
+struct ModeTag {
+  static constexpr int value = M;
+};
 
 // Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48): each
 // permlane swap of a register with itself leaves the two values of a lane
@@ -79,13 +83,35 @@ struct AttnArgs {
   float* part_ml;  // [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
 };
 
-// Source of one row of a split: an FP4 entry (page base, entry in page) or
-// a window row (byte offset of the row), or nothing.
-struct RowSrc {
-  int64_t base;  // FP4: page byte offset; window: row byte offset; -1: absent
-  int kind;      // 0 absent, 1 FP4 entry (entry index in page in `e`), 2 window row
-  int e;
-};
+// Hoisted LDS addresses: byte offsets in the workgroup's LDS, passed through
+// an empty asm so that the compiler keeps them in registers instead of
+// recomputing the swizzle in every sub-chunk.
+typedef __attribute__((address_space(3))) half_t lds_half_t;
+typedef __attribute__((address_space(3))) v8h lds_v8h_t;
+typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+__device__ __forceinline__ uint32_t lds_addr(const half_t* p) {
+  uint32_t x = (uint32_t)(uintptr_t)(const lds_half_t*)p;
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// Row loads through global-address-space pointers: the row pointers are
+// passed through LDS, and plain (flat) loads of them would also count on the
+// LDS wait counter, so every LDS wait would wait for the row loads as well.
+typedef const __attribute__((address_space(1))) v2u gbl_v2u_t;
+typedef const __attribute__((address_space(1))) uint32_t gbl_u32_t;
+__device__ __forceinline__ v2u gld8(const uint8_t* p) { return *(gbl_v2u_t*)p; }
+__device__ __forceinline__ uint32_t gld4(const uint8_t* p) { return *(gbl_u32_t*)p; }
+__device__ __forceinline__ void lds_st16(uint32_t addr, v8h v) { *(lds_v8h_t*)(uintptr_t)addr = v; }
+__device__ __forceinline__ v8h lds_ld16(uint32_t addr) { return *(const lds_v8h_t*)(uintptr_t)addr; }
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 4 halves that lane 4j + i / 4 points at, for j = 0..3
+__device__ __forceinline__ v4h lds_ld_tr(uint32_t addr) {
+  return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(uintptr_t)addr));
+}
+
+// Kinds of row content a split can hold (decided per split, the same for
+// every wave): only FP4 entries (rows < topk), only window rows, or both.
+enum SplitMode { kMixed = 0, kFp4Only = 1, kWindowOnly = 2 };
 
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
@@ -93,7 +119,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float alph[4][16];       // per wave: rescale factor per head
   __shared__ const uint8_t* rptr0[kRowsPerSplit];  // codes (FP4) or window row start
   __shared__ const uint8_t* rptr1[kRowsPerSplit];  // scale row (FP4) or window row start + 8
-  __shared__ int rkind[kRowsPerSplit];
+  __shared__ __attribute__((aligned(16))) int rkind[kRowsPerSplit];
+  __shared__ __attribute__((aligned(16))) float rbias[kRowsPerSplit];  // 0 present, -inf absent
 
   // XCD-aware order: workgroup id % 8 picks the XCD (and its L2).  The NHT
   // head tiles of one (split, b, t) unit take ids 8 apart, so they share an
@@ -148,232 +175,276 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     rptr0[threadIdx.x] = p0;
     rptr1[threadIdx.x] = p1;
     rkind[threadIdx.x] = kind;
+    rbias[threadIdx.x] = kind != 0 ? 0.0f : -__builtin_inff();
   }
 
-  // ---- Q slice as the B operand: head ht*16+col, channels 128*wave + 32*s + 8*g .. +8
+  // ---- Q slice as the B operand: head ht*16+col, channels 128*wave + 32*s
+  // + 8*g .. +8, kept as packed half pairs
   v8h qb[4];
   {
     const uint16_t* qrow = a.q + (((int64_t)bt * a.H) + ht * 16 + col) * kD + 128 * wave + 8 * g;
+    v4u raw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const v4u*>(qrow + 32 * s);
+    // the packed words pass through an empty asm so that the compiler keeps
+    // them packed instead of re-packing the halves before every MFMA
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const v4u raw = *reinterpret_cast<const v4u*>(qrow + 32 * s);
+      v4u pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float f0 = u2f(raw[e] << 16), f1 = u2f(raw[e] & 0xFFFF0000u);
-        qb[s][2 * e] = (_Float16)f0;
-        qb[s][2 * e + 1] = (_Float16)f1;
+        const h2_t h = {(_Float16)u2f(raw[s][e] << 16), (_Float16)u2f(raw[s][e] & 0xFFFF0000u)};
+        pk[e] = __builtin_bit_cast(uint32_t, h);
       }
+      asm volatile("" : "+v"(pk));
+      qb[s] = __builtin_bit_cast(v8h, pk);
     }
   }
-  __syncthreads();
 
-  // ---- issue every code load of the split up front.  Lane (rg, cg) of
-  // wave w dequantizes rows 4*rg .. 4*rg+3 of each 32-row sub-chunk,
-  // channels 128*w + 16*cg .. +16: per row 8 code bytes + 1 scale byte
-  // (FP4) or 16 bytes (window).
+  // lane (rg, cg) of wave w dequantizes rows 4*rg .. 4*rg+3 of each 32-row
+  // sub-chunk, channels 128*w + 16*cg .. +16 (16-byte chunks 2cg, 2cg+1 of
+  // the wave's tile); odd channel groups store their two chunks in the other
+  // order (keeps each store instruction conflict-free)
   const int rg = lane >> 3, cg = lane & 7;
+  const int odd = cg & 1;
   const int ch0 = 128 * wave + 16 * cg;
-  constexpr int kSubs = kRowsPerSplit / kSub;  // 4
-  // Two unconditional 8-byte loads per row (no branch, so no load waits on
-  // another's destination registers): FP4 row -> 16 code nibbles and the
-  // dword holding the scale byte; window row -> its 16 FP8 codes; absent row
-  // -> the pool's first bytes, discarded.
-  // lane offsets from the row bases: FP4 codes at ch0/2, scale dword at
-  // (ch0/16) & ~3; window bytes at ch0 (both halves)
-  const int off_fp4_0 = ch0 / 2, off_fp4_1 = (ch0 / 16) & ~3;
-  v2u lo8[kSubs][4], hi8[kSubs][4];
-#pragma unroll
-  for (int sc = 0; sc < kSubs; ++sc)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = sc * kSub + 4 * rg + i;
-      const bool fp4 = rkind[rr] == 1;
-      lo8[sc][i] = *reinterpret_cast<const v2u*>(rptr0[rr] + (fp4 ? off_fp4_0 : ch0));
-      hi8[sc][i] = *reinterpret_cast<const v2u*>(rptr1[rr] + (fp4 ? off_fp4_1 : ch0));
-    }
-
-  float m_run = -__builtin_inff();  // running max (log2 units) of head `col`
-  float l_run = 0.0f;               // running sum of head `col`
-  v4f o_acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o_acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
   half_t* my_kr = kr[wave];
-
+  uint32_t st_addr[4][2];
 #pragma unroll
-  for (int sc = 0; sc < kSubs; ++sc) {
-    const int sub = row0 + sc * kSub;
-    if (sub >= row1) break;
-    // ---- dequantize: 4 rows x 16 channels (chunks 2cg, 2cg+1) per lane into
-    // the swizzled row-major tile; odd channel groups store their two chunks
-    // in the other order (keeps each store instruction conflict-free), so
-    // they convert their two 8-channel halves in the other order too
-    const int odd = cg & 1;
-    // wave-uniform: does this sub-chunk hold a window row?  If not, absent
-    // rows take a zero scale and every lane runs the FP4 conversion alone
-    const int kind_l = rkind[sc * kSub + (lane & (kSub - 1))];
-    const bool fp4_only = __ballot(lane < kSub && kind_l == 2) == 0;
-    v8h rv[4][2];
+  for (int i = 0; i < 4; ++i) {
+    st_addr[i][0] = lds_addr(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]);
+    st_addr[i][1] = lds_addr(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]);
+  }
+  // Q.K operand rows: lane (g, col) reads row col (+16), channels 32s + 8g
+  uint32_t qk_addr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kind = rkind[sc * kSub + 4 * rg + i];
-      // hardware conversions with unit scale are exact for every FP4 and
-      // E4M3 code (element 0 = low nibble / low byte); the E4M3 block scale
-      // is applied by one packed fp16 multiply per channel pair, exact since
-      // the product has at most 6 significant bits and lies in fp16 range
-      h2_t v[8];
-      if (fp4_only || kind == 1) {
-        const uint32_t scode = (hi8[sc][i][0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
-        // absent row (only reached when fp4_only): zero scale, zero row
-        const uint32_t spair = kind == 1 ? scode | (scode << 8) : 0u;
-        const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, false);
-        const uint32_t half[2] = {odd ? lo8[sc][i][1] : lo8[sc][i][0], odd ? lo8[sc][i][0] : lo8[sc][i][1]};
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 0) * s2;
-          v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 1) * s2;
-          v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 2) * s2;
-          v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 3) * s2;
-        }
-      } else {
-        // window row (kind 2): 16 E4M3 codes; absent row (kind 0): zeros
-        const bool w = kind == 2;
-        const v2u lo = odd ? hi8[sc][i] : lo8[sc][i], hi = odd ? lo8[sc][i] : hi8[sc][i];
-        const uint32_t c4[4] = {w ? lo[0] : 0u, w ? lo[1] : 0u, w ? hi[0] : 0u, w ? hi[1] : 0u};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          v[2 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, false);
-          v[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, true);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rv[i][0][2 * e] = v[e][0];
-        rv[i][0][2 * e + 1] = v[e][1];
-        rv[i][1][2 * e] = v[4 + e][0];
-        rv[i][1][2 * e + 1] = v[4 + e][1];
-      }
-      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]) = rv[i][0];
-      *reinterpret_cast<v8h*>(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]) = rv[i][1];
-    }
-    // bit r: row sub+r is present
-    const uint32_t vmask = (uint32_t)__ballot(lane < kSub && kind_l != 0);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- partial logits S^T (32 rows x 16 heads) over this wave's 128 channels
-    v4f sacc[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sacc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8h ka = *reinterpret_cast<const v8h*>(&my_kr[tile_off(rt * 16 + col, 4 * s + g)]);
-        sacc[rt] = mfma16(ka, qb[s], sacc[rt]);
-      }
-      ssum[sc & 1][wave][rt][lane] = sacc[rt];
-    }
-    // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
-    // and this buffer is rewritten only after the next sub-chunk's barrier
-    __syncthreads();
-    v4f st[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      st[rt] = ssum[sc & 1][0][rt][lane];
-      st[rt] = st[rt] + ssum[sc & 1][1][rt][lane];
-      st[rt] = st[rt] + ssum[sc & 1][2][rt][lane];
-      st[rt] = st[rt] + ssum[sc & 1][3][rt][lane];
-    }
-
-    // ---- online softmax for head `col` over rows 4g+i (+16)
-    float lg[8];
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = rt * 16 + 4 * g + i;
-        const bool ok = (vmask >> rr) & 1u;
-        const float v = ok ? st[rt][i] * a.sm_scale_log2 : -__builtin_inff();
-        lg[rt * 4 + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = rows4_max(mx);
-    // Lazy reference: the running reference m_run moves only when a logit
-    // exceeds it by more than 8 (log2 units), so weights p stay <= 2^8 (exact
-    // range for the fp16 P operand and far from fp32 overflow) and the
-    // accumulator rescale is skipped while no head's reference moves.  The
-    // result is the same softmax: sums and outputs share the reference.
-    const bool grow = mx > m_run + 8.0f;  // m_run = -inf: any valid row grows it
-    const float m_new = grow ? mx : m_run;
-    // v_exp_f32 directly: its arguments are <= 8 or -inf (exp2(-inf) = 0), and
-    // results below the smallest normal (weights under 2^-126 of the
-    // reference) flush to 0.  While no row of head `col` has been valid, m_new
-    // is -inf; subtracting 0 instead keeps p = 0 and alpha = 0 (it scales
-    // only zeros then) rather than forming -inf - -inf.
-    const float m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
-    float psum = 0.0f;
-    v8h pa;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float p = __builtin_amdgcn_exp2f(lg[k] - m_sub);
-      psum += p;
-      pa[k] = (_Float16)p;
-    }
-    psum = rows4_sum(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rescale output rows (heads 4g+i) by their alpha, only when some head
-    // with a nonzero accumulator moved its reference (wave-uniform test;
-    // every wave of the workgroup takes the same decision)
-    // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
-    if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
-      if (lane < 16) alph[wave][lane] = alpha;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
-    }
-
-    // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128)
-    // P's K slice for lane (g, col) is rows {4g..4g+3, 16+4g..16+4g+3}.  The
-    // matching V column (channel 16c + col over those rows) comes from the
-    // row-major tile through the transposing LDS load: within each 16-lane
-    // group, lane i receives element i % 4 of the 4 halves that lane
-    // 4j + i / 4 points at, for j = 0..3.  Lane (g, col) therefore points at
-    // row 4g + col / 4 (+16), channels 16c + 4 (col % 4) .. +3.
+  for (int s = 0; s < 4; ++s) qk_addr[s] = lds_addr(&my_kr[tile_off(col, 4 * s + g)]);
+  // P.V operand: the V column (channel 16c + col over P's K slice, rows
+  // {4g..4g+3, 16+4g..16+4g+3}) comes from the row-major tile through the
+  // transposing load, so lane (g, col) points at row 4g + col / 4 (+16),
+  // channels 16c + 4 (col % 4) .. +3
+  uint32_t pv_addr[8];
+  {
     const int tr_row = 4 * g + (col >> 2);
     const int tq = col & 3;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const half_t* p0 = &my_kr[tile_off(tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)];
-      const half_t* p1 = &my_kr[tile_off(16 + tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)];
-      const v4h v0 = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(p0)));
-      const v4h v1 = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(p1)));
-      const v8h vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      o_acc[c] = mfma16(pa, vb, o_acc[c]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    for (int c = 0; c < 8; ++c) pv_addr[c] = lds_addr(&my_kr[tile_off(tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)]);
   }
+  constexpr int kRowBytes16 = 16 * kRowHalves * 2;  // 16 rows of the tile, in bytes
+  // LDS-only barriers throughout: the row loads stay in flight across them
+  lds_barrier();
 
-  // ---- write this split's partials
-  const int64_t pidx = ((int64_t)bt * NHT + ht) * a.n_splits + split;
-  float* po = a.part_o + pidx * 16 * kD;
+  // The whole sub-chunk loop, specialised by what the split's rows can be.
+  auto run = [&](auto mode_tag) {
+    constexpr int kMode = decltype(mode_tag)::value;
+    constexpr int kSubs = kRowsPerSplit / kSub;  // 4
+    // ---- issue every code load of the split up front: per row 8 code
+    // bytes + the dword holding the scale byte (FP4) or 16 bytes (window);
+    // absent rows read the pool's first bytes, discarded
+    const int off_fp4_0 = ch0 / 2, off_fp4_1 = (ch0 / 16) & ~3;
+    v2u lo8[kSubs][4], hi8[kSubs][4];
+    bool present[kSubs][4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+    for (int sc = 0; sc < kSubs; ++sc) {
+      const v4i k4 = *reinterpret_cast<const v4i*>(&rkind[sc * kSub + 4 * rg]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) po[(4 * g + i) * kD + 128 * wave + c * 16 + col] = o_acc[c][i];
-  if (wave == 0 && lane < 16) {
-    a.part_ml[pidx * 32 + lane] = m_run;
-    a.part_ml[pidx * 32 + 16 + lane] = l_run;
-  }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = sc * kSub + 4 * rg + i;
+        if (kMode == kFp4Only) {
+          lo8[sc][i] = gld8(rptr0[rr] + off_fp4_0);
+          hi8[sc][i][0] = gld4(rptr1[rr] + off_fp4_1);
+          hi8[sc][i][1] = 0u;
+          present[sc][i] = k4[i] == 1;
+        } else if (kMode == kWindowOnly) {
+          lo8[sc][i] = gld8(rptr0[rr] + ch0);
+          hi8[sc][i] = gld8(rptr1[rr] + ch0);
+          present[sc][i] = k4[i] == 2;
+        } else {
+          const bool fp4 = k4[i] == 1;
+          lo8[sc][i] = gld8(rptr0[rr] + (fp4 ? off_fp4_0 : ch0));
+          hi8[sc][i] = gld8(rptr1[rr] + (fp4 ? off_fp4_1 : ch0));
+          present[sc][i] = k4[i] != 0;
+        }
+      }
+      // keep the loads in sub-chunk order: the wait counter retires them in
+      // issue order, so sub-chunk 0 then waits only for its own rows
+      asm volatile("" ::: "memory");
+    }
+
+    float m_run = -__builtin_inff();  // running reference (log2 units) of head `col`
+    float l_run = 0.0f;               // running sum of head `col`
+    v4f o_acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o_acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int sc = 0; sc < kSubs; ++sc) {
+      const int sub = row0 + sc * kSub;
+      if (sub >= row1) break;
+      // ---- dequantize 4 rows x 16 channels into the swizzled tile.
+      // Hardware conversions with unit scale are exact for every FP4 and
+      // E4M3 code (element 0 = low nibble / low byte); the E4M3 block scale
+      // is applied by one packed fp16 multiply per channel pair, exact since
+      // the product has at most 6 significant bits and lies in fp16 range.
+      // Odd channel groups convert their two 8-channel halves in the other
+      // order, to match their store order.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h2_t v[8];
+        const v2u lo = lo8[sc][i], hi = hi8[sc][i];
+        auto fp4_row = [&]() {
+          // absent row: zero scale, zero row (FP4 codes are all finite).  The
+          // mask is opaque so that the scale load stays unconditional (a
+          // select on `present` would let the compiler sink the load into a
+          // branch and wait for it there).
+          uint32_t pm = present[sc][i] ? 0xFFFFFFFFu : 0u;
+          asm volatile("" : "+v"(pm));
+          const uint32_t scode = (hi[0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
+          const uint32_t spair = (scode * 0x101u) & pm;
+          const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, false);
+          const uint32_t half[2] = {odd ? lo[1] : lo[0], odd ? lo[0] : lo[1]};
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 0) * s2;
+            v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 1) * s2;
+            v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 2) * s2;
+            v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 3) * s2;
+          }
+        };
+        auto fp8_row = [&](bool w) {
+          // window row: 16 E4M3 codes; absent row: zeros (its bytes may hold
+          // NaN codes, and its V must be 0 to meet p = 0)
+          const v2u x = odd ? hi : lo, y = odd ? lo : hi;
+          const uint32_t c4[4] = {w ? x[0] : 0u, w ? x[1] : 0u, w ? y[0] : 0u, w ? y[1] : 0u};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            v[2 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, false);
+            v[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, true);
+          }
+        };
+        if (kMode == kFp4Only) {
+          fp4_row();
+        } else if (kMode == kWindowOnly) {
+          fp8_row(present[sc][i]);
+        } else {
+          const int kind = rkind[sc * kSub + 4 * rg + i];
+          if (kind == 1) fp4_row();
+          else fp8_row(kind == 2);
+        }
+        v8h r0, r1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r0[2 * e] = v[e][0];
+          r0[2 * e + 1] = v[e][1];
+          r1[2 * e] = v[4 + e][0];
+          r1[2 * e + 1] = v[4 + e][1];
+        }
+        lds_st16(st_addr[i][0], r0);
+        lds_st16(st_addr[i][1], r1);
+      }
+      wave_lds_order();
+
+      // ---- partial logits S^T (32 rows x 16 heads) over this wave's 128 channels
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        v4f sacc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc = mfma16(lds_ld16(qk_addr[s] + rt * kRowBytes16), qb[s], sacc);
+        ssum[sc & 1][wave][rt][lane] = sacc;
+      }
+      // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
+      // and this buffer is rewritten only after the next sub-chunk's barrier
+      lds_barrier();
+      // row biases (0 or -inf) of rows 4g..4g+3 and 16+4g..16+4g+3
+      const v4f bias0 = *reinterpret_cast<const v4f*>(&rbias[sc * kSub + 4 * g]);
+      const v4f bias1 = *reinterpret_cast<const v4f*>(&rbias[sc * kSub + 16 + 4 * g]);
+      v4f part[4][2];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) part[w4][rt] = ssum[sc & 1][w4][rt][lane];
+      // fixed order: ((w0 + w1) + w2) + w3
+      v4f st[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) st[rt] = ((part[0][rt] + part[1][rt]) + part[2][rt]) + part[3][rt];
+
+      // ---- online softmax for head `col` over rows 4g+i (+16)
+      float lg[8];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // fma with a zero addend is the rounded product; -inf masks the row
+        lg[i] = __builtin_fmaf(st[0][i], a.sm_scale_log2, bias0[i]);
+        lg[4 + i] = __builtin_fmaf(st[1][i], a.sm_scale_log2, bias1[i]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, lg[k]);
+      mx = rows4_max(mx);
+      // Lazy reference: the running reference m_run moves only when a logit
+      // exceeds it by more than 8 (log2 units), so weights p stay <= 2^8 (exact
+      // range for the fp16 P operand and far from fp32 overflow) and the
+      // accumulator rescale is skipped while no head's reference moves.  The
+      // result is the same softmax: sums and outputs share the reference.
+      const bool grow = mx > m_run + 8.0f;  // m_run = -inf: any valid row grows it
+      const float m_new = grow ? mx : m_run;
+      // v_exp_f32 directly: its arguments are <= 8 or -inf (exp2(-inf) = 0),
+      // and results below the smallest normal (weights under 2^-126 of the
+      // reference) flush to 0.  While no row of head `col` has been valid,
+      // m_new is -inf; subtracting 0 instead keeps p = 0 and alpha = 0 (it
+      // scales only zeros then) rather than forming -inf - -inf.
+      const float m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+      float psum = 0.0f;
+      v8h pa;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = __builtin_amdgcn_exp2f(lg[k] - m_sub);
+        psum += p;
+        pa[k] = (_Float16)p;
+      }
+      psum = rows4_sum(psum);
+      l_run = l_run * alpha + psum;
+      // rescale output rows (heads 4g+i) by their alpha, only when some head
+      // with a nonzero accumulator moved its reference (wave-uniform test;
+      // every wave of the workgroup takes the same decision)
+      // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
+      if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
+        if (lane < 16) alph[wave][lane] = alpha;
+        wave_lds_order();
+        const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
+      }
+      m_run = m_new;
+
+      // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v4h v0 = lds_ld_tr(pv_addr[c]);
+        const v4h v1 = lds_ld_tr(pv_addr[c] + kRowBytes16);
+        const v8h vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o_acc[c] = mfma16(pa, vb, o_acc[c]);
+      }
+      wave_lds_order();
+    }
+
+    // ---- write this split's partials
+    const int64_t pidx = ((int64_t)bt * NHT + ht) * a.n_splits + split;
+    float* po = a.part_o + pidx * 16 * kD;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[(4 * g + i) * kD + 128 * wave + c * 16 + col] = o_acc[c][i];
+    if (wave == 0 && lane < 16) {
+      a.part_ml[pidx * 32 + lane] = m_run;
+      a.part_ml[pidx * 32 + 16 + lane] = l_run;
+    }
+  };
+  if (row1 <= a.topk) run(ModeTag<kFp4Only>{});
+  else if (row0 >= a.topk) run(ModeTag<kWindowOnly>{});
+  else run(ModeTag<kMixed>{});
 }
 
 struct CombineArgs {

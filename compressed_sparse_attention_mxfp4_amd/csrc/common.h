@@ -48,6 +48,22 @@ __device__ __forceinline__ int64_t phys_page(const int32_t* __restrict__ page_ta
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Orders this lane's LDS accesses around a hand-off to other lanes of the
+// wave: the LDS executes one wave's instructions in order, so keeping the
+// compiler from moving memory accesses across this point is enough.
+__device__ __forceinline__ void wave_lds_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Events recorded around launches of each kernel (csa2_time_kernel).
 struct KernelEvents {
   hipEvent_t start = nullptr, stop = nullptr;

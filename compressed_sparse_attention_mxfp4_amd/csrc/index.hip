@@ -107,22 +107,6 @@ __device__ __forceinline__ uint32_t group8_max(uint32_t m) {
   return m;
 }
 
-// Orders this lane's LDS accesses around a hand-off to other lanes of the
-// wave: the LDS executes one wave's instructions in order, so keeping the
-// compiler from moving memory accesses across this point is enough.
-__device__ __forceinline__ void wave_lds_order() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Workgroup barrier that orders LDS accesses only: global loads in flight
-// stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Row stride of the block-maxima buffer: ceil(max_n / 8) rounded up to a
 // multiple of 4 so every row starts 16-byte aligned.
 __host__ __device__ __forceinline__ int bm_stride(int max_n) {
