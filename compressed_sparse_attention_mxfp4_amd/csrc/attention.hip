@@ -457,8 +457,9 @@ struct CombineArgs {
 };
 
 // One workgroup per (b, t, h), 128 threads of 4 channels: merge the splits'
-// (max, sum, output).  The split weights are formed once (one wave, in
-// registers), then every thread issues its loads for all splits together.
+// (max, sum, output).  Wave 0 loads the (max, sum) pairs first, then every
+// thread issues its loads of all splits' output rows; the split weights are
+// formed (one wave, in registers) while those are in flight.
 constexpr int kMaxSplits = (CSA2_MAX_TOPK + CSA2_SWA + kRowsPerSplit - 1) / kRowsPerSplit;
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
@@ -469,10 +470,26 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
   const int NHT = a.H >> 4, ht = h >> 4, hh = h & 15;
   const int64_t base = ((int64_t)bt * NHT + ht) * a.n_splits;
   const int lane = lane_id();
+  const bool in = lane < a.n_splits;
+  float ms = -__builtin_inff(), ls = 0.0f;
+  if (threadIdx.x < 64 && in) {
+    ms = a.part_ml[(base + lane) * 32 + hh];
+    ls = a.part_ml[(base + lane) * 32 + 16 + hh];
+  }
+  // loads complete in issue order: keep the pairs ahead of the rows
+  asm volatile("" ::: "memory");
+  const int c = threadIdx.x * 4;
+  // unconditional loads (splits past n_splits re-read the last one and are
+  // not used), so that no branch separates them and each waits only for its own
+  v4f po[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int sc = min(s, a.n_splits - 1);
+    po[s] = *reinterpret_cast<const v4f*>(a.part_o + ((base + sc) * 16 + hh) * kD + c);
+  }
+  // every row load is issued before the first wait for the pairs
+  asm volatile("" : "+v"(ms), "+v"(ls)::"memory");
   if (threadIdx.x < 64) {
-    const bool in = lane < a.n_splits;
-    const float ms = in ? a.part_ml[(base + lane) * 32 + hh] : -__builtin_inff();
-    const float ls = in ? a.part_ml[(base + lane) * 32 + 16 + hh] : 0.0f;
     float M = ms;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
@@ -481,21 +498,17 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
     // fixed-order sum over the splits (lane order)
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
-    if (in) wsplit[lane] = wgt;
+    // splits past n_splits get weight 0 (their re-read rows are finite)
+    if (lane < kMaxSplits) wsplit[lane] = in ? wgt : 0.0f;
     if (lane == 0) {
       inv_l = 1.0f / L;
       if (a.out_lse) a.out_lse[(int64_t)bt * a.H + h] = (M + log2f(L)) * 0.69314718055994530942f;
     }
   }
-  __syncthreads();
-  const int c = threadIdx.x * 4;
+  lds_barrier();
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s >= a.n_splits) break;
-    const v4f po = *reinterpret_cast<const v4f*>(a.part_o + ((base + s) * 16 + hh) * kD + c);
-    acc += wsplit[s] * po;
-  }
+  for (int s = 0; s < kMaxSplits; ++s) acc += wsplit[s] * po[s];
   *reinterpret_cast<v4f*>(a.out + ((int64_t)bt * a.H + h) * kD + c) = acc * inv_l;
 }
 
