@@ -33,6 +33,7 @@ OP_INDEX_FULL, OP_INDEX_REINDEX, OP_SPARSE_ATTN = 1, 2, 3
 EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
+    "csa2_test_keep_histograms",
 )
 
 # kernel ids for csa2_time_kernel
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH):
     L.csa2_abi_version.restype = ctypes.c_int
     L.csa2_time_kernel.argtypes = [ctypes.c_int, P, P]
     L.csa2_time_kernel.restype = ctypes.c_int
+    L.csa2_test_keep_histograms.argtypes = [ctypes.c_int]
+    L.csa2_test_keep_histograms.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L

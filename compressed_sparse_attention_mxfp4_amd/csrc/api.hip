@@ -33,7 +33,7 @@ extern "C" const char* csa2_status_str(int status) {
   }
 }
 
-extern "C" int csa2_abi_version(void) { return 100; }
+extern "C" int csa2_abi_version(void) { return 101; }
 
 namespace csa2 {
 KernelEvents& kernel_events(int kernel) {
@@ -48,5 +48,17 @@ extern "C" int csa2_time_kernel(int kernel, void* start_event, void* stop_event)
   csa2::KernelEvents& e = csa2::kernel_events(kernel);
   e.start = reinterpret_cast<hipEvent_t>(start_event);
   e.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return CSA2_OK;
+}
+
+namespace csa2 {
+bool& keep_histograms() {
+  static bool keep = false;
+  return keep;
+}
+}  // namespace csa2
+
+extern "C" int csa2_test_keep_histograms(int on) {
+  csa2::keep_histograms() = on != 0;
   return CSA2_OK;
 }

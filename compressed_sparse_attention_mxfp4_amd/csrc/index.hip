@@ -136,8 +136,9 @@ struct ScoreArgs {
   int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
   int chunks_per_wg;      // chunks of one row per workgroup
   int wg_per_row;         // workgroups per row
-  uint32_t* hist;         // [B][T][2][kHistBins], zeroed before the launch: counts of the
-                          // visible entries' and the blocks' score keys by their top 10 bits
+  uint32_t* hist;         // [B][T][2][kHistBins]: counts of the visible entries' and the
+                          // blocks' score keys by their top 10 bits (cleared by the scan)
+  int clear_hist;         // 0 only under the test aid that keeps the histograms
 };
 
 // Adds 1 to bin `bin` of a histogram of 16-bit counters packed two per word.
@@ -426,6 +427,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   RowCtx rc;
   if (have_row) row_ctx<POOL>(a, row, t_full, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  // clear this workgroup's share of its row's global level-1 histograms: the
+  // row's workgroups add into them only at their ends.  Device-scope atomics,
+  // so that the clear and the other workgroups' adds are ordered at the same
+  // point whichever caches they pass.  A workgroup that starts only after
+  // another of its row has already added would drop those counts; the
+  // selection checks its counts against the list and then counts the list's
+  // keys itself, so such a histogram costs time, not correctness.
+  if (row < a.rows && a.clear_hist) {
+    const int words = (POOL ? 1 : a.T) * 2 * kHistBins;
+    uint32_t* gh = a.hist + (int64_t)(POOL ? row : row * a.T) * 2 * kHistBins;
+    const int k = blockIdx.x % a.wg_per_row;
+    const int per = (words + a.wg_per_row - 1) / a.wg_per_row;
+    const int w1 = min(words, (k + 1) * per);
+    for (int i = k * per + (int)threadIdx.x; i < w1; i += blockDim.x) atomicAnd(&gh[i], 0u);
+  }
   lds_barrier();
 
   // Full mode: the physical pages of this wave's chunks, lane k holding the
@@ -640,11 +656,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   }
 }
 
-// Clears the level-1 histograms before a scan.
-__global__ void hist_zero_kernel(uint32_t* h, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) h[i] = 0u;
-}
-
 // ---------------------------------------------------------------- selection
 //
 // One workgroup per (b, t) row.  Keys are order-preserving uint32 images of
@@ -662,6 +673,7 @@ struct SelShared {
   uint32_t stage[kMaxKPT * kSelThreads];  // the block maxima, in transit to their threads
   uint32_t bins[kBins];                   // one radix level's histogram
   int wave_tot[kSelWaves];
+  int wave_tot2[kSelWaves];
   int misc[8];
   int pool_blk[CSA2_MAX_POOL_BLOCKS];
 };
@@ -707,6 +719,17 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   return before + x - v;
 }
 
+// Sum over the workgroup (every thread returns it).
+__device__ int block_sum(int v, SelShared& sh) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int x = wave_sum(v);
+  if (lane == 0) sh.wave_tot2[wave] = x;
+  lds_barrier();
+  // wave_tot2 is written again only after later barriers
+  return wave_sum(lane < kSelWaves ? sh.wave_tot2[lane] : 0);
+}
+
 // One wave, histogram h of 2,048 bins (lane l owns bins [2048 - 32(l+1),
 // 2048 - 32l), lane 0 has the highest digits).  For the rank x >= 1 (counted
 // from the top) returns the bin holding it (-1 if the histogram holds fewer
@@ -743,14 +766,13 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint
 // KPT t + r), order (key desc, position asc); key 0 marks an empty slot.
 // Two steps, so that the first overlaps the loads of the keys:
 //
-// topk_level1: from `l1v`, the histogram the scan accumulated of the list's
-//    keys by their top 10 bits (thread t holds bin t), the number of valid
-//    keys and, with more than K, the first radix digit of the K-th largest
-//    key.  The histogram may count more keys than the list holds, but only
-//    keys below the K-th: bins above the crossing then hold the same counts
-//    as the list's own keys, the crossing bin is the same, and the list
-//    holds more than K valid keys exactly when the histogram does, or
-//    exactly K.
+// topk_level1: the number of valid keys of the list (from each thread's
+//    count) and, with more than K, the first radix digit of the K-th largest
+//    key from `l1v`, the histogram the scan accumulated of the list's keys by
+//    their top 10 bits (thread t holds bin t).  The histogram may count more
+//    keys than the list holds, but only keys below the K-th: bins above the
+//    crossing then hold the same counts as the list's own keys, and the
+//    crossing bin is the same.
 // topk_finish: the next two digits (11 + 11 bits) from histograms of the
 //    list's keys that match the prefix so far, which gives the K-th largest
 //    key tau; then every key above tau, and the first keys (in position
@@ -758,8 +780,14 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint
 //    place in ascending position order.  A thread's rank base is a prefix
 //    over the threads' counts, since its positions are contiguous.  Returns
 //    the number selected.
+//    The histogram is only a hint: such a selection (every key above tau and
+//    the first keys equal to tau) holds every key that ranks above one of its
+//    own, so it is the top K exactly when it holds K keys.  The count is
+//    checked before anything is emitted; when the histogram disagrees with
+//    the list (a workgroup of the scan cleared its share after another had
+//    flushed into it), the first digit is counted from the list's own keys
+//    and the selection is redone.
 struct TopkState {
-  int n_valid;
   uint32_t prefix, msk;
   int rem;
   bool l1_ok;
@@ -786,19 +814,22 @@ __device__ TopkState topk_level1(uint32_t l1v, int K, SelShared& sh) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tid = (int)threadIdx.x;
-  TopkState st{0, 0u, 0u, K, true};
+  TopkState st{0u, 0u, K, true};
   // the level-1 digits occupy bins [0, 1024)
   sh.bins[tid] = l1v;
   sh.bins[tid + kSelThreads] = 0u;
   const int wv = wave_sum((int)l1v);
   if (lane == 0) sh.wave_tot[wave] = wv;
   lds_barrier();
-  st.n_valid = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
-  if (st.n_valid > K) {
+  // the crossing is looked for whenever the histogram holds K keys; whether
+  // the list holds more than K is decided from its own keys
+  const int n_hist = wave_sum(lane < kSelWaves ? sh.wave_tot[lane] : 0);
+  st.l1_ok = n_hist >= K;
+  if (st.l1_ok) {
     int ab;
     const int d = bins_cross(sh, K, &ab);
     if (d < 0) {
-      st.l1_ok = false;  // never for a consistent input (see topk_finish)
+      st.l1_ok = false;
     } else {
       st.prefix = (uint32_t)d << 22;
       st.msk = 1023u << 22;
@@ -815,71 +846,95 @@ __device__ int topk_finish(const uint32_t (&key)[KPT], int K, TopkState st, SelS
   static_assert(KPT <= kMaxKPT, "keys per thread");
   const int tid = (int)threadIdx.x;
   uint32_t* bins = sh.bins;
-  uint32_t tau = 0;  // with tau = 0 every valid key is selected
-  int need_eq = 0;
-  if (st.n_valid > K) {
-    uint32_t prefix = st.prefix, msk = st.msk;
-    int rem = st.rem;
-    // histogram of digit (key >> shift) & dmask over the keys matching the prefix
-    auto build = [&](int shift, uint32_t dmask) {
-      bins[tid] = 0u;
-      bins[tid + kSelThreads] = 0u;
-      lds_barrier();
+  // valid keys of the list
+  int nv = 0;
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const uint32_t k = key[r];
-        if (k != 0u && (k & msk) == prefix) atomicAdd(&bins[(k >> shift) & dmask], 1u);
+  for (int r = 0; r < KPT; ++r) nv += key[r] != 0u ? 1 : 0;
+  const int n_valid = block_sum(nv, sh);
+  const int expect = min(K, n_valid);
+#pragma clang loop unroll(disable)
+  for (int attempt = 0;; ++attempt) {
+    // the digit shifts pass through an empty asm in every attempt, so that
+    // the compiler does not hoist the keys' digits out of the loop (that
+    // would hold several copies of the keys in registers)
+    int sh0 = 0;
+    asm volatile("" : "+s"(sh0));
+    uint32_t tau = 0;  // with tau = 0 every valid key is selected
+    int need_eq = 0;
+    if (n_valid > K) {
+      uint32_t prefix = st.prefix, msk = st.msk;
+      int rem = st.rem;
+      // histogram of digit (key >> shift) & dmask over the keys matching the prefix
+      auto build = [&](int shift, uint32_t dmask) {
+        bins[tid] = 0u;
+        bins[tid + kSelThreads] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+          const uint32_t k = key[r];
+          if (k != 0u && (k & msk) == prefix) atomicAdd(&bins[(k >> shift) & dmask], 1u);
+        }
+        lds_barrier();
+      };
+      int d, ab;
+      if (!st.l1_ok) {
+        // the first digit from the list's own keys
+        build(22 + sh0, 1023u);
+        d = bins_cross(sh, rem, &ab);
+        prefix = (uint32_t)d << 22;
+        msk = 1023u << 22;
+        rem -= ab;
       }
-      lds_barrier();
-    };
-    int d, ab;
-    if (!st.l1_ok) {
-      // the scan's histogram holds fewer than K keys above the list's K-th
-      // (never for a consistent input): count the list's own keys instead
-      build(22, 1023u);
-      d = bins_cross(sh, rem, &ab);
-      prefix = (uint32_t)d << 22;
-      msk = 1023u << 22;
-      rem -= ab;
-    }
 #pragma unroll
-    for (int shift = 11; shift >= 0; shift -= 11) {
-      build(shift, 2047u);
-      d = bins_cross(sh, rem, &ab);
-      prefix |= (uint32_t)d << shift;
-      msk |= 2047u << shift;
-      rem -= ab;
+      for (int shift = 11; shift >= 0; shift -= 11) {
+        build(shift + sh0, 2047u);
+        d = bins_cross(sh, rem, &ab);
+        prefix |= (uint32_t)d << shift;
+        msk |= 2047u << shift;
+        rem -= ab;
+      }
+      tau = prefix;
+      need_eq = rem;
     }
-    tau = prefix;
-    need_eq = rem;
-  }
 
-  // ---- 3. emit in position order
-  uint32_t gt_m = 0, eq_m = 0;
+    // ---- 3. count, check, emit in position order
+    uint32_t gt_m = 0, eq_m = 0;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    gt_m |= (key[r] > tau ? 1u : 0u) << r;
-    eq_m |= (key[r] != 0u && key[r] == tau ? 1u : 0u) << r;
+    for (int r = 0; r < KPT; ++r) {
+      gt_m |= (key[r] > tau ? 1u : 0u) << r;
+      eq_m |= (key[r] != 0u && key[r] == tau ? 1u : 0u) << r;
+    }
+    const int ngt = __builtin_popcount(gt_m), neq = __builtin_popcount(eq_m);
+    int tot;
+    // both totals are at most 32,768: the 16-bit halves never carry
+    const int pre = block_excl_scan(ngt | (neq << 16), sh, &tot);
+    const int gt_tot = tot & 0xFFFF, eq_tot = (int)((uint32_t)tot >> 16);
+    const int got = gt_tot + min(eq_tot, max(need_eq, 0));
+    if (got != expect && attempt == 0) {
+      // the histogram disagreed with the list (workgroup-uniform decision)
+      st.l1_ok = false;
+      st.prefix = 0u;
+      st.msk = 0u;
+      st.rem = K;
+      continue;
+    }
+    const int gt_before = pre & 0xFFFF, eq_before = (int)((uint32_t)pre >> 16);
+    // this thread's keys equal to tau that are taken: the first ones in
+    // position order, up to need_eq over the whole list
+    uint32_t sel = gt_m, m = eq_m;
+    for (int take = min(max(need_eq - eq_before, 0), neq); take > 0; --take) {
+      sel |= m & (~m + 1u);
+      m &= m - 1u;
+    }
+    // ranks stay below K whatever the counts (only a wrong count could
+    // exceed it, and the recount above leaves none)
+    int rank = gt_before + min(eq_before, max(need_eq, 0));
+    while (sel != 0u && rank < K) {
+      emit(rank++, KPT * tid + __builtin_ctz(sel));
+      sel &= sel - 1u;
+    }
+    return min(got, K);
   }
-  const int ngt = __builtin_popcount(gt_m), neq = __builtin_popcount(eq_m);
-  int tot;
-  // both totals are at most 32,768: the 16-bit halves never carry
-  const int pre = block_excl_scan(ngt | (neq << 16), sh, &tot);
-  const int gt_tot = tot & 0xFFFF, eq_tot = (int)((uint32_t)tot >> 16);
-  const int gt_before = pre & 0xFFFF, eq_before = (int)((uint32_t)pre >> 16);
-  // this thread's keys equal to tau that are taken: the first ones in
-  // position order, up to need_eq over the whole list
-  uint32_t sel = gt_m, m = eq_m;
-  for (int take = min(max(need_eq - eq_before, 0), neq); take > 0; --take) {
-    sel |= m & (~m + 1u);
-    m &= m - 1u;
-  }
-  int rank = gt_before + min(eq_before, need_eq);
-  while (sel != 0u) {
-    emit(rank++, KPT * tid + __builtin_ctz(sel));
-    sel &= sel - 1u;
-  }
-  return gt_tot + min(eq_tot, need_eq);
 }
 
 struct SelectArgs {
@@ -1055,13 +1110,10 @@ extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_
   return align256((size_t)B * T * pool_blocks * 8 * 4) + hist_bytes(B, T);
 }
 
-// Launches the histogram clear, then the scan.
-int launch_scan(bool pool, const csa2::ScoreArgs& sa, int T_grid, int B, int T, hipStream_t stream) {
-  const int nh = B * T * 2 * csa2::kHistBins;
-  hipLaunchKernelGGL(csa2::hist_zero_kernel, dim3(std::min((nh + 1023) / 1024, 64)), dim3(1024), 0, stream,
-                     sa.hist, nh);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+// Launches the scan (which also clears the level-1 histograms).
+int launch_scan(bool pool, const csa2::ScoreArgs& sa, int T_grid, hipStream_t stream) {
   csa2::ScoreArgs args = sa;
+  args.clear_hist = csa2::keep_histograms() ? 0 : 1;
   const int gx = score_grid(args.rows, args.chunks_per_row, T_grid, &args.chunks_per_wg, &args.wg_per_row);
   if (pool)
     CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads), stream,
@@ -1105,7 +1157,7 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
       align256((size_t)B * T * csa2::bm_stride(max_n_entries) * 4));
   sa.rows = B;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
-  st = launch_scan(false, sa, T, B, T, (hipStream_t)stream);
+  st = launch_scan(false, sa, T, (hipStream_t)stream);
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -1157,7 +1209,7 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
                                         align256((size_t)B * T * pool_blocks * 8 * 4));
   sa.rows = B * T;
   sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
-  st = launch_scan(true, sa, 1, B, T, (hipStream_t)stream);
+  st = launch_scan(true, sa, 1, (hipStream_t)stream);
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;

@@ -187,6 +187,17 @@ enum csa2_kernel {
  */
 int csa2_time_kernel(int kernel, void *start_event, void *stop_event);
 
+/*
+ * Test aid (not part of the method): with `on` nonzero, the indexer scans
+ * stop clearing their level-1 histograms in the workspace, so the selection
+ * starts from whatever counts the workspace already holds (for example a
+ * previous call's).  The selection checks those counts against the list it
+ * ranks and counts the list's own keys when they disagree, so the results
+ * stay exact; this switch lets a test reach that path.  Process-wide setting,
+ * not thread-safe.  Returns CSA2_OK.
+ */
+int csa2_test_keep_histograms(int on);
+
 /* Workspace bytes a call needs (op = enum csa2_op; `heads` = HI for the
  * indexer calls, H for attention; `max_n_entries` unused for attention). */
 size_t csa2_workspace_bytes(int op, int32_t B, int32_t T, int32_t heads, int32_t max_n_entries,

@@ -301,6 +301,35 @@ def test_index_deterministic():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("poison", ["stale", "random"])
+def test_index_recount_when_histogram_disagrees(oracle, poison):
+    """The selection takes the scan's level-1 histogram as a hint only.  With
+    the scans told to keep the histograms, they hold a previous call's counts
+    plus this call's ("stale") or random words ("random"); the selections
+    must notice the disagreement, count their lists' own keys and still
+    return the exact Full and Reindex results."""
+    say(f"index with a {poison} level-1 histogram (selection recount)")
+    wl = small_workload([40000, 9000], T=2, HI=16, topk=512, seed=21)
+    other = synth.layer_inputs("full", wl.B, wl.T, 16, 16, 22)
+    layer = wl.layers[0]
+    ws = csa2.Workspace()
+    args = (dev(wl.kidx_pool), dev(wl.paging.page_table), dev(wl.n_entries))
+    ref = oracle_index_full(oracle, wl, layer)
+    csa2.index_full(dev(other.q_idx), dev(other.w), *args, wl.max_n, wl.topk, 2048, ws=ws)
+    if poison == "random":
+        ws.buf.copy_(torch.randint(0, 256, ws.buf.shape, dtype=torch.uint8, device="cuda"))
+    csa2.lib().csa2_test_keep_histograms(1)
+    try:
+        got = csa2.index_full(dev(layer.q_idx), dev(layer.w), *args, wl.max_n, wl.topk, 2048, ws=ws)
+        assert_index_equal(got, ref)
+        rtk = csa2.index_reindex(dev(other.q_idx), dev(other.w), *args, got[1], got[2], wl.topk, ws=ws)
+    finally:
+        csa2.lib().csa2_test_keep_histograms(0)
+    ref_rtk = oracle.index_reindex(other.q_idx, other.w, wl.kidx_pool, wl.paging.page_table,
+                                   wl.n_entries, ref[1], ref[2], wl.topk)
+    assert np.array_equal(host(rtk), ref_rtk)
+
+
 def test_group_128k_b8_full_reindex_reuse(oracle):
     say("group 128K ctx B=8: Full -> Reindex -> Reuse")
     wl = synth.workload("group_128k_b8")
