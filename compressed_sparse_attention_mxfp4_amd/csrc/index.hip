@@ -427,6 +427,51 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   RowCtx rc;
   if (have_row) row_ctx<POOL>(a, row, t_full, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  const int n_tok = POOL ? 1 : a.T;
+
+  // ---- every load that needs nothing loaded first is issued here, ahead of
+  // the keys (the wait counter retires loads in issue order): the raw query
+  // words of this thread's limb items, the head weights, and (Full mode)
+  // the page-table words of this wave's first 64 chunks, read before the
+  // row's length is known and checked against it afterwards.  The loads are
+  // unconditional (clamped indices; words that are not needed are masked
+  // by opaque masks at their use), so that no branch separates them and the
+  // compiler keeps no load of them inside one.
+  // Limb item (token, row tile rt, slice s, lane L): head tile_head(rt, L &
+  // 15), channels 16 gL + 8 s + e (s < 2) or 64 + 16 gL + 8 (s - 2) + e
+  // (e < 8, gL = L >> 4), the keys' order in the slices.
+  constexpr int kLimbIters = CSA2_MAX_T * kRT * 4 * 64 / kScoreThreads;
+  const int n_items = n_tok * kRT * 4 * 64;  // 1024 n_tok, a power of two
+  uint32_t qraw[kLimbIters][2], qkeep[kLimbIters];
+#pragma unroll
+  for (int j = 0; j < kLimbIters; ++j) {
+    const int it = (int)threadIdx.x + j * kScoreThreads;
+    const int iw = it & (n_items - 1);
+    const int L = iw & 63, sl = (iw >> 6) & 3, rt = (iw >> 8) & 3, tk = iw >> 10;
+    const int t = POOL ? rc.t : tk;
+    const int h = tile_head(rt, L & 15), gL = L >> 4;
+    const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        a.q_idx + (((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)) * kDI + ch);
+    qraw[j][0] = src[0];
+    qraw[j][1] = src[1];
+    qkeep[j] = (it < n_items && h < HI) ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(qkeep[j]));
+  }
+  uint32_t wraw, wkeep;
+  {
+    const int i = min((int)threadIdx.x, n_tok * 64 - 1);
+    const int tk = i >> 6, h = i & 63;
+    const int t = POOL ? rc.t : tk;
+    wraw = __float_as_uint(a.w[((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)]);
+    wkeep = ((int)threadIdx.x < n_tok * 64 && h < HI) ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(wkeep));
+  }
+  int page_word = -1;
+  if (!POOL) {
+    const int ck = c0 + slice + lane * n_slices;
+    page_word = a.page_table[(int64_t)rc.b * a.max_pages + max(0, min(ck, a.max_pages - 1))];
+  }
   // clear this workgroup's share of its row's global level-1 histograms: the
   // row's workgroups add into them only at their ends.  Device-scope atomics,
   // so that the clear and the other workgroups' adds are ordered at the same
@@ -456,10 +501,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   auto page_of = [&](int k) -> int64_t {
     return POOL ? 0 : (int64_t)__builtin_amdgcn_readlane(wave_pages, k & 63);
   };
+  // every early load has arrived here (they went out together): waiting
+  // for them before the key loads leaves nothing to wait for in the limb work
+#pragma unroll
+  for (int j = 0; j < kLimbIters; ++j) asm volatile("" ::"v"(qraw[j][0]), "v"(qraw[j][1]));
+  asm volatile("" ::"v"(wraw), "v"(page_word));
   ChunkKeys cur;
   bool cur_ok = false;
   if (active) {
-    fill_pages(0);
+    if (!POOL) {
+      // chunk_page on the early page-table word
+      const int ck = c0 + slice + lane * n_slices;
+      wave_pages = (ck < c1 && ck * kChunk < rc.n && ck < a.max_pages && page_word >= 0 && page_word < a.n_pages)
+                       ? page_word : -1;
+    }
     const int64_t pg0 = page_of(0);
 #pragma unroll
     for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, rc, chunk, pg0, st, g, col, cur.k[st]);
@@ -467,51 +522,39 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   }
 
   // ---- the workgroup's queries in f16 limbs: ql = Mq mod 2^7 and qm =
-  // floor(Mq / 2^7) of M = q * 2^9 (exact small integers).  Item (token,
-  // row tile rt, slice s, lane L): head tile_head(rt, L & 15), channels
-  // 16 gL + 8 s + e (s < 2) or 64 + 16 gL + 8 (s - 2) + e (e < 8, gL = L >> 4),
-  // the keys' order in the slices.
+  // floor(Mq / 2^7) of M = q * 2^9 (exact small integers), from the raw words
   if (have_row) {
-    const int n_tok = POOL ? 1 : a.T;
-    const int b = rc.b;
-    for (int it = threadIdx.x; it < n_tok * kRT * 4 * 64; it += blockDim.x) {
+#pragma unroll
+    for (int j = 0; j < kLimbIters; ++j) {
+      const int it = (int)threadIdx.x + j * kScoreThreads;
+      if (it >= n_items) break;
       const int L = it & 63, sl = (it >> 6) & 3, rt = (it >> 8) & 3, tk = it >> 10;
-      const int t = POOL ? rc.t : tk;
-      const int h = tile_head(rt, L & 15), gL = L >> 4;
-      const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
-      uint32_t c[2] = {0u, 0u};
-      if (h < HI) {
-        const uint32_t* src =
-            reinterpret_cast<const uint32_t*>(a.q_idx + (((int64_t)b * a.T + t) * HI + h) * kDI + ch);
-        c[0] = src[0];
-        c[1] = src[1];
-      }
       v8h ql, qm;
       bool bad = false;
 #pragma unroll
       for (int wd = 0; wd < 2; ++wd)
 #pragma unroll
         for (int wsel = 0; wsel < 2; ++wsel) {
-          const v2f m2 = wsel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[wd], 512.0f, true)
-                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[wd], 512.0f, false);
+          const uint32_t c = qraw[j][wd] & qkeep[j];
+          const v2f m2 = wsel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 512.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 512.0f, false);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int e = 4 * wd + 2 * wsel + j;
-            const float hi = floorf(m2[j] * 0x1p-7f);
-            const float lo = m2[j] - hi * 128.0f;  // exact: both are small integers
+          for (int jj = 0; jj < 2; ++jj) {
+            const int e = 4 * wd + 2 * wsel + jj;
+            const float hi = floorf(m2[jj] * 0x1p-7f);
+            const float lo = m2[jj] - hi * 128.0f;  // exact: both are small integers
             ql[e] = (_Float16)lo;
             qm[e] = (_Float16)hi;
-            bad = bad || !(fabsf(m2[j]) < 16384.0f);
+            bad = bad || !(fabsf(m2[jj]) < 16384.0f);
           }
         }
       sm.qlimb[tk][rt][sl][0][L] = ql;
       sm.qlimb[tk][rt][sl][1][L] = qm;
       if (bad) atomicOr(&sm.qbad[tk], 1u);
     }
-    for (int i = threadIdx.x; i < n_tok * 64; i += blockDim.x) {
-      const int tk = i >> 6, h = i & 63;
-      const int t = POOL ? rc.t : tk;
-      sm.wsh[tk][h] = h < HI ? a.w[((int64_t)b * a.T + t) * HI + h] * 0x1p-9f : 0.0f;
+    if ((int)threadIdx.x < n_tok * 64) {
+      const int tk = (int)threadIdx.x >> 6, h = (int)threadIdx.x & 63;
+      sm.wsh[tk][h] = __uint_as_float(wraw & wkeep) * 0x1p-9f;  // 0 past HI
     }
   }
   lds_barrier();
