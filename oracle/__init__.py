@@ -164,6 +164,63 @@ def pool_entry(kv_pool: np.ndarray, page: int, off: int):
             base[PAGE * ENTRY_CODES + off * NGROUPS:PAGE * ENTRY_CODES + (off + 1) * NGROUPS])
 
 
+# ------------------------------------------- indexer keys in MXFP4 (next step)
+# Knowledge note "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+# Compression", "FP4 main KV" and "Reconstructing the 890-byte cache budget"
+# on "Inside DeepSeek V4.1 Flash": the pages' own indexer-key format is E2M1
+# elements with one E8M0 (power-of-two) scale per 32 channels, 68 B per
+# 128-channel entry.  Reading: entry e of a page holds its 128 codes in 64
+# bytes at e * 64 (channel 2i in the low nibble of byte i), the page's 64 x 4
+# scale bytes follow at 4096 + e * 4 (byte g: channels 32g .. 32g + 31);
+# 4,352 B per page.  E8M0 code s means 2^(s - 127).  Supported scales:
+# 119 <= s <= 133 (2^-8 .. 2^6), a precondition: every key value is then a
+# multiple of 2^-9 of magnitude <= 384, i.e. exactly an E4M3 value, and the
+# score is the same exact function of the keys as for E4M3 keys.
+MX_ENTRY_CODES = 64
+MX_NGROUPS = 4
+MX_ENTRY_BYTES = MX_ENTRY_CODES + MX_NGROUPS   # 68
+MX_PAGE_BYTES = PAGE * MX_ENTRY_BYTES          # 4,352
+MX_SCALE_MIN, MX_SCALE_MAX = 119, 133
+
+
+def mxfp4_key_values(kidx_mx: np.ndarray) -> np.ndarray:
+    """MXFP4 indexer-key pool uint8 [P, 4352] -> binary64 key values [P, 64, 128]."""
+    pool = np.ascontiguousarray(kidx_mx, dtype=np.uint8).reshape(-1, MX_PAGE_BYTES)
+    P = pool.shape[0]
+    codes = pool[:, :PAGE * MX_ENTRY_CODES].reshape(P, PAGE, MX_ENTRY_CODES)
+    nib = np.empty((P, PAGE, DI), np.uint8)
+    nib[:, :, 0::2] = codes & 0xF
+    nib[:, :, 1::2] = codes >> 4
+    scales = pool[:, PAGE * MX_ENTRY_CODES:].reshape(P, PAGE, MX_NGROUPS)
+    if np.any((scales < MX_SCALE_MIN) | (scales > MX_SCALE_MAX)):
+        raise ValueError("E8M0 scale outside the supported range 2^-8 .. 2^6")
+    scale = np.exp2(scales.astype(np.float64) - 127.0)                 # [P, 64, 4]
+    return e2m1_decode(nib) * np.repeat(scale, DI // MX_NGROUPS, axis=2)
+
+
+def mxfp4_keys_to_e4m3(kidx_mx: np.ndarray) -> np.ndarray:
+    """The same keys as E4M3 codes [P, 64, 128] (an exact re-encoding under the
+    scale precondition; raises if a value has no E4M3 code)."""
+    v = mxfp4_key_values(kidx_mx)
+    table = e4m3_decode(np.arange(256))
+    code_of = {}
+    for c in range(256):
+        x = table[c]
+        if np.isnan(x):
+            continue
+        key = (float(x), bool(np.signbit(x)))
+        code_of.setdefault(key, c)
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    uniq, inv = np.unique(np.stack([flat, np.signbit(flat).astype(np.float64)], 1), axis=0, return_inverse=True)
+    for i, (x, sb) in enumerate(uniq):
+        c = code_of.get((float(x), bool(sb)))
+        if c is None:
+            raise ValueError(f"key value {x!r} has no E4M3 code")
+        out[inv.reshape(-1) == i] = c
+    return out.reshape(v.shape)
+
+
 # ---------------------------------------------------------------- a2..a6: indexer
 def index_scores(q_codes: np.ndarray, w: np.ndarray, key_codes: np.ndarray) -> np.ndarray:
     """q_codes uint8 [H,128], w float32 [H], key_codes uint8 [n,128] -> float32 [n]."""
@@ -224,6 +281,16 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, topk_k, pool_blocks):
             out_topk[b, t] = topk(s, topk_k)
             out_pool[b, t], out_n[b, t] = pool(s, pool_blocks)
     return out_topk, out_pool, out_n
+
+
+def index_full_mxfp4(q_idx, w, kidx_mx, page_table, n_entries, topk_k, pool_blocks):
+    """Full mode over MXFP4 indexer keys (same outputs as index_full)."""
+    return index_full(q_idx, w, mxfp4_keys_to_e4m3(kidx_mx), page_table, n_entries, topk_k, pool_blocks)
+
+
+def index_reindex_mxfp4(q_idx, w, kidx_mx, page_table, n_entries, pool_, pool_n, topk_k):
+    """Reindex mode over MXFP4 indexer keys (same output as index_reindex)."""
+    return index_reindex(q_idx, w, mxfp4_keys_to_e4m3(kidx_mx), page_table, n_entries, pool_, pool_n, topk_k)
 
 
 def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool_, pool_n, topk_k):

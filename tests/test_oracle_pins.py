@@ -423,3 +423,51 @@ def test_sparse_attn_with_all_entries_selected_is_dense(oracle):
         rows = np.concatenate([ent, oracle.e4m3_decode(L.swa[0, t:t + 128])])
         ref = _sdpa64(oracle.bf16_to_f64(L.q[0, t]), rows, 1.0)
         assert np.allclose(out[0, t], ref, atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------------------------ MXFP4 indexer keys
+_E2M1_BY_HAND = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_mxfp4_key_conversion_exact_for_every_code_and_scale(oracle):
+    """Every E2M1 code under every supported E8M0 scale becomes the E4M3 code of
+    exactly code * 2^(s - 127) (values written out from the format definition)."""
+    for s in range(oracle.MX_SCALE_MIN, oracle.MX_SCALE_MAX + 1):
+        page = np.zeros((1, oracle.MX_PAGE_BYTES), np.uint8)
+        page[0, 4096:] = 127
+        for c in range(16):
+            page[0, c * 64] = c              # entry c, channel 0 (low nibble)
+            page[0, 4096 + c * 4] = s        # its channels 0..31
+        e4 = oracle.mxfp4_keys_to_e4m3(page)
+        got = oracle.e4m3_decode(e4[0, :16, 0])
+        want = np.array([(-1.0 if c & 8 else 1.0) * _E2M1_BY_HAND[c & 7] * 2.0 ** (s - 127) for c in range(16)])
+        assert np.array_equal(got, want), s
+        assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_mxfp4_key_layout_by_hand(oracle):
+    page = np.zeros((2, oracle.MX_PAGE_BYTES), np.uint8)
+    page[:, 4096:] = 127
+    e = 5
+    page[1, e * 64 + 0] = 0x2F       # ch0: code 0xF = -6, ch1: code 0x2 = 1.0
+    page[1, e * 64 + 16] = 0x70      # ch32: 0, ch33: code 7 = 6
+    page[1, e * 64 + 63] = 0x90      # ch126: 0, ch127: code 9 = -0.5
+    page[1, 4096 + e * 4 + 0] = 128  # channels 0..31 scaled by 2
+    page[1, 4096 + e * 4 + 1] = 125  # channels 32..63 by 1/4
+    page[1, 4096 + e * 4 + 3] = 133  # channels 96..127 by 64
+    v = oracle.mxfp4_key_values(page)
+    assert v[1, e, 0] == -12.0 and v[1, e, 1] == 2.0
+    assert v[1, e, 32] == 0.0 and v[1, e, 33] == 1.5
+    assert v[1, e, 126] == 0.0 and v[1, e, 127] == -32.0
+    assert np.count_nonzero(v) == 4
+
+
+def test_mxfp4_key_scale_range_enforced(oracle):
+    page = np.zeros((1, oracle.MX_PAGE_BYTES), np.uint8)
+    page[0, 4096:] = 127
+    page[0, 4096] = oracle.MX_SCALE_MAX + 1
+    with pytest.raises(ValueError):
+        oracle.mxfp4_key_values(page)
+    page[0, 4096] = oracle.MX_SCALE_MIN - 1
+    with pytest.raises(ValueError):
+        oracle.mxfp4_key_values(page)
