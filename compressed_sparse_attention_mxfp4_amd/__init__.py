@@ -28,12 +28,13 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 D, DI, PAGE, BLOCK, SWA = 512, 128, 64, 8, 128
 PAGE_BYTES, KIDX_PAGE_BYTES = 18432, 8192
+MX_KIDX_PAGE_BYTES = 4352  # MXFP4 indexer keys: 64 x 64 code bytes + 64 x 4 E8M0 scales
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_SPARSE_ATTN = 1, 2, 3
 
 EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
-    "csa2_test_keep_histograms",
+    "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
 )
 
 # kernel ids for csa2_time_kernel
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH):
                                   P, sz, P]
     L.csa2_index_reindex.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, P, P, i32, i32, P, P,
                                      sz, P]
+    L.csa2_index_full_mxfp4.argtypes = L.csa2_index_full.argtypes
+    L.csa2_index_reindex_mxfp4.argtypes = L.csa2_index_reindex.argtypes
     L.csa2_sparse_attn.argtypes = [P, ctypes.c_float, P, i64, P, i32, P, P, i32, P, i32, i32, i32,
                                    P, P, P, sz, P]
     L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32]
@@ -80,7 +83,8 @@ def load(path: str = LIB_PATH):
     L.csa2_time_kernel.restype = ctypes.c_int
     L.csa2_test_keep_histograms.argtypes = [ctypes.c_int]
     L.csa2_test_keep_histograms.restype = ctypes.c_int
-    for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn"):
+    for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
+               "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -173,10 +177,18 @@ def quantize_kv(kv_bf16, dst_slot, kv_pool, stream=None):
     return kv_pool
 
 
+def _kidx_arg(kidx_pool, mxfp4):
+    torch = _torch()
+    if mxfp4:
+        return _ptr(kidx_pool, torch.uint8, "kidx_pool", (None, MX_KIDX_PAGE_BYTES), 2)
+    return _ptr(kidx_pool, torch.uint8, "kidx_pool", (None, PAGE, DI), 3)
+
+
 def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, pool_blocks=2048,
-               out_topk=None, out_pool=None, out_pool_n=None, ws=None, stream=None):
+               out_topk=None, out_pool=None, out_pool_n=None, ws=None, stream=None, mxfp4=False):
     """Full-mode indexer.  q_idx [B,T,HI,128] uint8 (E4M3), w [B,T,HI] float32,
-    kidx_pool [P,64,128] uint8, page_table [B,max_pages] int32, n_entries [B] int32."""
+    kidx_pool [P,64,128] uint8 E4M3 keys (or, with mxfp4=True, [P,4352] uint8 in
+    the MXFP4 page layout), page_table [B,max_pages] int32, n_entries [B] int32."""
     torch = _torch()
     B, T, HI, _ = q_idx.shape
     dev = q_idx.device
@@ -188,22 +200,23 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, 
         out_pool_n = torch.empty((B, T), dtype=torch.int32, device=dev)
     nb = workspace_bytes(OP_INDEX_FULL, B, T, HI, max_n_entries, topk)
     buf = _ws(ws, nb)
-    st = lib().csa2_index_full(
+    fn = lib().csa2_index_full_mxfp4 if mxfp4 else lib().csa2_index_full
+    st = fn(
         _ptr(q_idx, torch.uint8, "q_idx", (B, T, HI, DI), 4), _ptr(w, torch.float32, "w", (B, T, HI), 3),
-        _ptr(kidx_pool, torch.uint8, "kidx_pool", (None, PAGE, DI), 3), kidx_pool.shape[0],
+        _kidx_arg(kidx_pool, mxfp4), kidx_pool.shape[0],
         _ptr(page_table, torch.int32, "page_table", (B, None), 2), page_table.shape[1],
         _ptr(n_entries, torch.int32, "n_entries", (B,), 1), int(max_n_entries), B, T, HI, int(topk),
         int(pool_blocks), _ptr(out_topk, torch.int32, "out_topk", (B, T, topk), 3),
         _ptr(out_pool, torch.int32, "out_pool", (B, T, pool_blocks), 3),
         _ptr(out_pool_n, torch.int32, "out_pool_n", (B, T), 2), ctypes.c_void_p(buf.data_ptr()),
         buf.numel(), _stream(stream))
-    _check("csa2_index_full", st)
+    _check("csa2_index_full_mxfp4" if mxfp4 else "csa2_index_full", st)
     return out_topk, out_pool, out_pool_n
 
 
 def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool, pool_n, topk, out_topk=None,
-                  ws=None, stream=None):
-    """Reindex-mode indexer over the pool written by index_full."""
+                  ws=None, stream=None, mxfp4=False):
+    """Reindex-mode indexer over the pool written by index_full (keys as for index_full)."""
     torch = _torch()
     B, T, HI, _ = q_idx.shape
     P = pool.shape[2]
@@ -211,15 +224,16 @@ def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool, pool_n, topk
         out_topk = torch.empty((B, T, topk), dtype=torch.int32, device=q_idx.device)
     nb = workspace_bytes(OP_INDEX_REINDEX, B, T, HI, 0, topk)
     buf = _ws(ws, nb)
-    st = lib().csa2_index_reindex(
+    fn = lib().csa2_index_reindex_mxfp4 if mxfp4 else lib().csa2_index_reindex
+    st = fn(
         _ptr(q_idx, torch.uint8, "q_idx", (B, T, HI, DI), 4), _ptr(w, torch.float32, "w", (B, T, HI), 3),
-        _ptr(kidx_pool, torch.uint8, "kidx_pool", (None, PAGE, DI), 3), kidx_pool.shape[0],
+        _kidx_arg(kidx_pool, mxfp4), kidx_pool.shape[0],
         _ptr(page_table, torch.int32, "page_table", (B, None), 2), page_table.shape[1],
         _ptr(n_entries, torch.int32, "n_entries", (B,), 1), B, T, HI,
         _ptr(pool, torch.int32, "pool", (B, T, P), 3), _ptr(pool_n, torch.int32, "pool_n", (B, T), 2),
         P, int(topk), _ptr(out_topk, torch.int32, "out_topk", (B, T, topk), 3),
         ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream))
-    _check("csa2_index_reindex", st)
+    _check("csa2_index_reindex_mxfp4" if mxfp4 else "csa2_index_reindex", st)
     return out_topk
 
 

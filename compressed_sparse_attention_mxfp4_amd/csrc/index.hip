@@ -54,6 +54,12 @@ constexpr int kMaxWaveChunks = 1024;         // chunks one wave may take in one 
 constexpr int kMaxWgChunks = 1016;
 // Level-1 histogram of the selections: score keys by their top 10 bits.
 constexpr int kHistBins = 1024;
+// MXFP4 indexer keys: per page 64 entries x 64 code bytes (channel 2i in the
+// low nibble of byte i), then 64 x 4 E8M0 scale bytes (byte g: channels
+// 32g .. 32g + 31)
+constexpr int kMxCodes = 64;
+constexpr int kMxScaleOff = kPage * kMxCodes;        // 4,096
+constexpr int kMxPageBytes = kMxScaleOff + kPage * 4;  // 4,352
 constexpr int kBufferFlags = 0x00020000;     // raw buffer descriptor word 3 (32-bit data, no swizzle)
 
 // General split of the 4 FP8 codes of one dword: M = value * 2^9 (exact
@@ -79,6 +85,44 @@ __device__ __forceinline__ void limbs3(v4u codes, v4i& lo, v4i& mid, v4i& top) {
   for (int d = 0; d < 4; ++d) {
     uint32_t l, m, t;
     limbs3_word(codes[d], l, m, t);
+    lo[d] = (int)l;
+    mid[d] = (int)m;
+    top[d] = (int)t;
+  }
+}
+
+// E8M0 scale code -> its binary32 value times 2^e (codes 119 .. 133 and
+// small e keep it a normal number)
+__device__ __forceinline__ float e8m0_times_pow2(uint32_t s, int e) { return __uint_as_float((s + e) << 23); }
+
+// General limbs of one MXFP4 half (s2 = 0: channels [16g, 16g+16), 1:
+// [64+16g, 64+16g+16)), in the layout limbs3 gives FP8 codes: M = value * 2^9
+// is an exact integer (|M| <= 384 * 2^9 < 2^18) under the supported scales.
+__device__ __forceinline__ void limbs3_mx(const v4u (&mx)[2], int s2, int g, v4i& lo, v4i& mid, v4i& top) {
+  const uint32_t s = (mx[1][0] >> (8 * (2 * s2 + (g >> 1)))) & 0xFFu;
+  const float sc = e8m0_times_pow2(s, 9);  // scale * 2^9
+  uint32_t M[16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t wd = mx[0][2 * s2 + i];
+    const v2f m0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 0);
+    const v2f m1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 1);
+    const v2f m2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 2);
+    const v2f m3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, sc, 3);
+    const float v[8] = {m0[0], m0[1], m1[0], m1[1], m2[0], m2[1], m3[0], m3[1]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) M[8 * i + e] = (uint32_t)(int)v[e];
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t l = 0u, m = 0u, t = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = M[4 * d + i];
+      l |= (x & 127u) << (8 * i);
+      m |= ((x >> 7) & 127u) << (8 * i);
+      t |= ((x >> 14) & 255u) << (8 * i);
+    }
     lo[d] = (int)l;
     mid[d] = (int)m;
     top[d] = (int)t;
@@ -205,9 +249,41 @@ __device__ __forceinline__ int64_t chunk_page(const ScoreArgs& a, const RowCtx& 
 // mode: `pg` is the chunk's page (chunk_page), read through a buffer
 // descriptor whose record count ends at the sub-tile's last visible entry,
 // so the loads need no predicate (the hardware returns zero past the count).
-template <bool POOL>
+// MXFP4 keys (MX): k[0] holds the 16 + 16 channels' code bytes (dwords 0, 1:
+// channels [16g, 16g+16); dwords 2, 3: [64+16g, 64+16g+16)), k[1][0] the
+// entry's 4 scale bytes.
+template <bool POOL, bool MX>
 __device__ __forceinline__ void load_sub(const ScoreArgs& a, const RowCtx& r, int chunk, int64_t pg, int st,
                                          int g, int col, v4u (&k)[2]) {
+  if (MX) {
+    v2u c0 = {0u, 0u}, c1 = {0u, 0u};
+    uint32_t sw = 0u;
+    if (!POOL) {
+      const int nv = pg >= 0 ? min(r.n - chunk * kChunk, kChunk) : 0;
+      const uint8_t* page = a.kidx + (pg >= 0 ? pg * kMxPageBytes : 0);
+      const int nst = __builtin_amdgcn_readfirstlane(min(max(nv - 16 * st, 0), 16));
+      const __amdgpu_buffer_rsrc_t rc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(page + st * 16 * kMxCodes), 0, nst * kMxCodes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rsc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(page + kMxScaleOff + st * 16 * 4), 0, nst * 4, kBufferFlags);
+      const uint32_t lofs = (uint32_t)(col * kMxCodes + 8 * g);
+      c0 = __builtin_amdgcn_raw_buffer_load_b64(rc, lofs, 0, 0);
+      c1 = __builtin_amdgcn_raw_buffer_load_b64(rc, lofs + 32, 0, 0);
+      sw = __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)(col * 4), 0, 0);
+    } else {
+      const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
+      if (j >= 0) {
+        const int64_t p = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
+        const uint8_t* page = a.kidx + p * kMxPageBytes;
+        c0 = *reinterpret_cast<const v2u*>(page + (j & 63) * kMxCodes + 8 * g);
+        c1 = *reinterpret_cast<const v2u*>(page + (j & 63) * kMxCodes + 32 + 8 * g);
+        sw = *reinterpret_cast<const uint32_t*>(page + kMxScaleOff + (j & 63) * 4);
+      }
+    }
+    k[0] = v4u{c0[0], c0[1], c1[0], c1[1]};
+    k[1] = v4u{sw, 0u, 0u, 0u};
+    return;
+  }
   if (!POOL) {
     const int nv = pg >= 0 ? min(r.n - chunk * kChunk, kChunk) : 0;
     const uint8_t* base = a.kidx + (pg >= 0 ? pg * (kPage * kDI) : 0) + st * 16 * kDI;
@@ -234,12 +310,12 @@ __device__ __forceinline__ void load_sub(const ScoreArgs& a, const RowCtx& r, in
 
 // Loads all sub-tiles of a chunk; returns whether the page is usable (Full
 // mode; true in pool mode).
-template <bool POOL>
+template <bool POOL, bool MX>
 __device__ __forceinline__ bool load_chunk(const ScoreArgs& a, const RowCtx& r, int chunk, int g, int col,
                                            ChunkKeys& ck) {
   const int64_t pg = POOL ? 0 : chunk_page(a, r, chunk);
 #pragma unroll
-  for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, r, chunk, pg, st, g, col, ck.k[st]);
+  for (int st = 0; st < kSub; ++st) load_sub<POOL, MX>(a, r, chunk, pg, st, g, col, ck.k[st]);
   return POOL || pg >= 0;
 }
 
@@ -330,19 +406,24 @@ __device__ __forceinline__ void general_query(const ScoreArgs& a, int64_t qrow0,
 // partial sums per dot combined exactly in binary64 and rounded once.
 // Reads the chunk's codes again; returns this lane's entry score before
 // validity masking.  wreg[rt][i] holds w * 2^-9 of head tile_head(rt, 4 g + i).
-template <bool POOL>
+template <bool POOL, bool MX>
 __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx& rc, int chunk, const GenQuery& gq,
                                                const v4f (&wreg)[kRT], bool& page_ok) {
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
   ChunkKeys raw;
-  page_ok = load_chunk<POOL>(a, rc, chunk, g, col, raw);
+  page_ok = load_chunk<POOL, MX>(a, rc, chunk, g, col, raw);
   float s_mine = 0.0f;
 #pragma unroll
   for (int st = 0; st < kSub; ++st) {
     v4i kl[2], km[2], kt[2];
+    if (MX) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) limbs3(raw.k[st][s2], kl[s2], km[s2], kt[s2]);
+      for (int s2 = 0; s2 < 2; ++s2) limbs3_mx(raw.k[st], s2, g, kl[s2], km[s2], kt[s2]);
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) limbs3(raw.k[st][s2], kl[s2], km[s2], kt[s2]);
+    }
     v4f p[kRT];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
@@ -389,7 +470,7 @@ __device__ __forceinline__ float general_chunk(const ScoreArgs& a, const RowCtx&
 // pairwise head sum in registers.  Chunks with an entry over the fast
 // path's bound, and rows whose query has some |q| >= 32, are only marked
 // here and scored after the main loop by the general path.
-template <bool POOL>
+template <bool POOL, bool MX>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   struct __attribute__((aligned(16))) Lds {
     // per token: the f16 limbs ql, qm of the query, in the order the waves
@@ -517,7 +598,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     }
     const int64_t pg0 = page_of(0);
 #pragma unroll
-    for (int st = 0; st < kSub; ++st) load_sub<POOL>(a, rc, chunk, pg0, st, g, col, cur.k[st]);
+    for (int st = 0; st < kSub; ++st) load_sub<POOL, MX>(a, rc, chunk, pg0, st, g, col, cur.k[st]);
     cur_ok = POOL || pg0 >= 0;
   }
 
@@ -599,22 +680,41 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       // channel order of the query slices
       __builtin_amdgcn_sched_barrier(0);
       v8h kf[4];
+      if (MX) {
+        // MXFP4: E2M1 codes times the group's power-of-two scale, exact in
+        // f16 for the supported scales (multiples of 2^-9 up to 384); code
+        // dword i of half hf holds the 8 channels of slice 2 hf + i
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < 2; ++hf) {
+          const float sc = e8m0_times_pow2((cur.k[st][1][0] >> (8 * (2 * hf + (g >> 1)))) & 0xFFu, 0);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const h2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, false);
-          const h2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, true);
-          const int slice = 2 * hf + (d >> 1), e = 4 * (d & 1);
-          kf[slice][e + 0] = lo2[0];
-          kf[slice][e + 1] = lo2[1];
-          kf[slice][e + 2] = hi2[0];
-          kf[slice][e + 3] = hi2[1];
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t wd = cur.k[st][0][2 * hf + i];
+            const h2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 0);
+            const h2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 1);
+            const h2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 2);
+            const h2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, sc, 3);
+            kf[2 * hf + i] = v8h{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+          }
         }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const h2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, false);
+            const h2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.k[st][hf][d], 1.0f, true);
+            const int slice = 2 * hf + (d >> 1), e = 4 * (d & 1);
+            kf[slice][e + 0] = lo2[0];
+            kf[slice][e + 1] = lo2[1];
+            kf[slice][e + 2] = hi2[0];
+            kf[slice][e + 3] = hi2[1];
+          }
+      }
       // the same sub-tile of the next chunk streams into the freed registers
       // (after the conversions have read them)
       __builtin_amdgcn_sched_barrier(0);
-      load_sub<POOL>(a, rc, next, next_pg, st, g, col, cur.k[st]);
+      load_sub<POOL, MX>(a, rc, next, next_pg, st, g, col, cur.k[st]);
       __builtin_amdgcn_sched_barrier(0);
       // the 8 MFMAs of each row tile, then the sub-tile's Gram matrix
       v4f sl4[kRT], sm4[kRT];
@@ -677,7 +777,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       if (!((my_defer[k >> 5] >> (k & 31)) & 1u)) continue;
       const int ck = c0 + slice + k * n_slices;
       bool ok;
-      const float s = general_chunk<POOL>(a, rc, ck, gq, wreg, ok);
+      const float s = general_chunk<POOL, MX>(a, rc, ck, gq, wreg, ok);
       emit_chunk<POOL>(a, rc, ck, s, ok, hist_s, hist_bm);
     }
   }
@@ -1153,26 +1253,30 @@ extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_
   return align256((size_t)B * T * pool_blocks * 8 * 4) + hist_bytes(B, T);
 }
 
-// Launches the scan (which also clears the level-1 histograms).
-int launch_scan(bool pool, const csa2::ScoreArgs& sa, int T_grid, hipStream_t stream) {
+// Launches the scan (which also clears the level-1 histograms); `mx`: the
+// indexer keys are in the MXFP4 page layout.
+int launch_scan(bool pool, bool mx, const csa2::ScoreArgs& sa, int T_grid, hipStream_t stream) {
   csa2::ScoreArgs args = sa;
   args.clear_hist = csa2::keep_histograms() ? 0 : 1;
   const int gx = score_grid(args.rows, args.chunks_per_row, T_grid, &args.chunks_per_wg, &args.wg_per_row);
-  if (pool)
-    CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, csa2::score_kernel<true>, dim3(gx), dim3(csa2::kScoreThreads), stream,
-                args);
+  const dim3 grid(gx), block(csa2::kScoreThreads);
+  if (pool && mx)
+    CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, (csa2::score_kernel<true, true>), grid, block, stream, args);
+  else if (pool)
+    CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, (csa2::score_kernel<true, false>), grid, block, stream, args);
+  else if (mx)
+    CSA2_LAUNCH(CSA2_K_SCORE_FULL, (csa2::score_kernel<false, true>), grid, block, stream, args);
   else
-    CSA2_LAUNCH(CSA2_K_SCORE_FULL, csa2::score_kernel<false>, dim3(gx), dim3(csa2::kScoreThreads), stream,
-                args);
+    CSA2_LAUNCH(CSA2_K_SCORE_FULL, (csa2::score_kernel<false, false>), grid, block, stream, args);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }
 
-extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
-                               int64_t n_pages, const int32_t* page_table, int32_t max_pages,
-                               const int32_t* n_entries, int32_t max_n_entries, int32_t B,
-                               int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
-                               int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
-                               size_t ws_bytes, csa2_stream_t stream) {
+namespace {
+int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool, int64_t n_pages,
+                    const int32_t* page_table, int32_t max_pages, const int32_t* n_entries,
+                    int32_t max_n_entries, int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                    int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws, size_t ws_bytes,
+                    csa2_stream_t stream) {
   int st = check_index_common(q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T,
                               HI, topk, pool_blocks);
   if (st) return st;
@@ -1200,7 +1304,7 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
       align256((size_t)B * T * csa2::bm_stride(max_n_entries) * 4));
   sa.rows = B;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
-  st = launch_scan(false, sa, T, (hipStream_t)stream);
+  st = launch_scan(false, mx, sa, T, (hipStream_t)stream);
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -1220,12 +1324,11 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }
 
-extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
-                                  int64_t n_pages, const int32_t* page_table, int32_t max_pages,
-                                  const int32_t* n_entries, int32_t B, int32_t T, int32_t HI,
-                                  const int32_t* pool, const int32_t* pool_n, int32_t pool_blocks,
-                                  int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
-                                  csa2_stream_t stream) {
+int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                       int64_t n_pages, const int32_t* page_table, int32_t max_pages, const int32_t* n_entries,
+                       int32_t B, int32_t T, int32_t HI, const int32_t* pool, const int32_t* pool_n,
+                       int32_t pool_blocks, int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
+                       csa2_stream_t stream) {
   int st = check_index_common(q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T,
                               HI, topk, pool_blocks);
   if (st) return st;
@@ -1252,7 +1355,7 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
                                         align256((size_t)B * T * pool_blocks * 8 * 4));
   sa.rows = B * T;
   sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
-  st = launch_scan(true, sa, 1, (hipStream_t)stream);
+  st = launch_scan(true, mx, sa, 1, (hipStream_t)stream);
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -1269,4 +1372,45 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
   CSA2_LAUNCH(CSA2_K_SELECT_REINDEX, csa2::select_kernel<false>, dim3(B * T),
               dim3(csa2::kSelThreads), (hipStream_t)stream, se);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                               int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                               const int32_t* n_entries, int32_t max_n_entries, int32_t B,
+                               int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                               int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
+                               size_t ws_bytes, csa2_stream_t stream) {
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+                         T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_mxfp4(const uint8_t* q_idx, const float* w, const uint8_t* kidx_mx,
+                                     int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                     const int32_t* n_entries, int32_t max_n_entries, int32_t B,
+                                     int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                     int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
+                                     size_t ws_bytes, csa2_stream_t stream) {
+  return index_full_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+                         T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                                  int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                  const int32_t* n_entries, int32_t B, int32_t T, int32_t HI,
+                                  const int32_t* pool, const int32_t* pool_n, int32_t pool_blocks,
+                                  int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
+                                  csa2_stream_t stream) {
+  return index_reindex_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T, HI, pool,
+                            pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_reindex_mxfp4(const uint8_t* q_idx, const float* w, const uint8_t* kidx_mx,
+                                        int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                        const int32_t* n_entries, int32_t B, int32_t T, int32_t HI,
+                                        const int32_t* pool, const int32_t* pool_n, int32_t pool_blocks,
+                                        int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
+                                        csa2_stream_t stream) {
+  return index_reindex_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, B, T, HI, pool,
+                            pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
 }

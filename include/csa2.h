@@ -54,6 +54,7 @@ extern "C" {
 #define CSA2_ENTRY_BYTES 288       /* 256 + 32 */
 #define CSA2_PAGE_BYTES 18432      /* 64 x 288: 64 x 256 B codes, then 64 x 32 B scales */
 #define CSA2_KIDX_PAGE_BYTES 8192  /* 64 x 128 B FP8 indexer keys */
+#define CSA2_MX_KIDX_PAGE_BYTES 4352  /* 64 x (64 B E2M1 codes) + 64 x 4 E8M0 scales */
 #define CSA2_BLOCK 8               /* positions per pool block */
 #define CSA2_SWA 128               /* sliding-window rows per query token */
 #define CSA2_MAX_TOPK 2048
@@ -143,6 +144,34 @@ int csa2_index_reindex(const uint8_t *q_idx, const float *w, const uint8_t *kidx
                        const int32_t *pool, const int32_t *pool_n, int32_t pool_blocks,
                        int32_t topk, int32_t *out_topk, void *ws, size_t ws_bytes,
                        csa2_stream_t stream);
+
+/*
+ * Full and Reindex modes over indexer keys in the pages' own format: E2M1
+ * elements with one E8M0 scale per 32 channels, 68 B per 128-channel entry
+ * (knowledge note, "FP4 main KV"; "Inside DeepSeek V4.1 Flash",
+ * "Reconstructing the 890-byte cache budget").  Arguments, outputs, errors
+ * and the score are those of csa2_index_full / csa2_index_reindex, except the
+ * key pool:
+ *   kidx_mx [n_pages][4352] bytes.  Page layout: entry e's 64 code bytes at
+ *           e * 64 (channel 2i in the low nibble of byte i, nibble = sign << 3
+ *           | magnitude code), then entry e's 4 scale bytes at 4096 + e * 4
+ *           (byte g scales channels 32g .. 32g + 31; code s means 2^(s - 127)).
+ * Precondition (not checked on the device): every scale code s of a visible
+ * entry satisfies 119 <= s <= 133 (2^-8 .. 2^6).  Every key value is then a
+ * multiple of 2^-9 of magnitude <= 384 and the scores are exact as above.
+ */
+int csa2_index_full_mxfp4(const uint8_t *q_idx, const float *w, const uint8_t *kidx_mx,
+                          int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                          const int32_t *n_entries, int32_t max_n_entries, int32_t B, int32_t T,
+                          int32_t HI, int32_t topk, int32_t pool_blocks, int32_t *out_topk,
+                          int32_t *out_pool, int32_t *out_pool_n, void *ws, size_t ws_bytes,
+                          csa2_stream_t stream);
+int csa2_index_reindex_mxfp4(const uint8_t *q_idx, const float *w, const uint8_t *kidx_mx,
+                             int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                             const int32_t *n_entries, int32_t B, int32_t T, int32_t HI,
+                             const int32_t *pool, const int32_t *pool_n, int32_t pool_blocks,
+                             int32_t topk, int32_t *out_topk, void *ws, size_t ws_bytes,
+                             csa2_stream_t stream);
 
 /*
  * Sparse attention over the selected FP4 entries merged with the FP8 window.

@@ -199,26 +199,30 @@ def mxfp4_key_values(kidx_mx: np.ndarray) -> np.ndarray:
 
 
 def mxfp4_keys_to_e4m3(kidx_mx: np.ndarray) -> np.ndarray:
-    """The same keys as E4M3 codes [P, 64, 128] (an exact re-encoding under the
-    scale precondition; raises if a value has no E4M3 code)."""
-    v = mxfp4_key_values(kidx_mx)
-    table = e4m3_decode(np.arange(256))
-    code_of = {}
-    for c in range(256):
-        x = table[c]
-        if np.isnan(x):
-            continue
-        key = (float(x), bool(np.signbit(x)))
-        code_of.setdefault(key, c)
-    flat = v.reshape(-1)
-    out = np.empty(flat.shape, np.uint8)
-    uniq, inv = np.unique(np.stack([flat, np.signbit(flat).astype(np.float64)], 1), axis=0, return_inverse=True)
-    for i, (x, sb) in enumerate(uniq):
-        c = code_of.get((float(x), bool(sb)))
-        if c is None:
-            raise ValueError(f"key value {x!r} has no E4M3 code")
-        out[inv.reshape(-1) == i] = c
-    return out.reshape(v.shape)
+    """The same keys as E4M3 codes [P, 64, 128]: an exact re-encoding under the
+    scale precondition (raises if a code/scale pair has no E4M3 code)."""
+    pool = np.ascontiguousarray(kidx_mx, dtype=np.uint8).reshape(-1, MX_PAGE_BYTES)
+    mxfp4_key_values(pool[:1])  # format check on one page; the full check follows below
+    scales = pool[:, PAGE * MX_ENTRY_CODES:].reshape(pool.shape[0], PAGE, MX_NGROUPS)
+    if np.any((scales < MX_SCALE_MIN) | (scales > MX_SCALE_MAX)):
+        raise ValueError("E8M0 scale outside the supported range 2^-8 .. 2^6")
+    # table[s, c]: the E4M3 code whose value is exactly E2M1(c) * 2^(s - 127)
+    e4 = e4m3_decode(np.arange(256))
+    e2 = e2m1_decode(np.arange(16))
+    table = np.zeros((256, 16), np.uint8)
+    for sc in range(MX_SCALE_MIN, MX_SCALE_MAX + 1):
+        for c in range(16):
+            x = e2[c] * 2.0 ** (sc - 127)
+            hit = [k for k in range(256) if e4[k] == x and np.signbit(e4[k]) == np.signbit(x)]
+            if not hit:
+                raise ValueError(f"E2M1 code {c} at scale code {sc} has no E4M3 code")
+            table[sc, c] = hit[0]
+    codes = pool[:, :PAGE * MX_ENTRY_CODES].reshape(pool.shape[0], PAGE, MX_ENTRY_CODES)
+    nib = np.empty((pool.shape[0], PAGE, DI), np.uint8)
+    nib[:, :, 0::2] = codes & 0xF
+    nib[:, :, 1::2] = codes >> 4
+    sc_ch = np.repeat(scales, DI // MX_NGROUPS, axis=2)
+    return table[sc_ch, nib]
 
 
 # ---------------------------------------------------------------- a2..a6: indexer

@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 101
+    assert L.csa2_abi_version() == 102
 
 
 def test_workspace_sizes(L):
@@ -92,6 +92,26 @@ def test_index_reindex_argument_errors(L):
     assert _reindex(L, topk=17) == UNSUPPORTED
     assert _reindex(L, HI=10) == UNSUPPORTED
     assert _reindex(L, ws_bytes=0) == WORKSPACE
+
+
+def test_mxfp4_index_argument_errors(L):
+    """The MXFP4-key calls share the checks of the E4M3-key ones."""
+    full = lambda **kw: _full(L, **kw)
+    saved = L.csa2_index_full
+    try:
+        L.csa2_index_full = L.csa2_index_full_mxfp4
+        assert full(q=None) == INVALID
+        assert full(HI=6) == UNSUPPORTED
+        assert full(max_n=262145) == UNSUPPORTED
+        assert full(ws=None) == WORKSPACE
+    finally:
+        L.csa2_index_full = saved
+    r = lambda q=X, pool=X, topk=8, HI=4: L.csa2_index_reindex_mxfp4(q, X, X, 1, X, 1, X, 1, 1, HI, pool, X, 16,
+                                                                     topk, X, X, 1 << 30, None)
+    assert r(q=None) == INVALID
+    assert r(pool=None) == INVALID
+    assert r(topk=17) == UNSUPPORTED
+    assert r(HI=10) == UNSUPPORTED
 
 
 def _attn(L, q=X, sm=1.0, topk=8, B=1, T=1, H=16, out=X, ws=X, ws_bytes=1 << 30):

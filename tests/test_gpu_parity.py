@@ -292,6 +292,65 @@ def test_index_full_1m_b4(oracle):
         assert len(pos) <= 16384 and set(tk[b, 0]) <= set(pos)
 
 
+# ------------------------------------------------------------------ MXFP4 indexer keys
+@pytest.mark.parametrize("scales", ["typical", "range_edges"])
+def test_index_full_mxfp4_scores_bitexact(oracle, scales):
+    """Full mode over MXFP4 indexer keys: the scan's scores bit for bit, and the
+    top-k and pool, against the oracle.  "range_edges" draws scale codes at both
+    ends of the supported range (2^-8, 2^-7, 2^5, 2^6), so large keys send
+    chunks to the general path and tiny ones stay on the fast path."""
+    n = [3000, 1000, 777]
+    sc = (125, 126, 127) if scales == "typical" else (119, 120, 132, 133)
+    say(f"index full MXFP4 keys, scores bit-exact n={n} T=2 HI=64 scales={sc}")
+    wl = small_workload(n, T=2, HI=64, topk=256, seed=31)
+    mx = synth.mxfp4_key_pool(wl.paging.n_pages, 41, sc)
+    L = wl.layers[0]
+    ws = csa2.Workspace()
+    got = csa2.index_full(dev(L.q_idx), dev(L.w), dev(mx), dev(wl.paging.page_table), dev(wl.n_entries),
+                          wl.max_n, wl.topk, wl.pool_blocks, ws=ws, mxfp4=True)
+    stride = (wl.max_n + 7) & ~7
+    s_gpu = host(ws.buf)[: len(n) * 2 * stride * 4].view(np.float32).reshape(len(n), 2, stride)
+    e4 = oracle.mxfp4_keys_to_e4m3(mx)
+    for b, nb in enumerate(n):
+        keys = oracle.gather_keys(e4, wl.paging.page_table[b], nb)
+        for t in range(2):
+            ref = oracle.index_scores(L.q_idx[b, t], L.w[b, t], keys)
+            assert np.array_equal(s_gpu[b, t, :nb].view(np.uint32), ref.view(np.uint32)), (b, t)
+    ref = oracle.index_full_mxfp4(L.q_idx, L.w, mx, wl.paging.page_table, wl.n_entries, wl.topk,
+                                  wl.pool_blocks)
+    assert_index_equal(got, ref)
+
+
+@pytest.mark.parametrize("T,HI,topk", [(1, 8, 64), (4, 16, 2048)])
+def test_index_full_and_reindex_mxfp4_ragged(oracle, T, HI, topk):
+    n = [1, 7, 9, 1025, 16389, 40000]
+    say(f"index full + reindex MXFP4 keys ragged n={n} T={T} HI={HI} k={topk}")
+    wl = small_workload(n, T=T, HI=HI, topk=topk, seed=T * 10 + HI)
+    mx = synth.mxfp4_key_pool(wl.paging.n_pages, 43)
+    L = wl.layers[0]
+    other = synth.layer_inputs("full", wl.B, T, HI, 16, 44)
+    args = (dev(mx), dev(wl.paging.page_table), dev(wl.n_entries))
+    got = csa2.index_full(dev(L.q_idx), dev(L.w), *args, wl.max_n, topk, 2048, mxfp4=True)
+    ref = oracle.index_full_mxfp4(L.q_idx, L.w, mx, wl.paging.page_table, wl.n_entries, topk, 2048)
+    assert_index_equal(got, ref)
+    rtk = csa2.index_reindex(dev(other.q_idx), dev(other.w), *args, got[1], got[2], topk, mxfp4=True)
+    ref_rtk = oracle.index_reindex_mxfp4(other.q_idx, other.w, mx, wl.paging.page_table, wl.n_entries,
+                                         ref[1], ref[2], topk)
+    assert np.array_equal(host(rtk), ref_rtk)
+
+
+def test_index_full_mxfp4_1m_b4(oracle):
+    say("index full 1M ctx B=4 HI=64 k=2048 over MXFP4 keys (full size)")
+    wl = synth.workload("full_1m_b4")
+    mx = synth.mxfp4_key_pool(wl.paging.n_pages, 45)
+    L = wl.layers[0]
+    got = csa2.index_full(dev(L.q_idx), dev(L.w), dev(mx), dev(wl.paging.page_table), dev(wl.n_entries),
+                          wl.max_n, wl.topk, wl.pool_blocks, mxfp4=True)
+    ref = oracle.index_full_mxfp4(L.q_idx, L.w, mx, wl.paging.page_table, wl.n_entries, wl.topk,
+                                  wl.pool_blocks)
+    assert_index_equal(got, ref)
+
+
 def test_index_deterministic():
     say("index full twice, identical")
     wl = small_workload([30000, 12345], T=2, HI=32, topk=1024, seed=9)
