@@ -67,11 +67,12 @@ class HipEvents:
             self.rt.hipEventDestroy(e)
 
 
-def algorithmic_bytes(wl):
-    """Bytes the method must move per layer step (inputs read + outputs written)."""
+def algorithmic_bytes(wl, key_bytes=128):
+    """Bytes the method must move per layer step (inputs read + outputs written);
+    key_bytes: bytes per indexer key (128 E4M3, 68 MXFP4)."""
     n = int(np.sum(wl.n_entries))
     B, T, H, HI, k = wl.B, wl.T, wl.H, wl.HI, wl.topk
-    scan = n * 128 + B * T * HI * (128 + 4)                 # indexer keys + queries + weights
+    scan = n * key_bytes + B * T * HI * (128 + 4)           # indexer keys + queries + weights
     idx_out = B * T * (k + wl.pool_blocks + 1) * 4           # top-k, pool, count
     sel = min(k, int(wl.n_entries.min()))
     gather = B * T * sel * 288                               # selected FP4 entries
@@ -100,8 +101,9 @@ def measured_traffic():
 def counters_driver(args):
     """Launch sequence for rocprofv3 counter runs: a plain 256 MiB device copy
     (calibrates FETCH_SIZE / WRITE_SIZE), then 3 times each: the Full indexer
-    of the workload, its sparse attention over the indexer's top-k, and the
-    cache write of all of the workload's rows (1,048,576 at 1M context)."""
+    of the workload, the same over MXFP4 indexer keys, the cache write of all
+    of the workload's rows (1,048,576 at 1M context) and the sparse attention
+    over the indexer's top-k."""
     import torch
     import compressed_sparse_attention_mxfp4_amd as csa2
     from compressed_sparse_attention_mxfp4_amd import synth
@@ -121,6 +123,12 @@ def counters_driver(args):
     for _ in range(3):
         topk = csa2.index_full(q, w, kidx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks, ws=ws)[0]
     torch.cuda.synchronize()
+    # the same Full call over MXFP4 indexer keys (68 B per entry)
+    kmx = d(synth.mxfp4_key_pool(wl.paging.n_pages, 45))
+    for _ in range(3):
+        csa2.index_full(q, w, kmx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks, ws=ws, mxfp4=True)
+    torch.cuda.synchronize()
+    del kmx
     kv_src = d(wl.kv_source.view(np.int16)).view(torch.bfloat16)
     slots = d(wl.paging.all_slots())
     kv = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
@@ -136,7 +144,7 @@ def counters_driver(args):
     return 0
 
 
-def cpu_baseline(wl, min_seconds=12.0, max_reps=40):
+def cpu_baseline(wl, min_seconds=12.0, max_reps=40, kidx_mx=None):
     """The oracle, as it stands, on the same layer step; all host cores it uses."""
     import oracle
     oracle.build(force=False)
@@ -144,8 +152,12 @@ def cpu_baseline(wl, min_seconds=12.0, max_reps=40):
     offs = np.concatenate([[0], np.cumsum(wl.n_entries)[:-1]])
     reps, t0 = 0, time.perf_counter()
     while True:
-        tk, _, _ = oracle.index_full(L.q_idx, L.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries,
-                                     wl.topk, wl.pool_blocks)
+        if kidx_mx is not None:
+            tk, _, _ = oracle.index_full_mxfp4(L.q_idx, L.w, kidx_mx, wl.paging.page_table, wl.n_entries,
+                                               wl.topk, wl.pool_blocks)
+        else:
+            tk, _, _ = oracle.index_full(L.q_idx, L.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries,
+                                         wl.topk, wl.pool_blocks)
         for b in range(wl.B):
             for t in range(wl.T):
                 sel = tk[b, t][tk[b, t] >= 0].astype(np.int64)
@@ -169,6 +181,9 @@ def main():
     ap.add_argument("--workload", default="full_1m_b4")
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (> 512 MB touched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kidx-format", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="indexer-key format: E4M3 (128 B per entry) or the pages' MXFP4 (68 B per entry, "
+                         "random synthetic codes and scales)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the counter-calibration sequence (for rocprofv3 --pmc runs)")
@@ -205,7 +220,9 @@ def main():
     q, swa = up(L.q.view(np.int16), torch.bfloat16), up(L.swa)
     kv_src = up(wl.kv_source.view(np.int16), torch.bfloat16)
     slots = up(wl.paging.all_slots())
-    kidx0 = up(wl.kidx_pool)
+    mx = args.kidx_format == "mxfp4"
+    kidx_mx = synth.mxfp4_key_pool(wl.paging.n_pages, 45) if mx else None
+    kidx0 = up(kidx_mx if mx else wl.kidx_pool)
     kv0 = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device=dev)
     csa2.quantize_kv(kv_src, slots, kv0)
     kidx = [kidx0] + [kidx0.clone() for _ in range(args.copies - 1)]
@@ -227,7 +244,7 @@ def main():
         c = i % args.copies
         csa2.quantize_kv(new_rows, new_slots, kvp[c], stream=strm)
         csa2.index_full(q_idx, w, kidx[c], pt, ne, wl.max_n, wl.topk, wl.pool_blocks, out_topk=out_topk,
-                        out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=strm)
+                        out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=strm, mxfp4=mx)
         csa2.sparse_attn(q, wl.sm_scale, kvp[c], pt, ne, out_topk, swa, out=out, ws=ws_a, stream=strm)
 
     for i in range(args.warmup):
@@ -301,7 +318,7 @@ def main():
 
     ms_per_step = total_ms / K
     value = 1000.0 / ms_per_step
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, 68 if mx else 128)
     scan_gbs = nbytes["scan"] / (kern_us["score_full"] * 1e-6) / 1e9
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
     log(f"{K} steps ({'eager' if graphs is None else 'graph replay'}): {ms_per_step * 1000:.1f} us/step "
@@ -324,7 +341,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "query_tokens": T,
                    "context_tokens": int(wl.max_n) * 4, "entries_per_seq": int(wl.max_n),
                    "indexer_heads": wl.HI, "heads": H, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
-                   "cache_copies_rotated": args.copies,
+                   "indexer_key_format": args.kidx_format, "cache_copies_rotated": args.copies,
                    "launch": "eager" if graphs is None else "hip_graph_replay"},
         "hbm_tb_s": round(step_gbs / 1000.0, 3),
         "hbm_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -332,12 +349,12 @@ def main():
         "kernel_avg_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": {"kernel": "score_kernel (Full-mode exact score scan)", "bound": "hbm",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None if mx else measured_traffic(),
                      "algorithmic_bytes_per_launch": nbytes["scan"]},
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, kidx_mx=kidx_mx)
         log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
     print(json.dumps(result), flush=True)
     return 0

@@ -71,13 +71,14 @@ def fp8_normal(shape, seed: int, std: float = 1.0) -> np.ndarray:
     return fp8_bits(normal(shape, seed, std))
 
 
-def mxfp4_key_pool(n_pages: int, seed: int, scale_codes=(125, 126, 127)) -> np.ndarray:
+def mxfp4_key_pool(n_pages: int, seed: int, scale_codes=(126,)) -> np.ndarray:
     """Random indexer-key pool in the MXFP4 page layout (uint8 [n_pages, 4352]):
-    E2M1 codes drawn with more weight on small magnitudes, random signs, and
-    E8M0 scale codes drawn from `scale_codes`.  Pure random draws: no
-    quantization happens here."""
+    E2M1 magnitude codes drawn with the frequencies that |x| / 0.5 rounds to
+    for x ~ N(0, 1) (so that, at the default scale 2^-1, the keys have the
+    spread of N(0, 1) keys), random signs, and E8M0 scale codes drawn from
+    `scale_codes`.  Pure random draws: no quantization happens here."""
     rng = np.random.default_rng(seed)
-    mag_p = np.array([0.14, 0.2, 0.18, 0.15, 0.12, 0.1, 0.07, 0.04])
+    mag_p = np.array([0.10, 0.19, 0.17, 0.15, 0.18, 0.13, 0.07, 0.01])
     nib = rng.choice(8, size=(n_pages, PAGE, DI), p=mag_p).astype(np.uint8)
     nib |= (rng.random((n_pages, PAGE, DI)) < 0.5).astype(np.uint8) << 3
     codes = (nib[:, :, 0::2] | (nib[:, :, 1::2] << 4)).reshape(n_pages, PAGE * DI // 2)
