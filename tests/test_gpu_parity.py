@@ -230,6 +230,24 @@ def test_index_full_ragged(oracle, T, HI, topk):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
+def test_empty_sequence_index_and_attention(oracle):
+    """A sequence with no entries: its top-k is all -1, its pool empty, and its
+    attention runs over the window rows alone."""
+    n = [0, 5, 3000]
+    say(f"index + attention with an empty sequence n={n} T=2 HI=8 k=64")
+    wl = small_workload(n, T=2, HI=8, topk=64, seed=61)
+    L = wl.layers[0]
+    got = gpu_index_full(wl, L)
+    ref = oracle_index_full(oracle, wl, L)
+    assert_index_equal(got, ref)
+    assert (ref[0][0] == -1).all() and (ref[2][0] == 0).all()
+    kv_pool = torch.zeros((max(wl.paging.n_pages, 1), csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(bf16_dev(wl.kv_source), dev(wl.paging.all_slots()), kv_pool)
+    out = csa2.sparse_attn(bf16_dev(L.q), wl.sm_scale, kv_pool, dev(wl.paging.page_table), dev(wl.n_entries),
+                           got[0], dev(L.swa))
+    check_attention(oracle, wl, L, ref[0], host(out))
+
+
 def test_index_full_ties(oracle):
     say("index full with tied scores (repeated keys)")
     n = [5000, 700]
