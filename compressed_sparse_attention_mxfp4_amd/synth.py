@@ -86,6 +86,14 @@ def mxfp4_key_pool(n_pages: int, seed: int, scale_codes=(126,)) -> np.ndarray:
     return np.ascontiguousarray(np.concatenate([codes, scales], axis=1))
 
 
+def rope_table(max_pos: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary angle table float32 [max_pos, 32, 2] = (cos, sin) of pos * base^(-i/32),
+    computed in binary64 and rounded once (an input: the caller chooses the angles)."""
+    i = np.arange(32, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * base ** (-i / 32.0)[None, :]
+    return np.ascontiguousarray(np.stack([np.cos(ang), np.sin(ang)], axis=2).astype(np.float32))
+
+
 @dataclass
 class Paging:
     """Logical -> physical page mapping shared by the main-KV and indexer-key pools."""

@@ -149,6 +149,69 @@ def quantize_kv(x_bf16: np.ndarray, dst_slot: np.ndarray, pool: np.ndarray) -> n
     return pool
 
 
+# -------------------------------- fused RoPE + cache writes (next step)
+# Knowledge note "FP4 main KV": the main KV is quantized after RoPE; the
+# indexer keys are E4M3.  The pages give neither the rotary channels nor the
+# angles.  Readings: the last 64 channels of each 512-channel main-KV row and
+# of each 128-channel indexer key are rotary; channel pairs (2i, 2i + 1) of
+# that slice turn by the angle of pair i at the row's position, given by the
+# caller as a binary32 table cs[pos][i] = (cos, sin), i < 32.  With x, y the
+# pair's bf16 values (exact in binary32):
+#   x' = fl(fl(x c) - fl(y s)),  y' = fl(fl(x s) + fl(y c))
+# every product and sum its own binary32 operation, then x', y' are rounded
+# to bf16 (nearest, ties to even).  The rotated bf16 rows are written as by
+# the cache write (main KV, FP4) and as E4M3 nearest-even codes saturating at
+# 448 (indexer keys).
+ROPE_PAIRS = 32
+KV_ROPE_START, KIDX_ROPE_START = D - 2 * ROPE_PAIRS, DI - 2 * ROPE_PAIRS
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bf16 bit patterns, nearest with ties to even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def rope_rows(x_bf16: np.ndarray, pos: np.ndarray, rope_cs: np.ndarray, start: int) -> np.ndarray:
+    """Rotate channels start .. start + 63 of bf16 rows [R, C] (see above)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).copy()
+    R = x.shape[0]
+    cs = np.asarray(rope_cs, dtype=np.float32)[np.asarray(pos, dtype=np.int64)]   # [R, 32, 2]
+    f = bf16_to_f64(x[:, start:start + 2 * ROPE_PAIRS]).astype(np.float32).reshape(R, ROPE_PAIRS, 2)
+    xe, yo, c, sn = f[:, :, 0], f[:, :, 1], cs[:, :, 0], cs[:, :, 1]
+    xr = np.subtract(np.multiply(xe, c, dtype=np.float32), np.multiply(yo, sn, dtype=np.float32), dtype=np.float32)
+    yr = np.add(np.multiply(xe, sn, dtype=np.float32), np.multiply(yo, c, dtype=np.float32), dtype=np.float32)
+    out = np.stack([xr, yr], axis=2).reshape(R, 2 * ROPE_PAIRS)
+    x[:, start:start + 2 * ROPE_PAIRS] = f32_to_bf16_rne(out)
+    return x
+
+
+def e4m3_codes_of_bf16(x_bf16: np.ndarray) -> np.ndarray:
+    """E4M3 nearest-even codes (saturating at 448) of bf16 values."""
+    table = np.array([e4m3_nearest(v) for v in bf16_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))],
+                     dtype=np.uint8) if not hasattr(e4m3_codes_of_bf16, "_t") else e4m3_codes_of_bf16._t
+    e4m3_codes_of_bf16._t = table
+    return table[np.asarray(x_bf16, dtype=np.uint16)]
+
+
+def rope_write_caches(kv_bf16, kidx_bf16, pos, rope_cs, dst_slot, kv_pool, kidx_pool):
+    """Fused RoPE + cache writes: main-KV rows [R, 512] into the FP4 pool
+    [P, 18432], indexer keys [R, 128] into the E4M3 pool [P, 64, 128], in
+    place; rows whose slot lies outside the pools or whose position lies
+    outside the table are skipped."""
+    pos = np.asarray(pos, dtype=np.int64)
+    slot = np.asarray(dst_slot, dtype=np.int64)
+    ok = (pos >= 0) & (pos < len(rope_cs)) & (slot >= 0) & (slot < kv_pool.shape[0] * PAGE)
+    kv = rope_rows(np.asarray(kv_bf16)[ok], pos[ok], rope_cs, KV_ROPE_START)
+    ki = rope_rows(np.asarray(kidx_bf16)[ok], pos[ok], rope_cs, KIDX_ROPE_START)
+    quantize_kv(kv, slot[ok], kv_pool)
+    codes = e4m3_codes_of_bf16(ki)
+    s = slot[ok]
+    kidx_pool[s // PAGE, s % PAGE] = codes
+    return kv_pool, kidx_pool
+
+
 def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, ENTRY_CODES)
     scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, NGROUPS)

@@ -471,3 +471,76 @@ def test_mxfp4_key_scale_range_enforced(oracle):
     page[0, 4096] = oracle.MX_SCALE_MIN - 1
     with pytest.raises(ValueError):
         oracle.mxfp4_key_values(page)
+
+
+# ------------------------------------------------------------------ fused RoPE + cache writes
+def test_bf16_rne_matches_torch(oracle):
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(200000, generator=g, dtype=torch.float32) * torch.exp2(torch.randint(-20, 20, (200000,), generator=g).float())
+    # plus exact ties: bf16 value + half an ulp
+    t = (torch.randint(0, 1 << 15, (4096,), generator=g).to(torch.int32) << 16) | 0x8000
+    x = torch.cat([x, t.view(torch.float32)])
+    x = x[torch.isfinite(x)]
+    want = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16_rne(x.numpy()), want)
+
+
+def test_rope_special_angles(oracle):
+    rng = np.random.default_rng(1)
+    x = synth.bf16_bits(torch.randn(64, 512, generator=torch.Generator().manual_seed(2)))
+    table = np.zeros((3, 32, 2), np.float32)
+    table[0, :, 0] = 1.0                      # angle 0: identity
+    table[1, :, 1] = 1.0                      # angle pi/2: (x, y) -> (-y, x)
+    table[2, :, 0] = -1.0                     # angle pi: (x, y) -> (-x, -y)
+    for p, fn in [(0, lambda a, b: (a, b)), (1, lambda a, b: (-b, a)), (2, lambda a, b: (-a, -b))]:
+        out = oracle.rope_rows(x, np.full(64, p), table, oracle.KV_ROPE_START)
+        assert np.array_equal(out[:, :448], x[:, :448])
+        v = oracle.bf16_to_f64(x[:, 448:]).reshape(64, 32, 2)
+        ex, ey = fn(v[:, :, 0], v[:, :, 1])
+        w = oracle.bf16_to_f64(out[:, 448:]).reshape(64, 32, 2)
+        assert np.array_equal(w[:, :, 0], ex) and np.array_equal(w[:, :, 1], ey), p
+    assert rng is not None
+
+
+def test_rope_general_angle_within_one_rounding(oracle):
+    """At general angles the result is the binary64 rotation rounded twice
+    (binary32 steps, then bf16): within 1 bf16 ulp plus the binary32 error."""
+    x = synth.bf16_bits(torch.randn(256, 128, generator=torch.Generator().manual_seed(3)))
+    table = synth.rope_table(1000)
+    pos = np.random.default_rng(4).integers(0, 1000, 256)
+    out = oracle.rope_rows(x, pos, table, oracle.KIDX_ROPE_START)
+    v = oracle.bf16_to_f64(x[:, 64:]).reshape(256, 32, 2)
+    c, s = table[pos, :, 0].astype(np.float64), table[pos, :, 1].astype(np.float64)
+    ex = v[:, :, 0] * c - v[:, :, 1] * s
+    ey = v[:, :, 0] * s + v[:, :, 1] * c
+    w = oracle.bf16_to_f64(out[:, 64:]).reshape(256, 32, 2)
+    mag = np.maximum(np.abs(v[:, :, 0]), np.abs(v[:, :, 1]))
+    assert (np.abs(w[:, :, 0] - ex) <= 2.0 ** -8 * np.abs(ex) + 2.0 ** -22 * mag).all()
+    assert (np.abs(w[:, :, 1] - ey) <= 2.0 ** -8 * np.abs(ey) + 2.0 ** -22 * mag).all()
+    # the rotation keeps the pair's length up to those roundings
+    assert np.allclose(np.hypot(w[:, :, 0], w[:, :, 1]), np.hypot(v[:, :, 0], v[:, :, 1]), rtol=2 ** -7)
+
+
+def test_rope_write_caches_layout_and_skips(oracle):
+    R = 10
+    kv = synth.bf16_bits(torch.randn(R, 512, generator=torch.Generator().manual_seed(6)))
+    ki = synth.bf16_bits(torch.randn(R, 128, generator=torch.Generator().manual_seed(7)))
+    table = synth.rope_table(50)
+    pos = np.array([0, 1, 2, 3, 49, 50, -1, 5, 6, 7])          # 50 and -1: outside the table
+    slot = np.array([0, 64, 65, 130, 5, 6, 7, 200, -1, 191])   # 200, -1: outside 3 pages
+    kvp = np.zeros((3, oracle.PAGE_BYTES), np.uint8)
+    kip = np.zeros((3, 64, 128), np.uint8)
+    oracle.rope_write_caches(kv, ki, pos, table, slot, kvp, kip)
+    for r in range(R):
+        written = 0 <= pos[r] < 50 and 0 <= slot[r] < 192
+        pg, off = divmod(int(slot[r]), 64) if 0 <= slot[r] < 192 else (None, None)
+        if not written:
+            if pg is not None:
+                assert not kip[pg, off].any()
+            continue
+        rot = oracle.rope_rows(ki[r:r + 1], pos[r:r + 1], table, 64)
+        assert np.array_equal(kip[pg, off], oracle.e4m3_codes_of_bf16(rot[0]))
+        rk = oracle.rope_rows(kv[r:r + 1], pos[r:r + 1], table, 448)
+        codes, scales = oracle.quantize_rows(rk)
+        c, sc = oracle.pool_entry(kvp, pg, off)
+        assert np.array_equal(c, codes[0]) and np.array_equal(sc, scales[0])
