@@ -35,11 +35,13 @@ EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
     "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
+    "csa2_rope_write_caches",
 )
 
 # kernel ids for csa2_time_kernel
 K_QUANTIZE, K_SCORE_FULL, K_SELECT_FULL, K_SCORE_REINDEX, K_SELECT_REINDEX = 1, 2, 3, 4, 5
-K_ATTN_SPLIT, K_ATTN_COMBINE = 6, 7
+K_ATTN_SPLIT, K_ATTN_COMBINE, K_ROPE_WRITE = 6, 7, 8
+ROPE_PAIRS = 32  # rotary channel pairs: the last 64 channels of main-KV rows and indexer keys
 
 
 class Csa2Error(RuntimeError):
@@ -66,6 +68,7 @@ def load(path: str = LIB_PATH):
     L = ctypes.CDLL(path)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.csa2_quantize_kv.argtypes = [P, i64, P, P, i64, P]
+    L.csa2_rope_write_caches.argtypes = [P, P, i64, P, P, i64, P, P, P, i64, P]
     L.csa2_index_full.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32, P, P, P,
                                   P, sz, P]
     L.csa2_index_reindex.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, P, P, i32, i32, P, P,
@@ -84,7 +87,7 @@ def load(path: str = LIB_PATH):
     L.csa2_test_keep_histograms.argtypes = [ctypes.c_int]
     L.csa2_test_keep_histograms.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-               "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4"):
+               "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -175,6 +178,25 @@ def quantize_kv(kv_bf16, dst_slot, kv_pool, stream=None):
     p = _ptr(kv_pool, torch.uint8, "kv_pool", (None, PAGE_BYTES), 2)
     _check("csa2_quantize_kv", lib().csa2_quantize_kv(a, R, s, p, kv_pool.shape[0], _stream(stream)))
     return kv_pool
+
+
+def rope_write_caches(kv_bf16, kidx_bf16, pos, rope_cs, dst_slot, kv_pool, kidx_pool, stream=None):
+    """Fused RoPE + cache writes: kv_bf16 [R,512] and kidx_bf16 [R,128] bf16 (pre-RoPE),
+    pos [R] int64, rope_cs [max_pos,32,2] float32 (cos, sin), dst_slot [R] int64,
+    kv_pool [P,18432] uint8 and kidx_pool [P,64,128] uint8 (written in place)."""
+    torch = _torch()
+    R = kv_bf16.shape[0]
+    a = _ptr(kv_bf16, torch.bfloat16, "kv_bf16", (R, D), 2)
+    k = _ptr(kidx_bf16, torch.bfloat16, "kidx_bf16", (R, DI), 2)
+    p = _ptr(pos, torch.int64, "pos", (R,), 1)
+    c = _ptr(rope_cs, torch.float32, "rope_cs", (None, ROPE_PAIRS, 2), 3)
+    s = _ptr(dst_slot, torch.int64, "dst_slot", (R,), 1)
+    kv = _ptr(kv_pool, torch.uint8, "kv_pool", (None, PAGE_BYTES), 2)
+    ki = _ptr(kidx_pool, torch.uint8, "kidx_pool", (kv_pool.shape[0], PAGE, DI), 3)
+    _check("csa2_rope_write_caches",
+           lib().csa2_rope_write_caches(a, k, R, p, c, rope_cs.shape[0], s, kv, ki, kv_pool.shape[0],
+                                        _stream(stream)))
+    return kv_pool, kidx_pool
 
 
 def _kidx_arg(kidx_pool, mxfp4):

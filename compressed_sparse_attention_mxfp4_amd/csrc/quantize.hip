@@ -62,25 +62,12 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   return e ? u2f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-__global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __restrict__ x,
-                                                          int64_t rows,
-                                                          const int64_t* __restrict__ slot,
-                                                          uint8_t* __restrict__ pool,
-                                                          int64_t n_pages) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t r = gid >> 5;      // row
-  const int g = (int)(gid & 31);   // 16-channel group
-  const bool live = r < rows;
-  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int64_t s = -1;
-  if (live) {
-    const v4u* src = reinterpret_cast<const v4u*>(x + r * kD + g * 16);
-    v4u a = __builtin_nontemporal_load(src);
-    v4u b = __builtin_nontemporal_load(src + 1);
-    h[0] = a.x; h[1] = a.y; h[2] = a.z; h[3] = a.w;
-    h[4] = b.x; h[5] = b.y; h[6] = b.z; h[7] = b.w;
-    s = slot[r];
-  }
+// FP4 group of 16 bf16 channels (h[j]: channels 2j low, 2j + 1 high):
+// E2M1 nibbles in w0 (channels 0..7) and w1 (channels 8..15), scale code sc.
+struct Fp4Group {
+  uint32_t w0, w1, sc;
+};
+__device__ __forceinline__ Fp4Group fp4_group(const uint32_t (&h)[8]) {
   // amax over 16 bf16 magnitudes (pairs of bit patterns)
   u16x2 mag[8];
 #pragma unroll
@@ -135,19 +122,128 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
     const uint32_t y01 = x01 | (x01 >> 4), y23 = x23 | (x23 >> 4);
     return __builtin_amdgcn_perm(y23, y01, 0x06040200u);
   };
-  const uint32_t w0 = pack4(0), w1 = pack4(4);
-  // four neighbouring groups' scale bytes -> one dword store
-  const uint32_t s1 = __shfl_down(sc, 1, 4), s2 = __shfl_down(sc, 2, 4), s3 = __shfl_down(sc, 3, 4);
-  const bool ok = live && s >= 0 && s < n_pages * kPage;
+  return {pack4(0), pack4(4), sc};
+}
+
+// Stores one row's group (lanes g = 0..31 of a row, all executing): 8 code
+// bytes per lane, and the scale bytes of four neighbouring groups as one
+// dword from the first of them.
+__device__ __forceinline__ void store_fp4_group(const Fp4Group& q, int g, bool ok, int64_t s,
+                                                uint8_t* __restrict__ pool) {
+  const uint32_t s1 = __shfl_down(q.sc, 1, 4), s2 = __shfl_down(q.sc, 2, 4), s3 = __shfl_down(q.sc, 3, 4);
   if (ok) {
     const int64_t page = s >> 6, off = s & 63;
     uint8_t* base = pool + page * kPageBytes;
-    v2u cw = {w0, w1};
+    v2u cw = {q.w0, q.w1};
     __builtin_nontemporal_store(cw, reinterpret_cast<v2u*>(base + off * kEntryCodes + g * 8));
     if ((g & 3) == 0) {
-      uint32_t sw = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+      uint32_t sw = q.sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
       __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t*>(base + kPage * kEntryCodes +
                                                                   off * kEntryScales + g));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t rows,
+                                                          const int64_t* __restrict__ slot,
+                                                          uint8_t* __restrict__ pool,
+                                                          int64_t n_pages) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = gid >> 5;      // row
+  const int g = (int)(gid & 31);   // 16-channel group
+  const bool live = r < rows;
+  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t s = -1;
+  if (live) {
+    const v4u* src = reinterpret_cast<const v4u*>(x + r * kD + g * 16);
+    v4u a = __builtin_nontemporal_load(src);
+    v4u b = __builtin_nontemporal_load(src + 1);
+    h[0] = a.x; h[1] = a.y; h[2] = a.z; h[3] = a.w;
+    h[4] = b.x; h[5] = b.y; h[6] = b.z; h[7] = b.w;
+    s = slot[r];
+  }
+  const Fp4Group q = fp4_group(h);
+  store_fp4_group(q, g, live && s >= 0 && s < n_pages * kPage, s, pool);
+}
+
+// ---------------------------------------------------------------------------
+// Fused RoPE + cache writes (knowledge note "FP4 main KV": the main KV is
+// quantized after RoPE; the indexer keys are E4M3).  The rotary channels and
+// angles are the caller's: the last 64 channels of each main-KV row and of
+// each indexer key turn in pairs (2i, 2i + 1) by the angle of pair i at the
+// row's position, cs[pos][i] = (cos, sin) in binary32.  Each product and
+// each sum is its own binary32 operation, the results are rounded to bf16
+// (nearest, ties to even), then written as by the FP4 cache write (main KV)
+// and as E4M3 nearest-even codes saturating at 448 (indexer keys).
+//
+// One wave per row: lanes 0..31 take the main KV's 16-channel groups as the
+// cache write does (groups 28..31 rotate first); lanes 32..63 take four
+// indexer-key channels each (lanes 48..63 rotate) and store one dword of
+// codes.  Per row 1,280 B of bf16 and 16 B of position and slot are read,
+// 256 B of angles (twice, the second time from cache), and 416 B written.
+
+// bf16 bit pattern nearest to a finite binary32 value, ties to even.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = f2u(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Rotates one pair (x = low half, y = high half of xy, bf16) by (c, s).
+__device__ __forceinline__ uint32_t rope_pair(uint32_t xy, float c, float s) {
+#pragma clang fp contract(off)
+  const float x = u2f(xy << 16), y = u2f(xy & 0xFFFF0000u);
+  const float xr = x * c - y * s;
+  const float yr = x * s + y * c;
+  return bf16_rne_bits(xr) | (bf16_rne_bits(yr) << 16);
+}
+
+// E4M3 code of a bf16 value (bit pattern b): sign copied, magnitude nearest
+// with ties to even, saturating at 448.  The magnitude is exact in binary32.
+__device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t b) {
+  return ((b >> 8) & 0x80u) | e4m3_rne_pos(u2f((b & 0x7FFFu) << 16));
+}
+
+__global__ __launch_bounds__(256) void rope_write_kernel(
+    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ kidx, int64_t rows,
+    const int64_t* __restrict__ pos, const float* __restrict__ cs, int64_t max_pos,
+    const int64_t* __restrict__ slot, uint8_t* __restrict__ kv_pool,
+    uint8_t* __restrict__ kidx_pool, int64_t n_pages) {
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // one wave per row
+  const int lane = (int)(threadIdx.x & 63);
+  if (r >= rows) return;  // whole waves only
+  const int64_t p = pos[r], s = slot[r];
+  const bool ok = p >= 0 && p < max_pos && s >= 0 && s < n_pages * kPage;
+  const float* __restrict__ crow = cs + (ok ? p : 0) * (2 * 32);
+  if (lane < 32) {
+    const int g = lane;
+    const v4u* src = reinterpret_cast<const v4u*>(kv + r * kD + g * 16);
+    const v4u a = __builtin_nontemporal_load(src);
+    const v4u b = __builtin_nontemporal_load(src + 1);
+    uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (g >= 28 && ok) {  // channels 448 + 16 (g - 28) ..: pairs 8 (g - 28) ..
+      const v4f* t = reinterpret_cast<const v4f*>(crow + (g - 28) * 16);
+      const v4f t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3];
+      h[0] = rope_pair(h[0], t0.x, t0.y); h[1] = rope_pair(h[1], t0.z, t0.w);
+      h[2] = rope_pair(h[2], t1.x, t1.y); h[3] = rope_pair(h[3], t1.z, t1.w);
+      h[4] = rope_pair(h[4], t2.x, t2.y); h[5] = rope_pair(h[5], t2.z, t2.w);
+      h[6] = rope_pair(h[6], t3.x, t3.y); h[7] = rope_pair(h[7], t3.z, t3.w);
+    }
+    store_fp4_group(fp4_group(h), g, ok, s, kv_pool);
+  } else {
+    const int l = lane - 32;  // channels 4l .. 4l + 3
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(kidx + r * kDI + l * 4));
+    uint32_t h0 = v.x, h1 = v.y;
+    if (l >= 16 && ok) {  // channels 64 + 4 (l - 16) ..: pairs 2 (l - 16), + 1
+      const v4f t = *reinterpret_cast<const v4f*>(crow + (l - 16) * 4);
+      h0 = rope_pair(h0, t.x, t.y);
+      h1 = rope_pair(h1, t.z, t.w);
+    }
+    const uint32_t w = e4m3_of_bf16(h0 & 0xFFFFu) | (e4m3_of_bf16(h0 >> 16) << 8) |
+                       (e4m3_of_bf16(h1 & 0xFFFFu) << 16) | (e4m3_of_bf16(h1 >> 16) << 24);
+    if (ok) {
+      uint8_t* dst = kidx_pool + (s >> 6) * (int64_t)(kPage * kDI) + (s & 63) * kDI + l * 4;
+      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
     }
   }
 }
@@ -165,5 +261,26 @@ extern "C" int csa2_quantize_kv(const uint16_t* kv_bf16, int64_t rows, const int
   if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   CSA2_LAUNCH(CSA2_K_QUANTIZE, csa2::quantize_kv_kernel, dim3((uint32_t)blocks), dim3(256),
               (hipStream_t)stream, kv_bf16, rows, dst_slot, kv_pool, n_pages);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
+}
+
+extern "C" int csa2_rope_write_caches(const uint16_t* kv_bf16, const uint16_t* kidx_bf16,
+                                      int64_t rows, const int64_t* pos, const float* rope_cs,
+                                      int64_t max_pos, const int64_t* dst_slot, uint8_t* kv_pool,
+                                      uint8_t* kidx_pool, int64_t n_pages, csa2_stream_t stream) {
+  if (rows < 0 || n_pages < 0 || max_pos < 0) return CSA2_ERR_INVALID_ARG;
+  if (rows == 0) return CSA2_OK;
+  if (!kv_bf16 || !kidx_bf16 || !pos || !rope_cs || !dst_slot || !kv_pool || !kidx_pool)
+    return CSA2_ERR_INVALID_ARG;
+  if (((uintptr_t)kv_bf16 & 15) || ((uintptr_t)kidx_bf16 & 7) || ((uintptr_t)rope_cs & 15) ||
+      ((uintptr_t)kv_pool & 7) || ((uintptr_t)kidx_pool & 3))
+    return CSA2_ERR_INVALID_ARG;
+  if (n_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
+  if (max_pos > ((int64_t)1 << 40) / 256) return CSA2_ERR_UNSUPPORTED;
+  const int64_t blocks = (rows + 3) / 4;  // four rows (waves) per 256-thread block
+  if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+  CSA2_LAUNCH(CSA2_K_ROPE_WRITE, csa2::rope_write_kernel, dim3((uint32_t)blocks), dim3(256),
+              (hipStream_t)stream, kv_bf16, kidx_bf16, rows, pos, rope_cs, max_pos, dst_slot,
+              kv_pool, kidx_pool, n_pages);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

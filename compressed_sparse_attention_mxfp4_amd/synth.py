@@ -229,6 +229,27 @@ def cache_write_rows(R: int = 1048576, seed: int = 0):
     return x, slots, n_pages
 
 
+def kidx_rows(n: int, seed: int, channel_log10_range=(-3.0, 2.5)) -> np.ndarray:
+    """Indexer-key source rows (bf16 bits, [n, 128]): N(0,1) draws times a
+    per-channel 10**U(lo, hi), so that the E4M3 write meets subnormal codes
+    and saturation at 448 as well as the normal range."""
+    g = _gen(seed)
+    x = torch.randn(n, DI, generator=g, dtype=torch.float32)
+    lo, hi = channel_log10_range
+    c = 10.0 ** (lo + (hi - lo) * torch.rand(DI, generator=g, dtype=torch.float64))
+    return bf16_bits(x * c.to(torch.float32))
+
+
+def rope_write_rows(R: int = 1048576, seed: int = 0):
+    """Fused RoPE + cache-write workload: the cache-write rows and pages of
+    ``cache_write_rows``, indexer-key rows from ``kidx_rows``, row j at
+    position j of an R-position angle table."""
+    x, slots, n_pages = cache_write_rows(R, seed)
+    ki = kidx_rows(R, seed + 2)
+    pos = np.arange(R, dtype=np.int64)
+    return x, ki, pos, rope_table(R), slots, n_pages
+
+
 def random_topk(B: int, T: int, k: int, n_entries, seed: int, frac_valid: float = 1.0) -> np.ndarray:
     """Seeded index sets for attention-only tests: distinct ascending positions < n_b,
     the first ``frac_valid`` of the k slots valid, the rest -1."""

@@ -99,6 +99,38 @@ int csa2_quantize_kv(const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_s
                      uint8_t *kv_pool, int64_t n_pages, csa2_stream_t stream);
 
 /*
+ * Fused RoPE + cache writes.  Knowledge note, "FP4 main KV": the main KV is
+ * quantized after RoPE; the indexer keys are FP8 (E4M3).  The pages do not
+ * give the rotary channels or the angles; this call takes them as follows.
+ * The last 64 channels of each main-KV row (448..511) and of each indexer
+ * key (64..127) are rotary: channels (2i, 2i + 1) of that slice, i < 32,
+ * turn by the angle of pair i at the row's position, given by the caller as
+ * rope_cs[pos][i] = (cos, sin).  With x, y the pair's bf16 values:
+ *   x' = fl(fl(x cos) - fl(y sin)),  y' = fl(fl(x sin) + fl(y cos))
+ * (each product and sum one binary32 operation, no fused multiply-add),
+ * then x', y' rounded to bf16, nearest with ties to even.  The rotated main
+ * KV is written exactly as csa2_quantize_kv writes it; the rotated indexer
+ * key as E4M3 codes, nearest with ties to even, saturating at +-448, sign
+ * copied (so -0 and negative values that round to 0 give 0x80).
+ *   kv_bf16   [rows][512] bf16 (16-byte aligned), pre-RoPE main-KV rows.
+ *   kidx_bf16 [rows][128] bf16 (8-byte aligned), pre-RoPE indexer keys.
+ *   pos       [rows] int64 positions; rope_cs [max_pos][32][2] float
+ *             (16-byte aligned).
+ *   dst_slot  [rows] int64 physical page * 64 + offset, shared by both pools.
+ *   kv_pool   [n_pages][18432] bytes, the layout of csa2_quantize_kv.
+ *   kidx_pool [n_pages][64][128] bytes, the E4M3 key pool of csa2_index_full.
+ * Rows whose slot lies outside [0, n_pages * 64) or whose position lies
+ * outside [0, max_pos) are skipped (neither pool is written).  Inputs are
+ * only read.  Returns CSA2_ERR_INVALID_ARG for negative sizes, a null or
+ * misaligned pointer (rows > 0), CSA2_ERR_UNSUPPORTED beyond 2^40 bytes of
+ * pool or table, CSA2_ERR_LAUNCH if the launch fails.
+ */
+int csa2_rope_write_caches(const uint16_t *kv_bf16, const uint16_t *kidx_bf16, int64_t rows,
+                           const int64_t *pos, const float *rope_cs, int64_t max_pos,
+                           const int64_t *dst_slot, uint8_t *kv_pool, uint8_t *kidx_pool,
+                           int64_t n_pages, csa2_stream_t stream);
+
+/*
  * Full mode of the hierarchical indexer.  Knowledge note, "Hierarchical
  * Sparse Indexer" (Figure 5): the Full layer scores all visible positions,
  * ranks blocks of 8 positions by their maximum score and keeps up to 2,048
@@ -203,7 +235,8 @@ enum csa2_kernel {
   CSA2_K_SELECT_REINDEX = 5,  /* Reindex-mode top-k selection */
   CSA2_K_ATTN_SPLIT = 6,      /* attention over row splits */
   CSA2_K_ATTN_COMBINE = 7,    /* merge of the splits */
-  CSA2_K_COUNT = 8
+  CSA2_K_ROPE_WRITE = 8,      /* fused RoPE + cache writes */
+  CSA2_K_COUNT = 9
 };
 
 /*

@@ -189,8 +189,11 @@ def rope_rows(x_bf16: np.ndarray, pos: np.ndarray, rope_cs: np.ndarray, start: i
 
 def e4m3_codes_of_bf16(x_bf16: np.ndarray) -> np.ndarray:
     """E4M3 nearest-even codes (saturating at 448) of bf16 values."""
-    table = np.array([e4m3_nearest(v) for v in bf16_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))],
-                     dtype=np.uint8) if not hasattr(e4m3_codes_of_bf16, "_t") else e4m3_codes_of_bf16._t
+    if not hasattr(e4m3_codes_of_bf16, "_t"):
+        with np.errstate(invalid="ignore"):       # the NaN patterns' entries are never used
+            vals = bf16_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+        e4m3_codes_of_bf16._t = np.array([e4m3_nearest(v) for v in vals], dtype=np.uint8)
+    table = e4m3_codes_of_bf16._t
     e4m3_codes_of_bf16._t = table
     return table[np.asarray(x_bf16, dtype=np.uint16)]
 

@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 102
+    assert L.csa2_abi_version() == 103
 
 
 def test_workspace_sizes(L):
@@ -134,6 +134,22 @@ def test_quantize_argument_errors(L):
     assert L.csa2_quantize_kv(None, 4, X, X, 1, None) == INVALID
     assert L.csa2_quantize_kv(X, -1, X, X, 1, None) == INVALID
     assert L.csa2_quantize_kv(X, 0, X, X, 1, None) == OK      # nothing to do, nothing launched
+
+
+def test_rope_write_argument_errors(L):
+    def call(kv=X, ki=X, rows=4, pos=X, cs=X, max_pos=100, slot=X, kvp=X, kip=X, n_pages=1):
+        return L.csa2_rope_write_caches(kv, ki, rows, pos, cs, max_pos, slot, kvp, kip, n_pages, None)
+    assert call(kv=None) == INVALID
+    assert call(kip=None) == INVALID
+    assert call(cs=None) == INVALID
+    assert call(rows=-1) == INVALID
+    assert call(max_pos=-1) == INVALID
+    assert call(n_pages=-1) == INVALID
+    assert call(cs=ctypes.c_void_p(0x1004)) == INVALID       # the angle table must be 16-byte aligned
+    assert call(kv=ctypes.c_void_p(0x1008)) == INVALID       # main-KV rows must be 16-byte aligned
+    assert call(ki=ctypes.c_void_p(0x1004)) == INVALID       # indexer keys must be 8-byte aligned
+    assert call(max_pos=1 << 40) == UNSUPPORTED
+    assert call(rows=0, kv=None, cs=None) == OK               # nothing to do, nothing launched
 
 
 def test_binding_refuses_cpu_tensors():

@@ -114,6 +114,69 @@ def test_quantize_parity_full_cache_write(oracle):
     assert np.array_equal(gs, scales)
 
 
+# ------------------------------------------------------------------ fused RoPE + cache writes
+def gpu_rope_write(kv, ki, pos, table, slots, n_pages, fill=0xAA):
+    kvp = torch.full((n_pages, csa2.PAGE_BYTES), fill, dtype=torch.uint8, device="cuda")
+    kip = torch.full((n_pages, 64, 128), fill, dtype=torch.uint8, device="cuda")
+    csa2.rope_write_caches(bf16_dev(kv), bf16_dev(ki), dev(pos.astype(np.int64)), dev(table),
+                           dev(slots.astype(np.int64)), kvp, kip)
+    return host(kvp), host(kip)
+
+
+def oracle_rope_write(oracle, kv, ki, pos, table, slots, n_pages, fill=0xAA):
+    kvp = np.full((n_pages, oracle.PAGE_BYTES), fill, np.uint8)
+    kip = np.full((n_pages, 64, 128), fill, np.uint8)
+    return oracle.rope_write_caches(kv, ki, pos, table, slots, kvp, kip)
+
+
+def test_rope_write_parity_mixed(oracle):
+    say("rope write 6011 rows: special groups, outliers, wide scales, skipped rows")
+    kv = np.concatenate([synth.kv_rows(2000, 11), synth.kv_rows(2000, 12, outlier_frac=0.05),
+                         synth.kv_rows(2000, 13, channel_log10_range=(-2.0, 2.0)), special_rows()])
+    R = len(kv)
+    ki = synth.kidx_rows(R, 14)
+    table = synth.rope_table(4096)
+    rng = np.random.default_rng(3)
+    pos = rng.integers(0, len(table), R).astype(np.int64)
+    n_pages = (R + 63) // 64 + 2
+    slots = rng.permutation(n_pages * 64)[:R].astype(np.int64)
+    slots[5], slots[6] = -1, n_pages * 64 + 3          # skipped: slot outside the pools
+    pos[7], pos[8] = -1, len(table)                     # skipped: position outside the table
+    got_kv, got_ki = gpu_rope_write(kv, ki, pos, table, slots, n_pages)
+    ref_kv, ref_ki = oracle_rope_write(oracle, kv, ki, pos, table, slots, n_pages)
+    assert np.array_equal(got_kv, ref_kv)
+    assert np.array_equal(got_ki, ref_ki)
+
+
+def test_rope_write_e4m3_every_finite_bf16(oracle):
+    say("rope write: every finite bf16 pattern through the E4M3 key write")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = bits[(bits & 0x7F80) != 0x7F80]             # 65,024 patterns = 1016 x 64
+    n = len(finite) // 64
+    ki = np.zeros((n, 128), np.uint16)
+    ki[:, :64] = finite.reshape(n, 64)                  # the channels that do not rotate
+    ki[:, 64:] = finite.reshape(n, 64)[::-1]            # and the rotary ones, turned by angle 0
+    kv = synth.kv_rows(n, 15)
+    table = synth.rope_table(3)
+    pos = np.zeros(n, np.int64)
+    slots = np.arange(n, dtype=np.int64)
+    n_pages = (n + 63) // 64
+    got_kv, got_ki = gpu_rope_write(kv, ki, pos, table, slots, n_pages)
+    assert np.array_equal(got_ki.reshape(-1, 128)[:n, :64].reshape(-1), oracle.e4m3_codes_of_bf16(finite))
+    ref_kv, ref_ki = oracle_rope_write(oracle, kv, ki, pos, table, slots, n_pages)
+    assert np.array_equal(got_ki, ref_ki)
+    assert np.array_equal(got_kv, ref_kv)
+
+
+def test_rope_write_parity_full(oracle):
+    say("rope write 1,048,576 rows at positions 0 .. 2^20 - 1, permuted pages")
+    kv, ki, pos, table, slots, n_pages = synth.rope_write_rows()
+    got_kv, got_ki = gpu_rope_write(kv, ki, pos, table, slots, n_pages, fill=0)
+    ref_kv, ref_ki = oracle_rope_write(oracle, kv, ki, pos, table, slots, n_pages, fill=0)
+    assert np.array_equal(got_ki, ref_ki)
+    assert np.array_equal(got_kv, ref_kv)
+
+
 # ------------------------------------------------------------------ a2..a6
 def gpu_index_full(wl, layer, topk=None, pool_blocks=None):
     topk = topk or wl.topk
