@@ -102,8 +102,8 @@ def counters_driver(args):
     """Launch sequence for rocprofv3 counter runs: a plain 256 MiB device copy
     (calibrates FETCH_SIZE / WRITE_SIZE), then 3 times each: the Full indexer
     of the workload, the same over MXFP4 indexer keys, the cache write of all
-    of the workload's rows (1,048,576 at 1M context) and the sparse attention
-    over the indexer's top-k."""
+    of the workload's rows (1,048,576 at 1M context), the fused RoPE + cache
+    writes of those rows and the sparse attention over the indexer's top-k."""
     import torch
     import compressed_sparse_attention_mxfp4_amd as csa2
     from compressed_sparse_attention_mxfp4_amd import synth
@@ -137,6 +137,15 @@ def counters_driver(args):
     for _ in range(3):
         csa2.quantize_kv(kv_src, slots, kv)
     torch.cuda.synchronize()
+    # fused RoPE + cache writes of the same rows, indexer keys too, row j at position j
+    R = kv_src.shape[0]
+    ki_src = d(synth.kidx_rows(R, 46).view(np.int16)).view(torch.bfloat16)
+    pos, table = d(np.arange(R, dtype=np.int64)), d(synth.rope_table(R))
+    kip = torch.zeros((wl.paging.n_pages, csa2.PAGE, csa2.DI), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        csa2.rope_write_caches(kv_src, ki_src, pos, table, slots, kv, kip)
+    torch.cuda.synchronize()
+    del ki_src, pos, table, kip
     for _ in range(3):
         csa2.sparse_attn(qa, wl.sm_scale, kv, pt, ne, topk, swa, ws=ws_a)
     torch.cuda.synchronize()

@@ -177,11 +177,16 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
 // (nearest, ties to even), then written as by the FP4 cache write (main KV)
 // and as E4M3 nearest-even codes saturating at 448 (indexer keys).
 //
-// One wave per row: lanes 0..31 take the main KV's 16-channel groups as the
-// cache write does (groups 28..31 rotate first); lanes 32..63 take four
-// indexer-key channels each (lanes 48..63 rotate) and store one dword of
-// codes.  Per row 1,280 B of bf16 and 16 B of position and slot are read,
-// 256 B of angles (twice, the second time from cache), and 416 B written.
+// Two rows per wave, as in the cache write: lanes 0..31 take the first
+// row's 16-channel main-KV groups, lanes 32..63 the second row's; lanes
+// 0..7 of each half also take that row's eight indexer-key groups.  Rotary
+// are main-KV groups 28..31 and indexer-key groups 4..7 (disjoint lanes, so
+// one rotation pass serves both): each takes eight pairs, 64 B of the row's
+// angles.  No branch precedes the loads (out-of-range rows are clamped and
+// not stored), so a wave has its rows, positions and slots in flight at once
+// and then its angles.  Per row 1,280 B of bf16 and 16 B of position and slot
+// are read, 256 B of angles (twice, the second time from cache), 416 B
+// written.
 
 // bf16 bit pattern nearest to a finite binary32 value, ties to even.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -199,9 +204,16 @@ __device__ __forceinline__ uint32_t rope_pair(uint32_t xy, float c, float s) {
 }
 
 // E4M3 code of a bf16 value (bit pattern b): sign copied, magnitude nearest
-// with ties to even, saturating at 448.  The magnitude is exact in binary32.
+// with ties to even, saturating at 448, without branches.  From 2^-6 up the
+// 7-bit bf16 mantissa is rounded to 3 bits on the bit pattern (a carry moves
+// into the exponent, as it should), and the exponent is rebased from bias
+// 127 to bias 7; below 2^-6 the E4M3 steps are 2^-9 and the code is the
+// value times 2^9 rounded to an integer (exact product, rint ties to even).
 __device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t b) {
-  return ((b >> 8) & 0x80u) | e4m3_rne_pos(u2f((b & 0x7FFFu) << 16));
+  const uint32_t m = b & 0x7FFFu;
+  const uint32_t nrm = min(((m + 7u + ((m >> 4) & 1u)) >> 4) - (120u << 3), 0x7Eu);
+  const uint32_t sub = (uint32_t)__builtin_rintf(u2f(min(m, 121u << 7) << 16) * 512.0f);
+  return ((b >> 8) & 0x80u) | (m >= (121u << 7) ? nrm : sub);
 }
 
 __global__ __launch_bounds__(256) void rope_write_kernel(
@@ -209,42 +221,56 @@ __global__ __launch_bounds__(256) void rope_write_kernel(
     const int64_t* __restrict__ pos, const float* __restrict__ cs, int64_t max_pos,
     const int64_t* __restrict__ slot, uint8_t* __restrict__ kv_pool,
     uint8_t* __restrict__ kidx_pool, int64_t n_pages) {
-  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // one wave per row
   const int lane = (int)(threadIdx.x & 63);
-  if (r >= rows) return;  // whole waves only
-  const int64_t p = pos[r], s = slot[r];
-  const bool ok = p >= 0 && p < max_pos && s >= 0 && s < n_pages * kPage;
-  const float* __restrict__ crow = cs + (ok ? p : 0) * (2 * 32);
-  if (lane < 32) {
-    const int g = lane;
-    const v4u* src = reinterpret_cast<const v4u*>(kv + r * kD + g * 16);
-    const v4u a = __builtin_nontemporal_load(src);
-    const v4u b = __builtin_nontemporal_load(src + 1);
-    uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    if (g >= 28 && ok) {  // channels 448 + 16 (g - 28) ..: pairs 8 (g - 28) ..
-      const v4f* t = reinterpret_cast<const v4f*>(crow + (g - 28) * 16);
-      const v4f t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3];
-      h[0] = rope_pair(h[0], t0.x, t0.y); h[1] = rope_pair(h[1], t0.z, t0.w);
-      h[2] = rope_pair(h[2], t1.x, t1.y); h[3] = rope_pair(h[3], t1.z, t1.w);
-      h[4] = rope_pair(h[4], t2.x, t2.y); h[5] = rope_pair(h[5], t2.z, t2.w);
-      h[6] = rope_pair(h[6], t3.x, t3.y); h[7] = rope_pair(h[7], t3.z, t3.w);
+  const int half = lane >> 5, g = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 2;  // the wave's first row (uniform)
+  const int64_t ra = min(r0, rows - 1), rb = min(r0 + 1, rows - 1);
+  const int64_t r = half ? rb : ra;
+  const bool live = r0 + half < rows;
+  const v4u* src = reinterpret_cast<const v4u*>(kv + r * kD + g * 16);
+  const v4u a = __builtin_nontemporal_load(src);
+  const v4u b = __builtin_nontemporal_load(src + 1);
+  uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t k[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (g < 8) {
+    const v4u* ks = reinterpret_cast<const v4u*>(kidx + r * kDI + g * 16);
+    const v4u c = __builtin_nontemporal_load(ks);
+    const v4u d = __builtin_nontemporal_load(ks + 1);
+    k[0] = c.x; k[1] = c.y; k[2] = c.z; k[3] = c.w; k[4] = d.x; k[5] = d.y; k[6] = d.z; k[7] = d.w;
+  }
+  const int64_t pa = pos[ra], pb = pos[rb], sa = slot[ra], sb = slot[rb];
+  const int64_t p = half ? pb : pa, s = half ? sb : sa;
+  // a row that is skipped is computed at position 0 (max_pos > 0), not stored
+  const bool ok = live & (p >= 0) & (p < max_pos) & (s >= 0) & (s < n_pages * kPage);
+  const int64_t pc = ok ? p : 0;
+  const bool kv_rot = g >= 28, k_rot = (g >= 4) & (g < 8);
+  if (kv_rot | k_rot) {  // eight pairs: (cos, sin) of pairs 8 rot .. 8 rot + 7
+    const int rot = kv_rot ? g - 28 : g - 4;
+    const v4f* t = reinterpret_cast<const v4f*>(cs + pc * (2 * 32) + rot * 16);
+    const v4f t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3];
+    uint32_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = kv_rot ? h[j] : k[j];
+    x[0] = rope_pair(x[0], t0.x, t0.y); x[1] = rope_pair(x[1], t0.z, t0.w);
+    x[2] = rope_pair(x[2], t1.x, t1.y); x[3] = rope_pair(x[3], t1.z, t1.w);
+    x[4] = rope_pair(x[4], t2.x, t2.y); x[5] = rope_pair(x[5], t2.z, t2.w);
+    x[6] = rope_pair(x[6], t3.x, t3.y); x[7] = rope_pair(x[7], t3.z, t3.w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = kv_rot ? x[j] : h[j];
+      k[j] = kv_rot ? k[j] : x[j];
     }
-    store_fp4_group(fp4_group(h), g, ok, s, kv_pool);
-  } else {
-    const int l = lane - 32;  // channels 4l .. 4l + 3
-    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(kidx + r * kDI + l * 4));
-    uint32_t h0 = v.x, h1 = v.y;
-    if (l >= 16 && ok) {  // channels 64 + 4 (l - 16) ..: pairs 2 (l - 16), + 1
-      const v4f t = *reinterpret_cast<const v4f*>(crow + (l - 16) * 4);
-      h0 = rope_pair(h0, t.x, t.y);
-      h1 = rope_pair(h1, t.z, t.w);
-    }
-    const uint32_t w = e4m3_of_bf16(h0 & 0xFFFFu) | (e4m3_of_bf16(h0 >> 16) << 8) |
-                       (e4m3_of_bf16(h1 & 0xFFFFu) << 16) | (e4m3_of_bf16(h1 >> 16) << 24);
-    if (ok) {
-      uint8_t* dst = kidx_pool + (s >> 6) * (int64_t)(kPage * kDI) + (s & 63) * kDI + l * 4;
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
-    }
+  }
+  store_fp4_group(fp4_group(h), g, ok, s, kv_pool);
+  if (g < 8 && ok) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = e4m3_of_bf16(k[2 * j] & 0xFFFFu) | (e4m3_of_bf16(k[2 * j] >> 16) << 8) |
+             (e4m3_of_bf16(k[2 * j + 1] & 0xFFFFu) << 16) | (e4m3_of_bf16(k[2 * j + 1] >> 16) << 24);
+    uint8_t* dst = kidx_pool + (s >> 6) * (int64_t)(kPage * kDI) + (s & 63) * kDI + g * 16;
+    __builtin_nontemporal_store((v4u){w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u*>(dst));
   }
 }
 
@@ -270,14 +296,15 @@ extern "C" int csa2_rope_write_caches(const uint16_t* kv_bf16, const uint16_t* k
                                       uint8_t* kidx_pool, int64_t n_pages, csa2_stream_t stream) {
   if (rows < 0 || n_pages < 0 || max_pos < 0) return CSA2_ERR_INVALID_ARG;
   if (rows == 0) return CSA2_OK;
+  if (max_pos == 0) return CSA2_OK;  // every row skipped
   if (!kv_bf16 || !kidx_bf16 || !pos || !rope_cs || !dst_slot || !kv_pool || !kidx_pool)
     return CSA2_ERR_INVALID_ARG;
-  if (((uintptr_t)kv_bf16 & 15) || ((uintptr_t)kidx_bf16 & 7) || ((uintptr_t)rope_cs & 15) ||
-      ((uintptr_t)kv_pool & 7) || ((uintptr_t)kidx_pool & 3))
+  if (((uintptr_t)kv_bf16 & 15) || ((uintptr_t)kidx_bf16 & 15) || ((uintptr_t)rope_cs & 15) ||
+      ((uintptr_t)kv_pool & 7) || ((uintptr_t)kidx_pool & 15))
     return CSA2_ERR_INVALID_ARG;
   if (n_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
   if (max_pos > ((int64_t)1 << 40) / 256) return CSA2_ERR_UNSUPPORTED;
-  const int64_t blocks = (rows + 3) / 4;  // four rows (waves) per 256-thread block
+  const int64_t blocks = (rows + 7) / 8;  // two rows per wave, four waves per block
   if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   CSA2_LAUNCH(CSA2_K_ROPE_WRITE, csa2::rope_write_kernel, dim3((uint32_t)blocks), dim3(256),
               (hipStream_t)stream, kv_bf16, kidx_bf16, rows, pos, rope_cs, max_pos, dst_slot,

@@ -194,7 +194,6 @@ def e4m3_codes_of_bf16(x_bf16: np.ndarray) -> np.ndarray:
             vals = bf16_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))
         e4m3_codes_of_bf16._t = np.array([e4m3_nearest(v) for v in vals], dtype=np.uint8)
     table = e4m3_codes_of_bf16._t
-    e4m3_codes_of_bf16._t = table
     return table[np.asarray(x_bf16, dtype=np.uint16)]
 
 
