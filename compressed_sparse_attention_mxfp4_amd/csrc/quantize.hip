@@ -177,16 +177,20 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
 // (nearest, ties to even), then written as by the FP4 cache write (main KV)
 // and as E4M3 nearest-even codes saturating at 448 (indexer keys).
 //
-// Two rows per wave, as in the cache write: lanes 0..31 take the first
-// row's 16-channel main-KV groups, lanes 32..63 the second row's; lanes
-// 0..7 of each half also take that row's eight indexer-key groups.  Rotary
-// are main-KV groups 28..31 and indexer-key groups 4..7 (disjoint lanes, so
-// one rotation pass serves both): each takes eight pairs, 64 B of the row's
-// angles.  No branch precedes the loads (out-of-range rows are clamped and
-// not stored), so a wave has its rows, positions and slots in flight at once
-// and then its angles.  Per row 1,280 B of bf16 and 16 B of position and slot
-// are read, 256 B of angles (twice, the second time from cache), 416 B
-// written.
+// Two rows per wave: lanes 0..31 serve the first row, lanes 32..63 the
+// second, and every lane g (0..31 within its half) does the same work:
+//  - main-KV group g (16 channels), quantized as by the cache write;
+//  - rotary main-KV pair g (channels 448 + 2g, 449 + 2g), loaded once more as
+//    one dword (a cache hit) and turned there; groups 28..31 then collect
+//    their eight turned pairs from lanes 8 (g - 28) .. 8 (g - 28) + 7 by
+//    lane permutes before quantizing;
+//  - indexer-key channels 4g .. 4g + 3, turned in place where rotary
+//    (g >= 16: pairs 2 (g - 16), + 1), rounded to E4M3 and stored as a dword.
+// Spreading the turns and the E4M3 rounding over all lanes, rather than over
+// the 8 lanes that hold the rotary main-KV groups and the 16 that hold
+// indexer-key groups, is what keeps the vector instruction count per row
+// below the time the row's bytes take.  Per row 1,280 B of bf16 and 16 B of
+// position and slot are read, 256 B of angles (from HBM once), 416 B written.
 
 // bf16 bit pattern nearest to a finite binary32 value, ties to even.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -225,52 +229,39 @@ __global__ __launch_bounds__(256) void rope_write_kernel(
   const int half = lane >> 5, g = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 2;  // the wave's first row (uniform)
+  // rows past the end are loaded clamped and not stored: no branch ahead of
+  // the loads, so all of them are in flight at once
   const int64_t ra = min(r0, rows - 1), rb = min(r0 + 1, rows - 1);
   const int64_t r = half ? rb : ra;
-  const bool live = r0 + half < rows;
-  const v4u* src = reinterpret_cast<const v4u*>(kv + r * kD + g * 16);
+  const uint16_t* krow = kv + r * kD;
+  const v4u* src = reinterpret_cast<const v4u*>(krow + g * 16);
   const v4u a = __builtin_nontemporal_load(src);
   const v4u b = __builtin_nontemporal_load(src + 1);
-  uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t k[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (g < 8) {
-    const v4u* ks = reinterpret_cast<const v4u*>(kidx + r * kDI + g * 16);
-    const v4u c = __builtin_nontemporal_load(ks);
-    const v4u d = __builtin_nontemporal_load(ks + 1);
-    k[0] = c.x; k[1] = c.y; k[2] = c.z; k[3] = c.w; k[4] = d.x; k[5] = d.y; k[6] = d.z; k[7] = d.w;
-  }
+  const uint32_t kv_pair = *reinterpret_cast<const uint32_t*>(krow + kD - 64 + 2 * g);
+  const v2u kk = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(kidx + r * kDI + g * 4));
   const int64_t pa = pos[ra], pb = pos[rb], sa = slot[ra], sb = slot[rb];
   const int64_t p = half ? pb : pa, s = half ? sb : sa;
-  // a row that is skipped is computed at position 0 (max_pos > 0), not stored
-  const bool ok = live & (p >= 0) & (p < max_pos) & (s >= 0) & (s < n_pages * kPage);
-  const int64_t pc = ok ? p : 0;
-  const bool kv_rot = g >= 28, k_rot = (g >= 4) & (g < 8);
-  if (kv_rot | k_rot) {  // eight pairs: (cos, sin) of pairs 8 rot .. 8 rot + 7
-    const int rot = kv_rot ? g - 28 : g - 4;
-    const v4f* t = reinterpret_cast<const v4f*>(cs + pc * (2 * 32) + rot * 16);
-    const v4f t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3];
-    uint32_t x[8];
+  // a row that is skipped is turned at position 0 (max_pos > 0), not stored
+  const bool ok = (r0 + half < rows) & (p >= 0) & (p < max_pos) & (s >= 0) & (s < n_pages * kPage);
+  const float* crow = cs + (ok ? p : 0) * (2 * 32);
+  const v2f t1 = *reinterpret_cast<const v2f*>(crow + 2 * g);          // pair g
+  const v4f t2 = *reinterpret_cast<const v4f*>(crow + 4 * (g & 15));   // pairs 2 (g & 15), + 1
+  const uint32_t kv_turned = rope_pair(kv_pair, t1.x, t1.y);
+  const uint32_t k0r = rope_pair(kk.x, t2.x, t2.y), k1r = rope_pair(kk.y, t2.z, t2.w);
+  const uint32_t k0 = g >= 16 ? k0r : kk.x, k1 = g >= 16 ? k1r : kk.y;
+  uint32_t h[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int from = (half << 5) + ((g & 3) << 3);  // lanes 28..31: pairs 8 (g - 28) ..
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = kv_rot ? h[j] : k[j];
-    x[0] = rope_pair(x[0], t0.x, t0.y); x[1] = rope_pair(x[1], t0.z, t0.w);
-    x[2] = rope_pair(x[2], t1.x, t1.y); x[3] = rope_pair(x[3], t1.z, t1.w);
-    x[4] = rope_pair(x[4], t2.x, t2.y); x[5] = rope_pair(x[5], t2.z, t2.w);
-    x[6] = rope_pair(x[6], t3.x, t3.y); x[7] = rope_pair(x[7], t3.z, t3.w);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h[j] = kv_rot ? x[j] : h[j];
-      k[j] = kv_rot ? k[j] : x[j];
-    }
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t v = (uint32_t)__shfl((int)kv_turned, from + j, 64);
+    h[j] = g >= 28 ? v : h[j];
   }
   store_fp4_group(fp4_group(h), g, ok, s, kv_pool);
-  if (g < 8 && ok) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = e4m3_of_bf16(k[2 * j] & 0xFFFFu) | (e4m3_of_bf16(k[2 * j] >> 16) << 8) |
-             (e4m3_of_bf16(k[2 * j + 1] & 0xFFFFu) << 16) | (e4m3_of_bf16(k[2 * j + 1] >> 16) << 24);
-    uint8_t* dst = kidx_pool + (s >> 6) * (int64_t)(kPage * kDI) + (s & 63) * kDI + g * 16;
-    __builtin_nontemporal_store((v4u){w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u*>(dst));
+  if (ok) {
+    const uint32_t w = e4m3_of_bf16(k0 & 0xFFFFu) | (e4m3_of_bf16(k0 >> 16) << 8) |
+                       (e4m3_of_bf16(k1 & 0xFFFFu) << 16) | (e4m3_of_bf16(k1 >> 16) << 24);
+    uint8_t* dst = kidx_pool + (s >> 6) * (int64_t)(kPage * kDI) + (s & 63) * kDI + g * 4;
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
   }
 }
 
@@ -299,13 +290,12 @@ extern "C" int csa2_rope_write_caches(const uint16_t* kv_bf16, const uint16_t* k
   if (max_pos == 0) return CSA2_OK;  // every row skipped
   if (!kv_bf16 || !kidx_bf16 || !pos || !rope_cs || !dst_slot || !kv_pool || !kidx_pool)
     return CSA2_ERR_INVALID_ARG;
-  if (((uintptr_t)kv_bf16 & 15) || ((uintptr_t)kidx_bf16 & 15) || ((uintptr_t)rope_cs & 15) ||
-      ((uintptr_t)kv_pool & 7) || ((uintptr_t)kidx_pool & 15))
+  if (((uintptr_t)kv_bf16 & 15) || ((uintptr_t)kidx_bf16 & 7) || ((uintptr_t)rope_cs & 15) ||
+      ((uintptr_t)kv_pool & 7) || ((uintptr_t)kidx_pool & 3))
     return CSA2_ERR_INVALID_ARG;
   if (n_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
   if (max_pos > ((int64_t)1 << 40) / 256) return CSA2_ERR_UNSUPPORTED;
   const int64_t blocks = (rows + 7) / 8;  // two rows per wave, four waves per block
-  if (blocks > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
   CSA2_LAUNCH(CSA2_K_ROPE_WRITE, csa2::rope_write_kernel, dim3((uint32_t)blocks), dim3(256),
               (hipStream_t)stream, kv_bf16, kidx_bf16, rows, pos, rope_cs, max_pos, dst_slot,
               kv_pool, kidx_pool, n_pages);
