@@ -214,6 +214,43 @@ def rope_write_caches(kv_bf16, kidx_bf16, pos, rope_cs, dst_slot, kv_pool, kidx_
     return kv_pool, kidx_pool
 
 
+# -------------------------------------------------- sequence compressor (next step)
+# "Inside DeepSeek V4.1 Flash", deep dive "Causal Encoder-Decoder" (its symbol
+# table and equation 1): global KV entries C and compression weights Z are
+# both projected per source position, one main KV entry stands for m source
+# positions, and CSA2 groups non-overlapping positions with no absolute
+# positional term (section on CSA2 simplifying sequence compression).  The
+# pages give no formula for how Z weighs C.  Reading: per channel, a softmax
+# over the m positions of the group of Z, applied to C elementwise:
+#   entry[g][c] = sum_i w_i[c] C[g m + i][c],
+#   w_i[c] = exp(Z[g m + i][c]) / sum_j exp(Z[g m + j][c]).
+# Only complete groups form entries.  Computed here in binary64 (the max is
+# subtracted before exp, which leaves the weights unchanged).
+def compress(c_bf16: np.ndarray, z_bf16: np.ndarray, m: int) -> np.ndarray:
+    """Entries [G, 512] float64 of the first G = rows // m complete groups."""
+    c = bf16_to_f64(np.asarray(c_bf16, dtype=np.uint16))
+    z = bf16_to_f64(np.asarray(z_bf16, dtype=np.uint16))
+    G = c.shape[0] // m
+    c = c[:G * m].reshape(G, m, -1)
+    z = z[:G * m].reshape(G, m, -1)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    w = e / e.sum(axis=1, keepdims=True)
+    return (w * c).sum(axis=1)
+
+
+def compress_abs(c_bf16: np.ndarray, z_bf16: np.ndarray, m: int) -> np.ndarray:
+    """sum_i w_i |C_i| per entry and channel (the scale of rounding errors)."""
+    c = np.abs(bf16_to_f64(np.asarray(c_bf16, dtype=np.uint16)))
+    return compress(f64_to_bf16_trunc(c), z_bf16, m)
+
+
+def f64_to_bf16_trunc(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that are already bf16 (exact conversion)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "not a bf16 value"
+    return (u >> 16).astype(np.uint16)
+
+
 def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, ENTRY_CODES)
     scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, NGROUPS)

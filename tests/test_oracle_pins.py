@@ -544,3 +544,62 @@ def test_rope_write_caches_layout_and_skips(oracle):
         codes, scales = oracle.quantize_rows(rk)
         c, sc = oracle.pool_entry(kvp, pg, off)
         assert np.array_equal(c, codes[0]) and np.array_equal(sc, scales[0])
+
+
+# ------------------------------------------------------------ sequence compressor
+def _bf16(x):
+    return synth.bf16_bits(torch.as_tensor(np.asarray(x, np.float32)))
+
+
+def test_compress_m1_is_identity(oracle):
+    c, z = synth.kv_rows(9, 60), synth.kv_rows(9, 61)
+    out = oracle.compress(c, z, 1)
+    assert np.array_equal(out, oracle.bf16_to_f64(c))
+
+
+def test_compress_equal_weights_give_the_mean(oracle):
+    c = synth.kv_rows(12, 62)
+    zrow = synth.kv_rows(3, 63)
+    z = np.repeat(zrow, 4, axis=0)                   # the same Z at the 4 positions of a group
+    out = oracle.compress(c, z, 4)
+    mean = oracle.bf16_to_f64(c).reshape(3, 4, -1).sum(axis=1) / 4.0
+    assert np.allclose(out, mean, rtol=0, atol=1e-15 * np.abs(oracle.bf16_to_f64(c)).max())
+
+
+def test_compress_two_positions_closed_form(oracle):
+    # m = 2: w_0 = 1 / (1 + e^(z_1 - z_0)), entry = c_1 + w_0 (c_0 - c_1), element by element
+    c, z = synth.kv_rows(4, 64), synth.kv_rows(4, 65)
+    cf, zf = oracle.bf16_to_f64(c), oracle.bf16_to_f64(z)
+    out = oracle.compress(c, z, 2)
+    for g in range(2):
+        for ch in range(0, 512, 37):
+            w0 = 1.0 / (1.0 + math.exp(zf[2 * g + 1, ch] - zf[2 * g, ch]))
+            want = cf[2 * g + 1, ch] + w0 * (cf[2 * g, ch] - cf[2 * g + 1, ch])
+            assert abs(out[g, ch] - want) <= 1e-15 * (abs(cf[2 * g, ch]) + abs(cf[2 * g + 1, ch]))
+
+
+def test_compress_order_within_group_and_dominant_weight(oracle):
+    c, z = synth.kv_rows(16, 66), synth.kv_rows(16, 67)
+    perm = np.concatenate([g * 8 + np.random.default_rng(g).permutation(8) for g in range(2)])
+    a, b = oracle.compress(c, z, 8), oracle.compress(c[perm], z[perm], 8)
+    assert np.allclose(a, b, rtol=1e-14, atol=1e-14)
+    # one position at Z = +40, the rest at -40: the entry is that position's C
+    zd = np.full((16, 512), -40.0, np.float32)
+    zd[3] = zd[8 + 5] = 40.0
+    out = oracle.compress(c, _bf16(zd), 8)
+    cf = oracle.bf16_to_f64(c)
+    assert np.allclose(out[0], cf[3], rtol=1e-30, atol=8 * math.exp(-80) * np.abs(cf).max())
+    assert np.allclose(out[1], cf[13], rtol=1e-30, atol=8 * math.exp(-80) * np.abs(cf).max())
+
+
+def test_compress_brute_force_and_partial_group(oracle):
+    # m = 4 over 2 groups plus 3 trailing rows (no entry), by the definition in plain loops
+    c, z = synth.kv_rows(11, 68), synth.kv_rows(11, 69)
+    cf, zf = oracle.bf16_to_f64(c), oracle.bf16_to_f64(z)
+    out = oracle.compress(c, z, 4)
+    assert out.shape == (2, 512)
+    for g in range(2):
+        for ch in (0, 1, 255, 448, 511):
+            num = sum(math.exp(zf[4 * g + i, ch]) * cf[4 * g + i, ch] for i in range(4))
+            den = sum(math.exp(zf[4 * g + i, ch]) for i in range(4))
+            assert abs(out[g, ch] - num / den) <= 1e-14 * max(1.0, abs(num / den))
