@@ -35,12 +35,12 @@ EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
     "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
-    "csa2_rope_write_caches",
+    "csa2_rope_write_caches", "csa2_compress",
 )
 
 # kernel ids for csa2_time_kernel
 K_QUANTIZE, K_SCORE_FULL, K_SELECT_FULL, K_SCORE_REINDEX, K_SELECT_REINDEX = 1, 2, 3, 4, 5
-K_ATTN_SPLIT, K_ATTN_COMBINE, K_ROPE_WRITE = 6, 7, 8
+K_ATTN_SPLIT, K_ATTN_COMBINE, K_ROPE_WRITE, K_COMPRESS = 6, 7, 8, 9
 ROPE_PAIRS = 32  # rotary channel pairs: the last 64 channels of main-KV rows and indexer keys
 
 
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH):
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.csa2_quantize_kv.argtypes = [P, i64, P, P, i64, P]
     L.csa2_rope_write_caches.argtypes = [P, P, i64, P, P, i64, P, P, P, i64, P]
+    L.csa2_compress.argtypes = [P, P, i64, i32, P, P]
     L.csa2_index_full.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32, P, P, P,
                                   P, sz, P]
     L.csa2_index_reindex.argtypes = [P, P, P, i64, P, i32, P, i32, i32, i32, P, P, i32, i32, P, P,
@@ -87,7 +88,8 @@ def load(path: str = LIB_PATH):
     L.csa2_test_keep_histograms.argtypes = [ctypes.c_int]
     L.csa2_test_keep_histograms.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-               "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches"):
+               "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches",
+               "csa2_compress"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -197,6 +199,20 @@ def rope_write_caches(kv_bf16, kidx_bf16, pos, rope_cs, dst_slot, kv_pool, kidx_
            lib().csa2_rope_write_caches(a, k, R, p, c, rope_cs.shape[0], s, kv, ki, kv_pool.shape[0],
                                         _stream(stream)))
     return kv_pool, kidx_pool
+
+
+def compress(c_bf16, z_bf16, m, out=None, stream=None):
+    """Sequence compressor: c_bf16, z_bf16 [R,512] bf16 -> entries [R // m, 512] bf16
+    (a softmax over each group's m positions of Z weighs C, per channel)."""
+    torch = _torch()
+    R = c_bf16.shape[0]
+    if out is None:
+        out = torch.empty((R // max(int(m), 1), D), dtype=torch.bfloat16, device=c_bf16.device)
+    a = _ptr(c_bf16, torch.bfloat16, "c_bf16", (R, D), 2)
+    b = _ptr(z_bf16, torch.bfloat16, "z_bf16", (R, D), 2)
+    o = _ptr(out, torch.bfloat16, "out", (R // max(int(m), 1), D), 2)
+    _check("csa2_compress", lib().csa2_compress(a, b, R, int(m), o, _stream(stream)))
+    return out
 
 
 def _kidx_arg(kidx_pool, mxfp4):

@@ -99,6 +99,32 @@ int csa2_quantize_kv(const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_s
                      uint8_t *kv_pool, int64_t n_pages, csa2_stream_t stream);
 
 /*
+ * Non-overlapping sequence compressor, the producer of the main-KV entries.
+ * "Inside DeepSeek V4.1 Flash", deep dive "Causal Encoder-Decoder" (symbol
+ * table, equation 1): C (main KV) and Z (compression weights) are projected
+ * per source position and one entry stands for m positions; CSA2 groups
+ * non-overlapping positions and has no absolute positional term.  The pages
+ * give no formula; this call computes, per channel c of entry g,
+ *   entry[g][c] = sum_i w_i C[g m + i][c],  w_i = softmax_i(Z[g m + i][c]),
+ * i < m (a softmax over the group's positions), in binary32 with the weights
+ * exp(Z - max Z) from the hardware base-2 exponential, rounded to bf16
+ * (nearest, ties to even).  Error: within 2^-8 |entry| (the bf16 rounding)
+ * plus 2^-18 sum_i w_i |C_i| of the exact value.
+ *   c_bf16, z_bf16 [rows][512] finite bf16 (16-byte aligned), the source
+ *                  positions.
+ *   m              1, 2, 4 or 8 (the pages: 2 in the encoder, 1 in the
+ *                  decoder; 4 for 4:1 compression).
+ *   out_bf16       [rows / m][512] bf16 (16-byte aligned): the entries of the
+ *                  complete groups; a trailing partial group forms none.
+ * Feed out_bf16 to csa2_quantize_kv to write the entries into the FP4 pool.
+ * Returns CSA2_ERR_INVALID_ARG for rows < 0, m <= 0, a null or misaligned
+ * pointer (when an entry is formed), CSA2_ERR_UNSUPPORTED for other m,
+ * CSA2_ERR_LAUNCH if the launch fails.
+ */
+int csa2_compress(const uint16_t *c_bf16, const uint16_t *z_bf16, int64_t rows, int32_t m,
+                  uint16_t *out_bf16, csa2_stream_t stream);
+
+/*
  * Fused RoPE + cache writes.  Knowledge note, "FP4 main KV": the main KV is
  * quantized after RoPE; the indexer keys are FP8 (E4M3).  The pages do not
  * give the rotary channels or the angles; this call takes them as follows.
@@ -236,7 +262,8 @@ enum csa2_kernel {
   CSA2_K_ATTN_SPLIT = 6,      /* attention over row splits */
   CSA2_K_ATTN_COMBINE = 7,    /* merge of the splits */
   CSA2_K_ROPE_WRITE = 8,      /* fused RoPE + cache writes */
-  CSA2_K_COUNT = 9
+  CSA2_K_COMPRESS = 9,        /* sequence compressor */
+  CSA2_K_COUNT = 10
 };
 
 /*

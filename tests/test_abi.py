@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 103
+    assert L.csa2_abi_version() == 104
 
 
 def test_workspace_sizes(L):
@@ -150,6 +150,16 @@ def test_rope_write_argument_errors(L):
     assert call(ki=ctypes.c_void_p(0x1004)) == INVALID       # indexer keys must be 8-byte aligned
     assert call(max_pos=1 << 40) == UNSUPPORTED
     assert call(rows=0, kv=None, cs=None) == OK               # nothing to do, nothing launched
+
+
+def test_compress_argument_errors(L):
+    assert L.csa2_compress(X, X, -1, 4, X, None) == INVALID
+    assert L.csa2_compress(X, X, 8, 0, X, None) == INVALID
+    assert L.csa2_compress(X, X, 8, 3, X, None) == UNSUPPORTED
+    assert L.csa2_compress(X, X, 8, 16, X, None) == UNSUPPORTED
+    assert L.csa2_compress(None, X, 8, 4, X, None) == INVALID
+    assert L.csa2_compress(X, X, 8, 4, ctypes.c_void_p(0x1008), None) == INVALID   # misaligned output
+    assert L.csa2_compress(None, None, 3, 4, None, None) == OK       # no complete group, nothing launched
 
 
 def test_binding_refuses_cpu_tensors():

@@ -177,6 +177,48 @@ def test_rope_write_parity_full(oracle):
     assert np.array_equal(got_kv, ref_kv)
 
 
+# ------------------------------------------------------------------ sequence compressor
+def check_compress(oracle, c, z, m, got):
+    """|got - exact| <= 2^-8 |exact| (bf16 rounding) + 2^-18 sum_i w_i |C_i| (binary32 steps)."""
+    exact = oracle.compress(c, z, m)
+    scale = oracle.compress_abs(c, z, m)
+    g = got.astype(np.float64)
+    err = np.abs(g - exact)
+    bound = 2.0 ** -8 * np.abs(exact) + 2.0 ** -18 * scale
+    assert g.shape == exact.shape
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
+    # the share of entries equal to the bf16 nearest the exact value (the rest sit within the
+    # binary32 error of a rounding boundary)
+    near = oracle.f32_to_bf16_rne(exact.astype(np.float32))
+    return float(np.mean(oracle.bf16_to_f64(near) == g))
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_compress_parity(oracle, m):
+    R = 8 * 301 + 5                                  # ragged: a partial trailing group for m > 1
+    say(f"compress m={m} rows={R}")
+    c = synth.kv_rows(R, 70 + m, channel_log10_range=(-2.0, 2.0))
+    z = synth.kv_rows(R, 80 + m, outlier_frac=0.02)  # weights from near-uniform to one dominant position
+    got = csa2.compress(bf16_dev(c), bf16_dev(z), m)
+    g = host(got.view(torch.int16)).view(np.uint16)
+    frac = check_compress(oracle, c, z, m, oracle.bf16_to_f64(g))
+    say(f"compress m={m}: {frac:.4f} of entries equal to the exact value's nearest bf16")
+    assert frac > 0.99
+
+
+def test_compress_full_4to1(oracle):
+    say("compress 4:1, 1,048,576 source rows -> 262,144 entries, sampled against the oracle")
+    R = 1 << 20
+    c = synth.kv_rows(R, 90)
+    z = synth.kv_rows(R, 91)
+    got = csa2.compress(bf16_dev(c), bf16_dev(z), 4)
+    g = host(got.view(torch.int16)).view(np.uint16)
+    rng = np.random.default_rng(5)
+    pick = np.sort(rng.choice(R // 4, 4096, replace=False))
+    rows = (pick[:, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+    check_compress(oracle, c[rows], z[rows], 4, oracle.bf16_to_f64(g[pick]))
+
+
 # ------------------------------------------------------------------ a2..a6
 def gpu_index_full(wl, layer, topk=None, pool_blocks=None):
     topk = topk or wl.topk
