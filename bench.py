@@ -103,7 +103,8 @@ def counters_driver(args):
     (calibrates FETCH_SIZE / WRITE_SIZE), then 3 times each: the Full indexer
     of the workload, the same over MXFP4 indexer keys, the cache write of all
     of the workload's rows (1,048,576 at 1M context), the fused RoPE + cache
-    writes of those rows and the sparse attention over the indexer's top-k."""
+    writes of those rows, the compressor forming that many entries at 4:1
+    and the sparse attention over the indexer's top-k."""
     import torch
     import compressed_sparse_attention_mxfp4_amd as csa2
     from compressed_sparse_attention_mxfp4_amd import synth
@@ -146,6 +147,15 @@ def counters_driver(args):
         csa2.rope_write_caches(kv_src, ki_src, pos, table, slots, kv, kip)
     torch.cuda.synchronize()
     del ki_src, pos, table, kip
+    # the compressor at 4:1 over the source positions of the same entries (4 x the rows)
+    gen = torch.Generator(device="cuda").manual_seed(47)
+    csrc = torch.randn((4 * R, csa2.D), generator=gen, device="cuda").to(torch.bfloat16)
+    zsrc = torch.randn((4 * R, csa2.D), generator=gen, device="cuda").to(torch.bfloat16)
+    ent = torch.empty((R, csa2.D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        csa2.compress(csrc, zsrc, 4, out=ent)
+    torch.cuda.synchronize()
+    del csrc, zsrc, ent
     for _ in range(3):
         csa2.sparse_attn(qa, wl.sm_scale, kv, pt, ne, topk, swa, ws=ws_a)
     torch.cuda.synchronize()
