@@ -53,7 +53,8 @@ def test_e4m3_examples_from_format(oracle):
 def test_e4m3_nearest_matches_torch_cast_on_all_bf16(oracle):
     # every bf16 bit pattern with |x| <= 448 (torch's cast is RNE there)
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    x = oracle.bf16_to_f64(bits)
+    with np.errstate(invalid="ignore"):               # the NaN patterns, dropped below
+        x = oracle.bf16_to_f64(bits)
     keep = np.isfinite(x) & (np.abs(x) <= 448.0)
     xs = x[keep]
     ref = torch.from_numpy(xs.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
