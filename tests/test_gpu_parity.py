@@ -219,6 +219,25 @@ def test_compress_full_4to1(oracle):
     check_compress(oracle, c[rows], z[rows], 4, oracle.bf16_to_f64(g[pick]))
 
 
+def test_rope_write_and_compress_edges(oracle):
+    say("rope write: one row; empty angle table (every row skipped); compress: no complete group, one group")
+    kv, ki = synth.kv_rows(1, 31), synth.kidx_rows(1, 32)
+    table = synth.rope_table(10)
+    pos, slots = np.array([9], np.int64), np.array([70], np.int64)   # last position, page 1 offset 6
+    got_kv, got_ki = gpu_rope_write(kv, ki, pos, table, slots, 2)
+    ref_kv, ref_ki = oracle_rope_write(oracle, kv, ki, pos, table, slots, 2)
+    assert np.array_equal(got_kv, ref_kv) and np.array_equal(got_ki, ref_ki)
+    kv, ki = synth.kv_rows(5, 33), synth.kidx_rows(5, 34)
+    got_kv, got_ki = gpu_rope_write(kv, ki, np.zeros(5, np.int64), np.zeros((0, 32, 2), np.float32),
+                                    np.arange(5, dtype=np.int64), 1)
+    assert np.all(got_kv == 0xAA) and np.all(got_ki == 0xAA)
+    c, z = synth.kv_rows(8, 35), synth.kv_rows(8, 36)
+    none = csa2.compress(bf16_dev(c[:3]), bf16_dev(z[:3]), 4)
+    assert tuple(none.shape) == (0, 512)
+    one = csa2.compress(bf16_dev(c), bf16_dev(z), 8)
+    check_compress(oracle, c, z, 8, oracle.bf16_to_f64(host(one.view(torch.int16)).view(np.uint16)))
+
+
 # ------------------------------------------------------------------ a2..a6
 def gpu_index_full(wl, layer, topk=None, pool_blocks=None):
     topk = topk or wl.topk
