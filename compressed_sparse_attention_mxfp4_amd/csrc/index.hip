@@ -36,6 +36,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "fp4.h"
 
 // Every multiply and add of the score is its own binary32 operation: no
 // multiply-add contraction anywhere in this file.
@@ -1095,6 +1096,11 @@ struct SelectArgs {
   int32_t* out_pool;         // full: [B][T][pool_blocks]
   int32_t* out_pool_n;       // full: [B][T]
   const uint32_t* hist;      // [B][T][2][1024]: level-1 counts of entry scores, block maxima
+  // full, optional: the step's cache write, done by workgroup 0 before its selection
+  const uint16_t* wr_rows;   // [wr_n][512] bf16
+  const int64_t* wr_slots;   // [wr_n]
+  uint8_t* wr_pool;          // [wr_pages][18432]
+  int64_t wr_n, wr_pages;
 };
 
 // One workgroup per (b, t).  FULL: select the pool from block maxima, then
@@ -1105,6 +1111,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   const int row = blockIdx.x;  // b * T + t
   const int tid = (int)threadIdx.x;
+  if (FULL && row == 0 && a.wr_n > 0) {
+    // FP4 cache write of wr_n rows, 32 threads (16-channel groups) per row: whole rows per
+    // wave, so the four lanes of each scale dword are active together.  Nothing the indexer
+    // reads is written; the attention that reads these entries runs after this kernel.
+    for (int64_t t = tid; t < a.wr_n * 32; t += kSelThreads) {
+      const int64_t r = t >> 5;
+      const int g = (int)(t & 31);
+      const v4u* src = reinterpret_cast<const v4u*>(a.wr_rows + r * kD + g * 16);
+      const v4u x0 = src[0], x1 = src[1];
+      const uint32_t h[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const int64_t s = a.wr_slots[r];
+      store_fp4_group(fp4_group(h), g, s >= 0 && s < a.wr_pages * kPage, s, a.wr_pool);
+    }
+  }
   const int b = row / a.T;
   int n = min(a.n_entries[b], min(a.max_n, a.max_pages * kPage));
   n = max(n, 0);
@@ -1276,7 +1296,9 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
                     const int32_t* page_table, int32_t max_pages, const int32_t* n_entries,
                     int32_t max_n_entries, int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
                     int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws, size_t ws_bytes,
-                    csa2_stream_t stream) {
+                    csa2_stream_t stream, const uint16_t* wr_rows = nullptr, int64_t wr_n = 0,
+                    const int64_t* wr_slots = nullptr, uint8_t* wr_pool = nullptr,
+                    int64_t wr_pages = 0) {
   int st = check_index_common(q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T,
                               HI, topk, pool_blocks);
   if (st) return st;
@@ -1319,6 +1341,11 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
   se.out_pool = out_pool;
   se.out_pool_n = out_pool_n;
   se.hist = sa.hist;
+  se.wr_rows = wr_rows;
+  se.wr_slots = wr_slots;
+  se.wr_pool = wr_pool;
+  se.wr_n = wr_n;
+  se.wr_pages = wr_pages;
   CSA2_LAUNCH(CSA2_K_SELECT_FULL, csa2::select_kernel<true>, dim3(B * T), dim3(csa2::kSelThreads),
               (hipStream_t)stream, se);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
@@ -1413,4 +1440,23 @@ extern "C" int csa2_index_reindex_mxfp4(const uint8_t* q_idx, const float* w, co
                                         csa2_stream_t stream) {
   return index_reindex_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, B, T, HI, pool,
                             pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_write(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                                     int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                     const int32_t* n_entries, int32_t max_n_entries, int32_t B,
+                                     int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                     int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n,
+                                     const uint16_t* kv_bf16, int64_t rows, const int64_t* dst_slot,
+                                     uint8_t* kv_pool, int64_t kv_pages, void* ws, size_t ws_bytes,
+                                     csa2_stream_t stream) {
+  if (rows < 0 || kv_pages < 0) return CSA2_ERR_INVALID_ARG;
+  if (rows > CSA2_MAX_WRITE_ROWS) return CSA2_ERR_UNSUPPORTED;
+  if (rows > 0 && (!kv_bf16 || !dst_slot || !kv_pool || ((uintptr_t)kv_bf16 & 15) ||
+                   ((uintptr_t)kv_pool & 7)))
+    return CSA2_ERR_INVALID_ARG;
+  if (kv_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries,
+                         max_n_entries, B, T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n,
+                         ws, ws_bytes, stream, kv_bf16, rows, dst_slot, kv_pool, kv_pages);
 }

@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 104
+    assert L.csa2_abi_version() == 105
 
 
 def test_workspace_sizes(L):
@@ -160,6 +160,19 @@ def test_compress_argument_errors(L):
     assert L.csa2_compress(None, X, 8, 4, X, None) == INVALID
     assert L.csa2_compress(X, X, 8, 4, ctypes.c_void_p(0x1008), None) == INVALID   # misaligned output
     assert L.csa2_compress(None, None, 3, 4, None, None) == OK       # no complete group, nothing launched
+
+
+def test_index_full_write_argument_errors(L):
+    def call(kv=X, rows=4, slot=X, pool=X, kv_pages=1, B=1):
+        return L.csa2_index_full_write(X, X, X, 1, X, 1, X, 64, B, 1, 4, 8, 16, X, X, X,
+                                       kv, rows, slot, pool, kv_pages, X, 1 << 30, None)
+    assert call(rows=-1) == INVALID
+    assert call(kv_pages=-1) == INVALID
+    assert call(kv=None) == INVALID
+    assert call(pool=None) == INVALID
+    assert call(kv=ctypes.c_void_p(0x1008)) == INVALID            # rows must be 16-byte aligned
+    assert call(rows=1025) == UNSUPPORTED
+    assert call(rows=0, kv=None, slot=None, pool=None, B=0) == INVALID   # then the indexer's own checks
 
 
 def test_binding_refuses_cpu_tensors():
