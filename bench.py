@@ -261,13 +261,11 @@ def main():
 
     def step(i, strm):
         c = i % args.copies
-        # E4M3 keys: the cache write rides in the indexer's launches (csa2_index_full_write);
-        # it must land before the attention, which reads the new entries
-        if mx:
-            csa2.quantize_kv(new_rows, new_slots, kvp[c], stream=strm)
+        # the cache write rides in the indexer's launches (csa2_index_full[_mxfp4]_write); it
+        # lands before the attention, which reads the new entries
         csa2.index_full(q_idx, w, kidx[c], pt, ne, wl.max_n, wl.topk, wl.pool_blocks, out_topk=out_topk,
                         out_pool=out_pool, out_pool_n=out_pool_n, ws=ws_i, stream=strm, mxfp4=mx,
-                        write=None if mx else (new_rows, new_slots, kvp[c]))
+                        write=(new_rows, new_slots, kvp[c]))
         csa2.sparse_attn(q, wl.sm_scale, kvp[c], pt, ne, out_topk, swa, out=out, ws=ws_a, stream=strm)
 
     for i in range(args.warmup):
@@ -280,8 +278,6 @@ def main():
     # ---- pass 1: per-kernel durations (eager launches, event pair around each launch)
     kernels = {"score_full": csa2.K_SCORE_FULL, "select_full": csa2.K_SELECT_FULL,
                "attn_split": csa2.K_ATTN_SPLIT, "attn_combine": csa2.K_ATTN_COMBINE}
-    if mx:
-        kernels["quantize"] = csa2.K_QUANTIZE
     pairs = {name: (ev.create(K), ev.create(K)) for name in kernels}
     torch.cuda.synchronize()
     for i in range(K):

@@ -35,7 +35,7 @@ EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
     "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
-    "csa2_rope_write_caches", "csa2_compress", "csa2_index_full_write",
+    "csa2_rope_write_caches", "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
 )
 
 # kernel ids for csa2_time_kernel
@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH):
                                      sz, P]
     L.csa2_index_full_mxfp4.argtypes = L.csa2_index_full.argtypes
     L.csa2_index_full_write.argtypes = L.csa2_index_full.argtypes[:16] + [P, i64, P, P, i64, P, sz, P]
+    L.csa2_index_full_mxfp4_write.argtypes = L.csa2_index_full_write.argtypes
     L.csa2_index_reindex_mxfp4.argtypes = L.csa2_index_reindex.argtypes
     L.csa2_sparse_attn.argtypes = [P, ctypes.c_float, P, i64, P, i32, P, P, i32, P, i32, i32, i32,
                                    P, P, P, sz, P]
@@ -90,7 +91,7 @@ def load(path: str = LIB_PATH):
     L.csa2_test_keep_histograms.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
                "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches",
-               "csa2_compress", "csa2_index_full_write"):
+               "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -230,7 +231,7 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, 
     kidx_pool [P,64,128] uint8 E4M3 keys (or, with mxfp4=True, [P,4352] uint8 in
     the MXFP4 page layout), page_table [B,max_pages] int32, n_entries [B] int32.
     write=(kv_bf16 [R,512] bf16, dst_slot [R] int64, kv_pool [P',18432] uint8): the
-    step's FP4 cache write done in the same launches (E4M3 keys only)."""
+    step's FP4 cache write done in the same launches."""
     torch = _torch()
     B, T, HI, _ = q_idx.shape
     dev = q_idx.device
@@ -252,15 +253,13 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, 
         _ptr(out_pool_n, torch.int32, "out_pool_n", (B, T), 2))
     tail = (ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream))
     if write is not None:
-        if mxfp4:
-            raise ValueError("the fused cache write is built for E4M3 indexer keys")
         kv_bf16, dst_slot, kv_pool = write
         R = kv_bf16.shape[0]
         wargs = (_ptr(kv_bf16, torch.bfloat16, "kv_bf16", (R, D), 2), R,
                  _ptr(dst_slot, torch.int64, "dst_slot", (R,), 1),
                  _ptr(kv_pool, torch.uint8, "kv_pool", (None, PAGE_BYTES), 2), kv_pool.shape[0])
-        name = "csa2_index_full_write"
-        st = lib().csa2_index_full_write(*args, *wargs, *tail)
+        name = "csa2_index_full_mxfp4_write" if mxfp4 else "csa2_index_full_write"
+        st = getattr(lib(), name)(*args, *wargs, *tail)
     else:
         name = "csa2_index_full_mxfp4" if mxfp4 else "csa2_index_full"
         st = getattr(lib(), name)(*args, *tail)

@@ -33,7 +33,7 @@ extern "C" const char* csa2_status_str(int status) {
   }
 }
 
-extern "C" int csa2_abi_version(void) { return 105; }
+extern "C" int csa2_abi_version(void) { return 106; }
 
 namespace csa2 {
 KernelEvents& kernel_events(int kernel) {

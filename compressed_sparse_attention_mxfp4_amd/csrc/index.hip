@@ -1442,21 +1442,42 @@ extern "C" int csa2_index_reindex_mxfp4(const uint8_t* q_idx, const float* w, co
                             pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
 }
 
-extern "C" int csa2_index_full_write(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
-                                     int64_t n_pages, const int32_t* page_table, int32_t max_pages,
-                                     const int32_t* n_entries, int32_t max_n_entries, int32_t B,
-                                     int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
-                                     int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n,
-                                     const uint16_t* kv_bf16, int64_t rows, const int64_t* dst_slot,
-                                     uint8_t* kv_pool, int64_t kv_pages, void* ws, size_t ws_bytes,
-                                     csa2_stream_t stream) {
+static int index_full_write_impl(bool mx, const uint8_t* q_idx, const float* w,
+                                 const uint8_t* kidx_pool, int64_t n_pages,
+                                 const int32_t* page_table, int32_t max_pages,
+                                 const int32_t* n_entries, int32_t max_n_entries, int32_t B,
+                                 int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                 int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n,
+                                 const uint16_t* kv_bf16, int64_t rows, const int64_t* dst_slot,
+                                 uint8_t* kv_pool, int64_t kv_pages, void* ws, size_t ws_bytes,
+                                 csa2_stream_t stream) {
   if (rows < 0 || kv_pages < 0) return CSA2_ERR_INVALID_ARG;
   if (rows > CSA2_MAX_WRITE_ROWS) return CSA2_ERR_UNSUPPORTED;
   if (rows > 0 && (!kv_bf16 || !dst_slot || !kv_pool || ((uintptr_t)kv_bf16 & 15) ||
                    ((uintptr_t)kv_pool & 7)))
     return CSA2_ERR_INVALID_ARG;
   if (kv_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
-  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries,
+  return index_full_impl(mx, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries,
                          max_n_entries, B, T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n,
                          ws, ws_bytes, stream, kv_bf16, rows, dst_slot, kv_pool, kv_pages);
+}
+
+#define CSA2_INDEX_FULL_WRITE_PARAMS                                                            \
+  const uint8_t *q_idx, const float *w, const uint8_t *kidx, int64_t n_pages,                   \
+      const int32_t *page_table, int32_t max_pages, const int32_t *n_entries,                   \
+      int32_t max_n_entries, int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks, \
+      int32_t *out_topk, int32_t *out_pool, int32_t *out_pool_n, const uint16_t *kv_bf16,       \
+      int64_t rows, const int64_t *dst_slot, uint8_t *kv_pool, int64_t kv_pages, void *ws,       \
+      size_t ws_bytes, csa2_stream_t stream
+#define CSA2_INDEX_FULL_WRITE_ARGS                                                              \
+  q_idx, w, kidx, n_pages, page_table, max_pages, n_entries, max_n_entries, B, T, HI, topk,     \
+      pool_blocks, out_topk, out_pool, out_pool_n, kv_bf16, rows, dst_slot, kv_pool, kv_pages,  \
+      ws, ws_bytes, stream
+
+extern "C" int csa2_index_full_write(CSA2_INDEX_FULL_WRITE_PARAMS) {
+  return index_full_write_impl(false, CSA2_INDEX_FULL_WRITE_ARGS);
+}
+
+extern "C" int csa2_index_full_mxfp4_write(CSA2_INDEX_FULL_WRITE_PARAMS) {
+  return index_full_write_impl(true, CSA2_INDEX_FULL_WRITE_ARGS);
 }

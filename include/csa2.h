@@ -197,7 +197,8 @@ int csa2_index_full(const uint8_t *q_idx, const float *w, const uint8_t *kidx_po
  * entries (csa2_sparse_attn) launched after this call on the same stream sees
  * them, so the results equal the two calls in sequence; the step saves one
  * kernel launch.  Arguments as csa2_index_full and csa2_quantize_kv (rows
- * whose slot lies outside the pool are skipped), E4M3 indexer keys.
+ * whose slot lies outside the pool are skipped); csa2_index_full_mxfp4_write
+ * takes the indexer keys in the MXFP4 layout of csa2_index_full_mxfp4.
  * Returns CSA2_ERR_INVALID_ARG for rows < 0, kv_pages < 0, or (rows > 0) a
  * null or misaligned row or pool pointer; CSA2_ERR_UNSUPPORTED for rows >
  * CSA2_MAX_WRITE_ROWS; otherwise as csa2_index_full.
@@ -209,6 +210,14 @@ int csa2_index_full_write(const uint8_t *q_idx, const float *w, const uint8_t *k
                           int32_t *out_pool, int32_t *out_pool_n, const uint16_t *kv_bf16,
                           int64_t rows, const int64_t *dst_slot, uint8_t *kv_pool,
                           int64_t kv_pages, void *ws, size_t ws_bytes, csa2_stream_t stream);
+int csa2_index_full_mxfp4_write(const uint8_t *q_idx, const float *w, const uint8_t *kidx_mx,
+                                int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                                const int32_t *n_entries, int32_t max_n_entries, int32_t B,
+                                int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                int32_t *out_topk, int32_t *out_pool, int32_t *out_pool_n,
+                                const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_slot,
+                                uint8_t *kv_pool, int64_t kv_pages, void *ws, size_t ws_bytes,
+                                csa2_stream_t stream);
 
 /*
  * Reindex mode.  Knowledge note, "Hierarchical Sparse Indexer": later

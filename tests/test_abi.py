@@ -45,7 +45,7 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 105
+    assert L.csa2_abi_version() == 106
 
 
 def test_workspace_sizes(L):

@@ -354,19 +354,25 @@ def test_index_full_ragged(oracle, T, HI, topk):
     assert_index_equal(got, oracle_index_full(oracle, wl, wl.layers[0]))
 
 
-def test_index_full_with_fused_cache_write(oracle):
-    say("index_full_write: Full indexer with the step's cache write in the same launches")
+@pytest.mark.parametrize("mx", [False, True])
+def test_index_full_with_fused_cache_write(oracle, mx):
+    say(f"index_full{'_mxfp4' if mx else ''}_write: Full indexer with the step's cache write in the same launches")
     wl = small_workload([30000, 12345], T=2, HI=32, topk=1024, seed=12)
     L = wl.layers[0]
+    keys = synth.mxfp4_key_pool(wl.paging.n_pages, 14) if mx else wl.kidx_pool
     rows = synth.kv_rows(37, 13, outlier_frac=0.02)       # 37 rows: a partial last wave
     n_pages = wl.paging.n_pages
     slots = np.random.default_rng(4).permutation(n_pages * 64)[:37].astype(np.int64)
     slots[3] = -1
     kv = torch.full((n_pages, csa2.PAGE_BYTES), 0xAA, dtype=torch.uint8, device="cuda")
-    tk, pl, pn = csa2.index_full(dev(L.q_idx), dev(L.w), dev(wl.kidx_pool), dev(wl.paging.page_table),
-                                 dev(wl.n_entries), wl.max_n, wl.topk, wl.pool_blocks,
+    tk, pl, pn = csa2.index_full(dev(L.q_idx), dev(L.w), dev(keys), dev(wl.paging.page_table),
+                                 dev(wl.n_entries), wl.max_n, wl.topk, wl.pool_blocks, mxfp4=mx,
                                  write=(bf16_dev(rows), dev(slots), kv))
-    r_tk, r_pool, r_pn = oracle_index_full(oracle, wl, L)
+    if mx:
+        r_tk, r_pool, r_pn = oracle.index_full_mxfp4(L.q_idx, L.w, keys, wl.paging.page_table, wl.n_entries,
+                                                     wl.topk, wl.pool_blocks)
+    else:
+        r_tk, r_pool, r_pn = oracle_index_full(oracle, wl, L)
     assert np.array_equal(host(tk), r_tk) and np.array_equal(host(pl), r_pool) and np.array_equal(host(pn), r_pn)
     ref = np.full((n_pages, oracle.PAGE_BYTES), 0xAA, np.uint8)
     oracle.quantize_kv(rows, slots, ref)
