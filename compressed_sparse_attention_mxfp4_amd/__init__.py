@@ -21,6 +21,7 @@ __all__ = [
     "Csa2Error", "lib", "load", "quantize_kv", "index_full", "index_reindex", "sparse_attn",
     "workspace_bytes", "status_str", "Workspace", "D", "DI", "PAGE", "PAGE_BYTES",
     "KIDX_PAGE_BYTES", "BLOCK", "SWA", "OP_INDEX_FULL", "OP_INDEX_REINDEX", "OP_SPARSE_ATTN",
+    "index_full_noalloc", "NOALLOC_SCRATCH_BYTES", "ERR_SCRATCH",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,12 +31,15 @@ D, DI, PAGE, BLOCK, SWA = 512, 128, 64, 8, 128
 PAGE_BYTES, KIDX_PAGE_BYTES = 18432, 8192
 MX_KIDX_PAGE_BYTES = 4352  # MXFP4 indexer keys: 64 x 64 code bytes + 64 x 4 E8M0 scales
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_SPARSE_ATTN = 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 32 << 20  # csa2_index_full_noalloc's fixed per-GPU scratch
+ERR_SCRATCH = -5
 
 EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
     "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
     "csa2_rope_write_caches", "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
+    "csa2_index_full_noalloc",
 )
 
 # kernel ids for csa2_time_kernel
@@ -78,6 +82,7 @@ def load(path: str = LIB_PATH):
     L.csa2_index_full_write.argtypes = L.csa2_index_full.argtypes[:16] + [P, i64, P, P, i64, P, sz, P]
     L.csa2_index_full_mxfp4_write.argtypes = L.csa2_index_full_write.argtypes
     L.csa2_index_reindex_mxfp4.argtypes = L.csa2_index_reindex.argtypes
+    L.csa2_index_full_noalloc.argtypes = L.csa2_index_full.argtypes[:16] + [P]
     L.csa2_sparse_attn.argtypes = [P, ctypes.c_float, P, i64, P, i32, P, P, i32, P, i32, i32, i32,
                                    P, P, P, sz, P]
     L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32]
@@ -91,7 +96,8 @@ def load(path: str = LIB_PATH):
     L.csa2_test_keep_histograms.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
                "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches",
-               "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write"):
+               "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
+               "csa2_index_full_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -264,6 +270,31 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, 
         name = "csa2_index_full_mxfp4" if mxfp4 else "csa2_index_full"
         st = getattr(lib(), name)(*args, *tail)
     _check(name, st)
+    return out_topk, out_pool, out_pool_n
+
+
+def index_full_noalloc(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, pool_blocks=2048,
+                       out_topk=None, out_pool=None, out_pool_n=None, stream=None):
+    """index_full through csa2_index_full_noalloc: no workspace argument, the library's fixed
+    per-GPU scratch instead (E4M3 keys)."""
+    torch = _torch()
+    B, T, HI, _ = q_idx.shape
+    dev = q_idx.device
+    if out_topk is None:
+        out_topk = torch.empty((B, T, topk), dtype=torch.int32, device=dev)
+    if out_pool is None:
+        out_pool = torch.empty((B, T, pool_blocks), dtype=torch.int32, device=dev)
+    if out_pool_n is None:
+        out_pool_n = torch.empty((B, T), dtype=torch.int32, device=dev)
+    st = lib().csa2_index_full_noalloc(
+        _ptr(q_idx, torch.uint8, "q_idx", (B, T, HI, DI), 4), _ptr(w, torch.float32, "w", (B, T, HI), 3),
+        _kidx_arg(kidx_pool, False), kidx_pool.shape[0],
+        _ptr(page_table, torch.int32, "page_table", (B, None), 2), page_table.shape[1],
+        _ptr(n_entries, torch.int32, "n_entries", (B,), 1), int(max_n_entries), B, T, HI, int(topk),
+        int(pool_blocks), _ptr(out_topk, torch.int32, "out_topk", (B, T, topk), 3),
+        _ptr(out_pool, torch.int32, "out_pool", (B, T, pool_blocks), 3),
+        _ptr(out_pool_n, torch.int32, "out_pool_n", (B, T), 2), _stream(stream))
+    _check("csa2_index_full_noalloc", st)
     return out_topk, out_pool, out_pool_n
 
 

@@ -29,11 +29,12 @@ extern "C" const char* csa2_status_str(int status) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported size or shape";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_LAUNCH: return "kernel launch failed";
+    case CSA2_ERR_SCRATCH: return "request exceeds the fixed scratch of the no-allocation call";
     default: return "unknown status";
   }
 }
 
-extern "C" int csa2_abi_version(void) { return 106; }
+extern "C" int csa2_abi_version(void) { return 107; }
 
 namespace csa2 {
 KernelEvents& kernel_events(int kernel) {

@@ -34,6 +34,7 @@
 // 4) .. +15 of a 64-deep int8 slice); the 4 outputs of lane l are rows
 // 4*(l >> 4) + i, column l & 15.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "fp4.h"
@@ -1480,4 +1481,52 @@ extern "C" int csa2_index_full_write(CSA2_INDEX_FULL_WRITE_PARAMS) {
 
 extern "C" int csa2_index_full_mxfp4_write(CSA2_INDEX_FULL_WRITE_PARAMS) {
   return index_full_write_impl(true, CSA2_INDEX_FULL_WRITE_ARGS);
+}
+
+// ---------------------------------------------------------------- no allocation
+// csa2_index_full with its workspace in a fixed library-owned device array,
+// for callers that cannot allocate.  In host code `scratch` names a host-side
+// stand-in, not the device copy: its device address is looked up once per
+// GPU (with that GPU current) and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of the current GPU's copy of `scratch`.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return CSA2_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CSA2_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+}  // namespace
+
+extern "C" int csa2_index_full_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                                       int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                       const int32_t* n_entries, int32_t max_n_entries, int32_t B,
+                                       int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                       int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n,
+                                       csa2_stream_t stream) {
+  int st = check_index_common(q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T, HI,
+                              topk, pool_blocks);
+  if (st) return st;
+  if (!out_topk || !out_pool || !out_pool_n || max_n_entries <= 0) return CSA2_ERR_INVALID_ARG;
+  if (max_n_entries > CSA2_MAX_ENTRIES) return CSA2_ERR_UNSUPPORTED;
+  if (csa2_index_ws_bytes(CSA2_OP_INDEX_FULL, B, T, max_n_entries, pool_blocks) > CSA2_NOALLOC_SCRATCH_BYTES)
+    return CSA2_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st) return st;
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+                         T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws,
+                         CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }

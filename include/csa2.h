@@ -63,13 +63,15 @@ extern "C" {
 #define CSA2_MAX_INDEX_HEADS 64    /* indexer heads HI */
 #define CSA2_MAX_T 4               /* decode query tokens per sequence */
 #define CSA2_MAX_WRITE_ROWS 1024   /* rows of the cache write fused into csa2_index_full_write */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20) /* fixed per-GPU scratch of csa2_index_full_noalloc */
 
 enum csa2_status {
   CSA2_OK = 0,
   CSA2_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, k > limit */
   CSA2_ERR_UNSUPPORTED = -2, /* a size outside what the kernels are built for */
   CSA2_ERR_WORKSPACE = -3,   /* ws NULL or ws_bytes below csa2_workspace_bytes */
-  CSA2_ERR_LAUNCH = -4       /* the HIP launch reported an error */
+  CSA2_ERR_LAUNCH = -4,      /* the HIP launch reported an error */
+  CSA2_ERR_SCRATCH = -5      /* a no-allocation call needs more than its fixed scratch */
 };
 
 enum csa2_op {
@@ -218,6 +220,30 @@ int csa2_index_full_mxfp4_write(const uint8_t *q_idx, const float *w, const uint
                                 const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_slot,
                                 uint8_t *kv_pool, int64_t kv_pages, void *ws, size_t ws_bytes,
                                 csa2_stream_t stream);
+
+/*
+ * csa2_index_full for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, outputs, errors and kernels, without the workspace
+ * argument.  The workspace lives in a library-owned device array of
+ * CSA2_NOALLOC_SCRATCH_BYTES, one copy per GPU, looked up on the first call
+ * on that GPU (the caller's current device) and held until the process ends.
+ * The call allocates nothing and calls no allocating routine.  Every call on
+ * one GPU uses that GPU's one array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller;
+ * calls in sequence on one stream are safe.  Nothing in the array needs to
+ * start at zero: each call writes every part it later reads.
+ * Returns CSA2_ERR_SCRATCH (before anything is enqueued) when
+ * csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, T, HI, max_n_entries, topk)
+ * exceeds CSA2_NOALLOC_SCRATCH_BYTES (e.g. B * T = 4 at 262,144 entries fits),
+ * CSA2_ERR_LAUNCH if the array's address cannot be found; otherwise as
+ * csa2_index_full.
+ */
+int csa2_index_full_noalloc(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
+                            int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *n_entries, int32_t max_n_entries, int32_t B, int32_t T,
+                            int32_t HI, int32_t topk, int32_t pool_blocks, int32_t *out_topk,
+                            int32_t *out_pool, int32_t *out_pool_n, csa2_stream_t stream);
 
 /*
  * Reindex mode.  Knowledge note, "Hierarchical Sparse Indexer": later

@@ -45,7 +45,8 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 106
+    assert L.csa2_abi_version() == 107
+    assert "scratch" in csa2.status_str(csa2.ERR_SCRATCH)
 
 
 def test_workspace_sizes(L):
@@ -80,6 +81,23 @@ def test_index_full_argument_errors(L):
     assert _full(L, max_n=0) == INVALID
     assert _full(L, ws=None) == WORKSPACE
     assert _full(L, ws_bytes=16) == WORKSPACE
+
+
+def test_index_full_noalloc_argument_errors(L):
+    """The no-allocation call checks as csa2_index_full, then refuses what its fixed scratch cannot hold,
+    all before anything is launched."""
+    def call(q=X, max_n=64, B=1, T=1, HI=4, topk=8, pool_blocks=16, ot=X):
+        return L.csa2_index_full_noalloc(q, X, X, 1, X, 1, X, max_n, B, T, HI, topk, pool_blocks, ot, X, X, None)
+    assert call(q=None) == INVALID
+    assert call(ot=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(max_n=0) == INVALID
+    assert call(HI=6) == UNSUPPORTED
+    assert call(max_n=262145) == UNSUPPORTED
+    need = lambda B, T: csa2.workspace_bytes(csa2.OP_INDEX_FULL, B, T, 64, 262144, 2048)
+    assert need(4, 1) <= csa2.NOALLOC_SCRATCH_BYTES            # the 1M-context batch of 4 fits
+    assert need(32, 2) > csa2.NOALLOC_SCRATCH_BYTES
+    assert call(max_n=262144, B=32, T=2, HI=64, topk=2048, pool_blocks=2048) == csa2.ERR_SCRATCH
 
 
 def _reindex(L, q=X, pool=X, P=16, topk=8, HI=4, T=1, ws=X, ws_bytes=1 << 30):
