@@ -39,7 +39,7 @@ EXPORTS = (
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
     "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
     "csa2_rope_write_caches", "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
-    "csa2_index_full_noalloc",
+    "csa2_index_full_noalloc", "csa2_index_full_causal", "csa2_index_reindex_causal",
 )
 
 # kernel ids for csa2_time_kernel
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
     L.csa2_index_full_mxfp4_write.argtypes = L.csa2_index_full_write.argtypes
     L.csa2_index_reindex_mxfp4.argtypes = L.csa2_index_reindex.argtypes
     L.csa2_index_full_noalloc.argtypes = L.csa2_index_full.argtypes[:16] + [P]
+    L.csa2_index_full_causal.argtypes = L.csa2_index_full.argtypes[:7] + [P] + L.csa2_index_full.argtypes[7:]
+    L.csa2_index_reindex_causal.argtypes = L.csa2_index_reindex.argtypes[:7] + [P] + L.csa2_index_reindex.argtypes[7:]
     L.csa2_sparse_attn.argtypes = [P, ctypes.c_float, P, i64, P, i32, P, P, i32, P, i32, i32, i32,
                                    P, P, P, sz, P]
     L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32]
@@ -97,7 +99,7 @@ def load(path: str = LIB_PATH):
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
                "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches",
                "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
-               "csa2_index_full_noalloc"):
+               "csa2_index_full_noalloc", "csa2_index_full_causal", "csa2_index_reindex_causal"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -232,12 +234,13 @@ def _kidx_arg(kidx_pool, mxfp4):
 
 def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, pool_blocks=2048,
                out_topk=None, out_pool=None, out_pool_n=None, ws=None, stream=None, mxfp4=False,
-               write=None):
+               write=None, n_visible=None):
     """Full-mode indexer.  q_idx [B,T,HI,128] uint8 (E4M3), w [B,T,HI] float32,
     kidx_pool [P,64,128] uint8 E4M3 keys (or, with mxfp4=True, [P,4352] uint8 in
     the MXFP4 page layout), page_table [B,max_pages] int32, n_entries [B] int32.
     write=(kv_bf16 [R,512] bf16, dst_slot [R] int64, kv_pool [P',18432] uint8): the
-    step's FP4 cache write done in the same launches."""
+    step's FP4 cache write done in the same launches.
+    n_visible [B,T] int32: per-token causal visible counts (csa2_index_full_causal)."""
     torch = _torch()
     B, T, HI, _ = q_idx.shape
     dev = q_idx.device
@@ -258,7 +261,13 @@ def index_full(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries, topk, 
         _ptr(out_pool, torch.int32, "out_pool", (B, T, pool_blocks), 3),
         _ptr(out_pool_n, torch.int32, "out_pool_n", (B, T), 2))
     tail = (ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream))
-    if write is not None:
+    if n_visible is not None:
+        if write is not None or mxfp4:
+            raise ValueError("n_visible goes with E4M3 keys and no fused cache write")
+        nv = _ptr(n_visible, torch.int32, "n_visible", (B, T), 2)
+        name = "csa2_index_full_causal"
+        st = lib().csa2_index_full_causal(*args[:7], nv, *args[7:], *tail)
+    elif write is not None:
         kv_bf16, dst_slot, kv_pool = write
         R = kv_bf16.shape[0]
         wargs = (_ptr(kv_bf16, torch.bfloat16, "kv_bf16", (R, D), 2), R,
@@ -299,8 +308,9 @@ def index_full_noalloc(q_idx, w, kidx_pool, page_table, n_entries, max_n_entries
 
 
 def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool, pool_n, topk, out_topk=None,
-                  ws=None, stream=None, mxfp4=False):
-    """Reindex-mode indexer over the pool written by index_full (keys as for index_full)."""
+                  ws=None, stream=None, mxfp4=False, n_visible=None):
+    """Reindex-mode indexer over the pool written by index_full (keys as for index_full);
+    n_visible [B,T] int32: per-token causal visible counts (csa2_index_reindex_causal)."""
     torch = _torch()
     B, T, HI, _ = q_idx.shape
     P = pool.shape[2]
@@ -308,16 +318,23 @@ def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool, pool_n, topk
         out_topk = torch.empty((B, T, topk), dtype=torch.int32, device=q_idx.device)
     nb = workspace_bytes(OP_INDEX_REINDEX, B, T, HI, 0, topk)
     buf = _ws(ws, nb)
-    fn = lib().csa2_index_reindex_mxfp4 if mxfp4 else lib().csa2_index_reindex
-    st = fn(
-        _ptr(q_idx, torch.uint8, "q_idx", (B, T, HI, DI), 4), _ptr(w, torch.float32, "w", (B, T, HI), 3),
-        _kidx_arg(kidx_pool, mxfp4), kidx_pool.shape[0],
-        _ptr(page_table, torch.int32, "page_table", (B, None), 2), page_table.shape[1],
-        _ptr(n_entries, torch.int32, "n_entries", (B,), 1), B, T, HI,
+    head = (_ptr(q_idx, torch.uint8, "q_idx", (B, T, HI, DI), 4), _ptr(w, torch.float32, "w", (B, T, HI), 3),
+            _kidx_arg(kidx_pool, mxfp4), kidx_pool.shape[0],
+            _ptr(page_table, torch.int32, "page_table", (B, None), 2), page_table.shape[1],
+            _ptr(n_entries, torch.int32, "n_entries", (B,), 1))
+    if n_visible is not None:
+        if mxfp4:
+            raise ValueError("n_visible goes with E4M3 keys")
+        name = "csa2_index_reindex_causal"
+        head = head + (_ptr(n_visible, torch.int32, "n_visible", (B, T), 2),)
+    else:
+        name = "csa2_index_reindex_mxfp4" if mxfp4 else "csa2_index_reindex"
+    st = getattr(lib(), name)(
+        *head, B, T, HI,
         _ptr(pool, torch.int32, "pool", (B, T, P), 3), _ptr(pool_n, torch.int32, "pool_n", (B, T), 2),
         P, int(topk), _ptr(out_topk, torch.int32, "out_topk", (B, T, topk), 3),
         ctypes.c_void_p(buf.data_ptr()), buf.numel(), _stream(stream))
-    _check("csa2_index_reindex_mxfp4" if mxfp4 else "csa2_index_reindex", st)
+    _check(name, st)
     return out_topk
 
 

@@ -56,6 +56,9 @@ constexpr int kMaxWaveChunks = 1024;         // chunks one wave may take in one 
 constexpr int kMaxWgChunks = 1016;
 // Level-1 histogram of the selections: score keys by their top 10 bits.
 constexpr int kHistBins = 1024;
+// Full mode: a workgroup scores the keys for a group of at most 4 query
+// tokens of one sequence (each token's query limbs and histograms in LDS)
+constexpr int kGroupT = 4;
 // MXFP4 indexer keys: per page 64 entries x 64 code bytes (channel 2i in the
 // low nibble of byte i), then 64 x 4 E8M0 scale bytes (byte g: channels
 // 32g .. 32g + 31)
@@ -173,12 +176,14 @@ struct ScoreArgs {
   int max_n;
   int T;
   int HI;
+  const int32_t* n_vis;   // [B][T] per-token visible entries (causal counts), or null
+  int n_groups;           // full: token groups per sequence, ceil(T / 4)
   const int32_t* pool;    // pool mode
   const int32_t* pool_n;  // pool mode
   int pool_blocks;
   float* out_s;           // full: [B][T][s_stride(max_n)]; pool: [B][T][pool_blocks*8]
   float* out_bm;          // full: [B][T][bm_stride(max_n)]
-  int rows;               // full: B; pool: B*T
+  int rows;               // full: B * n_groups; pool: B*T
   int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
   int chunks_per_wg;      // chunks of one row per workgroup
   int wg_per_row;         // workgroups per row
@@ -204,18 +209,24 @@ struct RowCtx {
   const int32_t* pool_row = nullptr;
 };
 
+// Full mode: row = b * n_groups + token group, t_full the wave's token
+// (live: the token exists; the dead fourth slot of a group of three sees
+// nothing).  Token t of sequence b sees its first min(n_entries[b],
+// n_vis[b][t]) entries.
 template <bool POOL>
-__device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full, RowCtx& r) {
+__device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full, bool live, RowCtx& r) {
   if (POOL) {
     r.b = row / a.T;
     r.t = row % a.T;
   } else {
-    r.b = row;
+    r.b = row / a.n_groups;
     r.t = t_full;
   }
   int n = a.n_entries[r.b];
   n = min(n, a.max_n);
   n = max(0, min(n, a.max_pages * kPage));
+  if (a.n_vis != nullptr) n = max(0, min(n, a.n_vis[(int64_t)r.b * a.T + r.t]));
+  if (!live) n = 0;
   r.n = n;
   if (POOL) {
     r.pool_row = a.pool + (int64_t)row * a.pool_blocks;
@@ -477,40 +488,47 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   struct __attribute__((aligned(16))) Lds {
     // per token: the f16 limbs ql, qm of the query, in the order the waves
     // hold them: [row tile][slice][limb][lane]
-    v8h qlimb[CSA2_MAX_T][kRT][4][2][64];
-    float wsh[CSA2_MAX_T][kRT * 16];              // w * 2^-9 per head, 0 past HI
-    uint32_t qbad[CSA2_MAX_T];                    // nonzero: some |q| >= 32
+    v8h qlimb[kGroupT][kRT][4][2][64];
+    float wsh[kGroupT][kRT * 16];                 // w * 2^-9 per head, 0 past HI
+    uint32_t qbad[kGroupT];                       // nonzero: some |q| >= 32
     uint32_t defer[kWaves][kMaxWaveChunks / 32];  // chunks left to the general path
     // per token: level-1 histograms of entry scores and block maxima,
     // 16-bit counters packed two per word
-    uint32_t hist[CSA2_MAX_T][2][kHistBins / 2];
+    uint32_t hist[kGroupT][2][kHistBins / 2];
   };
   __shared__ Lds sm;
 
   for (int i = threadIdx.x; i < kWaves * kMaxWaveChunks / 32; i += blockDim.x) (&sm.defer[0][0])[i] = 0u;
-  for (int i = threadIdx.x; i < CSA2_MAX_T * kHistBins; i += blockDim.x) (&sm.hist[0][0][0])[i] = 0u;
-  if (threadIdx.x < CSA2_MAX_T) sm.qbad[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < kGroupT * kHistBins; i += blockDim.x) (&sm.hist[0][0][0])[i] = 0u;
+  if (threadIdx.x < kGroupT) sm.qbad[threadIdx.x] = 0u;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int g = lane >> 4;   // K slice group of the MFMA operands; head group of the outputs
   const int col = lane & 15;
   const int HI = a.HI;
-  const int t_full = POOL ? 0 : wave % a.T;
-  const int slice = POOL ? wave : wave / a.T;
-  const int n_slices = POOL ? kWaves : kWaves / a.T;
   const int row = blockIdx.x / a.wg_per_row;
+  // Full mode: tokens t0 .. t0 + Tg - 1 of the sequence, in Ts token slots
+  // (a group of three keeps a dead fourth slot, so that the slots divide the
+  // 8 waves); each wave takes one slot and a slice of the chunk range
+  const int t0 = POOL ? 0 : (row % a.n_groups) * kGroupT;
+  const int Tg = POOL ? 1 : min(kGroupT, a.T - t0);
+  const int Ts = Tg == 3 ? 4 : Tg;
+  const int slot = POOL ? 0 : wave % Ts;
+  const int t_full = POOL ? 0 : t0 + min(slot, Tg - 1);
+  const int slice = POOL ? wave : wave / Ts;
+  const int n_slices = POOL ? kWaves : kWaves / Ts;
   const int c0 = (blockIdx.x % a.wg_per_row) * a.chunks_per_wg;
   const int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
   const bool have_row = row < a.rows;
   int chunk = c0 + slice;
-  const bool active = have_row && chunk < c1;
-  uint32_t* hist_s = sm.hist[t_full][0];
-  uint32_t* hist_bm = sm.hist[t_full][1];
+  const bool active = have_row && chunk < c1 && slot < Tg;
+  uint32_t* hist_s = sm.hist[slot][0];
+  uint32_t* hist_bm = sm.hist[slot][1];
   RowCtx rc;
-  if (have_row) row_ctx<POOL>(a, row, t_full, rc);
+  if (have_row) row_ctx<POOL>(a, row, t_full, slot < Tg, rc);
   const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
-  const int n_tok = POOL ? 1 : a.T;
+  const int n_tok = POOL ? 1 : Ts;
 
   // ---- every load that needs nothing loaded first is issued here, ahead of
   // the keys (the wait counter retires loads in issue order): the raw query
@@ -523,7 +541,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // Limb item (token, row tile rt, slice s, lane L): head tile_head(rt, L &
   // 15), channels 16 gL + 8 s + e (s < 2) or 64 + 16 gL + 8 (s - 2) + e
   // (e < 8, gL = L >> 4), the keys' order in the slices.
-  constexpr int kLimbIters = CSA2_MAX_T * kRT * 4 * 64 / kScoreThreads;
+  constexpr int kLimbIters = kGroupT * kRT * 4 * 64 / kScoreThreads;
   const int n_items = n_tok * kRT * 4 * 64;  // 1024 n_tok, a power of two
   uint32_t qraw[kLimbIters][2], qkeep[kLimbIters];
 #pragma unroll
@@ -531,23 +549,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     const int it = (int)threadIdx.x + j * kScoreThreads;
     const int iw = it & (n_items - 1);
     const int L = iw & 63, sl = (iw >> 6) & 3, rt = (iw >> 8) & 3, tk = iw >> 10;
-    const int t = POOL ? rc.t : tk;
+    const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
     const int h = tile_head(rt, L & 15), gL = L >> 4;
     const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
         a.q_idx + (((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)) * kDI + ch);
     qraw[j][0] = src[0];
     qraw[j][1] = src[1];
-    qkeep[j] = (it < n_items && h < HI) ? 0xFFFFFFFFu : 0u;
+    qkeep[j] = (it < n_items && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
     asm volatile("" : "+v"(qkeep[j]));
   }
   uint32_t wraw, wkeep;
   {
     const int i = min((int)threadIdx.x, n_tok * 64 - 1);
     const int tk = i >> 6, h = i & 63;
-    const int t = POOL ? rc.t : tk;
+    const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
     wraw = __float_as_uint(a.w[((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)]);
-    wkeep = ((int)threadIdx.x < n_tok * 64 && h < HI) ? 0xFFFFFFFFu : 0u;
+    wkeep = ((int)threadIdx.x < n_tok * 64 && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
     asm volatile("" : "+v"(wkeep));
   }
   int page_word = -1;
@@ -563,8 +581,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // selection checks its counts against the list and then counts the list's
   // keys itself, so such a histogram costs time, not correctness.
   if (row < a.rows && a.clear_hist) {
-    const int words = (POOL ? 1 : a.T) * 2 * kHistBins;
-    uint32_t* gh = a.hist + (int64_t)(POOL ? row : row * a.T) * 2 * kHistBins;
+    const int words = Tg * 2 * kHistBins;
+    uint32_t* gh = a.hist + (POOL ? (int64_t)row : (int64_t)rc.b * a.T + t0) * 2 * kHistBins;
     const int k = blockIdx.x % a.wg_per_row;
     const int per = (words + a.wg_per_row - 1) / a.wg_per_row;
     const int w1 = min(words, (k + 1) * per);
@@ -651,12 +669,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
-      ql[rt][sl] = sm.qlimb[t_full][rt][sl][0][lane];
-      qm[rt][sl] = sm.qlimb[t_full][rt][sl][1][lane];
+      ql[rt][sl] = sm.qlimb[slot][rt][sl][0][lane];
+      qm[rt][sl] = sm.qlimb[slot][rt][sl][1][lane];
     }
-    wreg[rt] = *reinterpret_cast<const v4f*>(&sm.wsh[t_full][16 * g + 4 * rt]);
+    wreg[rt] = *reinterpret_cast<const v4f*>(&sm.wsh[slot][16 * g + 4 * rt]);
   }
-  const bool fast_q = sm.qbad[t_full] == 0u;
+  const bool fast_q = sm.qbad[slot] == 0u;
   uint32_t* my_defer = sm.defer[wave];
   int k_seq = 0;  // index of the current chunk among this wave's chunks
 
@@ -788,12 +806,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // ---- the workgroup's histograms into the row's (global, 32-bit) ones
   __syncthreads();
   if (row < a.rows) {
-    const int n_tok = POOL ? 1 : a.T;
-    for (int i = threadIdx.x; i < n_tok * kHistBins; i += blockDim.x) {
+    for (int i = threadIdx.x; i < Tg * kHistBins; i += blockDim.x) {
       const uint32_t v = (&sm.hist[0][0][0])[i];
       if (v == 0u) continue;
       const int t = i / kHistBins, h = (i / (kHistBins / 2)) & 1, wd = i % (kHistBins / 2);
-      const int64_t grow = POOL ? (int64_t)row : (int64_t)row * a.T + t;  // (b, t)
+      const int64_t grow = POOL ? (int64_t)row : (int64_t)rc.b * a.T + t0 + t;  // (b, t)
       uint32_t* gh = a.hist + (grow * 2 + h) * kHistBins + 2 * wd;
       if (v & 0xFFFFu) atomicAdd(gh, v & 0xFFFFu);
       if (v >> 16) atomicAdd(gh + 1, v >> 16);
@@ -1086,6 +1103,7 @@ struct SelectArgs {
   const float* s;        // full: [B][T][s_stride(max_n)]; reindex: [B][T][pool_blocks*8] (pool order)
   const float* bm;       // full: [B][T][bm_stride(max_n)]
   const int32_t* n_entries;
+  const int32_t* n_vis;      // [B][T] per-token visible entries, or null
   int max_n;
   int max_pages;
   int T;
@@ -1128,6 +1146,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
   const int b = row / a.T;
   int n = min(a.n_entries[b], min(a.max_n, a.max_pages * kPage));
+  if (a.n_vis != nullptr) n = min(n, a.n_vis[row]);
   n = max(n, 0);
   const int nb = (n + kBlock - 1) / kBlock;
   const int P = a.pool_blocks;
@@ -1254,7 +1273,7 @@ int check_index_common(const void* q_idx, const void* w, const void* kidx, int64
   if (topk <= 0 || topk > CSA2_MAX_TOPK || pool_blocks <= 0 || pool_blocks > CSA2_MAX_POOL_BLOCKS)
     return CSA2_ERR_INVALID_ARG;
   if (HI > CSA2_MAX_INDEX_HEADS || (HI % 4) != 0) return CSA2_ERR_UNSUPPORTED;
-  if (!(T == 1 || T == 2 || T == 4)) return CSA2_ERR_UNSUPPORTED;
+  if (T > CSA2_MAX_T) return CSA2_ERR_UNSUPPORTED;
   if (topk > pool_blocks) return CSA2_ERR_UNSUPPORTED;
   if (B > 65535 / T) return CSA2_ERR_UNSUPPORTED;
   return CSA2_OK;
@@ -1295,7 +1314,7 @@ int launch_scan(bool pool, bool mx, const csa2::ScoreArgs& sa, int T_grid, hipSt
 namespace {
 int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool, int64_t n_pages,
                     const int32_t* page_table, int32_t max_pages, const int32_t* n_entries,
-                    int32_t max_n_entries, int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                    const int32_t* n_vis, int32_t max_n_entries, int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
                     int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws, size_t ws_bytes,
                     csa2_stream_t stream, const uint16_t* wr_rows = nullptr, int64_t wr_n = 0,
                     const int64_t* wr_slots = nullptr, uint8_t* wr_pool = nullptr,
@@ -1319,20 +1338,24 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
   sa.max_n = max_n_entries;
   sa.T = T;
   sa.HI = HI;
+  sa.n_vis = n_vis;
+  sa.n_groups = (T + csa2::kGroupT - 1) / csa2::kGroupT;
   sa.out_s = reinterpret_cast<float*>(ws);
   sa.out_bm = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                        align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4));
   sa.hist = reinterpret_cast<uint32_t*>(
       reinterpret_cast<char*>(ws) + align256((size_t)B * T * csa2::s_stride(max_n_entries) * 4) +
       align256((size_t)B * T * csa2::bm_stride(max_n_entries) * 4));
-  sa.rows = B;
+  sa.rows = B * sa.n_groups;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
-  st = launch_scan(false, mx, sa, T, (hipStream_t)stream);
+  const int t_slots = T >= csa2::kGroupT ? csa2::kGroupT : (T == 3 ? 4 : T);
+  st = launch_scan(false, mx, sa, t_slots, (hipStream_t)stream);
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
   se.bm = sa.out_bm;
   se.n_entries = n_entries;
+  se.n_vis = n_vis;
   se.max_n = max_n_entries;
   se.max_pages = max_pages;
   se.T = T;
@@ -1354,7 +1377,7 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
 
 int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
                        int64_t n_pages, const int32_t* page_table, int32_t max_pages, const int32_t* n_entries,
-                       int32_t B, int32_t T, int32_t HI, const int32_t* pool, const int32_t* pool_n,
+                       const int32_t* n_vis, int32_t B, int32_t T, int32_t HI, const int32_t* pool, const int32_t* pool_n,
                        int32_t pool_blocks, int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
                        csa2_stream_t stream) {
   int st = check_index_common(q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T,
@@ -1375,6 +1398,8 @@ int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint
   sa.max_n = max_n;
   sa.T = T;
   sa.HI = HI;
+  sa.n_vis = n_vis;
+  sa.n_groups = 1;
   sa.pool = pool;
   sa.pool_n = pool_n;
   sa.pool_blocks = pool_blocks;
@@ -1388,6 +1413,7 @@ int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint
   csa2::SelectArgs se{};
   se.s = sa.out_s;
   se.n_entries = n_entries;
+  se.n_vis = n_vis;
   se.max_n = max_n;
   se.max_pages = max_pages;
   se.T = T;
@@ -1409,7 +1435,8 @@ extern "C" int csa2_index_full(const uint8_t* q_idx, const float* w, const uint8
                                int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
                                int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
                                size_t ws_bytes, csa2_stream_t stream) {
-  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, nullptr,
+                         max_n_entries, B,
                          T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws, ws_bytes, stream);
 }
 
@@ -1419,7 +1446,8 @@ extern "C" int csa2_index_full_mxfp4(const uint8_t* q_idx, const float* w, const
                                      int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
                                      int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
                                      size_t ws_bytes, csa2_stream_t stream) {
-  return index_full_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+  return index_full_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, nullptr,
+                         max_n_entries, B,
                          T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws, ws_bytes, stream);
 }
 
@@ -1429,7 +1457,8 @@ extern "C" int csa2_index_reindex(const uint8_t* q_idx, const float* w, const ui
                                   const int32_t* pool, const int32_t* pool_n, int32_t pool_blocks,
                                   int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
                                   csa2_stream_t stream) {
-  return index_reindex_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, B, T, HI, pool,
+  return index_reindex_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, nullptr, B, T,
+                            HI, pool,
                             pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
 }
 
@@ -1439,8 +1468,32 @@ extern "C" int csa2_index_reindex_mxfp4(const uint8_t* q_idx, const float* w, co
                                         const int32_t* pool, const int32_t* pool_n, int32_t pool_blocks,
                                         int32_t topk, int32_t* out_topk, void* ws, size_t ws_bytes,
                                         csa2_stream_t stream) {
-  return index_reindex_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, B, T, HI, pool,
+  return index_reindex_impl(true, q_idx, w, kidx_mx, n_pages, page_table, max_pages, n_entries, nullptr, B, T,
+                            HI, pool,
                             pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_causal(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                                      int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                      const int32_t* n_entries, const int32_t* n_visible, int32_t max_n_entries,
+                                      int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                                      int32_t* out_topk, int32_t* out_pool, int32_t* out_pool_n, void* ws,
+                                      size_t ws_bytes, csa2_stream_t stream) {
+  if (!n_visible) return CSA2_ERR_INVALID_ARG;
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, n_visible,
+                         max_n_entries, B, T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws, ws_bytes,
+                         stream);
+}
+
+extern "C" int csa2_index_reindex_causal(const uint8_t* q_idx, const float* w, const uint8_t* kidx_pool,
+                                         int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                         const int32_t* n_entries, const int32_t* n_visible, int32_t B, int32_t T,
+                                         int32_t HI, const int32_t* pool, const int32_t* pool_n,
+                                         int32_t pool_blocks, int32_t topk, int32_t* out_topk, void* ws,
+                                         size_t ws_bytes, csa2_stream_t stream) {
+  if (!n_visible) return CSA2_ERR_INVALID_ARG;
+  return index_reindex_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, n_visible, B, T,
+                            HI, pool, pool_n, pool_blocks, topk, out_topk, ws, ws_bytes, stream);
 }
 
 static int index_full_write_impl(bool mx, const uint8_t* q_idx, const float* w,
@@ -1458,7 +1511,7 @@ static int index_full_write_impl(bool mx, const uint8_t* q_idx, const float* w,
                    ((uintptr_t)kv_pool & 7)))
     return CSA2_ERR_INVALID_ARG;
   if (kv_pages > ((int64_t)1 << 40) / csa2::kPageBytes) return CSA2_ERR_UNSUPPORTED;
-  return index_full_impl(mx, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries,
+  return index_full_impl(mx, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, nullptr,
                          max_n_entries, B, T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n,
                          ws, ws_bytes, stream, kv_bf16, rows, dst_slot, kv_pool, kv_pages);
 }
@@ -1526,7 +1579,8 @@ extern "C" int csa2_index_full_noalloc(const uint8_t* q_idx, const float* w, con
   void* ws = nullptr;
   st = current_scratch(&ws);
   if (st) return st;
-  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, max_n_entries, B,
+  return index_full_impl(false, q_idx, w, kidx_pool, n_pages, page_table, max_pages, n_entries, nullptr,
+                         max_n_entries, B,
                          T, HI, topk, pool_blocks, out_topk, out_pool, out_pool_n, ws,
                          CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -250,6 +250,24 @@ def rope_write_rows(R: int = 1048576, seed: int = 0):
     return x, ki, pos, rope_table(R), slots, n_pages
 
 
+def prefill_counts(n_entries, T: int, ratio: int = 4, seed: int | None = None) -> np.ndarray:
+    """Per-token visible entries [B, T] (int32) of a prefill chunk whose T query tokens are the
+    last T source positions of each sequence: token t of sequence b sits at position
+    p = ratio * n_b + ratio - T + t and sees the floor((p + 1) / ratio) entries complete before it
+    (clipped to [0, n_b]).  With ``seed``, a quarter of the tokens instead get a random count in
+    [0, n_b + 16] (ragged per-token visibility, including none and more than the sequence holds)."""
+    n = np.asarray(n_entries, np.int64)
+    t = np.arange(T, dtype=np.int64)
+    p = ratio * n[:, None] + ratio - T + t[None, :]
+    out = np.clip((p + 1) // ratio, 0, n[:, None])
+    if seed is not None:
+        g = _gen(seed)
+        hit = (torch.rand(out.shape, generator=g) < 0.25).numpy()
+        rnd = (torch.rand(out.shape, generator=g, dtype=torch.float64).numpy() * (n[:, None] + 17)).astype(np.int64)
+        out = np.where(hit, rnd, out)
+    return out.astype(np.int32)
+
+
 def random_topk(B: int, T: int, k: int, n_entries, seed: int, frac_valid: float = 1.0) -> np.ndarray:
     """Seeded index sets for attention-only tests: distinct ascending positions < n_b,
     the first ``frac_valid`` of the k slots valid, the rest -1."""

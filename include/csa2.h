@@ -61,7 +61,7 @@ extern "C" {
 #define CSA2_MAX_POOL_BLOCKS 2048
 #define CSA2_MAX_ENTRIES 262144    /* per sequence: 1M tokens at 4:1 */
 #define CSA2_MAX_INDEX_HEADS 64    /* indexer heads HI */
-#define CSA2_MAX_T 4               /* decode query tokens per sequence */
+#define CSA2_MAX_T 256             /* query tokens per sequence (decode: 1..4; prefill chunks up to 256) */
 #define CSA2_MAX_WRITE_ROWS 1024   /* rows of the cache write fused into csa2_index_full_write */
 #define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20) /* fixed per-GPU scratch of csa2_index_full_noalloc */
 
@@ -182,7 +182,9 @@ int csa2_rope_write_caches(const uint16_t *kv_bf16, const uint16_t *kidx_bf16, i
  *              entries [8b, 8b+8) clipped to n) by (max score desc, block
  *              asc), ascending, -1 padded; out_pool_n [B][T] their count.
  * Requires topk <= pool_blocks (then the top-k lies inside the pool),
- * 4 <= HI <= 64 with HI % 4 == 0, T in {1, 2, 4}, max_n_entries <= 262144.
+ * 4 <= HI <= 64 with HI % 4 == 0, 1 <= T <= 256, B * T <= 65535,
+ * max_n_entries <= 262144.  Every token of a sequence sees all n_entries[b]
+ * entries (csa2_index_full_causal gives each token its own count).
  */
 int csa2_index_full(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
                     int64_t n_pages, const int32_t *page_table, int32_t max_pages,
@@ -220,6 +222,36 @@ int csa2_index_full_mxfp4_write(const uint8_t *q_idx, const float *w, const uint
                                 const uint16_t *kv_bf16, int64_t rows, const int64_t *dst_slot,
                                 uint8_t *kv_pool, int64_t kv_pages, void *ws, size_t ws_bytes,
                                 csa2_stream_t stream);
+
+/*
+ * Multi-token (prefill chunk) variants with causal visibility.  "Inside
+ * DeepSeek V4.1 Flash", "CED: build decoder memory without running the whole
+ * decoder", and the knowledge note's "CSA2: share cache, refresh selection
+ * only when needed": during prefill many query tokens of a sequence run the
+ * same Full / Reindex layers, each seeing only the compressed entries that
+ * are complete before it.  Arguments, outputs and errors as
+ * csa2_index_full / csa2_index_reindex, plus
+ *   n_visible [B][T] int32 (device): token t of sequence b sees its first
+ *             min(n_entries[b], n_visible[b][t]) entries (negative: none);
+ *             with 4:1 compression, a token at position p sees
+ *             floor((p + 1) / 4) entries.
+ * Each token's top-k and pool are those of csa2_index_full over its visible
+ * entries only (a pool block is clipped to them).  csa2_index_reindex_causal
+ * takes the pool csa2_index_full_causal wrote for the same tokens.
+ * Returns CSA2_ERR_INVALID_ARG when n_visible is NULL.
+ */
+int csa2_index_full_causal(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
+                           int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                           const int32_t *n_entries, const int32_t *n_visible, int32_t max_n_entries,
+                           int32_t B, int32_t T, int32_t HI, int32_t topk, int32_t pool_blocks,
+                           int32_t *out_topk, int32_t *out_pool, int32_t *out_pool_n, void *ws,
+                           size_t ws_bytes, csa2_stream_t stream);
+int csa2_index_reindex_causal(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
+                              int64_t n_pages, const int32_t *page_table, int32_t max_pages,
+                              const int32_t *n_entries, const int32_t *n_visible, int32_t B, int32_t T,
+                              int32_t HI, const int32_t *pool, const int32_t *pool_n, int32_t pool_blocks,
+                              int32_t topk, int32_t *out_topk, void *ws, size_t ws_bytes,
+                              csa2_stream_t stream);
 
 /*
  * csa2_index_full for callers that cannot allocate device memory (code under
@@ -301,7 +333,8 @@ int csa2_index_reindex_mxfp4(const uint8_t *q_idx, const float *w, const uint8_t
  *   out      [B][T][H][512] float; out_lse [B][T][H] float (natural log) or NULL.
  * For each (b, t, h) one softmax over J = {valid selected entries} U {window
  * rows}: logits sm_scale * q . x_j, out = sum_j p_j x_j (each 512-channel
- * row serves as key and value).  H must be 16, 32 or 64.
+ * row serves as key and value).  H must be 16, 32 or 64; 1 <= T <= 256
+ * (a prefill chunk's tokens each with their own index set and window rows).
  */
 int csa2_sparse_attn(const uint16_t *q, float sm_scale, const uint8_t *kv_pool, int64_t n_pages,
                      const int32_t *page_table, int32_t max_pages, const int32_t *n_entries,

@@ -373,16 +373,27 @@ def pool_positions(pool_blocks_row: np.ndarray, n_blocks: int, n: int) -> np.nda
     return np.array(pos, dtype=np.int32)
 
 
-def index_full(q_idx, w, kidx_pool, page_table, n_entries, topk_k, pool_blocks):
-    """Full mode for a batch: returns (topk [B,T,k], pool [B,T,pool_blocks], pool_n [B,T])."""
+def visible_count(n_entries, n_visible, b: int, t: int) -> int:
+    """Entries token t of sequence b sees: all n_entries[b], or with per-token causal
+    counts the first min(n_entries[b], n_visible[b, t]) ("Inside DeepSeek V4.1 Flash",
+    "CED": a prefill token sees only the compressed entries complete before it)."""
+    n = int(n_entries[b])
+    if n_visible is not None:
+        n = max(0, min(n, int(n_visible[b, t])))
+    return n
+
+
+def index_full(q_idx, w, kidx_pool, page_table, n_entries, topk_k, pool_blocks, n_visible=None):
+    """Full mode for a batch: returns (topk [B,T,k], pool [B,T,pool_blocks], pool_n [B,T]).
+    n_visible [B,T]: optional per-token causal visible counts."""
     B, T, HI, _ = q_idx.shape
     out_topk = np.zeros((B, T, topk_k), np.int32)
     out_pool = np.zeros((B, T, pool_blocks), np.int32)
     out_n = np.zeros((B, T), np.int32)
     for b in range(B):
-        n = int(n_entries[b])
-        keys = gather_keys(kidx_pool, page_table[b], n)
+        all_keys = gather_keys(kidx_pool, page_table[b], int(n_entries[b]))
         for t in range(T):
+            keys = all_keys[:visible_count(n_entries, n_visible, b, t)]
             s = index_scores(q_idx[b, t], w[b, t], keys)
             out_topk[b, t] = topk(s, topk_k)
             out_pool[b, t], out_n[b, t] = pool(s, pool_blocks)
@@ -399,13 +410,14 @@ def index_reindex_mxfp4(q_idx, w, kidx_mx, page_table, n_entries, pool_, pool_n,
     return index_reindex(q_idx, w, mxfp4_keys_to_e4m3(kidx_mx), page_table, n_entries, pool_, pool_n, topk_k)
 
 
-def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool_, pool_n, topk_k):
-    """Reindex mode: score only the pool's positions; returns topk [B,T,k]."""
+def index_reindex(q_idx, w, kidx_pool, page_table, n_entries, pool_, pool_n, topk_k, n_visible=None):
+    """Reindex mode: score only the pool's positions; returns topk [B,T,k].
+    n_visible [B,T]: optional per-token causal visible counts (pool blocks are clipped to them)."""
     B, T, HI, _ = q_idx.shape
     out = np.zeros((B, T, topk_k), np.int32)
     for b in range(B):
-        n = int(n_entries[b])
         for t in range(T):
+            n = visible_count(n_entries, n_visible, b, t)
             pos = pool_positions(pool_[b, t], int(pool_n[b, t]), n)
             pt = page_table[b]
             keys = kidx_pool[pt[pos // PAGE], pos % PAGE] if len(pos) else np.zeros((0, DI), np.uint8)

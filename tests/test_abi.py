@@ -75,12 +75,22 @@ def test_index_full_argument_errors(L):
     assert _full(L, pool_blocks=4096) == INVALID
     assert _full(L, HI=6) == UNSUPPORTED
     assert _full(L, HI=68) == UNSUPPORTED
-    assert _full(L, T=3) == UNSUPPORTED
+    assert _full(L, T=257) == UNSUPPORTED
+    assert _full(L, B=300, T=256) == UNSUPPORTED           # B * T above 65535
     assert _full(L, topk=32, pool_blocks=16) == UNSUPPORTED
     assert _full(L, max_n=262145) == UNSUPPORTED
     assert _full(L, max_n=0) == INVALID
     assert _full(L, ws=None) == WORKSPACE
     assert _full(L, ws_bytes=16) == WORKSPACE
+
+
+def test_causal_calls_need_counts(L):
+    full = L.csa2_index_full_causal(X, X, X, 1, X, 1, X, None, 64, 1, 1, 4, 8, 16, X, X, X, X, 1 << 30, None)
+    assert full == INVALID
+    re_ = L.csa2_index_reindex_causal(X, X, X, 1, X, 1, X, None, 1, 1, 4, X, X, 16, 8, X, X, 1 << 30, None)
+    assert re_ == INVALID
+    assert L.csa2_index_full_causal(X, X, X, 1, X, 1, X, X, 64, 1, 257, 4, 8, 16, X, X, X, X, 1 << 30,
+                                    None) == UNSUPPORTED
 
 
 def test_index_full_noalloc_argument_errors(L):
@@ -142,7 +152,7 @@ def test_sparse_attn_argument_errors(L):
     assert _attn(L, topk=0) == INVALID
     assert _attn(L, topk=4096) == INVALID
     assert _attn(L, H=48) == UNSUPPORTED
-    assert _attn(L, T=5) == UNSUPPORTED
+    assert _attn(L, T=257) == UNSUPPORTED
     assert _attn(L, sm=0.0) == INVALID
     assert _attn(L, sm=float("nan")) == INVALID
     assert _attn(L, ws=None) == WORKSPACE

@@ -345,7 +345,8 @@ def test_index_full_scores_bitexact(oracle, keys_kind):
             assert np.array_equal(s_gpu[b, t, :nb].view(np.uint32), ref.view(np.uint32)), (b, t)
 
 
-@pytest.mark.parametrize("T,HI,topk", [(1, 8, 64), (2, 16, 512), (4, 4, 2048), (2, 64, 2048)])
+@pytest.mark.parametrize("T,HI,topk", [(1, 8, 64), (2, 16, 512), (4, 4, 2048), (2, 64, 2048), (3, 8, 256),
+                                       (6, 16, 512)])
 def test_index_full_ragged(oracle, T, HI, topk):
     n = [1, 7, 8, 9, 100, 1023, 1025, 2047, 2048, 16389, 40000]
     say(f"index full ragged n={n} T={T} HI={HI} k={topk}")
@@ -581,6 +582,33 @@ def test_group_128k_b8_full_reindex_reuse(oracle):
                            dev(wl.n_entries), rtk, dev(reuse.swa))
     assert np.array_equal(host(rtk), before)
     check_attention(oracle, wl, reuse, ref_rtk, host(out), batches=[0, 3, 7])
+
+
+@pytest.mark.parametrize("T,n,HI,H,topk", [(64, [20000, 3001], 64, 64, 2048), (256, [16384], 16, 16, 512)])
+def test_prefill_causal_full_reindex_attention(oracle, T, n, HI, H, topk):
+    """A prefill chunk of T query tokens per sequence, each token seeing only its causal share of
+    the entries: Full and Reindex top-k, pools and counts bit-exact per token, attention within
+    the bound on sampled tokens."""
+    say(f"prefill chunk T={T} n={n} HI={HI} H={H} k={topk}: causal Full -> Reindex -> attention")
+    wl = small_workload(n, T=T, HI=HI, H=H, topk=topk, seed=T)
+    full = wl.layers[0]
+    reidx = synth.layer_inputs("reindex", wl.B, T, HI, H, T + 1)
+    n_vis = synth.prefill_counts(n, T, seed=T + 2)
+    pt, ne, nv = dev(wl.paging.page_table), dev(wl.n_entries), dev(n_vis)
+    tk, pl, pn = csa2.index_full(dev(full.q_idx), dev(full.w), dev(wl.kidx_pool), pt, ne, wl.max_n, topk, 2048,
+                                 n_visible=nv)
+    r_tk, r_pool, r_pn = oracle.index_full(full.q_idx, full.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries,
+                                           topk, 2048, n_visible=n_vis)
+    assert np.array_equal(host(pn), r_pn)
+    assert np.array_equal(host(pl), r_pool)
+    assert np.array_equal(host(tk), r_tk)
+    rtk = csa2.index_reindex(dev(reidx.q_idx), dev(reidx.w), dev(wl.kidx_pool), pt, ne, pl, pn, topk,
+                             n_visible=nv)
+    r_rtk = oracle.index_reindex(reidx.q_idx, reidx.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries, r_pool,
+                                 r_pn, topk, n_visible=n_vis)
+    assert np.array_equal(host(rtk), r_rtk)
+    out, _ = gpu_attention(wl, full, r_rtk)
+    check_attention(oracle, wl, full, r_rtk, out, tokens=[0, 1, T // 2, T - 1])
 
 
 # ------------------------------------------------------------------ a7

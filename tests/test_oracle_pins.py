@@ -373,6 +373,37 @@ def test_reindex_with_full_query_over_whole_context_equals_full(oracle):
     assert np.array_equal(tk, rtk)
 
 
+def test_causal_counts_equal_truncated_sequences(oracle):
+    """Per-token causal visibility (prefill chunk): token t's top-k and pool are those of the
+    sequence cut to its own visible count, checked by lexsort brute force per token; counts at or
+    past n_entries give the plain result, a count of 0 gives nothing."""
+    n_entries = np.array([9000, 3001], np.int32)
+    pg, kidx, full, reidx = _small_workload(n_entries, seed=4)
+    T = full.q_idx.shape[1]
+    n_vis = np.array([[8990, 9000 + 5], [0, 17]], np.int32)      # [B, T]
+    tk, pool_, pool_n = oracle.index_full(full.q_idx, full.w, kidx, pg.page_table, n_entries, 300, 512,
+                                          n_visible=n_vis)
+    rtk = oracle.index_reindex(reidx.q_idx, reidx.w, kidx, pg.page_table, n_entries, pool_, pool_n, 300,
+                               n_visible=n_vis)
+    for b in range(2):
+        keys = oracle.gather_keys(kidx, pg.page_table[b], int(n_entries[b]))
+        for t in range(T):
+            n_t = max(0, min(int(n_entries[b]), int(n_vis[b, t])))
+            s = oracle.index_scores(full.q_idx[b, t], full.w[b, t], keys[:n_t])
+            assert np.array_equal(tk[b, t], brute_topk(s, 300))
+            rb, rn = brute_pool(s, 512) if n_t else (np.full(512, -1, np.int32), 0)
+            assert pool_n[b, t] == rn and np.array_equal(pool_[b, t], rb)
+            pos = oracle.pool_positions(pool_[b, t], pool_n[b, t], n_t)
+            assert len(pos) == 0 or pos.max() < n_t
+            s2 = oracle.index_scores(reidx.q_idx[b, t], reidx.w[b, t], keys[:n_t])
+            assert np.array_equal(rtk[b, t], brute_topk(s2[pos], 300, pos))
+    plain = oracle.index_full(full.q_idx, full.w, kidx, pg.page_table, n_entries, 300, 512)
+    wide = oracle.index_full(full.q_idx, full.w, kidx, pg.page_table, n_entries, 300, 512,
+                             n_visible=np.full((2, T), 1 << 30, np.int32))
+    for a, b in zip(plain, wide):
+        assert np.array_equal(a, b)
+
+
 # ------------------------------------------------------------------ a7 attention
 def _sdpa64(q, rows, scale):
     qt = torch.from_numpy(q)[None, :, None, :]           # [1, H, 1, D]
