@@ -9,7 +9,8 @@ the oracle tests and the HIP path draw their inputs from this module.
 The five workloads follow the decode configurations the path is measured on:
 a small Full layer (8K context, batch 1), a Full -> Reindex -> Reuse group at
 128K context and batch 8, the 1M-token Full layer at batch 4, the 1M-row FP4
-cache write, and the 20-layer decoder schedule over ragged 32K..1M contexts.
+cache write, and the 20-layer decoder schedule over ragged 32K..1M contexts;
+a sixth is a 256-token prefill chunk at the end of a 1M-token sequence.
 """
 from __future__ import annotations
 
@@ -213,6 +214,14 @@ def workload(name: str) -> Workload:
         for li in range(20, 40):
             mode = "full" if li == 20 else ("reindex" if li in (24, 28, 32, 36) else "reuse")
             layers.append(layer_inputs(mode, B, T, HI, H, li))
+        return Workload(name, B, T, H, HI, k, 2048, 1.0 / math.sqrt(D), n, pg, kidx, kv, layers)
+    if name == "prefill_256t_1m":
+        # one prefill chunk of 256 query tokens at the end of a 1M-token sequence (4:1): a Full and
+        # a Reindex layer of the decoder run over the chunk, each token seeing its causal prefix
+        B, T, HI, H, k = 1, 256, 64, 64, 2048
+        n = np.array([1048576 // 4], np.int32)
+        pg, kidx, kv = _shared_cache(B, n, 30, 31)
+        layers = [layer_inputs(m, B, T, HI, H, 30 + i) for i, m in enumerate(("full", "reindex"))]
         return Workload(name, B, T, H, HI, k, 2048, 1.0 / math.sqrt(D), n, pg, kidx, kv, layers)
     raise KeyError(name)
 

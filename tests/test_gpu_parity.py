@@ -611,6 +611,46 @@ def test_prefill_causal_full_reindex_attention(oracle, T, n, HI, H, topk):
     check_attention(oracle, wl, full, r_rtk, out, tokens=[0, 1, T // 2, T - 1])
 
 
+def test_schedule_20l_b32_full_size(oracle):
+    """The 20-layer decoder schedule at full size: batch 32, 2 query tokens, ragged contexts
+    (8,342 .. 252,139 entries).  Layer 20 is Full (with the step's cache write), layers 24, 28,
+    32, 36 Reindex over layer 20's pool, the rest Reuse the latest indices.  Every Full and
+    Reindex top-k, pool and count is bit-exact for all 64 rows; attention is within the bound on
+    sampled rows of Full, Reindex and Reuse layers; Reuse leaves the index buffers unchanged."""
+    say("schedule 20 layers B=32 T=2 ragged 32K..1M: Full -> 4 x Reindex, attention per layer")
+    wl = synth.workload("schedule_20l_b32")
+    pt, ne = dev(wl.paging.page_table), dev(wl.n_entries)
+    kidx = dev(wl.kidx_pool)
+    kv_pool = torch.zeros((wl.paging.n_pages, csa2.PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(bf16_dev(wl.kv_source), dev(wl.paging.all_slots()), kv_pool)
+    by = {20 + i: L for i, L in enumerate(wl.layers)}
+    L = by[20]
+    tk, pl, pn = csa2.index_full(dev(L.q_idx), dev(L.w), kidx, pt, ne, wl.max_n, wl.topk, wl.pool_blocks)
+    r_tk, r_pool, r_pn = oracle_index_full(oracle, wl, L)
+    assert np.array_equal(host(pn), r_pn)
+    assert np.array_equal(host(pl), r_pool)
+    assert np.array_equal(host(tk), r_tk)
+    say("schedule: Full layer 20 bit-exact on all 64 rows")
+    latest = {20: (tk, r_tk)}
+    for li in (24, 28, 32, 36):
+        R = by[li]
+        rtk = csa2.index_reindex(dev(R.q_idx), dev(R.w), kidx, pt, ne, pl, pn, wl.topk)
+        r_rtk = oracle.index_reindex(R.q_idx, R.w, wl.kidx_pool, wl.paging.page_table, wl.n_entries, r_pool, r_pn,
+                                     wl.topk)
+        assert np.array_equal(host(rtk), r_rtk), li
+        latest[li] = (rtk, r_rtk)
+    say("schedule: Reindex layers 24, 28, 32, 36 bit-exact on all 64 rows")
+    order = np.argsort(wl.n_entries)
+    sample = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1]), 5})
+    for li in (20, 21, 24, 27, 36, 39):
+        src = max(x for x in latest if x <= li)
+        idx, ref_idx = latest[src]
+        before = host(idx).copy()
+        out = csa2.sparse_attn(bf16_dev(by[li].q), wl.sm_scale, kv_pool, pt, ne, idx, dev(by[li].swa))
+        assert np.array_equal(host(idx), before)
+        check_attention(oracle, wl, by[li], ref_idx, host(out), batches=sample)
+
+
 # ------------------------------------------------------------------ a7
 def check_attention(oracle, wl, layer, idx, out, batches=None, tokens=None, lse=None):
     offs = np.concatenate([[0], np.cumsum(wl.n_entries)[:-1]])
