@@ -71,9 +71,14 @@ class HipEvents:
         return evs
 
     def elapsed_ms(self, a, b):
+        """ms between two recorded events, or None (then the error is cleared, so that the
+        next runtime call does not report it): e.g. a kernel the call did not launch."""
         f = ctypes.c_float()
         st = self.rt.hipEventElapsedTime(ctypes.byref(f), a, b)
-        return float(f.value) if st == 0 else float("nan")
+        if st != 0:
+            self.rt.hipGetLastError()
+            return None
+        return float(f.value)
 
     def destroy(self, evs):
         for e in evs:
@@ -105,7 +110,9 @@ class KernelTimer:
         out = {}
         for label, name, s, e in self.spans:
             d = out.setdefault(label, {})
-            d[name] = d.get(name, 0.0) + 1000.0 * self.ev.elapsed_ms(s, e) / steps
+            ms = self.ev.elapsed_ms(s, e)
+            if ms is not None:       # None: the call did not launch this kernel
+                d[name] = d.get(name, 0.0) + 1000.0 * ms / steps
             self.ev.destroy([s, e])
         self.spans = []
         return out
@@ -439,6 +446,7 @@ def bench_layer(args):
     torch.cuda.synchronize()
     per = timer.collect(K)
     kern_us = {**per["index"], **per["attn"]}
+    kern_us.setdefault("attn_combine", 0.0)
     eager_ref = out_topk.clone(), out.clone()
 
     # ---- pass 2: whole steps, timed with one event pair around K steps

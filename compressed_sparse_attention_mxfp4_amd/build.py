@@ -28,6 +28,9 @@ def flags() -> list[str]:
             # keeps its accumulators in AGPRs and copies them around every
             # rescale and every partial-logit store
             "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            # private arrays stay in registers or scratch, never in LDS: the
+            # LDS is sized by hand for each kernel's occupancy
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -7,24 +7,32 @@
 // FP8).  Each 512-channel row is both key and value; one softmax runs over
 // the union of the rows.
 //
-// Work split: one workgroup per (b, t, 16-head tile, 128-row split of the
-// row list [top-k slots | 128 window rows]); its 4 waves own 128 channels
-// each.  The split's rows are resolved once (index, page) and all their code
-// bytes are loaded up front.  Per 32-row sub-chunk a wave converts its
-// channel slice to fp16 (hardware FP4 / E4M3 conversion, exact) into a
-// swizzled row-major LDS tile, computes partial logits over its channels
-// with f16 MFMA; the four partials are summed in fixed order through LDS,
-// every wave runs the same online softmax and accumulates P.V for its
-// channels, reading V transposed from the same tile.  Splits write (max,
-// sum, unnormalised output) and a combine kernel merges them.
+// Two kernels share the row handling.  Each splits the row list [top-k
+// slots | 128 window rows] of a (b, t) so that the grid has about one
+// workgroup per compute unit (the splits' partial results merged by a
+// combine kernel; with one split the output is written directly), resolves a
+// split's rows once (index -> page -> cache slot) into LDS, and keeps the row
+// loads of the next 32-row sub-chunks in flight while one is processed.
+//  - 64 heads (attn_heads_kernel, below): one workgroup per (b, t, split)
+//    serves every head, so each row is gathered and dequantized once into a
+//    shared LDS tile of fp16 rows.
+//  - 16 or 32 heads (attn_split_kernel): one workgroup per (b, t, 16-head
+//    tile, split); its 4 waves own 128 channels each.  Per sub-chunk a wave
+//    converts its channel slice to fp16 (hardware FP4 / E4M3 conversion,
+//    exact) straight into the Q.K operand and into a swizzled row-major LDS
+//    tile; the four partial logits are summed in fixed order through LDS,
+//    every wave runs the same online softmax and accumulates P.V for its
+//    channels, reading V transposed from the tile.
 #include "common.h"
 
 namespace csa2 {
 
 constexpr int kAttnThreads = 256;
-constexpr int kRowsPerSplit = 128;
 constexpr int kSub = 32;               // rows per sub-chunk
 constexpr int kRowHalves = 128;        // a wave's 128-channel slice of one row (256 B, 16 chunks of 16 B)
+constexpr int kMaxRows = CSA2_MAX_TOPK + CSA2_SWA;  // rows of one (b, t): 2,176
+// Workgroups the split count aims at (about one per compute unit).
+constexpr int kTargetWorkgroups = 256;
 
 // LDS tile of 32 rows x 128 fp16 channels, row-major, with 16-byte chunk k of
 // row r stored at chunk k ^ bitrev4(r & 15).  This one layout serves three
@@ -39,10 +47,6 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {  // in halves
 typedef _Float16 half_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-template <int M>
-struct ModeTag {
-  static constexpr int value = M;
-};
 
 // Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48): each
 // permlane swap of a register with itself leaves the two values of a lane
@@ -79,8 +83,11 @@ struct AttnArgs {
   int H;
   int BT;
   int n_splits;
-  float* part_o;   // [B*T][H/16][n_splits][16][512]
-  float* part_ml;  // [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
+  int split_rows;  // rows per split, a multiple of 32
+  float* part_o;   // n_splits > 1: [B*T][H/16][n_splits][16][512]
+  float* part_ml;  // n_splits > 1: [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
+  float* out;      // n_splits == 1: [B*T][H][512]
+  float* out_lse;  // n_splits == 1: [B*T][H] or null
 };
 
 // Hoisted LDS addresses: byte offsets in the workgroup's LDS, passed through
@@ -94,13 +101,9 @@ __device__ __forceinline__ uint32_t lds_addr(const half_t* p) {
   asm volatile("" : "+v"(x));
   return x;
 }
-// Row loads through global-address-space pointers: the row pointers are
-// passed through LDS, and plain (flat) loads of them would also count on the
-// LDS wait counter, so every LDS wait would wait for the row loads as well.
-typedef const __attribute__((address_space(1))) v2u gbl_v2u_t;
-typedef const __attribute__((address_space(1))) uint32_t gbl_u32_t;
-__device__ __forceinline__ v2u gld8(const uint8_t* p) { return *(gbl_v2u_t*)p; }
-__device__ __forceinline__ uint32_t gld4(const uint8_t* p) { return *(gbl_u32_t*)p; }
+// Row loads through global-address-space pointers, so that they count on
+// the vector-memory wait counter only (a flat load would also count on the
+// LDS counter and make every LDS wait of the loop wait for the row loads).
 __device__ __forceinline__ void lds_st16(uint32_t addr, v8h v) { *(lds_v8h_t*)(uintptr_t)addr = v; }
 __device__ __forceinline__ v8h lds_ld16(uint32_t addr) { return *(const lds_v8h_t*)(uintptr_t)addr; }
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
@@ -109,18 +112,63 @@ __device__ __forceinline__ v4h lds_ld_tr(uint32_t addr) {
   return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(uintptr_t)addr));
 }
 
-// Kinds of row content a split can hold (decided per split, the same for
-// every wave): only FP4 entries (rows < topk), only window rows, or both.
-enum SplitMode { kMixed = 0, kFp4Only = 1, kWindowOnly = 2 };
+// A row of the list: cache slot (physical page * 64 + offset) of a selected
+// entry, or one of these codes.
+constexpr int kRowAbsent = -1;   // empty top-k slot, or past the split's end
+constexpr int kRowWindow = -2;   // a window row (its place in the list gives which)
 
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
+// Kinds of row content a sub-chunk can hold (decided per sub-chunk, the same
+// for every wave): only FP4 entries (rows < topk), only window rows, or both.
+enum SubMode { kMixed = 0, kFp4Only = 1, kWindowOnly = 2 };
+
+// The row loads of one sub-chunk for one lane (g, col): rows col and
+// 16 + col, the wave's channels 128 w + 32 g .. + 31.  FP4 row: 16 code
+// bytes + the 16 scale bytes 16 (w / 2) .. + 15 of the entry (the lane's two
+// groups among them); window row: 32 E4M3 bytes; absent rows read the pool's
+// first bytes (discarded).
+struct SubLoads {
+  v4u lo[2], hi[2];
+  int s[2];  // the rows' slots (or kRowAbsent / kRowWindow)
+};
+
+typedef const __attribute__((address_space(1))) v4u gbl_v4u_t;
+__device__ __forceinline__ v4u gld16(const uint8_t* p) { return *(gbl_v4u_t*)p; }
+
+// rel0: the sub-chunk's first row in the split (rslot index); abs0: in the
+// whole list (window row w = list row - topk).
+// The loads are always issued, also for sub-chunks past the split's end
+// (their rows read as absent), so that every path through the loop has the
+// same loads in flight and each wait counts exactly the later sub-chunks'.
+__device__ __forceinline__ void issue_sub(const AttnArgs& a, const int* rslot, int rel0, int abs0, int n_rel,
+                                          int wave, int g, int col, const uint8_t* win_row0, SubLoads& L) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = 16 * rt + col;
+    const int s = rel0 + r < n_rel ? rslot[rel0 + r] : kRowAbsent;
+    L.s[rt] = s;
+    const uint8_t* p0 = a.kv_pool;
+    const uint8_t* p1 = a.kv_pool;
+    if (s >= 0) {
+      const uint8_t* page = a.kv_pool + (int64_t)(s >> 6) * kPageBytes;
+      p0 = page + (s & 63) * kEntryCodes + 64 * wave + 16 * g;
+      p1 = page + kPage * kEntryCodes + (s & 63) * kEntryScales + 16 * (wave >> 1);
+    } else if (s == kRowWindow) {
+      p0 = win_row0 + (int64_t)(abs0 + r - a.topk) * kD + 128 * wave + 32 * g;
+      p1 = p0 + 16;
+    }
+    // 16-byte loads at 16-byte aligned addresses inside the row they belong to
+    L.lo[rt] = gld16(p0);
+    L.hi[rt] = gld16(p1);
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
   __shared__ __attribute__((aligned(16))) v4f ssum[2][4][2][64];  // double-buffered by sub-chunk
   __shared__ __attribute__((aligned(16))) float alph[4][16];       // per wave: rescale factor per head
-  __shared__ const uint8_t* rptr0[kRowsPerSplit];  // codes (FP4) or window row start
-  __shared__ const uint8_t* rptr1[kRowsPerSplit];  // scale row (FP4) or window row start + 8
-  __shared__ __attribute__((aligned(16))) int rkind[kRowsPerSplit];
-  __shared__ __attribute__((aligned(16))) float rbias[kRowsPerSplit];  // 0 present, -inf absent
+  __shared__ __attribute__((aligned(16))) float qmax[4][16];       // per wave: max |q| per head
+  __shared__ __attribute__((aligned(16))) int rslot[kMaxRows + kSub];
 
   // XCD-aware order: workgroup id % 8 picks the XCD (and its L2).  The NHT
   // head tiles of one (split, b, t) unit take ids 8 apart, so they share an
@@ -142,83 +190,107 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
   n = min(n, a.max_pages * kPage);
 
   const int n_rows = a.topk + kSwa;
-  const int row0 = split * kRowsPerSplit;
-  const int row1 = min(n_rows, row0 + kRowsPerSplit);
+  const int row0 = split * a.split_rows;
+  const int row1 = min(n_rows, row0 + a.split_rows);
+  const int n_sub = (row1 - row0 + kSub - 1) / kSub;
   const int32_t* idx_row = a.topk_idx + (int64_t)bt * a.topk;
+  const uint8_t* win_row0 = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t) * kD;
 
-  // ---- resolve the split's rows once: FP4 entry address (index, page
-  // lookup) or window row; threads 0..127 take one row each
-  if (threadIdx.x < kRowsPerSplit) {
-    const int row = row0 + (int)threadIdx.x;
-    // absent rows point at the pool's first bytes (read and discarded)
-    const uint8_t* p0 = a.kv_pool;
-    const uint8_t* p1 = a.kv_pool;
-    int kind = 0;
-    if (row < row1) {
-      if (row < a.topk) {
-        const int j = idx_row[row];
-        if (j >= 0 && j < n) {
-          const int64_t pg = phys_page(a.page_table, a.max_pages, a.n_pages, b, j >> 6);
-          if (pg >= 0) {
-            const uint8_t* page = a.kv_pool + pg * kPageBytes;
-            p0 = page + (j & 63) * kEntryCodes;
-            p1 = page + kPage * kEntryCodes + (j & 63) * kEntryScales;
-            kind = 1;
-          }
-        }
-      } else {
-        p0 = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t + (row - a.topk)) * kD;
-        p1 = p0 + 8;
-        kind = 2;
-      }
-    }
-    rptr0[threadIdx.x] = p0;
-    rptr1[threadIdx.x] = p1;
-    rkind[threadIdx.x] = kind;
-    rbias[threadIdx.x] = kind != 0 ? 0.0f : -__builtin_inff();
+  // the query slice's raw words go out first (used after the row resolve)
+  v4u qraw[4];
+  {
+    const uint16_t* qrow = a.q + (((int64_t)bt * a.H) + ht * 16 + col) * kD + 128 * wave + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const v4u*>(qrow + 8 * s);
   }
 
-  // ---- Q slice as the B operand: head ht*16+col, channels 128*wave + 32*s
-  // + 8*g .. +8, kept as packed half pairs
-  v8h qb[4];
+  // ---- resolve the split's rows once (index, page lookup): FP4 entry slot,
+  // window row, or absent (also past the split's end, up to whole sub-chunks)
+  // (all index loads in flight together, then all page-table loads)
   {
-    const uint16_t* qrow = a.q + (((int64_t)bt * a.H) + ht * 16 + col) * kD + 128 * wave + 8 * g;
-    v4u raw[4];
+    constexpr int kPer = (kMaxRows + kSub + kAttnThreads - 1) / kAttnThreads;  // 9
+    const int n_rel = n_sub * kSub;
+    int jj[kPer];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const v4u*>(qrow + 32 * s);
-    // the packed words pass through an empty asm so that the compiler keeps
-    // them packed instead of re-packing the halves before every MFMA
+    for (int k = 0; k < kPer; ++k) {
+      const int row = row0 + (int)threadIdx.x + k * kAttnThreads;
+      jj[k] = idx_row[max(0, min(row, a.topk - 1))];
+    }
+    // (unconditional, clamped: a load inside a branch would be waited for there)
+    int pp[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int lp = max(0, min(jj[k] >> 6, a.max_pages - 1));
+      pp[k] = a.page_table[(int64_t)b * a.max_pages + lp];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int r = (int)threadIdx.x + k * kAttnThreads;
+      const int row = row0 + r;
+      int s = kRowAbsent;
+      if (row < row1) {
+        if (row < a.topk) {
+          const int j = jj[k];
+          if (j >= 0 && j < n && pp[k] >= 0 && pp[k] < a.n_pages) s = (int)((int64_t)pp[k] * kPage + (j & 63));
+        } else {
+          s = kRowWindow;
+        }
+      }
+      if (r < n_rel) rslot[r] = s;
+    }
+  }
+
+  // ---- Q slice as the B operand of S^T = K.Q^T: lane (g, col) holds head
+  // ht*16+col, channels 128*wave + 32*g + 8*s .. +8 as K slice s (the keys
+  // use the same order of the channels, so the dot product is unchanged).
+  // Each head's query is scaled by a power of two that puts its largest |q|
+  // in [2^14, 2^15), so that the fp16 operand never overflows; the logits
+  // take the inverse power back (exact).
+  v8h qb[4];
+  float q_unscale;
+  {
+    const v4u (&raw)[4] = qraw;
+    uint32_t mx = 0u;  // largest |q| bit pattern (bf16 in the high half)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max((raw[s][e] << 16) & 0x7FFF0000u, raw[s][e] & 0x7FFF0000u));
+    const float m4 = rows4_max(__uint_as_float(mx));
+    if (lane < 16) qmax[wave][lane] = m4;
+    __syncthreads();  // also publishes rslot
+    const float m = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
+    // exponent of the largest |q| (a normal or subnormal bf16): the scale is
+    // 2^(14 - e), kept a binary32 power of two (at most 2^127)
+    const int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 14;
+    const int sh = min(127, 14 - e);
+    const float up = __builtin_ldexpf(1.0f, sh);
+    q_unscale = __builtin_ldexpf(1.0f, -sh);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4u pk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const h2_t h = {(_Float16)u2f(raw[s][e] << 16), (_Float16)u2f(raw[s][e] & 0xFFFF0000u)};
-        pk[e] = __builtin_bit_cast(uint32_t, h);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const h2_t h = {(_Float16)(u2f(raw[s][e2] << 16) * up), (_Float16)(u2f(raw[s][e2] & 0xFFFF0000u) * up)};
+        pk[e2] = __builtin_bit_cast(uint32_t, h);
       }
+      // the packed words pass through an empty asm so that the compiler
+      // keeps them packed instead of re-packing the halves before every MFMA
       asm volatile("" : "+v"(pk));
       qb[s] = __builtin_bit_cast(v8h, pk);
     }
   }
+  const float lg_scale = a.sm_scale_log2 * q_unscale;  // per head `col`
 
-  // lane (rg, cg) of wave w dequantizes rows 4*rg .. 4*rg+3 of each 32-row
-  // sub-chunk, channels 128*w + 16*cg .. +16 (16-byte chunks 2cg, 2cg+1 of
-  // the wave's tile); odd channel groups store their two chunks in the other
-  // order (keeps each store instruction conflict-free)
-  const int rg = lane >> 3, cg = lane & 7;
-  const int odd = cg & 1;
-  const int ch0 = 128 * wave + 16 * cg;
+  // lane (g, col) dequantizes rows col and 16 + col of each 32-row
+  // sub-chunk, the wave's channels 32g .. 32g + 31 (16-byte chunks 4g ..
+  // 4g + 3 of the wave's tile), straight into the A operand of S^T = K.Q^T,
+  // and stores them into the tile for the transposed P.V reads
   half_t* my_kr = kr[wave];
-  uint32_t st_addr[4][2];
+  uint32_t st_addr[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st_addr[i][0] = lds_addr(&my_kr[tile_off(4 * rg + i, 2 * cg + odd)]);
-    st_addr[i][1] = lds_addr(&my_kr[tile_off(4 * rg + i, 2 * cg + (odd ^ 1))]);
-  }
-  // Q.K operand rows: lane (g, col) reads row col (+16), channels 32s + 8g
-  uint32_t qk_addr[4];
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qk_addr[s] = lds_addr(&my_kr[tile_off(col, 4 * s + g)]);
+    for (int s = 0; s < 4; ++s) st_addr[rt][s] = lds_addr(&my_kr[tile_off(16 * rt + col, 4 * g + s)]);
   // P.V operand: the V column (channel 16c + col over P's K slice, rows
   // {4g..4g+3, 16+4g..16+4g+3}) comes from the row-major tile through the
   // transposing load, so lane (g, col) points at row 4g + col / 4 (+16),
@@ -231,220 +303,608 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(AttnArgs a) {
     for (int c = 0; c < 8; ++c) pv_addr[c] = lds_addr(&my_kr[tile_off(tr_row, 2 * c + (tq >> 1)) + 4 * (tq & 1)]);
   }
   constexpr int kRowBytes16 = 16 * kRowHalves * 2;  // 16 rows of the tile, in bytes
-  // LDS-only barriers throughout: the row loads stay in flight across them
-  lds_barrier();
 
-  // The whole sub-chunk loop, specialised by what the split's rows can be.
-  auto run = [&](auto mode_tag) {
+  float m_run = -__builtin_inff();  // running reference (log2 units) of head `col`
+  float l_run = 0.0f;               // running sum of head `col`
+  v4f o_acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o_acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // One sub-chunk from its loaded bytes.
+  auto process = [&](int sc, const SubLoads& L, auto mode_tag) {
     constexpr int kMode = decltype(mode_tag)::value;
-    constexpr int kSubs = kRowsPerSplit / kSub;  // 4
-    // ---- issue every code load of the split up front: per row 8 code
-    // bytes + the dword holding the scale byte (FP4) or 16 bytes (window);
-    // absent rows read the pool's first bytes, discarded
-    const int off_fp4_0 = ch0 / 2, off_fp4_1 = (ch0 / 16) & ~3;
-    v2u lo8[kSubs][4], hi8[kSubs][4];
-    bool present[kSubs][4];
+    const int sub0 = sc * kSub;  // in the split's rows
+    // ---- dequantize rows col, 16 + col (32 channels each) into the Q.K
+    // operand.  Hardware conversions with unit scale are exact for every
+    // FP4 and E4M3 code (element 0 = low nibble / low byte); the E4M3 block
+    // scale is applied by one packed fp16 multiply per channel pair, exact
+    // since the product has at most 6 significant bits and lies in fp16 range.
+    v8h kA[2][4];
 #pragma unroll
-    for (int sc = 0; sc < kSubs; ++sc) {
-      const v4i k4 = *reinterpret_cast<const v4i*>(&rkind[sc * kSub + 4 * rg]);
+    for (int rt = 0; rt < 2; ++rt) {
+      const int s = L.s[rt];
+      const v4u lo = L.lo[rt], hi = L.hi[rt];
+      auto fp4_row = [&](bool present) {
+        // absent row: zero scales, zero row (FP4 codes are all finite).  The
+        // mask is opaque so that the select does not pull the loads into a
+        // branch.
+        uint32_t pm = present ? 0xFFFFFFFFu : 0u;
+        asm volatile("" : "+v"(pm));
+        // groups 8 wave + 2 g and + 1: bytes 8 (wave & 1) + 2 g, + 1 of hi
+        // (word 2 (wave & 1) + g / 2, picked by selects: g varies by lane)
+        const uint32_t wlo = (wave & 1) ? hi[2] : hi[0];
+        const uint32_t whi = (wave & 1) ? hi[3] : hi[1];
+        const uint32_t sw = (((g >> 1) ? whi : wlo) >> (16 * (g & 1))) & 0xFFFFu;
+        const uint32_t s0 = (sw & 0xFFu) * 0x101u & pm, s1 = (sw >> 8) * 0x101u & pm;
+        const h2_t sc0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, false);
+        const h2_t sc1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, false);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = sc * kSub + 4 * rg + i;
-        if (kMode == kFp4Only) {
-          lo8[sc][i] = gld8(rptr0[rr] + off_fp4_0);
-          hi8[sc][i][0] = gld4(rptr1[rr] + off_fp4_1);
-          hi8[sc][i][1] = 0u;
-          present[sc][i] = k4[i] == 1;
-        } else if (kMode == kWindowOnly) {
-          lo8[sc][i] = gld8(rptr0[rr] + ch0);
-          hi8[sc][i] = gld8(rptr1[rr] + ch0);
-          present[sc][i] = k4[i] == 2;
-        } else {
-          const bool fp4 = k4[i] == 1;
-          lo8[sc][i] = gld8(rptr0[rr] + (fp4 ? off_fp4_0 : ch0));
-          hi8[sc][i] = gld8(rptr1[rr] + (fp4 ? off_fp4_1 : ch0));
-          present[sc][i] = k4[i] != 0;
+        for (int d = 0; d < 4; ++d) {
+          const h2_t sc = d < 2 ? sc0 : sc1;
+          const h2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo[d], 1.0f, 0) * sc;
+          const h2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo[d], 1.0f, 1) * sc;
+          const h2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo[d], 1.0f, 2) * sc;
+          const h2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo[d], 1.0f, 3) * sc;
+          kA[rt][d] = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
         }
+      };
+      auto fp8_row = [&](bool w) {
+        // window row: 32 E4M3 codes; absent row: zeros (its bytes may hold
+        // NaN codes, and its V must be 0 to meet p = 0)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t c0 = w ? (d < 2 ? lo[2 * d] : hi[2 * d - 4]) : 0u;
+          const uint32_t c1 = w ? (d < 2 ? lo[2 * d + 1] : hi[2 * d - 3]) : 0u;
+          const h2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
+          const h2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
+          const h2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
+          const h2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, true);
+          kA[rt][d] = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        }
+      };
+      if (kMode == kFp4Only) {
+        fp4_row(s >= 0);
+      } else if (kMode == kWindowOnly) {
+        fp8_row(s == kRowWindow);
+      } else {
+        if (s >= 0) fp4_row(true);
+        else fp8_row(s == kRowWindow);
       }
-      // keep the loads in sub-chunk order: the wait counter retires them in
-      // issue order, so sub-chunk 0 then waits only for its own rows
-      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int d = 0; d < 4; ++d) lds_st16(st_addr[rt][d], kA[rt][d]);
     }
 
-    float m_run = -__builtin_inff();  // running reference (log2 units) of head `col`
-    float l_run = 0.0f;               // running sum of head `col`
-    v4f o_acc[8];
+    // ---- partial logits S^T (32 rows x 16 heads) over this wave's 128 channels
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o_acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt) {
+      v4f sacc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) sacc = mfma16(kA[rt][d], qb[d], sacc);
+      ssum[sc & 1][wave][rt][lane] = sacc;
+    }
+    // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
+    // and this buffer is rewritten only after the next sub-chunk's barrier;
+    // it also orders this wave's tile stores before its transposed reads
+    lds_barrier();
+    // rows 4g..4g+3 and 16+4g..16+4g+3 present (slot or window) or not
+    const v4i p0 = *reinterpret_cast<const v4i*>(&rslot[sub0 + 4 * g]);
+    const v4i p1 = *reinterpret_cast<const v4i*>(&rslot[sub0 + 16 + 4 * g]);
+    v4f part[4][2];
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) part[w4][rt] = ssum[sc & 1][w4][rt][lane];
+    // fixed order: ((w0 + w1) + w2) + w3
+    v4f st[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) st[rt] = ((part[0][rt] + part[1][rt]) + part[2][rt]) + part[3][rt];
 
+    // ---- online softmax for head `col` over rows 4g+i (+16)
+    float lg[8];
+    float mx = -__builtin_inff();
 #pragma unroll
-    for (int sc = 0; sc < kSubs; ++sc) {
-      const int sub = row0 + sc * kSub;
-      if (sub >= row1) break;
-      // ---- dequantize 4 rows x 16 channels into the swizzled tile.
-      // Hardware conversions with unit scale are exact for every FP4 and
-      // E4M3 code (element 0 = low nibble / low byte); the E4M3 block scale
-      // is applied by one packed fp16 multiply per channel pair, exact since
-      // the product has at most 6 significant bits and lies in fp16 range.
-      // Odd channel groups convert their two 8-channel halves in the other
-      // order, to match their store order.
+    for (int i = 0; i < 4; ++i) {
+      // fma with a zero addend is the rounded product; -inf masks the row
+      lg[i] = __builtin_fmaf(st[0][i], lg_scale, p0[i] != kRowAbsent ? 0.0f : -__builtin_inff());
+      lg[4 + i] = __builtin_fmaf(st[1][i], lg_scale, p1[i] != kRowAbsent ? 0.0f : -__builtin_inff());
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h2_t v[8];
-        const v2u lo = lo8[sc][i], hi = hi8[sc][i];
-        auto fp4_row = [&]() {
-          // absent row: zero scale, zero row (FP4 codes are all finite).  The
-          // mask is opaque so that the scale load stays unconditional (a
-          // select on `present` would let the compiler sink the load into a
-          // branch and wait for it there).
-          uint32_t pm = present[sc][i] ? 0xFFFFFFFFu : 0u;
-          asm volatile("" : "+v"(pm));
-          const uint32_t scode = (hi[0] >> (8 * (cg & 3))) & 0xFFu;  // group ch0/16 = 8w + cg
-          const uint32_t spair = (scode * 0x101u) & pm;
-          const h2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(spair, 1.0f, false);
-          const uint32_t half[2] = {odd ? lo[1] : lo[0], odd ? lo[0] : lo[1]};
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, lg[k]);
+    mx = rows4_max(mx);
+    // Lazy reference: the running reference m_run moves only when a logit
+    // exceeds it by more than 8 (log2 units), so weights p stay <= 2^8 (exact
+    // range for the fp16 P operand and far from fp32 overflow) and the
+    // accumulator rescale is skipped while no head's reference moves.  The
+    // result is the same softmax: sums and outputs share the reference.
+    const bool grow = mx > m_run + 8.0f;  // m_run = -inf: any valid row grows it
+    const float m_new = grow ? mx : m_run;
+    // v_exp_f32 directly: its arguments are <= 8 or -inf (exp2(-inf) = 0),
+    // and results below the smallest normal (weights under 2^-126 of the
+    // reference) flush to 0.  While no row of head `col` has been valid,
+    // m_new is -inf; subtracting 0 instead keeps p = 0 and alpha = 0 (it
+    // scales only zeros then) rather than forming -inf - -inf.
+    const float m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+    // the sums take the weights as the P.V product sees them (rounded to
+    // fp16), so that numerator and denominator use the same weights: the
+    // output is then a weighted mean of the rows whatever the rounding
+    float psum = 0.0f;
+    v8h pa;
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 0) * s2;
-            v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 1) * s2;
-            v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 2) * s2;
-            v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(half[d], 1.0f, 3) * s2;
-          }
-        };
-        auto fp8_row = [&](bool w) {
-          // window row: 16 E4M3 codes; absent row: zeros (its bytes may hold
-          // NaN codes, and its V must be 0 to meet p = 0)
-          const v2u x = odd ? hi : lo, y = odd ? lo : hi;
-          const uint32_t c4[4] = {w ? x[0] : 0u, w ? x[1] : 0u, w ? y[0] : 0u, w ? y[1] : 0u};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            v[2 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, false);
-            v[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c4[d], 1.0f, true);
-          }
-        };
-        if (kMode == kFp4Only) {
-          fp4_row();
-        } else if (kMode == kWindowOnly) {
-          fp8_row(present[sc][i]);
-        } else {
-          const int kind = rkind[sc * kSub + 4 * rg + i];
-          if (kind == 1) fp4_row();
-          else fp8_row(kind == 2);
-        }
-        v8h r0, r1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r0[2 * e] = v[e][0];
-          r0[2 * e + 1] = v[e][1];
-          r1[2 * e] = v[4 + e][0];
-          r1[2 * e + 1] = v[4 + e][1];
-        }
-        lds_st16(st_addr[i][0], r0);
-        lds_st16(st_addr[i][1], r1);
-      }
+    for (int k = 0; k < 8; ++k) {
+      pa[k] = (_Float16)__builtin_amdgcn_exp2f(lg[k] - m_sub);
+      psum += (float)pa[k];
+    }
+    psum = rows4_sum(psum);
+    l_run = l_run * alpha + psum;
+    // rescale output rows (heads 4g+i) by their alpha, only when some head
+    // with a nonzero accumulator moved its reference (wave-uniform test;
+    // every wave of the workgroup takes the same decision)
+    // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
+    if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
+      if (lane < 16) alph[wave][lane] = alpha;
       wave_lds_order();
+      const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
+    }
+    m_run = m_new;
 
-      // ---- partial logits S^T (32 rows x 16 heads) over this wave's 128 channels
+    // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128);
+    // every transposed read is issued before the first product
+    v8h vb[8];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        v4f sacc = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 8; ++c) {
+      const v4h v0 = lds_ld_tr(pv_addr[c]);
+      const v4h v1 = lds_ld_tr(pv_addr[c] + kRowBytes16);
+      vb[c] = v8h{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sacc = mfma16(lds_ld16(qk_addr[s] + rt * kRowBytes16), qb[s], sacc);
-        ssum[sc & 1][wave][rt][lane] = sacc;
+    for (int c = 0; c < 8; ++c) o_acc[c] = mfma16(pa, vb[c], o_acc[c]);
+    // the next sub-chunk's tile stores come after these reads
+    wave_lds_order();
+  };
+
+  // kind of the rows of sub-chunk sc (the same in every wave)
+  auto run_sub = [&](int sc, const SubLoads& L) {
+    const int r0 = row0 + sc * kSub, r1 = min(row1, r0 + kSub);
+    if (r1 <= a.topk) process(sc, L, std::integral_constant<int, kFp4Only>{});
+    else if (r0 >= a.topk) process(sc, L, std::integral_constant<int, kWindowOnly>{});
+    else process(sc, L, std::integral_constant<int, kMixed>{});
+  };
+
+  // ---- the sub-chunks through a ring of NB load buffers: the loads of the
+  // next NB - 1 sub-chunks are in flight while one is processed (the wait
+  // counter retires loads in issue order, so each sub-chunk waits only for
+  // its own rows)
+  // The ring turns by register copies, so that the loop body holds one copy
+  // of each sub-chunk kind's code.
+  const int n_rel = n_sub * kSub;
+  SubLoads buf[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) issue_sub(a, rslot, i * kSub, row0 + i * kSub, n_rel, wave, g, col, win_row0, buf[i]);
+  for (int sc = 0; sc < n_sub; ++sc) {
+    run_sub(sc, buf[0]);
+#pragma unroll
+    for (int i = 0; i + 1 < NB; ++i) buf[i] = buf[i + 1];
+    const int nx = sc + NB;
+    issue_sub(a, rslot, nx * kSub, row0 + nx * kSub, n_rel, wave, g, col, win_row0, buf[NB - 1]);
+  }
+
+  if (a.n_splits == 1) {
+    // ---- the whole list was this split's: normalize and write the output
+    // (heads 4g+i of lane (g, col) need their sums: lanes 0..15 hold l, m)
+    if (lane < 16) alph[wave][lane] = 1.0f / l_run;
+    wave_lds_order();
+    const v4f inv = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+    float* orow = a.out + ((int64_t)bt * a.H + ht * 16) * kD;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[(4 * g + i) * kD + 128 * wave + c * 16 + col] = o_acc[c][i] * inv[i];
+    if (a.out_lse && wave == 0 && lane < 16)
+      a.out_lse[(int64_t)bt * a.H + ht * 16 + lane] = (m_run + log2f(l_run)) * 0.69314718055994530942f;
+    return;
+  }
+  // ---- write this split's partials
+  const int64_t pidx = ((int64_t)bt * NHT + ht) * a.n_splits + split;
+  float* po = a.part_o + pidx * 16 * kD;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) po[(4 * g + i) * kD + 128 * wave + c * 16 + col] = o_acc[c][i];
+  if (wave == 0 && lane < 16) {
+    a.part_ml[pidx * 32 + lane] = m_run;
+    a.part_ml[pidx * 32 + 16 + lane] = l_run;
+  }
+}
+
+// ---------------------------------------------------------------- 64 heads
+// One workgroup per (b, t, split) serves all 64 heads, so that every row is
+// gathered and dequantized once: 8 waves dequantize the sub-chunk's 32 rows
+// (512 channels each) into a shared LDS tile.  Wave w = (head tile ht = w %
+// 4, channel half kh = w / 4) computes the logits S^T of all 32 rows for
+// its 16 heads over its 256 channels (that part of the query in registers);
+// the kh = 0 wave adds the other half's partial logits (fixed order), runs
+// the heads' online softmax and shares the fp16 weights P and the rescale
+// factors through LDS.  Wave w then owns output channels 64 w .. 64 w + 63
+// of all 64 heads and accumulates P.V from the tile, reading V transposed.
+constexpr int kHThreads = 512;
+constexpr int kTileRowHalves = kD;        // a tile row: 512 fp16 channels (64 chunks of 16 B)
+constexpr int kPStride = 40;              // P row (one head): 32 rows of fp16, padded to 80 B
+
+// Chunk k (8 channels) of tile row r sits at chunk k ^ bitrev4(r % 16) of
+// the row, which keeps all three access patterns free of bank conflicts: the
+// dequant stores and the Q.K operand loads (16 lanes: one chunk of 16 rows)
+// and the transposed P.V loads (16 lanes: 2 chunks of 4 rows).
+__device__ __forceinline__ int htile_off(int row, int chunk) {  // in halves
+  return row * kTileRowHalves + 8 * (chunk ^ swz(row));
+}
+
+// The row loads of one sub-chunk for lane L of wave w: row 16 (w % 2) +
+// L % 16, channels 32 c .. + 31 with c = 4 (w / 2) + L / 16.  FP4 row: 16
+// code bytes + the 16 scale bytes 16 (c / 8) .. + 15 of the entry (the
+// lane's two groups among them); window row: 32 E4M3 bytes.
+struct HLoads {
+  v4u lo, hi;
+  int s;
+};
+
+__device__ __forceinline__ void issue_hrow(const AttnArgs& a, const int* rslot, int rel, int abs_row, int n_rel,
+                                           int c32, const uint8_t* win_row0, HLoads& L) {
+  const int s = rel < n_rel ? rslot[rel] : kRowAbsent;
+  L.s = s;
+  const uint8_t* p0 = a.kv_pool;
+  const uint8_t* p1 = a.kv_pool;
+  if (s >= 0) {
+    const uint8_t* page = a.kv_pool + (int64_t)(s >> 6) * kPageBytes;
+    p0 = page + (s & 63) * kEntryCodes + 16 * c32;
+    p1 = page + kPage * kEntryCodes + (s & 63) * kEntryScales + 16 * (c32 >> 3);
+  } else if (s == kRowWindow) {
+    p0 = win_row0 + (int64_t)(abs_row - a.topk) * kD + 32 * c32;
+    p1 = p0 + 16;
+  }
+  L.lo = gld16(p0);
+  L.hi = gld16(p1);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t tile[2][kSub * kTileRowHalves];  // double-buffered
+  __shared__ __attribute__((aligned(16))) half_t pmat[64 * kPStride];            // P [head][row]
+  __shared__ __attribute__((aligned(16))) v4f spart[4][2][64];                   // kh = 1 partial logits
+  __shared__ __attribute__((aligned(16))) float salpha[64];
+  __shared__ __attribute__((aligned(16))) float sfin[2][64];                     // final m, l
+  __shared__ __attribute__((aligned(16))) float sqmax[2][64];
+  __shared__ int sgrow[4];
+  __shared__ __attribute__((aligned(16))) int rslot[kMaxRows + kSub];
+
+  const int unit = blockIdx.x;  // split + n_splits * (b*T + t)
+  if (unit >= a.n_splits * a.BT) return;
+  const int split = unit % a.n_splits;
+  const int bt = unit / a.n_splits;
+  const int b = bt / a.T, t = bt % a.T;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int ht = wave & 3, kh = wave >> 2;  // Q.K role
+  int n = a.n_entries[b];
+  n = min(n, a.max_pages * kPage);
+  const int n_rows = a.topk + kSwa;
+  const int row0 = split * a.split_rows;
+  const int row1 = min(n_rows, row0 + a.split_rows);
+  const int n_sub = (row1 - row0 + kSub - 1) / kSub;
+  const int n_rel = n_sub * kSub;
+  const int32_t* idx_row = a.topk_idx + (int64_t)bt * a.topk;
+  const uint8_t* win_row0 = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t) * kD;
+
+  // the query of head 16 ht + col, channels 256 kh + 32 s + 8 g .. + 7 (K
+  // slice s of the half), goes out first
+  v4u qraw[8];
+  {
+    const uint16_t* qrow = a.q + (((int64_t)bt * a.H) + ht * 16 + col) * kD + 256 * kh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qraw[s] = *reinterpret_cast<const v4u*>(qrow + 32 * s);
+  }
+
+  // ---- resolve the split's rows once (all index loads, then all page loads)
+  {
+    constexpr int kPer = (kMaxRows + kSub + kHThreads - 1) / kHThreads;  // 5
+    int jj[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int row = row0 + (int)threadIdx.x + k * kHThreads;
+      jj[k] = idx_row[max(0, min(row, a.topk - 1))];
+    }
+    int pp[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int lp = max(0, min(jj[k] >> 6, a.max_pages - 1));
+      pp[k] = a.page_table[(int64_t)b * a.max_pages + lp];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int r = (int)threadIdx.x + k * kHThreads;
+      const int row = row0 + r;
+      int sl = kRowAbsent;
+      if (row < row1) {
+        if (row < a.topk) {
+          const int j = jj[k];
+          if (j >= 0 && j < n && pp[k] >= 0 && pp[k] < a.n_pages) sl = (int)((int64_t)pp[k] * kPage + (j & 63));
+        } else {
+          sl = kRowWindow;
+        }
       }
-      // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
-      // and this buffer is rewritten only after the next sub-chunk's barrier
-      lds_barrier();
-      // row biases (0 or -inf) of rows 4g..4g+3 and 16+4g..16+4g+3
-      const v4f bias0 = *reinterpret_cast<const v4f*>(&rbias[sc * kSub + 4 * g]);
-      const v4f bias1 = *reinterpret_cast<const v4f*>(&rbias[sc * kSub + 16 + 4 * g]);
-      v4f part[4][2];
+      if (r < n_rel) rslot[r] = sl;
+    }
+  }
+  // each head's largest |q| over this wave's 256 channels (bf16 bits in the high half)
+  {
+    uint32_t mx = 0u;
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4)
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) part[w4][rt] = ssum[sc & 1][w4][rt][lane];
-      // fixed order: ((w0 + w1) + w2) + w3
-      v4f st[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) st[rt] = ((part[0][rt] + part[1][rt]) + part[2][rt]) + part[3][rt];
+      for (int e = 0; e < 4; ++e) mx = max(mx, max((qraw[s][e] << 16) & 0x7FFF0000u, qraw[s][e] & 0x7FFF0000u));
+    const float m = rows4_max(__uint_as_float(mx));
+    if (lane < 16) sqmax[kh][16 * ht + lane] = m;
+  }
+  __syncthreads();
 
-      // ---- online softmax for head `col` over rows 4g+i (+16)
+  // ---- the first sub-chunks' row loads (the ring below keeps NB in flight)
+  const int drow = 16 * (wave & 1) + (lane & 15);  // dequant role: this lane's row of a sub-chunk
+  const int c32 = 4 * (wave >> 1) + (lane >> 4);   // and its 32-channel piece
+  HLoads buf[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) issue_hrow(a, rslot, i * kSub + drow, row0 + i * kSub + drow, n_rel, c32, win_row0, buf[i]);
+
+  // ---- the query as the B operand, scaled per head by a power of two that
+  // puts its largest |q| in [2^14, 2^15) (fp16 never overflows; the logits
+  // take the inverse power back, exact)
+  v8h qb[8];
+  float lg_scale;
+  {
+    const float m = fmaxf(sqmax[0][16 * ht + col], sqmax[1][16 * ht + col]);
+    const int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 14;
+    const int sh = min(127, 14 - e);
+    const float up = __builtin_ldexpf(1.0f, sh);
+    lg_scale = a.sm_scale_log2 * __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      v4u pk;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const h2_t h = {(_Float16)(u2f(qraw[s][e2] << 16) * up), (_Float16)(u2f(qraw[s][e2] & 0xFFFF0000u) * up)};
+        pk[e2] = __builtin_bit_cast(uint32_t, h);
+      }
+      asm volatile("" : "+v"(pk));
+      qb[s] = __builtin_bit_cast(v8h, pk);
+    }
+  }
+
+  // LDS addresses (bytes) in tile buffer 0: the dequant stores (row drow,
+  // chunks 4 c32 + j), the Q.K operand reads (row 16 rt + col, chunk 4 s + g
+  // of the wave's half: slices s and s + 4 lie 256 bytes apart, since the
+  // swizzle keeps bits 4, 5 of the chunk), the transposed V reads (rows 8 g +
+  // col / 4 and + 4, channels 64 w + 16 ct + 4 (col % 4) .. + 3)
+  // (rows r and r + 16 share the swizzle: the second row tile is 16 KB on)
+  uint32_t st_addr[4], qk_addr[4], pv_addr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st_addr[j] = lds_addr(&tile[0][htile_off(drow, 4 * c32 + j)]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qk_addr[s] = lds_addr(&tile[0][htile_off(col, 32 * kh + 4 * s + g)]);
+  {
+    // K-elements of lane group g: rows 4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3
+    // (the second read 16 rows on, where the swizzle repeats; P is stored in
+    // the same order)
+    const int tr_row = 4 * g + (col >> 2), tq = col & 3;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      pv_addr[ct] = lds_addr(&tile[0][htile_off(tr_row, 8 * wave + 2 * ct + (tq >> 1)) + 4 * (tq & 1)]);
+  }
+  constexpr uint32_t kBufBytes = kSub * kTileRowHalves * 2;  // 32 KB
+  constexpr uint32_t kRows16 = 16 * kTileRowHalves * 2;      // 16 rows, bytes
+  // P row of a head holds its weights in the K order of the P.V product: row
+  // 16 rt + 4 g + i at 8 g + 4 rt + i.  Stores: head 16 ht + col, rows 16 rt
+  // + 4 g ..; reads: head 16 h4 + col, places 8 g .. 8 g + 7; head tiles lie
+  // 16 P rows apart
+  const uint32_t p_st = lds_addr(&pmat[(16 * ht + col) * kPStride + 8 * g]);
+  const uint32_t p_rd = lds_addr(&pmat[col * kPStride + 8 * g]);
+  constexpr uint32_t kPTile = 16 * kPStride * 2;
+
+  float m_run = -__builtin_inff();  // kh = 0: running reference (log2) of head 16 ht + col
+  float l_run = 0.0f;
+  v4f o_acc[4][4];                  // [head tile][channel tile]: heads 16 h4 + 4 g + i
+#pragma unroll
+  for (int h4 = 0; h4 < 4; ++h4)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) o_acc[h4][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // one code path for every sub-chunk: each lane's row is an FP4 entry, a
+  // window row or absent (lanes branch apart only in the one sub-chunk that
+  // holds both kinds)
+  auto process = [&](int sc, const HLoads& L) {
+    const uint32_t tb = (uint32_t)(sc & 1) * kBufBytes;
+    // ---- dequantize this lane's row piece (32 channels) into the tile
+    {
+      v8h d[4];
+      const int s = L.s;
+      auto fp4_row = [&](bool present) {
+        uint32_t pm = present ? 0xFFFFFFFFu : 0u;
+        asm volatile("" : "+v"(pm));
+        // groups 2 c32, 2 c32 + 1: bytes 2 (c32 % 8), + 1 of the 16 loaded
+        // scale bytes, picked by selects (a lane-dependent element index
+        // would put the load buffers in scratch memory)
+        const int wsel = (c32 & 7) >> 1;
+        const uint32_t w01 = (wsel & 1) ? L.hi[1] : L.hi[0];
+        const uint32_t w23 = (wsel & 1) ? L.hi[3] : L.hi[2];
+        const uint32_t sw = (((wsel & 2) ? w23 : w01) >> (16 * (c32 & 1))) & 0xFFFFu;
+        const uint32_t s0 = (sw & 0xFFu) * 0x101u & pm, s1 = (sw >> 8) * 0x101u & pm;
+        const h2_t sc0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, false);
+        const h2_t sc1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, false);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const h2_t scq = q < 2 ? sc0 : sc1;
+          const h2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(L.lo[q], 1.0f, 0) * scq;
+          const h2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(L.lo[q], 1.0f, 1) * scq;
+          const h2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(L.lo[q], 1.0f, 2) * scq;
+          const h2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(L.lo[q], 1.0f, 3) * scq;
+          d[q] = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        }
+      };
+      auto fp8_row = [&](bool w) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t c0 = w ? (q < 2 ? L.lo[2 * q] : L.hi[2 * q - 4]) : 0u;
+          const uint32_t c1 = w ? (q < 2 ? L.lo[2 * q + 1] : L.hi[2 * q - 3]) : 0u;
+          const h2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
+          const h2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
+          const h2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
+          const h2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, true);
+          d[q] = v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        }
+      };
+      if (s != kRowWindow) fp4_row(s >= 0);
+      else fp8_row(true);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lds_st16(st_addr[j] + tb, d[j]);
+    }
+    lds_barrier();  // 1: the tile is complete
+    // ---- Q.K role: partial logits of rows 16 rt + 4 g + i, head 16 ht + col,
+    // over this wave's channel half
+    v4f sacc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      sacc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v8h ka[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[s] = lds_ld16(qk_addr[s] + tb + kRows16 * (uint32_t)rt + 256u * (uint32_t)h);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[rt] = mfma16(ka[s], qb[4 * h + s], sacc[rt]);
+      }
+    }
+    if (kh == 1) {
+      spart[ht][0][lane] = sacc[0];
+      spart[ht][1][lane] = sacc[1];
+    }
+    lds_barrier();  // 2: the second halves' partial logits
+    if (kh == 0) {
+      // ---- logits (fixed order: first half + second half), online softmax
+      // with the lazy reference of the head-tile kernel above
+      const int sub0 = sc * kSub;
+      const v4i pr0 = *reinterpret_cast<const v4i*>(&rslot[sub0 + 4 * g]);
+      const v4i pr1 = *reinterpret_cast<const v4i*>(&rslot[sub0 + 16 + 4 * g]);
+      const v4f o0 = spart[ht][0][lane], o1 = spart[ht][1][lane];
       float lg[8];
       float mx = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // fma with a zero addend is the rounded product; -inf masks the row
-        lg[i] = __builtin_fmaf(st[0][i], a.sm_scale_log2, bias0[i]);
-        lg[4 + i] = __builtin_fmaf(st[1][i], a.sm_scale_log2, bias1[i]);
+        lg[i] = __builtin_fmaf(sacc[0][i] + o0[i], lg_scale, pr0[i] != kRowAbsent ? 0.0f : -__builtin_inff());
+        lg[4 + i] = __builtin_fmaf(sacc[1][i] + o1[i], lg_scale, pr1[i] != kRowAbsent ? 0.0f : -__builtin_inff());
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) mx = fmaxf(mx, lg[k]);
       mx = rows4_max(mx);
-      // Lazy reference: the running reference m_run moves only when a logit
-      // exceeds it by more than 8 (log2 units), so weights p stay <= 2^8 (exact
-      // range for the fp16 P operand and far from fp32 overflow) and the
-      // accumulator rescale is skipped while no head's reference moves.  The
-      // result is the same softmax: sums and outputs share the reference.
-      const bool grow = mx > m_run + 8.0f;  // m_run = -inf: any valid row grows it
+      const bool grow = mx > m_run + 8.0f;
       const float m_new = grow ? mx : m_run;
-      // v_exp_f32 directly: its arguments are <= 8 or -inf (exp2(-inf) = 0),
-      // and results below the smallest normal (weights under 2^-126 of the
-      // reference) flush to 0.  While no row of head `col` has been valid,
-      // m_new is -inf; subtracting 0 instead keeps p = 0 and alpha = 0 (it
-      // scales only zeros then) rather than forming -inf - -inf.
       const float m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+      const bool rescale = __ballot(grow && m_run != -__builtin_inff()) != 0;
       float psum = 0.0f;
-      v8h pa;
+      v4h pq[2];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float p = __builtin_amdgcn_exp2f(lg[k] - m_sub);
-        psum += p;
-        pa[k] = (_Float16)p;
+        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(lg[k] - m_sub);
+        pq[k >> 2][k & 3] = p;
+        psum += (float)p;
       }
       psum = rows4_sum(psum);
       l_run = l_run * alpha + psum;
-      // rescale output rows (heads 4g+i) by their alpha, only when some head
-      // with a nonzero accumulator moved its reference (wave-uniform test;
-      // every wave of the workgroup takes the same decision)
-      // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
-      if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
-        if (lane < 16) alph[wave][lane] = alpha;
-        wave_lds_order();
-        const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o_acc[c][i] *= al[i];
-      }
       m_run = m_new;
-
-      // ---- O (16 heads x 128 channels) += P (16 x 32 rows) . V (32 rows x 128)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v4h v0 = lds_ld_tr(pv_addr[c]);
-        const v4h v1 = lds_ld_tr(pv_addr[c] + kRowBytes16);
-        const v8h vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o_acc[c] = mfma16(pa, vb, o_acc[c]);
-      }
-      wave_lds_order();
+      for (int rt = 0; rt < 2; ++rt) *(__attribute__((address_space(3))) v4h*)(uintptr_t)(p_st + 8u * rt) = pq[rt];
+      if (lane < 16) salpha[16 * ht + lane] = alpha;
+      if (lane == 0) sgrow[ht] = rescale ? 1 : 0;
     }
-
-    // ---- write this split's partials
-    const int64_t pidx = ((int64_t)bt * NHT + ht) * a.n_splits + split;
-    float* po = a.part_o + pidx * 16 * kD;
+    lds_barrier();  // 3: P and the rescale factors
+    // ---- P.V role: rescale, then O[heads][64 w + 16 ct ..] += P . V
+    if ((sgrow[0] | sgrow[1] | sgrow[2] | sgrow[3]) != 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+      for (int h4 = 0; h4 < 4; ++h4) {
+        const v4f al = *reinterpret_cast<const v4f*>(&salpha[16 * h4 + 4 * g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[(4 * g + i) * kD + 128 * wave + c * 16 + col] = o_acc[c][i];
-    if (wave == 0 && lane < 16) {
-      a.part_ml[pidx * 32 + lane] = m_run;
-      a.part_ml[pidx * 32 + 16 + lane] = l_run;
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o_acc[h4][ct][i] *= al[i];
+      }
+    }
+    v8h vb[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const v4h v0 = lds_ld_tr(pv_addr[ct] + tb);
+      const v4h v1 = lds_ld_tr(pv_addr[ct] + tb + kRows16);
+      vb[ct] = v8h{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4) {
+      const v8h pa = lds_ld16(p_rd + kPTile * (uint32_t)h4);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) o_acc[h4][ct] = mfma16(pa, vb[ct], o_acc[h4][ct]);
     }
   };
-  if (row1 <= a.topk) run(ModeTag<kFp4Only>{});
-  else if (row0 >= a.topk) run(ModeTag<kWindowOnly>{});
-  else run(ModeTag<kMixed>{});
+
+  for (int sc = 0; sc < n_sub; ++sc) {
+    process(sc, buf[0]);
+#pragma unroll
+    for (int i = 0; i + 1 < NB; ++i) buf[i] = buf[i + 1];
+    const int nx = sc + NB;
+    issue_hrow(a, rslot, nx * kSub + drow, row0 + nx * kSub + drow, n_rel, c32, win_row0, buf[NB - 1]);
+  }
+
+  // ---- every head's (m, l) to all waves
+  if (kh == 0 && lane < 16) {
+    sfin[0][16 * ht + lane] = m_run;
+    sfin[1][16 * ht + lane] = l_run;
+  }
+  __syncthreads();
+  // lane (g, col) of wave w holds O[16 h4 + 4 g + i][64 w + 16 ct + col]
+  if (a.n_splits == 1) {
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4) {
+      const v4f lv = *reinterpret_cast<const v4f*>(&sfin[1][16 * h4 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float inv = 1.0f / lv[i];
+        float* orow = a.out + ((int64_t)bt * a.H + 16 * h4 + 4 * g + i) * kD + 64 * wave + col;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) orow[16 * ct] = o_acc[h4][ct][i] * inv;
+      }
+    }
+    if (a.out_lse && threadIdx.x < 64)
+      a.out_lse[(int64_t)bt * a.H + threadIdx.x] =
+          (sfin[0][threadIdx.x] + log2f(sfin[1][threadIdx.x])) * 0.69314718055994530942f;
+    return;
+  }
+  // ---- partials in the head-tile kernel's layout: [bt][ht][split][16][512]
+#pragma unroll
+  for (int h4 = 0; h4 < 4; ++h4) {
+    const int64_t pidx = ((int64_t)bt * 4 + h4) * a.n_splits + split;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* po = a.part_o + (pidx * 16 + 4 * g + i) * kD + 64 * wave + col;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) po[16 * ct] = o_acc[h4][ct][i];
+    }
+  }
+  if (threadIdx.x < 64) {
+    const int h = threadIdx.x;
+    const int64_t pidx = ((int64_t)bt * 4 + (h >> 4)) * a.n_splits + split;
+    a.part_ml[pidx * 32 + (h & 15)] = sfin[0][h];
+    a.part_ml[pidx * 32 + 16 + (h & 15)] = sfin[1][h];
+  }
 }
 
 struct CombineArgs {
@@ -460,55 +920,63 @@ struct CombineArgs {
 // (max, sum, output).  Wave 0 loads the (max, sum) pairs first, then every
 // thread issues its loads of all splits' output rows; the split weights are
 // formed (one wave, in registers) while those are in flight.
-constexpr int kMaxSplits = (CSA2_MAX_TOPK + CSA2_SWA + kRowsPerSplit - 1) / kRowsPerSplit;
+constexpr int kMaxSplits = 24;
+constexpr int kLoadRing = 3;  // sub-chunks whose row loads are in flight together
 
+template <int MAXS>
 __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
-  __shared__ float wsplit[kMaxSplits];
+  __shared__ float wsplit[MAXS];
   __shared__ float inv_l;
   const int h = blockIdx.x % a.H;
   const int bt = blockIdx.x / a.H;
   const int NHT = a.H >> 4, ht = h >> 4, hh = h & 15;
   const int64_t base = ((int64_t)bt * NHT + ht) * a.n_splits;
   const int lane = lane_id();
-  const bool in = lane < a.n_splits;
+  const int tid = (int)threadIdx.x;
+  // (max, sum) of split `tid` (threads 0..MAXS-1; MAXS <= 128)
+  const bool in = tid < a.n_splits;
   float ms = -__builtin_inff(), ls = 0.0f;
-  if (threadIdx.x < 64 && in) {
-    ms = a.part_ml[(base + lane) * 32 + hh];
-    ls = a.part_ml[(base + lane) * 32 + 16 + hh];
+  if (in) {
+    ms = a.part_ml[(base + tid) * 32 + hh];
+    ls = a.part_ml[(base + tid) * 32 + 16 + hh];
   }
   // loads complete in issue order: keep the pairs ahead of the rows
   asm volatile("" ::: "memory");
-  const int c = threadIdx.x * 4;
+  const int c = tid * 4;
   // unconditional loads (splits past n_splits re-read the last one and are
   // not used), so that no branch separates them and each waits only for its own
-  v4f po[kMaxSplits];
+  v4f po[MAXS];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < MAXS; ++s) {
     const int sc = min(s, a.n_splits - 1);
     po[s] = *reinterpret_cast<const v4f*>(a.part_o + ((base + sc) * 16 + hh) * kD + c);
   }
   // every row load is issued before the first wait for the pairs
   asm volatile("" : "+v"(ms), "+v"(ls)::"memory");
-  if (threadIdx.x < 64) {
-    float M = ms;
+  // the global maximum and the weighted sum, over the splits, in thread order
+  __shared__ float red[2][2];
+  float M = ms;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float wgt = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - M);
-    float L = wgt * ls;
-    // fixed-order sum over the splits (lane order)
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[0][tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  const float wgt = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - M);
+  float L = wgt * ls;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
-    // splits past n_splits get weight 0 (their re-read rows are finite)
-    if (lane < kMaxSplits) wsplit[lane] = in ? wgt : 0.0f;
-    if (lane == 0) {
-      inv_l = 1.0f / L;
-      if (a.out_lse) a.out_lse[(int64_t)bt * a.H + h] = (M + log2f(L)) * 0.69314718055994530942f;
-    }
+  for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+  if (lane == 0) red[1][tid >> 6] = L;
+  if (tid < MAXS) wsplit[tid] = in ? wgt : 0.0f;
+  __syncthreads();
+  if (tid == 0) {
+    const float Lt = red[1][0] + red[1][1];
+    inv_l = 1.0f / Lt;
+    if (a.out_lse) a.out_lse[(int64_t)bt * a.H + h] = (M + log2f(Lt)) * 0.69314718055994530942f;
   }
-  lds_barrier();
+  __syncthreads();
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) acc += wsplit[s] * po[s];
+  for (int s = 0; s < MAXS; ++s) acc += wsplit[s] * po[s];
   *reinterpret_cast<v4f*>(a.out + ((int64_t)bt * a.H + h) * kD + c) = acc * inv_l;
 }
 
@@ -516,11 +984,46 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
 
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-int n_splits_for(int topk) { return (topk + CSA2_SWA + csa2::kRowsPerSplit - 1) / csa2::kRowsPerSplit; }
+
+// 64 heads take the all-heads kernel (one workgroup per (b, t, split));
+// 16 or 32 heads the head-tile kernel (one per (b, t, head tile, split)).
+bool all_heads(int H) { return H == 64; }
+
+// Rows per split (a multiple of 32) and the number of splits of one (b, t)'s
+// [top-k | window] row list: about kTargetWorkgroups workgroups in all.
+void split_plan(int BT, int H, int topk, int* n_splits, int* split_rows) {
+  if (all_heads(H)) {
+    const int rows = topk + CSA2_SWA;
+    const int max_splits = std::min((rows + csa2::kSub - 1) / csa2::kSub, csa2::kMaxSplits);
+    int ns = std::max(1, std::min((csa2::kTargetWorkgroups + BT - 1) / BT, max_splits));
+    int per = (rows + ns - 1) / ns;
+    per = (per + csa2::kSub - 1) / csa2::kSub * csa2::kSub;
+    *split_rows = per;
+    *n_splits = (rows + per - 1) / per;
+    return;
+  }
+  const int rows = topk + CSA2_SWA;
+  const int max_splits = (rows + csa2::kSub - 1) / csa2::kSub;
+  const int units = BT * (H / 16);
+  // a large batch takes two splits per list (two workgroups per compute unit,
+  // so that one's waits hide behind the other's work)
+  const int target = units >= csa2::kTargetWorkgroups / 2 ? 2 * csa2::kTargetWorkgroups : csa2::kTargetWorkgroups;
+  int ns = (target + units - 1) / units;
+  ns = std::max(1, std::min(ns, max_splits));
+  // whole sub-chunks per split, rounded down (so at least ns splits), then
+  // no more than kMaxSplits splits
+  int per = std::max(csa2::kSub, rows / ns / csa2::kSub * csa2::kSub);
+  const int min_per = (rows + csa2::kMaxSplits - 1) / csa2::kMaxSplits;
+  if (per < min_per) per = (min_per + csa2::kSub - 1) / csa2::kSub * csa2::kSub;
+  *split_rows = per;
+  *n_splits = (rows + per - 1) / per;
+}
 }  // namespace
 
 extern "C" size_t csa2_attn_ws_bytes(int32_t B, int32_t T, int32_t H, int32_t topk) {
-  const size_t ns = (size_t)n_splits_for(topk);
+  int ns, per;
+  split_plan(B * T, H, topk, &ns, &per);
+  if (ns == 1) return 256;  // no partials
   const size_t units = (size_t)B * T * (H / 16) * ns;
   return align256(units * 16 * csa2::kD * 4) + align256(units * 32 * 4);
 }
@@ -532,12 +1035,16 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
                                 float* out_lse, void* ws, size_t ws_bytes, csa2_stream_t stream) {
   if (!q || !kv_pool || !page_table || !n_entries || !topk_idx || !swa || !out)
     return CSA2_ERR_INVALID_ARG;
+  // 16-byte rows of q and of the window are read with aligned loads
+  if (((uintptr_t)q & 15) || ((uintptr_t)swa & 15)) return CSA2_ERR_INVALID_ARG;
   if (B <= 0 || T <= 0 || H <= 0 || n_pages <= 0 || max_pages <= 0 || topk <= 0)
     return CSA2_ERR_INVALID_ARG;
   if (topk > CSA2_MAX_TOPK) return CSA2_ERR_INVALID_ARG;
   if (!(H == 16 || H == 32 || H == 64)) return CSA2_ERR_UNSUPPORTED;
   if (T > CSA2_MAX_T) return CSA2_ERR_UNSUPPORTED;
   if ((int64_t)B * T > 65535) return CSA2_ERR_UNSUPPORTED;
+  // cache slots (page * 64 + offset) are held as int32
+  if (n_pages > (int64_t)INT32_MAX / csa2::kPage) return CSA2_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return CSA2_ERR_INVALID_ARG;
   const size_t need = csa2_attn_ws_bytes(B, T, H, topk);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
@@ -554,16 +1061,27 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   aa.swa = swa;
   aa.T = T;
   aa.H = H;
-  aa.n_splits = n_splits_for(topk);
   aa.BT = B * T;
+  split_plan(B * T, H, topk, &aa.n_splits, &aa.split_rows);
   const size_t units = (size_t)B * T * (H / 16) * aa.n_splits;
-  aa.part_o = reinterpret_cast<float*>(ws);
-  aa.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(units * 16 * csa2::kD * 4));
+  if (aa.n_splits > 1) {
+    aa.part_o = reinterpret_cast<float*>(ws);
+    aa.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(units * 16 * csa2::kD * 4));
+  } else {
+    aa.out = out;
+    aa.out_lse = out_lse;
+  }
   const int n_units = aa.n_splits * B * T;
-  const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
-  CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel, dim3(grid),
-              dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
+  if (all_heads(H)) {
+    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel<2>, dim3(n_units),
+                dim3(csa2::kHThreads), (hipStream_t)stream, aa);
+  } else {
+    const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
+    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel<csa2::kLoadRing>, dim3(grid),
+                dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
+  }
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  if (aa.n_splits == 1) return CSA2_OK;
   csa2::CombineArgs ca{};
   ca.part_o = aa.part_o;
   ca.part_ml = aa.part_ml;
@@ -571,7 +1089,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   ca.n_splits = aa.n_splits;
   ca.out = out;
   ca.out_lse = out_lse;
-  CSA2_LAUNCH(CSA2_K_ATTN_COMBINE, csa2::attn_combine_kernel, dim3(B * T * H), dim3(128),
+  CSA2_LAUNCH(CSA2_K_ATTN_COMBINE, csa2::attn_combine_kernel<csa2::kMaxSplits>, dim3(B * T * H), dim3(128),
               (hipStream_t)stream, ca);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }

@@ -53,9 +53,11 @@ def test_workspace_sizes(L):
     full = csa2.workspace_bytes(csa2.OP_INDEX_FULL, 4, 1, 64, 262144, 2048)
     assert full >= 4 * 262144 * 4 + 4 * 32768 * 4
     assert csa2.workspace_bytes(csa2.OP_INDEX_REINDEX, 8, 1, 64, 0, 2048) >= 8 * 16384 * 4
+    # attention: a small batch splits each row list (fp32 partials of 16 heads x 512 per split);
+    # a large batch keeps one split per (b, t, head tile) and needs no partials
     attn = csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, 4, 1, 64, 0, 2048)
-    n_splits = (2048 + 128 + 127) // 128
-    assert attn >= 4 * 4 * n_splits * 16 * 512 * 4
+    assert attn >= 4 * 4 * 2 * 16 * 512 * 4
+    assert csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, 256, 1, 64, 0, 2048) <= 4096
     assert csa2.workspace_bytes(99, 1, 1, 1, 1, 1) == 0
     assert csa2.workspace_bytes(csa2.OP_INDEX_FULL, 0, 1, 64, 100, 8) == 0
 
