@@ -21,7 +21,8 @@ __all__ = [
     "Csa2Error", "lib", "load", "quantize_kv", "index_full", "index_reindex", "sparse_attn",
     "workspace_bytes", "status_str", "Workspace", "D", "DI", "PAGE", "PAGE_BYTES",
     "KIDX_PAGE_BYTES", "BLOCK", "SWA", "OP_INDEX_FULL", "OP_INDEX_REINDEX", "OP_SPARSE_ATTN",
-    "index_full_noalloc", "NOALLOC_SCRATCH_BYTES", "ERR_SCRATCH",
+    "index_full_noalloc", "NOALLOC_SCRATCH_BYTES", "ERR_SCRATCH", "ROW_BAD_SCALE", "ROW_UNRANKED",
+    "select_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,11 +34,13 @@ MX_KIDX_PAGE_BYTES = 4352  # MXFP4 indexer keys: 64 x 64 code bytes + 64 x 4 E8M
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_SPARSE_ATTN = 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 32 << 20  # csa2_index_full_noalloc's fixed per-GPU scratch
 ERR_SCRATCH = -5
+ROW_BAD_SCALE = -2   # indexer output mark: an MXFP4 key of the row has a scale code outside 119..133
+ROW_UNRANKED = -3    # indexer output mark under select_path(2): the candidate path declined the row
 
 EXPORTS = (
     "csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
     "csa2_workspace_bytes", "csa2_status_str", "csa2_abi_version", "csa2_time_kernel",
-    "csa2_test_keep_histograms", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
+    "csa2_test_select_path", "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4",
     "csa2_rope_write_caches", "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
     "csa2_index_full_noalloc", "csa2_index_full_causal", "csa2_index_reindex_causal",
 )
@@ -94,8 +97,8 @@ def load(path: str = LIB_PATH):
     L.csa2_abi_version.restype = ctypes.c_int
     L.csa2_time_kernel.argtypes = [ctypes.c_int, P, P]
     L.csa2_time_kernel.restype = ctypes.c_int
-    L.csa2_test_keep_histograms.argtypes = [ctypes.c_int]
-    L.csa2_test_keep_histograms.restype = ctypes.c_int
+    L.csa2_test_select_path.argtypes = [ctypes.c_int]
+    L.csa2_test_select_path.restype = ctypes.c_int
     for fn in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
                "csa2_index_full_mxfp4", "csa2_index_reindex_mxfp4", "csa2_rope_write_caches",
                "csa2_compress", "csa2_index_full_write", "csa2_index_full_mxfp4_write",
@@ -111,6 +114,11 @@ def lib():
 
 def status_str(status: int) -> str:
     return lib().csa2_status_str(int(status)).decode()
+
+
+def select_path(mode: int) -> None:
+    """Test aid: 0 default, 1 whole lists only, 2 candidate segments only."""
+    _check("csa2_test_select_path", lib().csa2_test_select_path(int(mode)))
 
 
 def workspace_bytes(op: int, B: int, T: int, heads: int, max_n_entries: int = 0, topk: int = 0) -> int:

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["api.hip", "quantize.hip", "compress.hip", "index.hip", "attention.hip"]
+SOURCES = ["api.hip", "quantize.hip", "compress.hip", "score.hip", "select.hip", "index.hip", "attention.hip"]
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,5 +1,6 @@
 // C ABI entry points that are not tied to one kernel family.
 #include "common.h"
+#include "index_common.h"
 
 extern "C" size_t csa2_index_ws_bytes(int op, int32_t B, int32_t T, int32_t max_n,
                                       int32_t pool_blocks);
@@ -34,7 +35,7 @@ extern "C" const char* csa2_status_str(int status) {
   }
 }
 
-extern "C" int csa2_abi_version(void) { return 107; }
+extern "C" int csa2_abi_version(void) { return 108; }
 
 namespace csa2 {
 KernelEvents& kernel_events(int kernel) {
@@ -52,14 +53,8 @@ extern "C" int csa2_time_kernel(int kernel, void* start_event, void* stop_event)
   return CSA2_OK;
 }
 
-namespace csa2 {
-bool& keep_histograms() {
-  static bool keep = false;
-  return keep;
-}
-}  // namespace csa2
-
-extern "C" int csa2_test_keep_histograms(int on) {
-  csa2::keep_histograms() = on != 0;
+extern "C" int csa2_test_select_path(int mode) {
+  if (mode < 0 || mode > 2) return CSA2_ERR_INVALID_ARG;
+  csa2::select_mode() = mode;
   return CSA2_OK;
 }

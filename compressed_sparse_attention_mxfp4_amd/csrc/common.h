@@ -69,8 +69,6 @@ struct KernelEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 KernelEvents& kernel_events(int kernel);
-// Test aid: the scans leave the level-1 histograms as they are.
-bool& keep_histograms();
 
 }  // namespace csa2
 

@@ -63,6 +63,9 @@ extern "C" {
 #define CSA2_MAX_INDEX_HEADS 64    /* indexer heads HI */
 #define CSA2_MAX_T 256             /* query tokens per sequence (decode: 1..4; prefill chunks up to 256) */
 #define CSA2_MAX_WRITE_ROWS 1024   /* rows of the cache write fused into csa2_index_full_write */
+/* Output marks of the indexer calls (every output slot of the (b, t) row): */
+#define CSA2_ROW_BAD_SCALE (-2)    /* an MXFP4 key of the row has a scale code outside 119..133 */
+#define CSA2_ROW_UNRANKED (-3)     /* test aid csa2_test_select_path(2) only: the fast path declined */
 #define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20) /* fixed per-GPU scratch of csa2_index_full_noalloc */
 
 enum csa2_status {
@@ -196,11 +199,11 @@ int csa2_index_full(const uint8_t *q_idx, const float *w, const uint8_t *kidx_po
 /*
  * csa2_index_full together with the step's FP4 cache write (csa2_quantize_kv
  * of `rows` rows into kv_pool, kv_pages pages), in the same launches: the
- * Full selection's first workgroup writes the rows before its selection.
+ * Full selection's workgroups write the rows before their selections.
  * The indexer reads nothing the write changes, and a reader of the new
  * entries (csa2_sparse_attn) launched after this call on the same stream sees
  * them, so the results equal the two calls in sequence; the step saves one
- * kernel launch.  Arguments as csa2_index_full and csa2_quantize_kv (rows
+ * kernel launch (the selection's workgroups share the rows).  Arguments as csa2_index_full and csa2_quantize_kv (rows
  * whose slot lies outside the pool are skipped); csa2_index_full_mxfp4_write
  * takes the indexer keys in the MXFP4 layout of csa2_index_full_mxfp4.
  * Returns CSA2_ERR_INVALID_ARG for rows < 0, kv_pages < 0, or (rows > 0) a
@@ -303,9 +306,13 @@ int csa2_index_reindex(const uint8_t *q_idx, const float *w, const uint8_t *kidx
  *           e * 64 (channel 2i in the low nibble of byte i, nibble = sign << 3
  *           | magnitude code), then entry e's 4 scale bytes at 4096 + e * 4
  *           (byte g scales channels 32g .. 32g + 31; code s means 2^(s - 127)).
- * Precondition (not checked on the device): every scale code s of a visible
- * entry satisfies 119 <= s <= 133 (2^-8 .. 2^6).  Every key value is then a
- * multiple of 2^-9 of magnitude <= 384 and the scores are exact as above.
+ * Scale codes 119 <= s <= 133 (2^-8 .. 2^6) are supported: every key value
+ * is then a multiple of 2^-9 of magnitude <= 384 and the scores are exact as
+ * above.  A (b, t) row whose scanned entries (Full: the token's visible
+ * entries; Reindex: the entries of its pool blocks) hold another scale code
+ * is reported instead of ranked: every out_topk slot of the row holds
+ * CSA2_ROW_BAD_SCALE, and in Full mode every out_pool slot and out_pool_n
+ * as well.  Other rows are unaffected.
  */
 int csa2_index_full_mxfp4(const uint8_t *q_idx, const float *w, const uint8_t *kidx_mx,
                           int64_t n_pages, const int32_t *page_table, int32_t max_pages,
@@ -367,15 +374,18 @@ enum csa2_kernel {
 int csa2_time_kernel(int kernel, void *start_event, void *stop_event);
 
 /*
- * Test aid (not part of the method): with `on` nonzero, the indexer scans
- * stop clearing their level-1 histograms in the workspace, so the selection
- * starts from whatever counts the workspace already holds (for example a
- * previous call's).  The selection checks those counts against the list it
- * ranks and counts the list's own keys when they disagree, so the results
- * stay exact; this switch lets a test reach that path.  Process-wide setting,
- * not thread-safe.  Returns CSA2_OK.
+ * Test aid (not part of the method): the path of the indexer selections.
+ * The scan leaves, per row, list and workgroup, the keys at or above a local
+ * threshold; the selection ranks their union when it can prove that union
+ * holds the exact top-k (or pool), and the whole list otherwise.
+ *   mode 0 (default): that choice; 1: always the whole lists; 2: the union
+ *   only: a row it cannot rank exactly gets CSA2_ROW_UNRANKED in every
+ *   output slot (and out_pool_n) instead.
+ * Modes 0 and 1 give identical results; 1 and 2 let a test reach each path.
+ * Process-wide setting, not thread-safe.  Returns CSA2_OK, or
+ * CSA2_ERR_INVALID_ARG for another mode.
  */
-int csa2_test_keep_histograms(int on);
+int csa2_test_select_path(int mode);
 
 /* Workspace bytes a call needs (op = enum csa2_op; `heads` = HI for the
  * indexer calls, H for attention; `max_n_entries` unused for attention). */

@@ -45,8 +45,15 @@ def test_status_strings_and_version(L):
     assert csa2.status_str(0) == "ok"
     assert "workspace" in csa2.status_str(WORKSPACE)
     assert csa2.status_str(12345) == "unknown status"
-    assert L.csa2_abi_version() == 107
+    assert L.csa2_abi_version() == 108
     assert "scratch" in csa2.status_str(csa2.ERR_SCRATCH)
+
+
+def test_select_path_test_aid(L):
+    assert L.csa2_test_select_path(3) == INVALID
+    assert L.csa2_test_select_path(-1) == INVALID
+    for mode in (1, 2, 0):
+        assert L.csa2_test_select_path(mode) == 0
 
 
 def test_workspace_sizes(L):

@@ -528,33 +528,94 @@ def test_index_deterministic():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("poison", ["stale", "random"])
-def test_index_recount_when_histogram_disagrees(oracle, poison):
-    """The selection takes the scan's level-1 histogram as a hint only.  With
-    the scans told to keep the histograms, they hold a previous call's counts
-    plus this call's ("stale") or random words ("random"); the selections
-    must notice the disagreement, count their lists' own keys and still
-    return the exact Full and Reindex results."""
-    say(f"index with a {poison} level-1 histogram (selection recount)")
-    wl = small_workload([40000, 9000], T=2, HI=16, topk=512, seed=21)
+@pytest.mark.parametrize("mode", [1, 2])
+def test_index_selection_paths(oracle, mode):
+    """The selections rank the union of the scan's candidate segments when they can show it
+    holds the exact top-k and pool, and the whole lists otherwise.  Mode 1 ranks the whole lists
+    always, mode 2 the segments only (a row they cannot rank would read ROW_UNRANKED); on random
+    scores both give the oracle's Full and Reindex results on every row."""
+    say(f"index full + reindex, selection path mode {mode}")
+    wl = small_workload([40000, 9000, 262144], T=2, HI=16, topk=512, seed=21)
     other = synth.layer_inputs("full", wl.B, wl.T, 16, 16, 22)
     layer = wl.layers[0]
-    ws = csa2.Workspace()
     args = (dev(wl.kidx_pool), dev(wl.paging.page_table), dev(wl.n_entries))
     ref = oracle_index_full(oracle, wl, layer)
-    csa2.index_full(dev(other.q_idx), dev(other.w), *args, wl.max_n, wl.topk, 2048, ws=ws)
-    if poison == "random":
-        ws.buf.copy_(torch.randint(0, 256, ws.buf.shape, dtype=torch.uint8, device="cuda"))
-    csa2.lib().csa2_test_keep_histograms(1)
-    try:
-        got = csa2.index_full(dev(layer.q_idx), dev(layer.w), *args, wl.max_n, wl.topk, 2048, ws=ws)
-        assert_index_equal(got, ref)
-        rtk = csa2.index_reindex(dev(other.q_idx), dev(other.w), *args, got[1], got[2], wl.topk, ws=ws)
-    finally:
-        csa2.lib().csa2_test_keep_histograms(0)
     ref_rtk = oracle.index_reindex(other.q_idx, other.w, wl.kidx_pool, wl.paging.page_table,
                                    wl.n_entries, ref[1], ref[2], wl.topk)
+    csa2.select_path(mode)
+    try:
+        got = csa2.index_full(dev(layer.q_idx), dev(layer.w), *args, wl.max_n, wl.topk, 2048)
+        rtk = csa2.index_reindex(dev(other.q_idx), dev(other.w), *args, got[1], got[2], wl.topk)
+        torch.cuda.synchronize()
+    finally:
+        csa2.select_path(0)
+    assert_index_equal(got, ref)
     assert np.array_equal(host(rtk), ref_rtk)
+
+
+def test_index_segments_decline_when_all_scores_tie(oracle):
+    """One sequence of 262,144 entries whose scores are all +0: every workgroup keeps all of its
+    keys, more than the selection takes from segments, so the candidate path declines the row
+    (mode 2: every slot and the count read ROW_UNRANKED) and the default path ranks the whole
+    lists, ties to the lowest indices, as the oracle does."""
+    say("index full 262,144 equal scores: the candidate path declines, the whole lists rank")
+    wl = small_workload([262144], T=1, HI=4, topk=2048, seed=13, q_codes=np.zeros((1, 1, 4, 128), np.uint8))
+    ref = oracle_index_full(oracle, wl, wl.layers[0])
+    csa2.select_path(2)
+    try:
+        declined = [host(x) for x in gpu_index_full(wl, wl.layers[0])]
+    finally:
+        csa2.select_path(0)
+    for x in declined:
+        assert (x == csa2.ROW_UNRANKED).all()
+    assert_index_equal(gpu_index_full(wl, wl.layers[0]), ref)
+
+
+def test_index_mxfp4_bad_scale_rows_reported(oracle):
+    """MXFP4 keys whose scale code lies outside 119..133 are reported, not ranked: a (b, t) row
+    whose scanned entries hold one reads ROW_BAD_SCALE in every top-k slot (Full: also every pool
+    slot and the count); a bad code in an entry the row does not see changes nothing, and the
+    other rows equal the oracle.  The oracle (which refuses such codes) sees the pool before the
+    codes were changed: the rows compared with it do not read the changed entries."""
+    n = [3000, 1000, 777]
+    say(f"index full + reindex MXFP4 with out-of-range scale codes n={n}")
+    wl = small_workload(n, T=2, HI=16, topk=256, seed=33)
+    mx_ok = synth.mxfp4_key_pool(wl.paging.n_pages, 47)
+    mx = mx_ok.copy()
+    pt = wl.paging.page_table
+
+    def set_scale(b, j, g, code):
+        mx[pt[b, j // 64], 4096 + (j % 64) * 4 + g] = code
+
+    set_scale(0, 3005, 1, 200)   # past n[0] on an allocated page: not visible
+    set_scale(1, 500, 2, 118)    # below the range
+    set_scale(2, 776, 0, 134)    # the last visible entry, above the range
+    L = wl.layers[0]
+    args = (dev(mx), dev(pt), dev(wl.n_entries))
+    tk, pl, pn = csa2.index_full(dev(L.q_idx), dev(L.w), *args, wl.max_n, wl.topk, 2048, mxfp4=True)
+    ref = oracle.index_full_mxfp4(L.q_idx, L.w, mx_ok, pt, wl.n_entries, wl.topk, 2048)
+    tk, pl, pn = host(tk), host(pl), host(pn)
+    assert np.array_equal(tk[0], ref[0][0]) and np.array_equal(pl[0], ref[1][0]) and np.array_equal(pn[0], ref[2][0])
+    for b in (1, 2):
+        assert (tk[b] == csa2.ROW_BAD_SCALE).all() and (pl[b] == csa2.ROW_BAD_SCALE).all()
+        assert (pn[b] == csa2.ROW_BAD_SCALE).all()
+    # Reindex over the oracle's pools: a row is reported when its pool holds the bad entry
+    other = synth.layer_inputs("full", wl.B, 2, 16, 16, 48)
+    rtk = host(csa2.index_reindex(dev(other.q_idx), dev(other.w), *args, dev(ref[1]), dev(ref[2]), wl.topk,
+                                  mxfp4=True))
+    ref_rtk = oracle.index_reindex_mxfp4(other.q_idx, other.w, mx_ok, pt, wl.n_entries, ref[1], ref[2], wl.topk)
+    n_reported = 0
+    for b in range(3):
+        for t in range(2):
+            blocks = set(ref[1][b, t, : ref[2][b, t]].tolist())
+            bad = (b == 1 and 500 // 8 in blocks) or (b == 2 and 776 // 8 in blocks)
+            if bad:
+                n_reported += 1
+                assert (rtk[b, t] == csa2.ROW_BAD_SCALE).all(), (b, t)
+            else:
+                assert np.array_equal(rtk[b, t], ref_rtk[b, t]), (b, t)
+    # sequence 2 has 98 blocks, all in its pools
+    assert n_reported >= 2
 
 
 def test_group_128k_b8_full_reindex_reuse(oracle):
