@@ -160,6 +160,8 @@ int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint
                               HI, topk, pool_blocks);
   if (st) return st;
   if (!pool || !pool_n || !out_topk) return CSA2_ERR_INVALID_ARG;
+  // the scan keeps physical entry indices (page * 64 + entry) in 32 bits
+  if (n_pages > (int64_t)INT32_MAX / csa2::kPage) return CSA2_ERR_UNSUPPORTED;
   const size_t need = csa2_index_ws_bytes(CSA2_OP_INDEX_REINDEX, B, T, 0, pool_blocks);
   if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
   const int max_n = (int)std::min<int64_t>((int64_t)max_pages * csa2::kPage, CSA2_MAX_ENTRIES);

@@ -149,7 +149,34 @@ struct ChunkKeys {
 struct RowCtx {
   int b = 0, t = 0, n = 0, n_pos = 0;
   const int32_t* pool_row = nullptr;
+  // pool mode: the workgroup's pool slots slot0 .. slot0 + nslots - 1
+  // resolved to physical entries (LDS, see pool_slot_word)
+  const int* pslot = nullptr;
+  int slot0 = 0, nslots = 0;
 };
+
+// Pool mode: the word of pool slot `slot`: (physical entry index of the
+// block's first entry) | (visible entries of the block - 1), or -1 when the
+// block is not visible or its page is not usable.  The physical index is a
+// multiple of 8 (blocks of 8 never cross a 64-entry page).
+__device__ __forceinline__ int pool_slot_word(const ScoreArgs& a, const RowCtx& r, int slot) {
+  const int nb = (r.n + kBlock - 1) / kBlock;
+  const int pn = r.n_pos / kBlock;
+  // both loads are unconditional (clamped indices, masked after)
+  const int blk = r.pool_row[max(0, min(slot, a.pool_blocks - 1))];
+  const int lp = max(0, min(blk >> 3, a.max_pages - 1));
+  const int pg = a.page_table[(int64_t)r.b * a.max_pages + lp];
+  const bool ok = slot < pn && blk >= 0 && blk < nb && pg >= 0 && pg < a.n_pages;
+  return ok ? (pg * kPage + (blk & 7) * kBlock) | (min(kBlock, r.n - blk * kBlock) - 1) : -1;
+}
+
+// Pool mode: physical entry of list position p (-1: not visible).
+__device__ __forceinline__ int pool_entry(const RowCtx& r, int p) {
+  const int li = (p >> 3) - r.slot0;
+  const int w = r.pslot[max(0, min(li, r.nslots - 1))];
+  const bool ok = p < r.n_pos && li >= 0 && li < r.nslots && w >= 0 && (p & 7) <= (w & 7);
+  return ok ? (w & ~7) + (p & 7) : -1;
+}
 
 // Full mode: row = b * n_groups + token group, t_full the wave's token
 // (live: the token exists; the dead fourth slot of a group of three sees
@@ -177,19 +204,6 @@ __device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full,
   } else {
     r.n_pos = n;
   }
-}
-
-// Position p of the row's list -> entry index j, or -1 when not visible.
-template <bool POOL>
-__device__ __forceinline__ int entry_of(const ScoreArgs& a, const RowCtx& r, int p) {
-  if (p >= r.n_pos) return -1;
-  int j = p;
-  if (POOL) {
-    const int blk = r.pool_row[p >> 3];
-    j = (blk >= 0 && blk < (r.n + kBlock - 1) / kBlock) ? blk * kBlock + (p & 7) : r.n;
-  }
-  if (j >= r.n) return -1;
-  return phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6) >= 0 ? j : -1;
 }
 
 // Physical page of a Full-mode chunk (logical page `chunk`), or -1 when
@@ -227,15 +241,19 @@ __device__ __forceinline__ void load_sub(const ScoreArgs& a, const RowCtx& r, in
       sw = __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)(col * 4), 0, 0);
       vis = col < nst ? 1u : 0u;
     } else {
-      const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
-      if (j >= 0) {
-        const int64_t p = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
-        const uint8_t* page = a.kidx + p * kMxPageBytes;
-        c0 = *reinterpret_cast<const v2u*>(page + (j & 63) * kMxCodes + 8 * g);
-        c1 = *reinterpret_cast<const v2u*>(page + (j & 63) * kMxCodes + 32 + 8 * g);
-        sw = *reinterpret_cast<const uint32_t*>(page + kMxScaleOff + (j & 63) * 4);
-        vis = 1u;
-      }
+      // every load is issued (entry 0 stands in for positions that are not
+      // visible, masked after)
+      const int e = pool_entry(r, chunk * kChunk + st * 16 + col);
+      const int ee = max(e, 0);
+      const uint8_t* page = a.kidx + (int64_t)(ee >> 6) * kMxPageBytes;
+      c0 = *reinterpret_cast<const v2u*>(page + (ee & 63) * kMxCodes + 8 * g);
+      c1 = *reinterpret_cast<const v2u*>(page + (ee & 63) * kMxCodes + 32 + 8 * g);
+      sw = *reinterpret_cast<const uint32_t*>(page + kMxScaleOff + (ee & 63) * 4);
+      const uint32_t m = e >= 0 ? 0xFFFFFFFFu : 0u;
+      c0 = v2u{c0[0] & m, c0[1] & m};
+      c1 = v2u{c1[0] & m, c1[1] & m};
+      sw &= m;
+      vis = m & 1u;
     }
     k[0] = v4u{c0[0], c0[1], c1[0], c1[1]};
     k[1] = v4u{sw, vis, 0u, 0u};
@@ -253,16 +271,15 @@ __device__ __forceinline__ void load_sub(const ScoreArgs& a, const RowCtx& r, in
     k[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lofs + 64, 0, 0);
     return;
   }
-  const int j = entry_of<POOL>(a, r, chunk * kChunk + st * 16 + col);
-  v4u k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
-  if (j >= 0) {
-    const int64_t p = phys_page(a.page_table, a.max_pages, a.n_pages, r.b, j >> 6);
-    const v4u* src = reinterpret_cast<const v4u*>(a.kidx + p * (kPage * kDI) + (j & 63) * kDI + 16 * g);
-    k0 = __builtin_nontemporal_load(src);
-    k1 = __builtin_nontemporal_load(src + 4);
-  }
-  k[0] = k0;
-  k[1] = k1;
+  // every load is issued (entry 0 stands in for positions that are not
+  // visible, masked after)
+  const int e = pool_entry(r, chunk * kChunk + st * 16 + col);
+  const v4u* src = reinterpret_cast<const v4u*>(a.kidx + (int64_t)max(e, 0) * kDI + 16 * g);
+  const v4u k0 = __builtin_nontemporal_load(src);
+  const v4u k1 = __builtin_nontemporal_load(src + 4);
+  const uint32_t m = e >= 0 ? 0xFFFFFFFFu : 0u;
+  k[0] = v4u{k0[0] & m, k0[1] & m, k0[2] & m, k0[3] & m};
+  k[1] = v4u{k1[0] & m, k1[1] & m, k1[2] & m, k1[3] & m};
 }
 
 // Nonzero when a visible MXFP4 entry's scale word (k[1] of load_sub) holds
@@ -294,7 +311,7 @@ __device__ __forceinline__ void emit_chunk(const ScoreArgs& a, const RowCtx& rc,
                                            bool page_ok, uint32_t* hist_s, uint32_t* hist_bm) {
   const int lane = lane_id();
   const int p = chunk * kChunk + lane;
-  const bool valid = POOL ? entry_of<POOL>(a, rc, p) >= 0 : (page_ok && p < rc.n);
+  const bool valid = POOL ? pool_entry(rc, p) >= 0 : (page_ok && p < rc.n);
   float* out_s_row = a.out_s + ((int64_t)rc.b * a.T + rc.t) *
                                    (POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n));
   // order-preserving key of the score; 0 (stored as NaN) when not visible
@@ -673,6 +690,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     // block maxima, 16-bit counters packed two per word
     uint32_t hist[kGroupT][2][kHistBins / 2];
     SegPlan plan[2 * kGroupT];                    // per (token, list): the segment's plan
+    int pslot[CSA2_MAX_POOL_BLOCKS];              // pool mode: the workgroup's slots (pool_slot_word)
     int scan_tot[kWaves];                         // block-wide prefix sums
   };
   __shared__ Lds sm;
@@ -754,6 +772,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   if (!POOL) {
     const int ck = c0 + slice + lane * n_slices;
     page_word = a.page_table[(int64_t)rc.b * a.max_pages + max(0, min(ck, a.max_pages - 1))];
+  }
+  if (POOL && have_row) {
+    // the workgroup's pool slots, resolved once to physical entries (the
+    // pool word and page-table word of a slot are the only dependent loads)
+    const int nsl = (c1 - c0) * kBlock;
+    for (int i = (int)threadIdx.x; i < nsl; i += kScoreThreads) sm.pslot[i] = pool_slot_word(a, rc, c0 * kBlock + i);
+    rc.pslot = sm.pslot;
+    rc.slot0 = c0 * kBlock;
+    rc.nslots = nsl;
   }
   lds_barrier();
 

@@ -287,6 +287,7 @@ int csa2_index_full_noalloc(const uint8_t *q_idx, const float *w, const uint8_t 
  *   pool [B][T][pool_blocks], pool_n [B][T]: as written by csa2_index_full.
  * Same score, ranking and output format as csa2_index_full's out_topk,
  * restricted to the positions of the first pool_n[b][t] pool blocks.
+ * Returns CSA2_ERR_UNSUPPORTED when n_pages * 64 exceeds INT32_MAX.
  */
 int csa2_index_reindex(const uint8_t *q_idx, const float *w, const uint8_t *kidx_pool,
                        int64_t n_pages, const int32_t *page_table, int32_t max_pages,

@@ -119,8 +119,8 @@ def test_index_full_noalloc_argument_errors(L):
     assert call(max_n=262144, B=32, T=2, HI=64, topk=2048, pool_blocks=2048) == csa2.ERR_SCRATCH
 
 
-def _reindex(L, q=X, pool=X, P=16, topk=8, HI=4, T=1, ws=X, ws_bytes=1 << 30):
-    return L.csa2_index_reindex(q, X, X, 1, X, 1, X, 1, T, HI, pool, X, P, topk, X, ws, ws_bytes, None)
+def _reindex(L, q=X, pool=X, P=16, topk=8, HI=4, T=1, ws=X, ws_bytes=1 << 30, n_pages=1):
+    return L.csa2_index_reindex(q, X, X, n_pages, X, 1, X, 1, T, HI, pool, X, P, topk, X, ws, ws_bytes, None)
 
 
 def test_index_reindex_argument_errors(L):
@@ -129,6 +129,7 @@ def test_index_reindex_argument_errors(L):
     assert _reindex(L, topk=17) == UNSUPPORTED
     assert _reindex(L, HI=10) == UNSUPPORTED
     assert _reindex(L, ws_bytes=0) == WORKSPACE
+    assert _reindex(L, n_pages=(2**31 - 1) // 64 + 1) == UNSUPPORTED
 
 
 def test_mxfp4_index_argument_errors(L):
