@@ -32,7 +32,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa2_oracle.c")
-_LIB = os.path.join(_HERE, "libcsa2_oracle.so")
+# (CSA2_ORACLE_LIB: another build of the same source, e.g. a sanitizer build)
+_LIB = os.environ.get("CSA2_ORACLE_LIB") or os.path.join(_HERE, "libcsa2_oracle.so")
 
 D = 512            # main-KV channels
 DI = 128           # indexer-key channels
