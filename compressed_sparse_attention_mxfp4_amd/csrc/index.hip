@@ -7,10 +7,12 @@
 //
 // Workspace, each part 256-byte aligned:
 //   Full:    scores [B][T][s_stride(max_n)] f32, block maxima
-//            [B][T][bm_stride(max_n)] f32, segment headers [B][T][2][W],
-//            segment candidates [B][T][2][W][pool_blocks + 64]
+//            [B][T][bm_stride(max_n)] f32, segment headers [B][T][2][S],
+//            segment candidates [B][T][2][seg_off_at(P, S)] (segment i at
+//            seg_off_at(P, i)), segment counts [B][T] int32
 //   Reindex: scores [B][T][pool_blocks * 8] f32, then the same segments
-// where W is the scan's workgroups per row (csa2_score_grid).
+// where S is the most segments a row can have: the static plan's
+// workgroups per row, or for the balanced plan up to 8 times the even share.
 #include <algorithm>
 #include <mutex>
 
@@ -38,8 +40,9 @@ int check_index_common(const void* q_idx, const void* w, const void* kidx, int64
 
 namespace {
 struct IndexLayout {
-  size_t s_off, bm_off, hdr_off, cand_off, total;
-  int wg_per_row, seg_cap;
+  size_t s_off, bm_off, hdr_off, cand_off, segn_off, total;
+  int max_segs, seg_k, segs_guess;
+  int64_t region;
 };
 
 // Full mode: rows of the scan are (sequence, group of up to 4 tokens);
@@ -56,17 +59,29 @@ IndexLayout index_layout(bool full, int32_t B, int32_t T, int32_t max_n, int32_t
     chunks = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
     t_slots = 1;
   }
-  int per = 0;
-  csa2_score_grid(rows, chunks, t_slots, &per, &L.wg_per_row);
-  L.seg_cap = csa2::seg_capacity(pool_blocks, pool_blocks);
+  int per = 0, W = 0;
+  csa2_score_grid(rows, chunks, t_slots, &per, &W);
+  L.seg_k = pool_blocks;  // >= topk
+  if (full && csa2_scan_balanced(rows, chunks)) {
+    // a row may take up to 8 times its even share of the workgroups
+    const int need = std::max(1, (chunks + csa2::kMaxWgChunks - 1) / csa2::kMaxWgChunks);
+    const int even = (csa2::kScanTarget + rows - 1) / rows;
+    L.max_segs = std::min(csa2::kMaxSegs, std::max(std::max(W, need), 8 * even));
+    L.segs_guess = std::max(1, csa2::kScanTarget / rows);
+  } else {
+    L.max_segs = W;
+    L.segs_guess = W;
+  }
+  L.region = csa2::seg_off_at(L.seg_k, L.max_segs);
   const size_t bt = (size_t)B * T;
   L.s_off = 0;
   const size_t s_bytes = full ? bt * csa2::s_stride(max_n) * 4 : bt * pool_blocks * csa2::kBlock * 4;
   L.bm_off = align256(s_bytes);
   const size_t bm_bytes = full ? bt * csa2::bm_stride(max_n) * 4 : 0;
   L.hdr_off = L.bm_off + align256(bm_bytes);
-  L.cand_off = L.hdr_off + align256(bt * 2 * L.wg_per_row * sizeof(csa2::SegHeader));
-  L.total = L.cand_off + align256(bt * 2 * L.wg_per_row * (size_t)L.seg_cap * sizeof(csa2::Cand));
+  L.cand_off = L.hdr_off + align256(bt * 2 * L.max_segs * sizeof(csa2::SegHeader));
+  L.segn_off = L.cand_off + align256(bt * 2 * (size_t)L.region * sizeof(csa2::Cand));
+  L.total = L.segn_off + align256(bt * sizeof(int32_t));
   return L;
 }
 
@@ -119,12 +134,14 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
   sa.out_bm = ws_at<float>(ws, lay.bm_off);
   sa.seg_hdr = ws_at<csa2::SegHeader>(ws, lay.hdr_off);
   sa.seg_cand = ws_at<csa2::Cand>(ws, lay.cand_off);
-  sa.seg_cap = lay.seg_cap;
+  sa.seg_n = ws_at<int32_t>(ws, lay.segn_off);
+  sa.max_segs = lay.max_segs;
+  sa.seg_k = lay.seg_k;
+  sa.seg_region = lay.region;
   sa.rows = B * sa.n_groups;
   sa.chunks_per_row = (max_n_entries + csa2::kChunk - 1) / csa2::kChunk;
   const int t_slots = T >= csa2::kGroupT ? csa2::kGroupT : (T == 3 ? 4 : T);
   st = csa2_launch_scan(false, mx, sa, t_slots, (hipStream_t)stream);
-  if (st == CSA2_OK && sa.wg_per_row != lay.wg_per_row) st = CSA2_ERR_LAUNCH;
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -141,8 +158,11 @@ int index_full_impl(bool mx, const uint8_t* q_idx, const float* w, const uint8_t
   se.out_pool_n = out_pool_n;
   se.seg_hdr = sa.seg_hdr;
   se.seg_cand = sa.seg_cand;
-  se.seg_cap = sa.seg_cap;
-  se.segs = sa.wg_per_row;
+  se.seg_n = sa.seg_n;
+  se.max_segs = sa.max_segs;
+  se.seg_k = sa.seg_k;
+  se.seg_region = sa.seg_region;
+  se.segs_guess = lay.segs_guess;
   se.wr_rows = wr_rows;
   se.wr_slots = wr_slots;
   se.wr_pool = wr_pool;
@@ -186,11 +206,13 @@ int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint
   sa.out_s = ws_at<float>(ws, lay.s_off);
   sa.seg_hdr = ws_at<csa2::SegHeader>(ws, lay.hdr_off);
   sa.seg_cand = ws_at<csa2::Cand>(ws, lay.cand_off);
-  sa.seg_cap = lay.seg_cap;
+  sa.seg_n = ws_at<int32_t>(ws, lay.segn_off);
+  sa.max_segs = lay.max_segs;
+  sa.seg_k = lay.seg_k;
+  sa.seg_region = lay.region;
   sa.rows = B * T;
   sa.chunks_per_row = (pool_blocks * csa2::kBlock + csa2::kChunk - 1) / csa2::kChunk;
   st = csa2_launch_scan(true, mx, sa, 1, (hipStream_t)stream);
-  if (st == CSA2_OK && sa.wg_per_row != lay.wg_per_row) st = CSA2_ERR_LAUNCH;
   if (st) return st;
   csa2::SelectArgs se{};
   se.s = sa.out_s;
@@ -206,8 +228,11 @@ int index_reindex_impl(bool mx, const uint8_t* q_idx, const float* w, const uint
   se.out_topk = out_topk;
   se.seg_hdr = sa.seg_hdr;
   se.seg_cand = sa.seg_cand;
-  se.seg_cap = sa.seg_cap;
-  se.segs = sa.wg_per_row;
+  se.seg_n = sa.seg_n;
+  se.max_segs = sa.max_segs;
+  se.seg_k = sa.seg_k;
+  se.seg_region = sa.seg_region;
+  se.segs_guess = lay.segs_guess;
   return csa2_launch_select(false, se, B * T, (hipStream_t)stream);
 }
 }  // namespace

@@ -90,11 +90,18 @@ struct ScoreArgs {
   float* out_bm;          // full: [B][T][bm_stride(max_n)]
   int rows;               // full: B * n_groups; pool: B*T
   int chunks_per_row;     // full: ceil(max_n/64); pool: ceil(pool_blocks/8)
-  int chunks_per_wg;      // chunks of one row per workgroup
-  int wg_per_row;         // workgroups per row = segments per (b, t) list
-  SegHeader* seg_hdr;     // [B*T][2][wg_per_row]
-  Cand* seg_cand;         // [B*T][2][wg_per_row][seg_cap]
-  int seg_cap;
+  // static plan: every row gets wg_per_row workgroups of chunks_per_wg chunks
+  int chunks_per_wg;
+  int wg_per_row;
+  // balanced plan (Full mode): kScanTarget workgroups shared out in
+  // proportion to the rows' visible chunks times tokens (scan_plan_balanced)
+  int balanced;
+  SegHeader* seg_hdr;     // [B*T][2][max_segs]
+  Cand* seg_cand;         // [B*T][2][seg_region]: segment i at seg_off_at(seg_k, i)
+  int32_t* seg_n;         // [B*T]: segments of the row (written by segment 0)
+  int max_segs;
+  int seg_k;              // the larger K of the two lists (capacities)
+  int64_t seg_region;
 };
 
 struct SelectArgs {
@@ -112,10 +119,13 @@ struct SelectArgs {
   int32_t* out_topk;         // [B][T][topk]
   int32_t* out_pool;         // full: [B][T][pool_blocks]
   int32_t* out_pool_n;       // full: [B][T]
-  const SegHeader* seg_hdr;  // the scan's segments
+  const SegHeader* seg_hdr;  // the scan's segments (ScoreArgs)
   const Cand* seg_cand;
-  int seg_cap;
-  int segs;                  // segments per (b, t) list
+  const int32_t* seg_n;
+  int max_segs;
+  int seg_k;
+  int64_t seg_region;
+  int segs_guess;            // the usual segment count (the candidates' early loads assume it)
   int mode;                  // test aid: 0 normal, 1 skip the segments, 2 segments only
   // full, optional: the step's cache write, spread over the workgroups
   const uint16_t* wr_rows;   // [wr_n][512] bf16
@@ -140,10 +150,26 @@ __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)v), 63);
 }
 
-// Segment slots per (b, t) list: K of the larger list plus a margin for keys
-// equal to the threshold.
-__host__ __device__ __forceinline__ int seg_capacity(int topk, int pool_blocks) {
-  return (topk > pool_blocks ? topk : pool_blocks) + 64;
+// Segment capacities.  Segment i of a row exists only when the row has more
+// than i segments, so its part's expected share of the top K is at most
+// 1.5 K / (i + 1); capacities come in bands of i + 1 in [2^b, 2^(b+1)):
+// twice the band's largest share plus a margin, at most K + 64.  Segment i
+// of a (row, list) starts at seg_off_at(K, i) of the list's region.
+__host__ __device__ __forceinline__ int seg_band(int i) {
+  int b = 0;
+  while ((2 << b) <= i + 1) ++b;
+  return b;
+}
+__host__ __device__ __forceinline__ int band_cap(int K, int b) {
+  const int c = (((3 * K) >> b) + 128 + 15) & ~15;
+  return c < K + 64 ? c : K + 64;
+}
+__host__ __device__ __forceinline__ int seg_cap_at(int K, int i) { return band_cap(K, seg_band(i)); }
+__host__ __device__ __forceinline__ int64_t seg_off_at(int K, int i) {
+  const int b = seg_band(i);
+  int64_t off = 0;
+  for (int bb = 0; bb < b; ++bb) off += (int64_t)(1 << bb) * band_cap(K, bb);
+  return off + (int64_t)(i + 1 - (1 << b)) * band_cap(K, b);
 }
 
 // Test aid: 0 normal; 1 the selections ignore the segments (full lists);
@@ -153,9 +179,11 @@ int& select_mode();
 
 }  // namespace csa2
 
-// Grid of the scan (workgroups per row etc.), the same on the host whenever
-// it is computed for one device and shape.
+// Static plan of the scan (workgroups per row etc.).
 int csa2_score_grid(int rows, int chunks_per_row, int T_slots, int* chunks_per_wg, int* wg_per_row);
+// Whether a Full-mode scan of `rows` rows of up to chunks_per_row chunks
+// takes the balanced plan (its kScanTarget workgroups cover any lengths).
+bool csa2_scan_balanced(int rows, int chunks_per_row);
 // Launches the scan over E4M3 (mx = false) or MXFP4 indexer keys; Full mode
 // (pool = false) or Reindex mode over the pool.  Fills in the grid fields.
 int csa2_launch_scan(bool pool, bool mx, csa2::ScoreArgs& sa, int T_slots, hipStream_t stream);

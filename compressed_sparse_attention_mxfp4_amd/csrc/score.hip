@@ -533,7 +533,8 @@ __device__ int block_excl_scan512(int v, int* scan_tot, int* total) {
 // 8 consecutive positions per thread and round (4,096 per round); a part of
 // one round is read once.
 template <bool POOL>
-__device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, int Ts, int Tg, int c0, int c1,
+__device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, int Ts, int Tg, int seg, int nseg,
+                               int c0, int c1,
                                uint32_t (&hist)[kGroupT][2][kHistBins / 2],
                                uint32_t (&fine)[2 * kGroupT][kFineBins], const uint32_t* mxbad, SegPlan* plan,
                                int* scan_tot) {
@@ -541,7 +542,7 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tid = threadIdx.x;
   const int n_pairs = POOL ? 1 : 2 * Tg;
-  const int seg = blockIdx.x % a.wg_per_row;
+  const int cap = seg_cap_at(a.seg_k, seg);
   const int64_t list_stride_s = POOL ? (int64_t)a.pool_blocks * kBlock : (int64_t)s_stride(a.max_n);
 
   // ---- 1. the plan of pair (token slot ts, list L), by wave ts + Ts L, which
@@ -569,7 +570,7 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
     // (which is still >= K)
     const int64_t n_row = max(len, 1);
     const int64_t share = ((int64_t)3 * K * total + 2 * n_row - 1) / (2 * n_row);
-    pl.m = (int)min((int64_t)total, min(share + 16, (int64_t)(a.seg_cap - 64)));
+    pl.m = (int)min((int64_t)total, min(share + 16, (int64_t)(cap - 64)));
     if (pl.m < pl.n_valid) {
       pl.coarse = coarse_crossing(hist[ts][L], (uint32_t)pl.m, &above, &total);
       pl.rem = pl.m - (int)above;
@@ -624,8 +625,8 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
     }
 
     // ---- 3. compaction: kept keys in list order
-    SegHeader* hdr = a.seg_hdr + (pl.bt * 2 + pl.list) * a.wg_per_row + seg;
-    Cand* cand = a.seg_cand + ((pl.bt * 2 + pl.list) * a.wg_per_row + seg) * (int64_t)a.seg_cap;
+    SegHeader* hdr = a.seg_hdr + (pl.bt * 2 + pl.list) * a.max_segs + seg;
+    Cand* cand = a.seg_cand + (pl.bt * 2 + pl.list) * a.seg_region + seg_off_at(a.seg_k, seg);
     int written = 0;
     for (int base = pl.p0; base < pl.p1; base += 8 * kScoreThreads) {
       const int q0 = base + 8 * tid;
@@ -640,7 +641,7 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if ((keep >> e) & 1u) {
-          if (o < a.seg_cap) cand[o] = Cand{keys[e], q0 + e};
+          if (o < cap) cand[o] = Cand{keys[e], q0 + e};
           ++o;
         }
       }
@@ -649,11 +650,148 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
     if (tid == 0) {
       uint32_t flags = 0u;
       if (written < pl.n_valid) flags |= kSegDropped;
-      if (written > a.seg_cap) flags |= kSegOverflow;
+      if (written > cap) flags |= kSegOverflow;
       if (mxbad[POOL ? 0 : p >> 1] != 0u) flags |= kSegBadScale;
-      *hdr = SegHeader{(uint32_t)min(written, a.seg_cap) | (flags << 24), pl.thr};
+      *hdr = SegHeader{(uint32_t)min(written, cap) | (flags << 24), pl.thr};
+      if (seg == 0 && pl.list == 0) a.seg_n[pl.bt] = nseg;
     }
   }
+}
+
+// Balanced plan of a Full-mode scan: the kScanTarget workgroups are shared
+// out over the rows (sequence, token group) in proportion to their work,
+// visible chunks (the group's largest visible count) times tokens.  Every
+// row first gets the workgroups its length needs under the per-workgroup
+// chunk cap, then a share of the rest; its chunks are split into whole
+// rounds of its waves.  Row r's workgroups follow those of rows < r.  Every
+// wave computes the whole plan from the rows' counts (at most kScanTarget
+// rows; lane L holds rows j * 64 + L, so groups of 64 rows past the last one
+// cost nothing), with no barrier, and takes its workgroup's part; workgroups
+// past the plan's total get row = rows (none).
+constexpr int kPlanRows = kScanTarget / 64;
+
+struct PlanRows {
+  int ch[kPlanRows], minw[kPlanRows], work[kPlanRows];
+};
+
+struct PlanPart {
+  int row, seg, nseg, c0, c1;
+};
+
+// floor(x / d) for 0 <= x < 2^24, 1 <= d < 2^24 and a quotient below 2^20:
+// the single-precision estimate is off by at most one either way.
+__device__ __forceinline__ int plan_div(int x, int d) {
+  int q = (int)((float)x * __builtin_amdgcn_rcpf((float)d));
+  const int r = x - q * d;
+  q += (r >= d) ? 1 : 0;
+  q -= (r < 0) ? 1 : 0;
+  return q;
+}
+
+// The waves' rounds (slices) of a row of tg tokens: 8 / tg slots, a group of
+// three taking four slots.
+__device__ __forceinline__ int plan_slices(int tg) { return tg == 1 ? kWaves : tg == 2 ? kWaves / 2 : kWaves / 4; }
+
+// Row r's token group: sequence b, first token t0, tokens tg.
+__device__ __forceinline__ void plan_group(const ScoreArgs& a, int r, int& b, int& t0, int& tg) {
+  if (a.n_groups == 1) {
+    b = r;
+    t0 = 0;
+  } else {
+    b = plan_div(r, a.n_groups);
+    t0 = (r - b * a.n_groups) * kGroupT;
+  }
+  tg = min(kGroupT, a.T - t0);
+}
+
+// Lane L's rows j * 64 + L: visible chunks, workgroups their length needs
+// (the per-workgroup cap is kMaxWgChunks for every token count), work.
+// Only loads and a little arithmetic.
+__device__ __forceinline__ PlanRows plan_row_counts(const ScoreArgs& a) {
+  PlanRows pr;
+#pragma unroll
+  for (int j = 0; j < kPlanRows; ++j) {
+    const int r = j * 64 + lane_id();
+    pr.ch[j] = 0;
+    pr.minw[j] = 0;
+    pr.work[j] = 0;
+    if (j * 64 >= a.rows) continue;  // uniform
+    if (r < a.rows) {
+      int b, t0, tg;
+      plan_group(a, r, b, t0, tg);
+      int n = min(min(a.n_entries[b], a.max_n), a.max_pages * kPage);
+      if (a.n_vis != nullptr) {
+        int nm = 0;
+        for (int k = 0; k < tg; ++k) nm = max(nm, min(n, a.n_vis[(int64_t)b * a.T + t0 + k]));
+        n = nm;
+      }
+      n = max(n, 0);
+      const int ch = (n + kChunk - 1) / kChunk;
+      pr.ch[j] = ch;
+      pr.minw[j] = max(1, (ch + kMaxWgChunks - 1) / kMaxWgChunks);
+      pr.work[j] = ch * tg;
+    }
+  }
+  return pr;
+}
+
+__device__ __forceinline__ PlanPart scan_plan_balanced(const ScoreArgs& a, const PlanRows& pr) {
+  const int lane = lane_id();
+  int sm_ = 0, sw_ = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanRows; ++j) {
+    sm_ += pr.minw[j];
+    sw_ += pr.work[j];
+  }
+  const int minw_tot = wave_sum(sm_), work_tot = wave_sum(sw_);
+  const int budget = max(0, kScanTarget - minw_tot);
+  const int wg = (int)blockIdx.x;
+  int base = 0;  // workgroups of the groups of rows before j
+  int hit = 0, hseg = 0, hnseg = 1, hc0 = 0, hc1 = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanRows; ++j) {
+    if (j * 64 >= a.rows) break;  // uniform
+    const int r = j * 64 + lane;
+    int w = 0, per = 1;
+    if (r < a.rows) {
+      int b, t0, tg;
+      plan_group(a, r, b, t0, tg);
+      const int slices = plan_slices(tg);
+      // budget <= 256 and work <= 4 * 4096: the product fits 24 bits
+      w = pr.minw[j] + (work_tot > 0 ? plan_div(budget * pr.work[j], work_tot) : 0);
+      w = min(w, a.max_segs);
+      const int ch = pr.ch[j];
+      if (ch > 0) {
+        per = plan_div(ch + w - 1, w);
+        per = (per + slices - 1) & ~(slices - 1);  // slices is a power of two
+        w = plan_div(ch + per - 1, per);
+      } else {
+        w = 1;
+      }
+    }
+    const int incl = (int)wave_incl_scan((uint32_t)w);
+    const int first = base + incl - w;
+    if (w > 0 && wg >= first && wg < first + w) {
+      hit = 1;
+      hseg = wg - first;
+      hnseg = w | (j << 16);
+      hc0 = hseg * per;
+      hc1 = min(pr.ch[j], hc0 + per);
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  const uint64_t m = __ballot(hit);
+  PlanPart p{a.rows, 0, 1, 0, 0};
+  if (m != 0) {
+    const int src = (int)__builtin_ctzll(m);
+    const int hn = __builtin_amdgcn_readlane(hnseg, src);
+    p.row = (hn >> 16) * 64 + src;
+    p.nseg = hn & 0xFFFF;
+    p.seg = __builtin_amdgcn_readlane(hseg, src);
+    p.c0 = __builtin_amdgcn_readlane(hc0, src);
+    p.c1 = __builtin_amdgcn_readlane(hc1, src);
+  }
+  return p;
 }
 
 // Scan.  POOL = false: Full mode, rows = sequences, the waves split
@@ -707,28 +845,34 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int g = lane >> 4;   // K slice group of the MFMA operands; head group of the outputs
   const int col = lane & 15;
   const int HI = a.HI;
-  const int row = blockIdx.x / a.wg_per_row;
+  // ---- this workgroup's row, segment of the row and chunk range: the
+  // static plan first; with the balanced plan its result replaces it, and
+  // the early loads below are issued again only when they differ (equal
+  // rows of the greatest length give the same plan)
+  int row = blockIdx.x / a.wg_per_row;
+  int seg = blockIdx.x % a.wg_per_row;
+  int nseg = a.wg_per_row;
+  int c0 = seg * a.chunks_per_wg;
+  int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
   // Full mode: tokens t0 .. t0 + Tg - 1 of the sequence, in Ts token slots
   // (a group of three keeps a dead fourth slot, so that the slots divide the
   // 8 waves); each wave takes one slot and a slice of the chunk range
-  const int t0 = POOL ? 0 : (row % a.n_groups) * kGroupT;
-  const int Tg = POOL ? 1 : min(kGroupT, a.T - t0);
-  const int Ts = Tg == 3 ? 4 : Tg;
-  const int slot = POOL ? 0 : wave % Ts;
-  const int t_full = POOL ? 0 : t0 + min(slot, Tg - 1);
-  const int slice = POOL ? wave : wave / Ts;
-  const int n_slices = POOL ? kWaves : kWaves / Ts;
-  const int c0 = (blockIdx.x % a.wg_per_row) * a.chunks_per_wg;
-  const int c1 = min(a.chunks_per_row, c0 + a.chunks_per_wg);
-  const bool have_row = row < a.rows;
-  int chunk = c0 + slice;
-  const bool active = have_row && chunk < c1 && slot < Tg;
-  uint32_t* hist_s = sm.hist[slot][0];
-  uint32_t* hist_bm = sm.hist[slot][1];
+  int t0, Tg, Ts, slot, t_full, slice, n_slices, n_tok;
   RowCtx rc;
-  if (have_row) row_ctx<POOL>(a, row, t_full, slot < Tg, rc);
-  const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
-  const int n_tok = POOL ? 1 : Ts;
+  auto set_row = [&]() {
+    const int rr = min(row, a.rows - 1);  // (a guess past the rows reads row rows - 1, unused)
+    t0 = POOL ? 0 : (rr % a.n_groups) * kGroupT;
+    Tg = POOL ? 1 : min(kGroupT, a.T - t0);
+    Ts = Tg == 3 ? 4 : Tg;
+    slot = POOL ? 0 : wave % Ts;
+    t_full = POOL ? 0 : t0 + min(slot, Tg - 1);
+    slice = POOL ? wave : wave / Ts;
+    n_slices = POOL ? kWaves : kWaves / Ts;
+    n_tok = POOL ? 1 : Ts;
+    rc = RowCtx{};
+    row_ctx<POOL>(a, rr, t_full, slot < Tg, rc);
+  };
+  set_row();
 
   // ---- every load that needs nothing loaded first is issued here, ahead of
   // the keys (the wait counter retires loads in issue order): the raw query
@@ -742,37 +886,80 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // 15), channels 16 gL + 8 s + e (s < 2) or 64 + 16 gL + 8 (s - 2) + e
   // (e < 8, gL = L >> 4), the keys' order in the slices.
   constexpr int kLimbIters = kGroupT * kRT * 4 * 64 / kScoreThreads;
-  const int n_items = n_tok * kRT * 4 * 64;  // 1024 n_tok, a power of two
   uint32_t qraw[kLimbIters][2], qkeep[kLimbIters];
-#pragma unroll
-  for (int j = 0; j < kLimbIters; ++j) {
-    const int it = (int)threadIdx.x + j * kScoreThreads;
-    const int iw = it & (n_items - 1);
-    const int L = iw & 63, sl = (iw >> 6) & 3, rt = (iw >> 8) & 3, tk = iw >> 10;
-    const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
-    const int h = tile_head(rt, L & 15), gL = L >> 4;
-    const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        a.q_idx + (((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)) * kDI + ch);
-    qraw[j][0] = src[0];
-    qraw[j][1] = src[1];
-    qkeep[j] = (it < n_items && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
-    asm volatile("" : "+v"(qkeep[j]));
-  }
   uint32_t wraw, wkeep;
-  {
-    const int i = min((int)threadIdx.x, n_tok * 64 - 1);
-    const int tk = i >> 6, h = i & 63;
-    const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
-    wraw = __float_as_uint(a.w[((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)]);
-    wkeep = ((int)threadIdx.x < n_tok * 64 && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
-    asm volatile("" : "+v"(wkeep));
-  }
   int page_word = -1;
-  if (!POOL) {
-    const int ck = c0 + slice + lane * n_slices;
-    page_word = a.page_table[(int64_t)rc.b * a.max_pages + max(0, min(ck, a.max_pages - 1))];
+  auto issue_early = [&]() {
+    const int n_items = n_tok * kRT * 4 * 64;  // 1024 n_tok, a power of two
+#pragma unroll
+    for (int j = 0; j < kLimbIters; ++j) {
+      const int it = (int)threadIdx.x + j * kScoreThreads;
+      const int iw = it & (n_items - 1);
+      const int L = iw & 63, sl = (iw >> 6) & 3, rt = (iw >> 8) & 3, tk = iw >> 10;
+      const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
+      const int h = tile_head(rt, L & 15), gL = L >> 4;
+      const int ch = sl < 2 ? 16 * gL + 8 * sl : 64 + 16 * gL + 8 * (sl - 2);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          a.q_idx + (((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)) * kDI + ch);
+      qraw[j][0] = src[0];
+      qraw[j][1] = src[1];
+      qkeep[j] = (it < n_items && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
+      asm volatile("" : "+v"(qkeep[j]));
+    }
+    {
+      const int i = min((int)threadIdx.x, n_tok * 64 - 1);
+      const int tk = i >> 6, h = i & 63;
+      const int t = POOL ? rc.t : t0 + min(tk, Tg - 1);
+      wraw = __float_as_uint(a.w[((int64_t)rc.b * a.T + t) * HI + min(h, HI - 1)]);
+      wkeep = ((int)threadIdx.x < n_tok * 64 && h < HI && (POOL || tk < Tg)) ? 0xFFFFFFFFu : 0u;
+      asm volatile("" : "+v"(wkeep));
+    }
+    if (!POOL) {
+      const int ck = c0 + slice + lane * n_slices;
+      page_word = a.page_table[(int64_t)rc.b * a.max_pages + max(0, min(ck, a.max_pages - 1))];
+    }
+  };
+  int wave_pages = -1;
+  ChunkKeys cur;
+  bool cur_ok = false;
+  // Full mode: the physical pages of this wave's chunks, lane k holding the
+  // page of its chunk number k0 + k (refilled every 64 chunks), so the loop
+  // reads them with readlane and issues no memory load of its own for them
+  // (a vector load there would wait for the key prefetch as well)
+  auto fill_pages = [&](int k0) {
+    const int ck = c0 + slice + (k0 + lane) * n_slices;
+    wave_pages = (!POOL && ck < c1) ? (int)chunk_page(a, rc, ck) : -1;
+  };
+  auto page_of = [&](int k) -> int64_t {
+    return POOL ? 0 : (int64_t)__builtin_amdgcn_readlane(wave_pages, k & 63);
+  };
+  // the balanced plan: its row counts go out first, then the early loads for
+  // the static plan's part; when the balanced plan gives another part, the
+  // early loads go out again for it
+  if (!POOL && a.balanced) {
+    const PlanRows prow = plan_row_counts(a);
+    issue_early();
+    const PlanPart pp = scan_plan_balanced(a, prow);
+    if (pp.row >= a.rows) return;  // past the plan (the same for the whole workgroup)
+    seg = pp.seg;
+    nseg = pp.nseg;
+    if (pp.row != row || pp.c0 != c0 || pp.c1 != c1) {
+      row = pp.row;
+      c0 = pp.c0;
+      c1 = pp.c1;
+      set_row();
+      issue_early();
+    }
+  } else {
+    issue_early();
   }
+  const bool have_row = row < a.rows;
+  int chunk = c0 + slice;
+  const bool active = have_row && chunk < c1 && slot < Tg;
+  uint32_t* hist_s = sm.hist[slot][0];
+  uint32_t* hist_bm = sm.hist[slot][1];
+  const int64_t qrow0 = ((int64_t)rc.b * a.T + rc.t) * HI;
+  const int n_items = n_tok * kRT * 4 * 64;
   if (POOL && have_row) {
     // the workgroup's pool slots, resolved once to physical entries (the
     // pool word and page-table word of a slot are the only dependent loads)
@@ -784,25 +971,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   }
   lds_barrier();
 
-  // Full mode: the physical pages of this wave's chunks, lane k holding the
-  // page of its chunk number k0 + k (refilled every 64 chunks), so the loop
-  // reads them with readlane and issues no memory load of its own for them
-  // (a vector load there would wait for the key prefetch as well)
-  int wave_pages = -1;
-  auto fill_pages = [&](int k0) {
-    const int ck = c0 + slice + (k0 + lane) * n_slices;
-    wave_pages = (!POOL && ck < c1) ? (int)chunk_page(a, rc, ck) : -1;
-  };
-  auto page_of = [&](int k) -> int64_t {
-    return POOL ? 0 : (int64_t)__builtin_amdgcn_readlane(wave_pages, k & 63);
-  };
   // every early load has arrived here (they went out together): waiting
   // for them before the key loads leaves nothing to wait for in the limb work
 #pragma unroll
   for (int j = 0; j < kLimbIters; ++j) asm volatile("" ::"v"(qraw[j][0]), "v"(qraw[j][1]));
   asm volatile("" ::"v"(wraw), "v"(page_word));
-  ChunkKeys cur;
-  bool cur_ok = false;
   if (active) {
     if (!POOL) {
       // chunk_page on the early page-table word
@@ -853,6 +1026,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     }
   }
   lds_barrier();
+
 
   if (active) {
   // this wave's token: limbs (A operands, row col of row tile rt is head
@@ -1002,7 +1176,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
   // ---- the candidate segments of this workgroup's part of each list
   __syncthreads();  // every wave's scores, block maxima and coarse counts are in place
-  if (have_row) write_segments<POOL>(a, rc, slot, Ts, Tg, c0, c1, sm.hist, sm.fine, sm.mxbad, sm.plan, sm.scan_tot);
+  if (have_row) write_segments<POOL>(a, rc, slot, Ts, Tg, seg, nseg, c0, c1, sm.hist, sm.fine, sm.mxbad, sm.plan, sm.scan_tot);
 }
 
 }  // namespace csa2
@@ -1024,9 +1198,17 @@ int csa2_score_grid(int rows, int chunks_per_row, int T_slots, int* chunks_per_w
   return rows * *wg_per_row;
 }
 
+bool csa2_scan_balanced(int rows, int chunks_per_row) {
+  const int need = (chunks_per_row + csa2::kMaxWgChunks - 1) / csa2::kMaxWgChunks;  // per row, at most
+  return rows <= csa2::kScanTarget && (int64_t)rows * std::max(need, 1) <= csa2::kScanTarget;
+}
+
 int csa2_launch_scan(bool pool, bool mx, csa2::ScoreArgs& sa, int T_slots, hipStream_t stream) {
-  const int gx = csa2_score_grid(sa.rows, sa.chunks_per_row, T_slots, &sa.chunks_per_wg, &sa.wg_per_row);
-  if (sa.wg_per_row > csa2::kMaxSegs) return CSA2_ERR_LAUNCH;
+  int gx = csa2_score_grid(sa.rows, sa.chunks_per_row, T_slots, &sa.chunks_per_wg, &sa.wg_per_row);
+  sa.balanced = (!pool && csa2_scan_balanced(sa.rows, sa.chunks_per_row)) ? 1 : 0;
+  if (sa.balanced) gx = csa2::kScanTarget;
+  else if (sa.wg_per_row > sa.max_segs) return CSA2_ERR_LAUNCH;
+  if (sa.max_segs > csa2::kMaxSegs) return CSA2_ERR_LAUNCH;
   const dim3 grid(gx), block(csa2::kScoreThreads);
   if (pool && mx)
     CSA2_LAUNCH(CSA2_K_SCORE_REINDEX, (csa2::score_kernel<true, true>), grid, block, stream, sa);

@@ -341,31 +341,34 @@ __device__ __forceinline__ int lds_topk(const uint32_t* keys, const uint32_t* pa
 }
 
 // Candidates of one (row, list), loaded ahead of the headers that say how
-// many there are: thread t covers segment t / tps, slots (t % tps) + tps r
-// (r < kSegR), with tps = 256 / W threads per segment; thread t < W also
-// reads header t.
+// many there are, for the usual segment count W (segs_guess): thread t
+// covers segment t / tps, slots (t % tps) + tps r (r < kSegR), with tps =
+// 256 / W threads per segment; thread t also reads header t (t < max_segs)
+// and every thread the row's segment count.
 constexpr int kSegR = 32;
 struct SegCands {
   v2u c[kSegR];
-  SegHeader h;    // header t (t < W)
+  SegHeader h;    // header t
   SegHeader own;  // header of segment t / tps
+  int nseg;       // the row's segments
 };
 
 __device__ __forceinline__ void seg_issue(const SelectArgs& a, int64_t bt, int list, SegCands& L) {
   const int tid = (int)threadIdx.x;
-  const int W = a.segs, tps = kSelThreads / W;
-  const int64_t seg0 = (bt * 2 + list) * W;
+  const int W = a.segs_guess, tps = kSelThreads / W;
+  const int64_t seg0 = (bt * 2 + list) * a.max_segs;
   // every load is issued, with clamped indices (masked later), so that none
   // waits for another
-  const v2u hv = *reinterpret_cast<const v2u*>(a.seg_hdr + seg0 + std::min(tid, W - 1));
+  L.nseg = a.seg_n[bt];
+  const v2u hv = *reinterpret_cast<const v2u*>(a.seg_hdr + seg0 + std::min(tid, a.max_segs - 1));
   L.h = SegHeader{hv[0], hv[1]};
   const int s = std::min(tid / tps, W - 1), j0 = tid % tps;
   const v2u ov = *reinterpret_cast<const v2u*>(a.seg_hdr + seg0 + s);
   L.own = SegHeader{ov[0], ov[1]};
-  const Cand* base = a.seg_cand + (seg0 + s) * a.seg_cap;
+  const Cand* base = a.seg_cand + (bt * 2 + list) * a.seg_region + seg_off_at(a.seg_k, s);
+  const int cap = seg_cap_at(a.seg_k, s);
 #pragma unroll
-  for (int r = 0; r < kSegR; ++r)
-    L.c[r] = *reinterpret_cast<const v2u*>(base + std::min(j0 + tps * r, a.seg_cap - 1));
+  for (int r = 0; r < kSegR; ++r) L.c[r] = *reinterpret_cast<const v2u*>(base + std::min(j0 + tps * r, cap - 1));
 }
 
 // Top K of a (row, list) from its segments (seg_issue): returns kSegBad when
@@ -378,8 +381,9 @@ __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int l
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int W = a.segs, tps = kSelThreads / W;
-  const int64_t seg0 = (bt * 2 + list) * W;
+  // the row's segments; the early loads are of use when it has the usual count
+  const int W = std::max(1, std::min(L.nseg, a.max_segs)), tps = kSelThreads / W;
+  const bool early = W == a.segs_guess;
   // ---- headers: offsets, total, flags, the highest threshold of a segment
   // that dropped keys, the largest count (one round through LDS)
   const bool mine = tid < W;
@@ -394,7 +398,7 @@ __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int l
   // segment's count)
   uint32_t lmax = 0u, lmin_inv = 0u;
   {
-    const bool in_seg = tid / tps < W;
+    const bool in_seg = early && tid / tps < W;
     const int own_cnt = in_seg ? (int)(L.own.count_flags & 0xFFFFFFu) : 0;
     const int j0 = tid % tps;
 #pragma unroll
@@ -422,7 +426,7 @@ __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int l
   const uint32_t thr_max = wave_max_u32(lane < kSelWaves ? sh.hdr_thr[lane] : 0u);
   const int cmax = (int)wave_max_u32(lane < kSelWaves ? sh.hdr_cmax[lane] : 0u);
   KeyStats ks;
-  ks.known = cmax <= tps * kSegR;  // every candidate was among the early loads
+  ks.known = early && cmax <= tps * kSegR;  // every candidate was among the early loads
   ks.n_valid = tot;
   ks.kmax = wave_max_u32(lane < kSelWaves ? sh.hdr_kmax[lane] : 0u);
   ks.kmin = ~wave_max_u32(lane < kSelWaves ? sh.hdr_kmin[lane] : 0u);
@@ -435,31 +439,37 @@ __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int l
   if (tot <= K && !complete) return kSegFail;
 
   // ---- the candidates in list order into the stage (keys, then positions
-  // at kPosOff); slots past the early loads' reach are loaded here
+  // at kPosOff); slots past the early loads' reach (all of them when the row
+  // has an unusual segment count) are loaded here
   {
     const int s = tid / tps, j0 = tid % tps;
     const int off_s = s < W ? sh.seg_off[s] : 0;
     const int cnt_s = s < W ? sh.seg_off[s + 1] - off_s : 0;
-    const int rmax = (cmax + tps - 1) / tps;  // slots any segment fills (the same for every thread)
+    int j_from = j0;
+    if (early) {
+      const int rmax = (cmax + tps - 1) / tps;  // slots any segment fills (the same for every thread)
 #pragma unroll
-    for (int r0 = 0; r0 < kSegR; r0 += 8) {
-      if (r0 < rmax) {
+      for (int r0 = 0; r0 < kSegR; r0 += 8) {
+        if (r0 < rmax) {
 #pragma unroll
-        for (int r = r0; r < r0 + 8; ++r) {
-          const int j = j0 + tps * r;
-          const bool in = j < cnt_s;
-          *(in ? sh.stage + off_s + j : sh.dummy + lane) = L.c[r][0];
-          *(in ? sh.stage + kPosOff + off_s + j : sh.dummy + lane) = L.c[r][1];
+          for (int r = r0; r < r0 + 8; ++r) {
+            const int j = j0 + tps * r;
+            const bool in = j < cnt_s;
+            *(in ? sh.stage + off_s + j : sh.dummy + lane) = L.c[r][0];
+            *(in ? sh.stage + kPosOff + off_s + j : sh.dummy + lane) = L.c[r][1];
+          }
         }
       }
+      j_from = j0 + tps * kSegR;
     }
-    if (cmax > tps * kSegR) {
-      const Cand* base = a.seg_cand + (seg0 + std::min(s, W - 1)) * a.seg_cap;
-      for (int j = j0 + tps * kSegR; j < cnt_s; j += 4 * tps) {
+    if (!early || cmax > tps * kSegR) {
+      const int sc = std::min(s, W - 1);
+      const Cand* base = a.seg_cand + (bt * 2 + list) * a.seg_region + seg_off_at(a.seg_k, sc);
+      const int cap = seg_cap_at(a.seg_k, sc);
+      for (int j = j_from; j < cnt_s; j += 4 * tps) {
         v2u c4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          c4[u] = *reinterpret_cast<const v2u*>(base + std::min(j + u * tps, a.seg_cap - 1));
+        for (int u = 0; u < 4; ++u) c4[u] = *reinterpret_cast<const v2u*>(base + std::min(j + u * tps, cap - 1));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (j + u * tps < cnt_s) {
@@ -658,7 +668,8 @@ int& select_mode() {
 }  // namespace csa2
 
 int csa2_launch_select(bool full, const csa2::SelectArgs& se, int rows, hipStream_t stream) {
-  if (se.segs < 1 || se.segs > csa2::kMaxSegs) return CSA2_ERR_LAUNCH;
+  if (se.max_segs < 1 || se.max_segs > csa2::kMaxSegs || se.segs_guess < 1 || se.segs_guess > se.max_segs)
+    return CSA2_ERR_LAUNCH;
   csa2::SelectArgs args = se;
   args.mode = csa2::select_mode();
   if (full)
