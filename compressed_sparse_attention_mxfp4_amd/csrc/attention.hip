@@ -523,14 +523,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 
 // ---------------------------------------------------------------- 64 heads
 // One workgroup per (b, t, split) serves all 64 heads, so that every row is
-// gathered and dequantized once: 8 waves dequantize the sub-chunk's 32 rows
-// (512 channels each) into a shared LDS tile.  Wave w = (head tile ht = w %
-// 4, channel half kh = w / 4) computes the logits S^T of all 32 rows for
-// its 16 heads over its 256 channels (that part of the query in registers);
-// the kh = 0 wave adds the other half's partial logits (fixed order), runs
-// the heads' online softmax and shares the fp16 weights P and the rescale
-// factors through LDS.  Wave w then owns output channels 64 w .. 64 w + 63
-// of all 64 heads and accumulates P.V from the tile, reading V transposed.
+// gathered and dequantized once, into a shared LDS tile of 32 rows x 512
+// channels (double-buffered).  Wave w = (head tile ht = w % 4, channel half
+// kh = w / 4) computes the logits S^T of all 32 rows for its 16 heads over
+// its 256 channels (that part of the query in registers).  Then the kh = 0
+// wave adds the other half's partial logits (fixed order), runs the heads'
+// online softmax and shares the fp16 weights P and the rescale factors
+// through LDS, while the four kh = 1 waves dequantize the next sub-chunk's
+// rows into the other tile buffer.  Wave w then owns output channels 64 w ..
+// 64 w + 63 of all 64 heads and accumulates P.V from the tile, reading V
+// transposed.  Two barriers per sub-chunk: after the logits, and after the
+// weights and the next tile.
 constexpr int kHThreads = 512;
 constexpr int kTileRowHalves = kD;        // a tile row: 512 fp16 channels (64 chunks of 16 B)
 constexpr int kPStride = 40;              // P row (one head): 32 rows of fp16, padded to 80 B
@@ -543,10 +546,11 @@ __device__ __forceinline__ int htile_off(int row, int chunk) {  // in halves
   return row * kTileRowHalves + 8 * (chunk ^ swz(row));
 }
 
-// The row loads of one sub-chunk for lane L of wave w: row 16 (w % 2) +
-// L % 16, channels 32 c .. + 31 with c = 4 (w / 2) + L / 16.  FP4 row: 16
-// code bytes + the 16 scale bytes 16 (c / 8) .. + 15 of the entry (the
-// lane's two groups among them); window row: 32 E4M3 bytes.
+// The row loads of one sub-chunk for lane L of kh = 1 wave w (v = w % 4):
+// row 16 (v % 2) + L % 16, channel pieces 32 c .. + 31 for c = 4 (v / 2) +
+// L / 16 and c + 8.  FP4 piece: 16 code bytes + the 16 scale bytes 16 (c /
+// 8) .. + 15 of the entry (the piece's two groups among them); window
+// piece: 32 E4M3 bytes.
 struct HLoads {
   v4u lo, hi;
   int s;
@@ -570,7 +574,6 @@ __device__ __forceinline__ void issue_hrow(const AttnArgs& a, const int* rslot, 
   L.hi = gld16(p1);
 }
 
-template <int NB>
 __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t tile[2][kSub * kTileRowHalves];  // double-buffered
   __shared__ __attribute__((aligned(16))) half_t pmat[64 * kPStride];            // P [head][row]
@@ -652,12 +655,22 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- the first sub-chunks' row loads (the ring below keeps NB in flight)
-  const int drow = 16 * (wave & 1) + (lane & 15);  // dequant role: this lane's row of a sub-chunk
-  const int c32 = 4 * (wave >> 1) + (lane >> 4);   // and its 32-channel piece
-  HLoads buf[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) issue_hrow(a, rslot, i * kSub + drow, row0 + i * kSub + drow, n_rel, c32, win_row0, buf[i]);
+  // ---- the first sub-chunks' row loads, kh = 1 waves (the ring below keeps
+  // two sub-chunks in flight)
+  const int dv = wave & 3;
+  const int drow = 16 * (dv & 1) + (lane & 15);  // dequant role: this lane's row of a sub-chunk
+  const int c32 = 4 * (dv >> 1) + (lane >> 4);   // and its 32-channel pieces c32, c32 + 8
+  HLoads buf[2][2];
+  // the kh = 0 waves issue the prologue's loads too, of absent rows (the
+  // pool's first bytes), so that every path reaches the loops with the same
+  // loads in flight and the waits on them count exactly
+  const int sc_pro = kh == 1 ? 0 : n_sub + 4;
+  auto issue_sub = [&](int sc, HLoads (&L)[2]) __attribute__((always_inline)) {
+    issue_hrow(a, rslot, sc * kSub + drow, row0 + sc * kSub + drow, n_rel, c32, win_row0, L[0]);
+    issue_hrow(a, rslot, sc * kSub + drow, row0 + sc * kSub + drow, n_rel, c32 + 8, win_row0, L[1]);
+  };
+  issue_sub(sc_pro, buf[0]);
+  issue_sub(sc_pro + 1, buf[1]);
 
   // ---- the query as the B operand, scaled per head by a power of two that
   // puts its largest |q| in [2^14, 2^15) (fp16 never overflows; the logits
@@ -689,9 +702,11 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   // swizzle keeps bits 4, 5 of the chunk), the transposed V reads (rows 8 g +
   // col / 4 and + 4, channels 64 w + 16 ct + 4 (col % 4) .. + 3)
   // (rows r and r + 16 share the swizzle: the second row tile is 16 KB on)
-  uint32_t st_addr[4], qk_addr[4], pv_addr[4];
+  uint32_t st_addr[2][4], qk_addr[4], pv_addr[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) st_addr[j] = lds_addr(&tile[0][htile_off(drow, 4 * c32 + j)]);
+  for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st_addr[pc][j] = lds_addr(&tile[0][htile_off(drow, 4 * (c32 + 8 * pc) + j)]);
 #pragma unroll
   for (int s = 0; s < 4; ++s) qk_addr[s] = lds_addr(&tile[0][htile_off(col, 32 * kh + 4 * s + g)]);
   {
@@ -721,20 +736,22 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o_acc[h4][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // one code path for every sub-chunk: each lane's row is an FP4 entry, a
-  // window row or absent (lanes branch apart only in the one sub-chunk that
-  // holds both kinds)
-  auto process = [&](int sc, const HLoads& L) {
+  // kh = 1 waves: dequantize this lane's two row pieces (32 channels each)
+  // of sub-chunk sc into tile buffer sc % 2.  One code path for every
+  // sub-chunk: each lane's row is an FP4 entry, a window row or absent
+  // (lanes branch apart only in the one sub-chunk that holds both kinds)
+  auto dequant = [&](int sc, const HLoads (&LL)[2]) __attribute__((always_inline)) {
     const uint32_t tb = (uint32_t)(sc & 1) * kBufBytes;
-    // ---- dequantize this lane's row piece (32 channels) into the tile
-    {
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {
+      const HLoads& L = LL[pc];
       v8h d[4];
       const int s = L.s;
       auto fp4_row = [&](bool present) {
         uint32_t pm = present ? 0xFFFFFFFFu : 0u;
         asm volatile("" : "+v"(pm));
-        // groups 2 c32, 2 c32 + 1: bytes 2 (c32 % 8), + 1 of the 16 loaded
-        // scale bytes, picked by selects (a lane-dependent element index
+        // groups 2 c, 2 c + 1 of piece c (c = c32 + 8 pc): bytes 2 (c % 8),
+        // + 1 of the 16 loaded scale bytes (c % 8 = c32 % 8), picked by selects (a lane-dependent element index
         // would put the load buffers in scratch memory)
         const int wsel = (c32 & 7) >> 1;
         const uint32_t w01 = (wsel & 1) ? L.hi[1] : L.hi[0];
@@ -768,9 +785,19 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
       if (s != kRowWindow) fp4_row(s >= 0);
       else fp8_row(true);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lds_st16(st_addr[j] + tb, d[j]);
+      for (int j = 0; j < 4; ++j) lds_st16(st_addr[pc][j] + tb, d[j]);
     }
-    lds_barrier();  // 1: the tile is complete
+  };
+
+  // slot: the ring slot of sub-chunk sc + 1 (its loads in, sub-chunk sc + 3's
+  // loads out); the loop below alternates the slots, so that no load result
+  // is copied (a copy would wait for the load)
+  // The two roles run their own copies of the loop (KH1: the wave's channel
+  // half, known at compile time), so that the kh = 1 waves issue their loads
+  // in every pass and each wait on them counts exactly the newer loads.
+  auto process = [&](auto kh_c, int sc, HLoads (&slot)[2]) __attribute__((always_inline)) {
+    constexpr bool KH1 = decltype(kh_c)::value;
+    const uint32_t tb = (uint32_t)(sc & 1) * kBufBytes;
     // ---- Q.K role: partial logits of rows 16 rt + 4 g + i, head 16 ht + col,
     // over this wave's channel half
     v4f sacc[2];
@@ -786,12 +813,12 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
         for (int s = 0; s < 4; ++s) sacc[rt] = mfma16(ka[s], qb[4 * h + s], sacc[rt]);
       }
     }
-    if (kh == 1) {
+    if constexpr (KH1) {
       spart[ht][0][lane] = sacc[0];
       spart[ht][1][lane] = sacc[1];
     }
-    lds_barrier();  // 2: the second halves' partial logits
-    if (kh == 0) {
+    lds_barrier();  // 1: the second halves' partial logits
+    if constexpr (!KH1) {
       // ---- logits (fixed order: first half + second half), online softmax
       // with the lazy reference of the head-tile kernel above
       const int sub0 = sc * kSub;
@@ -828,8 +855,15 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
       for (int rt = 0; rt < 2; ++rt) *(__attribute__((address_space(3))) v4h*)(uintptr_t)(p_st + 8u * rt) = pq[rt];
       if (lane < 16) salpha[16 * ht + lane] = alpha;
       if (lane == 0) sgrow[ht] = rescale ? 1 : 0;
+    } else {
+      // ---- the next sub-chunk's tile (its buffer was last read by the
+      // P.V of sub-chunk sc - 1, which every wave finished before barrier
+      // 1); past the last sub-chunk the rows are absent (zeros into a
+      // buffer no wave reads again, loads of the pool's first bytes)
+      dequant(sc + 1, slot);
+      issue_sub(sc + 3, slot);
     }
-    lds_barrier();  // 3: P and the rescale factors
+    lds_barrier();  // 2: P, the rescale factors and the next tile
     // ---- P.V role: rescale, then O[heads][64 w + 16 ct ..] += P . V
     if ((sgrow[0] | sgrow[1] | sgrow[2] | sgrow[3]) != 0) {
 #pragma unroll
@@ -856,13 +890,21 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
     }
   };
 
-  for (int sc = 0; sc < n_sub; ++sc) {
-    process(sc, buf[0]);
-#pragma unroll
-    for (int i = 0; i + 1 < NB; ++i) buf[i] = buf[i + 1];
-    const int nx = sc + NB;
-    issue_hrow(a, rslot, nx * kSub + drow, row0 + nx * kSub + drow, n_rel, c32, win_row0, buf[NB - 1]);
-  }
+  // the first tile, then one pass per sub-chunk (ring slot s % 2 holds
+  // sub-chunk s's loads)
+  if (kh == 1) dequant(0, buf[0]);
+  issue_sub(sc_pro + 2, buf[0]);
+  lds_barrier();
+  auto loop = [&](auto kh_c) __attribute__((always_inline)) {
+    int sc = 0;
+    for (; sc + 1 < n_sub; sc += 2) {
+      process(kh_c, sc, buf[1]);
+      process(kh_c, sc + 1, buf[0]);
+    }
+    if (sc < n_sub) process(kh_c, sc, buf[1]);
+  };
+  if (kh == 0) loop(std::false_type{});
+  else loop(std::true_type{});
 
   // ---- every head's (m, l) to all waves
   if (kh == 0 && lane < 16) {
@@ -1073,7 +1115,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   }
   const int n_units = aa.n_splits * B * T;
   if (all_heads(H)) {
-    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel<2>, dim3(n_units),
+    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel, dim3(n_units),
                 dim3(csa2::kHThreads), (hipStream_t)stream, aa);
   } else {
     const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
