@@ -13,10 +13,10 @@
 // combine kernel; with one split the output is written directly), resolves a
 // split's rows once (index -> page -> cache slot) into LDS, and keeps the row
 // loads of the next 32-row sub-chunks in flight while one is processed.
-//  - 64 heads (attn_heads_kernel, below): one workgroup per (b, t, split)
+//  - 64 heads, B*T >= 8 (attn_heads_kernel, below): one workgroup per (b, t, split)
 //    serves every head, so each row is gathered and dequantized once into a
 //    shared LDS tile of fp16 rows.
-//  - 16 or 32 heads (attn_split_kernel): one workgroup per (b, t, 16-head
+//  - otherwise (attn_split_kernel): one workgroup per (b, t, 16-head
 //    tile, split); its 4 waves own 128 channels each.  Per sub-chunk a wave
 //    converts its channel slice to fp16 (hardware FP4 / E4M3 conversion,
 //    exact) straight into the Q.K operand and into a swizzled row-major LDS
@@ -1027,14 +1027,19 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// 64 heads take the all-heads kernel (one workgroup per (b, t, split));
-// 16 or 32 heads the head-tile kernel (one per (b, t, head tile, split)).
-bool all_heads(int H) { return H == 64; }
+// 64 heads with B*T >= 8 take the all-heads kernel (one workgroup per (b,
+// t, split)); fewer heads or rows the head-tile kernel (one per (b, t, head
+// tile, split)).
+// (At B*T = 4, 1M context, the head-tile kernel's 272 workgroups finish the
+// replayed layer step ~4.5 us sooner than the all-heads kernel's 92; from
+// B*T = 8 on the all-heads kernel is faster: 62 against 67 us per 128K Full
+// layer at B = 8, 56 against 90 us per layer at B*T = 64.)
+bool all_heads(int H, int BT) { return H == 64 && BT >= 8; }
 
 // Rows per split (a multiple of 32) and the number of splits of one (b, t)'s
 // [top-k | window] row list: about kTargetWorkgroups workgroups in all.
 void split_plan(int BT, int H, int topk, int* n_splits, int* split_rows) {
-  if (all_heads(H)) {
+  if (all_heads(H, BT)) {
     const int rows = topk + CSA2_SWA;
     const int max_splits = std::min((rows + csa2::kSub - 1) / csa2::kSub, csa2::kMaxSplits);
     int ns = std::max(1, std::min((csa2::kTargetWorkgroups + BT - 1) / BT, max_splits));
@@ -1114,7 +1119,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
     aa.out_lse = out_lse;
   }
   const int n_units = aa.n_splits * B * T;
-  if (all_heads(H)) {
+  if (all_heads(H, B * T)) {
     CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel, dim3(n_units),
                 dim3(csa2::kHThreads), (hipStream_t)stream, aa);
   } else {

@@ -761,8 +761,12 @@ def test_attention_8k_b1(oracle):
     check_attention(oracle, wl, L, ref_tk, out, lse=lse)
 
 
+# 64 heads at B*T < 8 run the head-tile kernel, at B*T >= 8 (T >= 3 here,
+# three sequences) the all-heads kernel; k = 100 and 2,047 leave a sub-chunk
+# holding both top-k and window rows
 @pytest.mark.parametrize("H,T,k,frac", [(16, 1, 256, 1.0), (32, 2, 512, 0.7), (64, 1, 2048, 0.5),
-                                        (64, 2, 2048, 1.0), (16, 4, 8, 1.0), (64, 1, 100, 0.0)])
+                                        (64, 2, 2048, 1.0), (16, 4, 8, 1.0), (64, 1, 100, 0.0),
+                                        (64, 3, 2048, 0.5), (64, 4, 100, 0.0), (64, 3, 2047, 1.0)])
 def test_attention_random_index_sets(oracle, H, T, k, frac):
     say(f"attention random sets H={H} T={T} k={k} valid={frac}")
     n = [5000, 300, 9999]
@@ -773,14 +777,15 @@ def test_attention_random_index_sets(oracle, H, T, k, frac):
     check_attention(oracle, wl, L, idx, out, lse=lse)
 
 
-def test_attention_outlier_heavy(oracle):
-    say("attention with 5% +-8 outliers and sharp logits")
+@pytest.mark.parametrize("T", [1, 8])
+def test_attention_outlier_heavy(oracle, T):
+    say(f"attention with 5% +-8 outliers and sharp logits, T={T}")
     n = [4096]
-    wl = small_workload(n, T=1, H=64, topk=2048, seed=31)
+    wl = small_workload(n, T=T, H=64, topk=2048, seed=31)
     wl.kv_source = synth.kv_rows(4096, 32, outlier_frac=0.05)
     wl.sm_scale = 1.0 / 8.0
-    L = synth.layer_inputs("reuse", 1, 1, 0, 64, 33, q_std=1.0)
-    idx = synth.random_topk(1, 1, 2048, wl.n_entries, seed=34)
+    L = synth.layer_inputs("reuse", 1, T, 0, 64, 33, q_std=1.0)
+    idx = synth.random_topk(1, T, 2048, wl.n_entries, seed=34)
     out, _ = gpu_attention(wl, L, idx)
     check_attention(oracle, wl, L, idx, out)
 
