@@ -98,9 +98,11 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint
                                              int lane) {
   const v4u* hv = reinterpret_cast<const v4u*>(h + kBins - 64 * (lane + 1));
   uint32_t sum = 0;
+  // lane l reads its 16 quads starting at quad l % 16, so that 16 lanes read
+  // 16 different bank groups (the lanes' ranges lie 256 bytes apart)
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const v4u v = hv[q];
+    const v4u v = hv[(q + lane) & 15];
     sum += v[0] + v[1] + v[2] + v[3];
   }
   const uint32_t incl = wave_incl_scan(sum);
