@@ -390,6 +390,13 @@ def bench_layer(args):
     t0 = time.perf_counter()
     wl = synth.workload(args.workload)
     L = wl.layers[0]
+    if args.score_path == "general-q":
+        # indexer queries N(0, 64^2): every row has some |q| >= 32, so the scan scores it on the
+        # int8 three-limb path
+        L.q_idx = synth.fp8_normal(L.q_idx.shape, 901, std=64.0)
+    elif args.score_path == "general-k":
+        # indexer keys N(0, 4^2): every entry has sum k^2 > 500, so every chunk takes the int8 path
+        wl.kidx_pool = synth.fp8_normal(wl.kidx_pool.shape, 902, std=4.0)
     log(f"workload {args.workload} generated in {time.perf_counter() - t0:.1f} s")
     up = _uploader(torch, dev)
     pt, ne = up(wl.paging.page_table), up(wl.n_entries)
@@ -486,6 +493,7 @@ def bench_layer(args):
                    "context_tokens": int(wl.max_n) * 4, "entries_per_seq": int(wl.max_n),
                    "indexer_heads": wl.HI, "heads": H, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
                    "indexer_key_format": args.kidx_format, "cache_copies_rotated": args.copies,
+                   "score_path": args.score_path,
                    "launch": "eager" if graphs is None else "hip_graph_replay"},
         "hbm_tb_s": round(step_gbs / 1000.0, 3),
         "hbm_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -494,7 +502,8 @@ def bench_layer(args):
         "roofline": {"kernel": "score_kernel (Full-mode exact score scan)", "bound": "hbm",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if (mx or args.workload != "full_1m_b4") else measured_traffic(),
+                     "traffic": None if (mx or args.workload != "full_1m_b4" or args.score_path != "fast")
+                     else measured_traffic(),
                      "algorithmic_bytes_per_launch": nbytes["scan"]},
     }
     if not args.no_cpu_baseline:
@@ -867,6 +876,9 @@ def main():
     ap.add_argument("--kidx-format", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer-key format: E4M3 (128 B per entry) or the pages' MXFP4 (68 B per entry, "
                          "random synthetic codes and scales)")
+    ap.add_argument("--score-path", choices=["fast", "general-q", "general-k"], default="fast",
+                    help="indexer inputs of the default workload: N(0,1) (the f16 two-limb path), queries "
+                         "N(0, 64^2) (every row on the int8 general path) or keys N(0, 4^2) (every chunk on it)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the counter-calibration sequence (for rocprofv3 --pmc runs)")
