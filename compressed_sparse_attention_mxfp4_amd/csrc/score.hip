@@ -148,6 +148,8 @@ struct ChunkKeys {
 // Row context of a wave: sequence b, token t, visible entries n, pool row.
 struct RowCtx {
   int b = 0, t = 0, n = 0, n_pos = 0;
+  int n_raw = 0, nv_raw = 0, pn_raw = 0;  // the loaded counts, before row_ctx_finish
+  bool live = false;
   const int32_t* pool_row = nullptr;
   // pool mode: the workgroup's pool slots slot0 .. slot0 + nslots - 1
   // resolved to physical entries (LDS, see pool_slot_word)
@@ -182,8 +184,11 @@ __device__ __forceinline__ int pool_entry(const RowCtx& r, int p) {
 // (live: the token exists; the dead fourth slot of a group of three sees
 // nothing).  Token t of sequence b sees its first min(n_entries[b],
 // n_vis[b][t]) entries.
+// row_ctx_load only issues the count loads; row_ctx_finish, after the
+// workgroup's other early loads have gone out, turns them into the counts
+// (a load used at once would hold every later load back by a round trip).
 template <bool POOL>
-__device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full, bool live, RowCtx& r) {
+__device__ __forceinline__ void row_ctx_load(const ScoreArgs& a, int row, int t_full, bool live, RowCtx& r) {
   if (POOL) {
     r.b = row / a.T;
     r.t = row % a.T;
@@ -191,15 +196,30 @@ __device__ __forceinline__ void row_ctx(const ScoreArgs& a, int row, int t_full,
     r.b = row / a.n_groups;
     r.t = t_full;
   }
-  int n = a.n_entries[r.b];
-  n = min(n, a.max_n);
-  n = max(0, min(n, a.max_pages * kPage));
-  if (a.n_vis != nullptr) n = max(0, min(n, a.n_vis[(int64_t)r.b * a.T + r.t]));
-  if (!live) n = 0;
-  r.n = n;
+  r.live = live;
+  // vector loads (indices in VGPRs): a scalar load would share its wait
+  // counter with the kernel arguments' loads, so the next argument read
+  // would wait for it
+  int bi = r.b, vi = r.b * a.T + r.t, pi = row;
+  asm volatile("" : "+v"(bi), "+v"(vi), "+v"(pi));
+  r.n_raw = a.n_entries[bi];
+  r.nv_raw = a.n_vis != nullptr ? a.n_vis[vi] : 0x7FFFFFFF;
   if (POOL) {
     r.pool_row = a.pool + (int64_t)row * a.pool_blocks;
-    const int pn = max(0, min(a.pool_n[row], a.pool_blocks));
+    r.pn_raw = a.pool_n[pi];
+  }
+}
+
+template <bool POOL>
+__device__ __forceinline__ void row_ctx_finish(const ScoreArgs& a, RowCtx& r) {
+  int n = r.n_raw;
+  n = min(n, a.max_n);
+  n = max(0, min(n, a.max_pages * kPage));
+  n = max(0, min(n, r.nv_raw));
+  if (!r.live) n = 0;
+  r.n = n;
+  if (POOL) {
+    const int pn = max(0, min(r.pn_raw, a.pool_blocks));
     r.n_pos = pn * kBlock;
   } else {
     r.n_pos = n;
@@ -674,6 +694,13 @@ struct PlanRows {
   int ch[kPlanRows], minw[kPlanRows], work[kPlanRows];
 };
 
+// The loaded counts of lane L's rows j * 64 + L (clamped indices, every load
+// unconditional): n_entries and, with per-token counts, the group's tokens'.
+struct PlanRaw {
+  int n[kPlanRows];
+  int v[kPlanRows][kGroupT];
+};
+
 struct PlanPart {
   int row, seg, nseg, c0, c1;
 };
@@ -704,10 +731,24 @@ __device__ __forceinline__ void plan_group(const ScoreArgs& a, int r, int& b, in
   tg = min(kGroupT, a.T - t0);
 }
 
+__device__ __forceinline__ PlanRaw plan_row_loads(const ScoreArgs& a) {
+  PlanRaw pr;
+#pragma unroll
+  for (int j = 0; j < kPlanRows; ++j) {
+    const int r = min(j * 64 + lane_id(), a.rows - 1);
+    int b, t0, tg;
+    plan_group(a, r, b, t0, tg);
+    pr.n[j] = a.n_entries[b];
+#pragma unroll
+    for (int k = 0; k < kGroupT; ++k)
+      pr.v[j][k] = a.n_vis != nullptr ? a.n_vis[(int64_t)b * a.T + min(t0 + k, a.T - 1)] : 0x7FFFFFFF;
+  }
+  return pr;
+}
+
 // Lane L's rows j * 64 + L: visible chunks, workgroups their length needs
 // (the per-workgroup cap is kMaxWgChunks for every token count), work.
-// Only loads and a little arithmetic.
-__device__ __forceinline__ PlanRows plan_row_counts(const ScoreArgs& a) {
+__device__ __forceinline__ PlanRows plan_row_counts(const ScoreArgs& a, const PlanRaw& raw) {
   PlanRows pr;
 #pragma unroll
   for (int j = 0; j < kPlanRows; ++j) {
@@ -715,17 +756,15 @@ __device__ __forceinline__ PlanRows plan_row_counts(const ScoreArgs& a) {
     pr.ch[j] = 0;
     pr.minw[j] = 0;
     pr.work[j] = 0;
-    if (j * 64 >= a.rows) continue;  // uniform
     if (r < a.rows) {
       int b, t0, tg;
       plan_group(a, r, b, t0, tg);
-      int n = min(min(a.n_entries[b], a.max_n), a.max_pages * kPage);
-      if (a.n_vis != nullptr) {
-        int nm = 0;
-        for (int k = 0; k < tg; ++k) nm = max(nm, min(n, a.n_vis[(int64_t)b * a.T + t0 + k]));
-        n = nm;
-      }
-      n = max(n, 0);
+      int n = min(min(raw.n[j], a.max_n), a.max_pages * kPage);
+      int nm = 0;
+#pragma unroll
+      for (int k = 0; k < kGroupT; ++k)
+        if (k < tg) nm = max(nm, min(n, raw.v[j][k]));
+      n = max(nm, 0);
       const int ch = (n + kChunk - 1) / kChunk;
       pr.ch[j] = ch;
       pr.minw[j] = max(1, (ch + kMaxWgChunks - 1) / kMaxWgChunks);
@@ -870,7 +909,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     n_slices = POOL ? kWaves : kWaves / Ts;
     n_tok = POOL ? 1 : Ts;
     rc = RowCtx{};
-    row_ctx<POOL>(a, rr, t_full, slot < Tg, rc);
+    row_ctx_load<POOL>(a, rr, t_full, slot < Tg, rc);
   };
   set_row();
 
@@ -937,9 +976,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // the static plan's part; when the balanced plan gives another part, the
   // early loads go out again for it
   if (!POOL && a.balanced) {
-    const PlanRows prow = plan_row_counts(a);
+    const PlanRaw praw = plan_row_loads(a);
     issue_early();
-    const PlanPart pp = scan_plan_balanced(a, prow);
+    row_ctx_finish<POOL>(a, rc);
+    const PlanPart pp = scan_plan_balanced(a, plan_row_counts(a, praw));
     if (pp.row >= a.rows) return;  // past the plan (the same for the whole workgroup)
     seg = pp.seg;
     nseg = pp.nseg;
@@ -949,9 +989,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       c1 = pp.c1;
       set_row();
       issue_early();
+      row_ctx_finish<POOL>(a, rc);
     }
   } else {
     issue_early();
+    row_ctx_finish<POOL>(a, rc);
   }
   const bool have_row = row < a.rows;
   int chunk = c0 + slice;
