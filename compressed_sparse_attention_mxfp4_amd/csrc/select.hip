@@ -365,8 +365,10 @@ __device__ __forceinline__ void seg_issue(const SelectArgs& a, int64_t bt, int l
   const v2u hv = *reinterpret_cast<const v2u*>(a.seg_hdr + seg0 + std::min(tid, a.max_segs - 1));
   L.h = SegHeader{hv[0], hv[1]};
   const int s = std::min(tid / tps, W - 1), j0 = tid % tps;
-  const v2u ov = *reinterpret_cast<const v2u*>(a.seg_hdr + seg0 + s);
-  L.own = SegHeader{ov[0], ov[1]};
+  // (only the count of the own header is used: a 4-byte load, since a dead
+  // half of a wider load's destination could be reused early, and that
+  // reuse would wait for the load)
+  L.own = SegHeader{reinterpret_cast<const uint32_t*>(a.seg_hdr + seg0 + s)[0], 0u};
   const Cand* base = a.seg_cand + (bt * 2 + list) * a.seg_region + seg_off_at(a.seg_k, s);
   const int cap = seg_cap_at(a.seg_k, s);
 #pragma unroll
