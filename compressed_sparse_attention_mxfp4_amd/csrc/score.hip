@@ -1234,10 +1234,25 @@ int csa2_score_grid(int rows, int chunks_per_row, int T_slots, int* chunks_per_w
   per = ((per + slices - 1) / slices) * slices;  // whole rounds of the waves
   // each wave tracks at most kMaxWaveChunks chunks; the workgroup's 16-bit
   // histogram counters hold at most kMaxWgChunks chunks of one token
-  per = std::min(per, std::min(csa2::kMaxWaveChunks * slices, csa2::kMaxWgChunks));
+  const int cap = std::min(csa2::kMaxWaveChunks * slices, csa2::kMaxWgChunks);
+  per = std::min(per, cap);
+  int wpr = (chunks_per_row + per - 1) / per;
+  // more workgroups than one per compute unit: make the rounds whole, so
+  // that a short last round does not run on a few units while the rest idle
+  // (a 256-token prefill chunk at 1M context: 5 x 64 = 320 workgroups of
+  // 1,016 chunks become 512 of 512)
+  const int64_t total = (int64_t)rows * wpr;
+  if (total > csa2::kScanTarget) {
+    const int64_t rounds = (total + csa2::kScanTarget - 1) / csa2::kScanTarget;
+    const int want2 = (int)((rounds * csa2::kScanTarget + rows - 1) / rows);
+    int per2 = (chunks_per_row + want2 - 1) / want2;
+    per2 = ((per2 + slices - 1) / slices) * slices;
+    per = std::min(std::max(per2, slices), cap);
+    wpr = (chunks_per_row + per - 1) / per;
+  }
   *chunks_per_wg = per;
-  *wg_per_row = (chunks_per_row + per - 1) / per;
-  return rows * *wg_per_row;
+  *wg_per_row = wpr;
+  return rows * wpr;
 }
 
 bool csa2_scan_balanced(int rows, int chunks_per_row) {
