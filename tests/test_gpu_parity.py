@@ -777,6 +777,26 @@ def test_attention_random_index_sets(oracle, H, T, k, frac):
     check_attention(oracle, wl, L, idx, out, lse=lse)
 
 
+@pytest.mark.parametrize("H,T", [(64, 1), (64, 8), (16, 2)])
+def test_attention_query_magnitudes(oracle, H, T):
+    """Queries whose heads span 2^-24 .. 2^24 in scale (bf16, some far above fp16's 65,504, some
+    below its normal range): every head's fp16 operand is the bf16 query times a power of two
+    (exact), so the outputs stay within the bound on both attention kernels."""
+    say(f"attention with query heads scaled 2^-24 .. 2^24, H={H} T={T}")
+    n = [3000, 777]
+    wl = small_workload(n, T=T, H=H, topk=512, seed=41)
+    L = synth.layer_inputs("reuse", wl.B, T, 0, H, 42, q_std=1.0)
+    q = oracle.bf16_to_f64(L.q).reshape(wl.B, T, H, 512)
+    e = np.linspace(-24, 24, H).round()
+    q = q * (2.0 ** e)[None, None, :, None]
+    L.q = np.asarray(torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()).view(np.uint16)
+    wl.sm_scale = 2.0 ** -26
+    idx = synth.random_topk(wl.B, T, 512, wl.n_entries, seed=43)
+    out, _ = gpu_attention(wl, L, idx)
+    assert np.isfinite(out).all()
+    check_attention(oracle, wl, L, idx, out)
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_attention_outlier_heavy(oracle, T):
     say(f"attention with 5% +-8 outliers and sharp logits, T={T}")
