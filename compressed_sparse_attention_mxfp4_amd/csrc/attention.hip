@@ -12,7 +12,11 @@
 // workgroup per compute unit (the splits' partial results merged by a
 // combine kernel; with one split the output is written directly), resolves a
 // split's rows once (index -> page -> cache slot) into LDS, and keeps the row
-// loads of the next 32-row sub-chunks in flight while one is processed.
+// loads of the next 32-row sub-chunks in flight while one is processed.  The
+// head-tile kernel takes as many splits as fit one round of workgroups and
+// shares the 32-row sub-chunks out evenly (a second, partly filled round
+// would leave its workgroups sharing compute units, and the slowest of them
+// sets the kernel's time).
 //  - 64 heads, B*T >= 8 (attn_heads_kernel, below): one workgroup per (b, t, split)
 //    serves every head, so each row is gathered and dequantized once into a
 //    shared LDS tile of fp16 rows.
@@ -83,7 +87,9 @@ struct AttnArgs {
   int H;
   int BT;
   int n_splits;
-  int split_rows;  // rows per split, a multiple of 32
+  int split_rows;  // rows per split, a multiple of 32 (the head-tile kernel: the most of any split)
+  int split_base;  // head-tile kernel: split i has split_base + (i < split_extra) sub-chunks
+  int split_extra;
   float* part_o;   // n_splits > 1: [B*T][H/16][n_splits][16][512]
   float* part_ml;  // n_splits > 1: [B*T][H/16][n_splits][32]  (m[16] in log2 units, l[16])
   float* out;      // n_splits == 1: [B*T][H][512]
@@ -117,58 +123,129 @@ __device__ __forceinline__ v4h lds_ld_tr(uint32_t addr) {
 constexpr int kRowAbsent = -1;   // empty top-k slot, or past the split's end
 constexpr int kRowWindow = -2;   // a window row (its place in the list gives which)
 
-// Kinds of row content a sub-chunk can hold (decided per sub-chunk, the same
-// for every wave): only FP4 entries (rows < topk), only window rows, or both.
+// Kinds of row content a split can hold (decided per split, the same for
+// every wave): only FP4 entries (rows < topk), only window rows, or both.
 enum SubMode { kMixed = 0, kFp4Only = 1, kWindowOnly = 2 };
 
 // The row loads of one sub-chunk for one lane (g, col): rows col and
 // 16 + col, the wave's channels 128 w + 32 g .. + 31.  FP4 row: 16 code
 // bytes + the 16 scale bytes 16 (w / 2) .. + 15 of the entry (the lane's two
-// groups among them); window row: 32 E4M3 bytes; absent rows read the pool's
-// first bytes (discarded).
+// groups among them), or in a split of FP4 rows only just the 4 scale bytes
+// holding the lane's two (hi[rt][0]); window row: 32 E4M3 bytes; absent rows
+// read the pool's first bytes (discarded).
 struct SubLoads {
   v4u lo[2], hi[2];
   int s[2];  // the rows' slots (or kRowAbsent / kRowWindow)
 };
 
-typedef const __attribute__((address_space(1))) v4u gbl_v4u_t;
-__device__ __forceinline__ v4u gld16(const uint8_t* p) { return *(gbl_v4u_t*)p; }
+// Cache slot of list row `row` of a (b, t) (rows past row1 are absent):
+// j is its top-k index and pg the page-table word of j's page (both unused
+// for a window row).
+__device__ __forceinline__ int row_slot(const AttnArgs& a, int row, int row1, int n, int j, int pg) {
+  if (row >= row1) return kRowAbsent;
+  if (row >= a.topk) return kRowWindow;
+  return (j >= 0 && j < n && pg >= 0 && pg < a.n_pages) ? (int)((int64_t)pg * kPage + (j & 63)) : kRowAbsent;
+}
 
-// rel0: the sub-chunk's first row in the split (rslot index); abs0: in the
-// whole list (window row w = list row - topk).
-// The loads are always issued, also for sub-chunks past the split's end
-// (their rows read as absent), so that every path through the loop has the
-// same loads in flight and each wait counts exactly the later sub-chunks'.
-__device__ __forceinline__ void issue_sub(const AttnArgs& a, const int* rslot, int rel0, int abs0, int n_rel,
-                                          int wave, int g, int col, const uint8_t* win_row0, SubLoads& L) {
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = 16 * rt + col;
-    const int s = rel0 + r < n_rel ? rslot[rel0 + r] : kRowAbsent;
-    L.s[rt] = s;
-    const uint8_t* p0 = a.kv_pool;
-    const uint8_t* p1 = a.kv_pool;
-    if (s >= 0) {
-      const uint8_t* page = a.kv_pool + (int64_t)(s >> 6) * kPageBytes;
-      p0 = page + (s & 63) * kEntryCodes + 64 * wave + 16 * g;
-      p1 = page + kPage * kEntryCodes + (s & 63) * kEntryScales + 16 * (wave >> 1);
-    } else if (s == kRowWindow) {
-      p0 = win_row0 + (int64_t)(abs0 + r - a.topk) * kD + 128 * wave + 32 * g;
-      p1 = p0 + 16;
-    }
-    // 16-byte loads at 16-byte aligned addresses inside the row they belong to
-    L.lo[rt] = gld16(p0);
-    L.hi[rt] = gld16(p1);
+// The split's relative rows r0 + threadIdx.x + k * step < n_rel, one at a
+// time (the kernels resolve their first rows with all loads in flight; with
+// the launcher's row count per thread nothing is left here).
+__device__ __forceinline__ void resolve_rest(const AttnArgs& a, const int32_t* idx_row, int b, int n, int row0,
+                                          int row1, int r0, int step, int n_rel, int* rslot) {
+  for (int r = r0 + (int)threadIdx.x; r < n_rel; r += step) {
+    const int row = row0 + r;
+    const int j = idx_row[max(0, min(row, a.topk - 1))];
+    const int pg = a.page_table[(int64_t)b * a.max_pages + max(0, min(j >> 6, a.max_pages - 1))];
+    rslot[r] = row_slot(a, row, row1, n, j, pg);
   }
 }
 
-template <int NB>
+typedef const __attribute__((address_space(1))) v4u gbl_v4u_t;
+typedef const __attribute__((address_space(1))) uint32_t gbl_u32_t;
+__device__ __forceinline__ v4u gld16(const uint8_t* p) { return *(gbl_v4u_t*)p; }
+__device__ __forceinline__ uint32_t gld4(const uint8_t* p) { return *(gbl_u32_t*)p; }
+
+// The slot of the split's relative row rel (absent from n_rel on): the LDS
+// read is unconditional (index clamped), so that the reads of several rows
+// can go out together.
+__device__ __forceinline__ int row_at(const int* rslot, int rel, int n_rel) {
+  const int v = rslot[min(rel, n_rel - 1)];
+  return rel < n_rel ? v : kRowAbsent;
+}
+
+// The two 16-byte load addresses of a lane's piece of list row abs_row with
+// slot s: FP4 entry -> its codes at byte c_off and its scale bytes at s_off;
+// window row -> its bytes w_off and w_off + 16; absent -> the pool's first
+// bytes (read and discarded).  Chosen by selects, with no branch.
+struct RowPtrs {
+  const uint8_t* p0;
+  const uint8_t* p1;
+};
+__device__ __forceinline__ RowPtrs row_ptrs(const AttnArgs& a, int s, const uint8_t* win_row0, int abs_row, int c_off,
+                                            int s_off, int w_off) {
+  const uintptr_t pool = (uintptr_t)a.kv_pool;
+  const uintptr_t page = pool + (uintptr_t)(uint32_t)(s >> 6) * kPageBytes;  // (used only for s >= 0)
+  const uintptr_t f0 = page + (uint32_t)((s & 63) * kEntryCodes + c_off);
+  const uintptr_t f1 = page + (uint32_t)(kPage * kEntryCodes + (s & 63) * kEntryScales + s_off);
+  const uintptr_t w0 = (uintptr_t)win_row0 + (uintptr_t)(int64_t)((abs_row - a.topk) * kD + w_off);
+  const bool fp4 = s >= 0, win = s == kRowWindow;
+  uintptr_t q0 = win ? w0 : pool, q1 = win ? w0 + 16 : pool;
+  q0 = fp4 ? f0 : q0;
+  q1 = fp4 ? f1 : q1;
+  return RowPtrs{(const uint8_t*)q0, (const uint8_t*)q1};
+}
+
+// The slots of a lane (g, col)'s rows col and 16 + col of the sub-chunk
+// starting at relative row rel0 (read ahead of the loads they address).
+struct SubSlots {
+  int s[2];
+};
+__device__ __forceinline__ SubSlots read_sub(const int* rslot, int rel0, int n_rel, int col) {
+  return SubSlots{{row_at(rslot, rel0 + col, n_rel), row_at(rslot, rel0 + 16 + col, n_rel)}};
+}
+
+// abs0: the sub-chunk's first row in the whole list (window row w = list
+// row - topk).  The loads are always issued, also for sub-chunks past the
+// split's end (their rows read as absent), so that every path through the
+// loop has the same loads in flight and each wait counts exactly the later
+// sub-chunks'.
+// SC4: the split holds FP4 rows only (4-byte scale loads).
+template <bool SC4>
+__device__ __forceinline__ void issue_sub(const AttnArgs& a, const SubSlots& ss, int abs0, int wave, int g, int col,
+                                          const uint8_t* win_row0, SubLoads& L) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int s = ss.s[rt];
+    L.s[rt] = s;
+    // the lane's groups 8 w + 2 g, + 1: scale bytes 8 (w & 1) + 2 g, + 1 of
+    // the 16 at the scale offset, in the word 2 (w & 1) + g / 2
+    const RowPtrs rp = row_ptrs(a, s, win_row0, abs0 + 16 * rt + col, 64 * wave + 16 * g,
+                                16 * (wave >> 1) + (SC4 ? 4 * (2 * (wave & 1) + (g >> 1)) : 0), 128 * wave + 32 * g);
+    // 16-byte loads at 16-byte aligned addresses inside the row they belong to
+    L.lo[rt] = gld16(rp.p0);
+    if (SC4) L.hi[rt] = v4u{gld4(rp.p1), 0u, 0u, 0u};
+    else L.hi[rt] = gld16(rp.p1);
+  }
+}
+
+// KP: rows of the list each thread resolves (KP * 256 >= the split's rows)
+// MAXS > 0: every split has at most MAXS sub-chunks, and the sub-chunk loop
+// is unrolled whole (no loop-carried load buffers, whose copies into the
+// loop's registers would wait for the loads): sub-chunk sc uses buffer
+// sc % NB.  MAXS = 0: the sub-chunks go through a ring of NB load buffers.
+template <int NB, int KP, int MAXS>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
   __shared__ __attribute__((aligned(16))) v4f ssum[2][4][2][64];  // double-buffered by sub-chunk
   __shared__ __attribute__((aligned(16))) float alph[4][16];       // per wave: rescale factor per head
   __shared__ __attribute__((aligned(16))) float qmax[4][16];       // per wave: max |q| per head
   __shared__ __attribute__((aligned(16))) int rslot[kMaxRows + kSub];
+  // STRAIGHT: each row's two load bases (FP4 entry: its codes and its scale
+  // bytes; window row: its bytes and 16 bytes on; absent: the pool's first
+  // bytes), so that a lane's load addresses cost one add each
+  constexpr bool STRAIGHT = MAXS > 0;
+  constexpr int kRB = STRAIGHT ? MAXS * kSub : 1;
+  __shared__ __attribute__((aligned(16))) uint64_t rbase[kRB][2];
 
   // XCD-aware order: workgroup id % 8 picks the XCD (and its L2).  The NHT
   // head tiles of one (split, b, t) unit take ids 8 apart, so they share an
@@ -190,8 +267,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   n = min(n, a.max_pages * kPage);
 
   const int n_rows = a.topk + kSwa;
-  const int row0 = split * a.split_rows;
-  const int row1 = min(n_rows, row0 + a.split_rows);
+  // the split's sub-chunks: split_base each, one more for the first
+  // split_extra splits
+  const int row0 = kSub * (split * a.split_base + min(split, a.split_extra));
+  const int row1 = min(n_rows, row0 + kSub * (a.split_base + (split < a.split_extra ? 1 : 0)));
   const int n_sub = (row1 - row0 + kSub - 1) / kSub;
   const int32_t* idx_row = a.topk_idx + (int64_t)bt * a.topk;
   const uint8_t* win_row0 = a.swa + ((int64_t)b * (kSwa - 1 + a.T) + t) * kD;
@@ -208,7 +287,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   // window row, or absent (also past the split's end, up to whole sub-chunks)
   // (all index loads in flight together, then all page-table loads)
   {
-    constexpr int kPer = (kMaxRows + kSub + kAttnThreads - 1) / kAttnThreads;  // 9
+    constexpr int kPer = KP;
     const int n_rel = n_sub * kSub;
     int jj[kPer];
 #pragma unroll
@@ -226,18 +305,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = (int)threadIdx.x + k * kAttnThreads;
-      const int row = row0 + r;
-      int s = kRowAbsent;
-      if (row < row1) {
-        if (row < a.topk) {
-          const int j = jj[k];
-          if (j >= 0 && j < n && pp[k] >= 0 && pp[k] < a.n_pages) s = (int)((int64_t)pp[k] * kPage + (j & 63));
-        } else {
-          s = kRowWindow;
-        }
+      const int sl = row_slot(a, row0 + r, row1, n, jj[k], pp[k]);
+      if (r < n_rel) rslot[r] = sl;
+      if (STRAIGHT && r < kRB) {
+        // (rows past the split's end: absent)
+        const RowPtrs rp = row_ptrs(a, r < n_rel ? sl : kRowAbsent, win_row0, row0 + r, 0, 0, 0);
+        *reinterpret_cast<v4u*>(&rbase[r][0]) = __builtin_bit_cast(v4u, RowPtrs{rp.p0, rp.p1});
       }
-      if (r < n_rel) rslot[r] = s;
     }
+    resolve_rest(a, idx_row, b, n, row0, row1, kPer * kAttnThreads, kAttnThreads, n_rel, rslot);
   }
 
   // ---- Q slice as the B operand of S^T = K.Q^T: lane (g, col) holds head
@@ -246,31 +322,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   // Each head's query is scaled by a power of two that puts its largest |q|
   // in [2^14, 2^15), so that the fp16 operand never overflows; the logits
   // take the inverse power back (exact).
+  // ---- the sub-chunks' rows go through NB load buffers: the loads of NB
+  // sub-chunks are in flight while the first of them is processed (the wait
+  // counter retires loads in issue order, so each sub-chunk waits only for
+  // its own rows)
+  const int n_rel = n_sub * kSub;
+  SubLoads buf[NB];
   v8h qb[4];
-  float q_unscale;
+  float lg_scale;  // per head `col`
   {
-    const v4u (&raw)[4] = qraw;
     uint32_t mx = 0u;  // largest |q| bit pattern (bf16 in the high half)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mx = max(mx, max((raw[s][e] << 16) & 0x7FFF0000u, raw[s][e] & 0x7FFF0000u));
+      for (int e = 0; e < 4; ++e) mx = max(mx, max((qraw[s][e] << 16) & 0x7FFF0000u, qraw[s][e] & 0x7FFF0000u));
     const float m4 = rows4_max(__uint_as_float(mx));
     if (lane < 16) qmax[wave][lane] = m4;
     __syncthreads();  // also publishes rslot
+  }
+  // the query in fp16 (after the first row loads are out)
+  auto q_convert = [&]() __attribute__((always_inline)) {
     const float m = fmaxf(fmaxf(qmax[0][col], qmax[1][col]), fmaxf(qmax[2][col], qmax[3][col]));
     // exponent of the largest |q| (a normal or subnormal bf16): the scale is
     // 2^(14 - e), kept a binary32 power of two (at most 2^127)
     const int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 14;
     const int sh = min(127, 14 - e);
     const float up = __builtin_ldexpf(1.0f, sh);
-    q_unscale = __builtin_ldexpf(1.0f, -sh);
+    lg_scale = a.sm_scale_log2 * __builtin_ldexpf(1.0f, -sh);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4u pk;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const h2_t h = {(_Float16)(u2f(raw[s][e2] << 16) * up), (_Float16)(u2f(raw[s][e2] & 0xFFFF0000u) * up)};
+        const h2_t h = {(_Float16)(u2f(qraw[s][e2] << 16) * up), (_Float16)(u2f(qraw[s][e2] & 0xFFFF0000u) * up)};
         pk[e2] = __builtin_bit_cast(uint32_t, h);
       }
       // the packed words pass through an empty asm so that the compiler
@@ -278,8 +362,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       asm volatile("" : "+v"(pk));
       qb[s] = __builtin_bit_cast(v8h, pk);
     }
-  }
-  const float lg_scale = a.sm_scale_log2 * q_unscale;  // per head `col`
+  };
 
   // lane (g, col) dequantizes rows col and 16 + col of each 32-row
   // sub-chunk, the wave's channels 32g .. 32g + 31 (16-byte chunks 4g ..
@@ -331,10 +414,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
         uint32_t pm = present ? 0xFFFFFFFFu : 0u;
         asm volatile("" : "+v"(pm));
         // groups 8 wave + 2 g and + 1: bytes 8 (wave & 1) + 2 g, + 1 of hi
-        // (word 2 (wave & 1) + g / 2, picked by selects: g varies by lane)
+        // (word 2 (wave & 1) + g / 2, picked by selects: g varies by lane;
+        // in a split of FP4 rows only that word alone was loaded)
         const uint32_t wlo = (wave & 1) ? hi[2] : hi[0];
         const uint32_t whi = (wave & 1) ? hi[3] : hi[1];
-        const uint32_t sw = (((g >> 1) ? whi : wlo) >> (16 * (g & 1))) & 0xFFFFu;
+        const uint32_t wsel = kMode == kFp4Only ? hi[0] : ((g >> 1) ? whi : wlo);
+        const uint32_t sw = (wsel >> (16 * (g & 1))) & 0xFFFFu;
         const uint32_t s0 = (sw & 0xFFu) * 0x101u & pm, s1 = (sw >> 8) * 0x101u & pm;
         const h2_t sc0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, false);
         const h2_t sc1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, false);
@@ -461,37 +546,106 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       const v4h v1 = lds_ld_tr(pv_addr[c] + kRowBytes16);
       vb[c] = v8h{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
+    // (kept apart: the scheduler would otherwise pair each read with its
+    // product and wait out every read's latency in turn)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) o_acc[c] = mfma16(pa, vb[c], o_acc[c]);
     // the next sub-chunk's tile stores come after these reads
     wave_lds_order();
   };
 
-  // kind of the rows of sub-chunk sc (the same in every wave)
-  auto run_sub = [&](int sc, const SubLoads& L) {
-    const int r0 = row0 + sc * kSub, r1 = min(row1, r0 + kSub);
-    if (r1 <= a.topk) process(sc, L, std::integral_constant<int, kFp4Only>{});
-    else if (r0 >= a.topk) process(sc, L, std::integral_constant<int, kWindowOnly>{});
-    else process(sc, L, std::integral_constant<int, kMixed>{});
+  // The loop over the sub-chunks for one kind of split (the same for every
+  // wave): only FP4 entries (rows < topk), only window rows, or both.
+  // Ring: each round unrolls NB sub-chunks, so buffer j always holds
+  // sub-chunk NB r + j and no load result is copied inside the loop.  A
+  // sub-chunk's buffer is refilled with the loads of the sub-chunk NB later
+  // (absent rows past the split's end), whose slots are read from LDS before
+  // the processing.
+  auto ring = [&](auto mode_tag) __attribute__((always_inline)) {
+    constexpr bool SC4 = decltype(mode_tag)::value == kFp4Only;
+    // lane offsets from a row's load bases: FP4 rows the codes 64 w + 16 g
+    // .. + 15 and the word of scale bytes 16 (w / 2) + 8 (w & 1) + 2 g (its
+    // two groups); window rows the bytes 128 w + 32 g .. + 31
+    const int o0 = SC4 ? 64 * wave + 16 * g : 128 * wave + 32 * g;
+    const int o1 = SC4 ? 16 * (wave >> 1) + 4 * (2 * (wave & 1) + (g >> 1)) : 128 * wave + 32 * g;
+    constexpr bool BASES = STRAIGHT && decltype(mode_tag)::value != kMixed;
+    // the loads of sub-chunk sc into L from its rows' slots (and with BASES
+    // their load bases), read from LDS beforehand
+    auto issue_from = [&](int sc, const SubSlots& ss, const v4u (&rb)[2], SubLoads& L)
+                          __attribute__((always_inline)) {
+      if constexpr (BASES) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const RowPtrs base = __builtin_bit_cast(RowPtrs, rb[rt]);
+          L.s[rt] = ss.s[rt];
+          L.lo[rt] = gld16(base.p0 + o0);
+          if (SC4) L.hi[rt] = v4u{gld4(base.p1 + o1), 0u, 0u, 0u};
+          else L.hi[rt] = gld16(base.p1 + o1);
+        }
+      } else {
+        issue_sub<SC4>(a, ss, row0 + sc * kSub, wave, g, col, win_row0, L);
+      }
+    };
+    auto read_bases = [&](int sc, v4u (&rb)[2]) __attribute__((always_inline)) {
+      if constexpr (BASES) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) rb[rt] = *reinterpret_cast<const v4u*>(&rbase[sc * kSub + 16 * rt + col][0]);
+      }
+    };
+    // the first NB sub-chunks' row loads (everything they need read from LDS
+    // together first), then the query's conversion
+    {
+      v4u rb[NB][2];
+      SubSlots ss[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        ss[i] = read_sub(rslot, i * kSub, n_rel, col);
+        read_bases(i, rb[i]);
+      }
+      // (in sub-chunk order: the wait counter retires loads in issue order,
+      // so each sub-chunk then waits only for its own rows)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        issue_from(i, ss[i], rb[i], buf[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    q_convert();
+    if constexpr (STRAIGHT) {
+#pragma unroll
+      for (int sc = 0; sc < MAXS; ++sc) {
+        if (sc < n_sub) {
+          if (sc + NB < MAXS) {
+            // sub-chunk sc + NB refills this buffer after the processing
+            v4u rb[2];
+            const SubSlots ns = read_sub(rslot, (sc + NB) * kSub, n_rel, col);
+            read_bases(sc + NB, rb);
+            process(sc, buf[sc % NB], mode_tag);
+            issue_from(sc + NB, ns, rb, buf[sc % NB]);
+          } else {
+            process(sc, buf[sc % NB], mode_tag);
+          }
+        }
+      }
+    } else {
+      for (int sc0 = 0; sc0 < n_sub; sc0 += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int sc = sc0 + j;
+          if (sc < n_sub) {
+            const int nx = sc + NB;
+            const SubSlots ns = read_sub(rslot, nx * kSub, n_rel, col);
+            process(sc, buf[j], mode_tag);
+            issue_sub<SC4>(a, ns, row0 + nx * kSub, wave, g, col, win_row0, buf[j]);
+          }
+        }
+      }
+    }
   };
-
-  // ---- the sub-chunks through a ring of NB load buffers: the loads of the
-  // next NB - 1 sub-chunks are in flight while one is processed (the wait
-  // counter retires loads in issue order, so each sub-chunk waits only for
-  // its own rows)
-  // The ring turns by register copies, so that the loop body holds one copy
-  // of each sub-chunk kind's code.
-  const int n_rel = n_sub * kSub;
-  SubLoads buf[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) issue_sub(a, rslot, i * kSub, row0 + i * kSub, n_rel, wave, g, col, win_row0, buf[i]);
-  for (int sc = 0; sc < n_sub; ++sc) {
-    run_sub(sc, buf[0]);
-#pragma unroll
-    for (int i = 0; i + 1 < NB; ++i) buf[i] = buf[i + 1];
-    const int nx = sc + NB;
-    issue_sub(a, rslot, nx * kSub, row0 + nx * kSub, n_rel, wave, g, col, win_row0, buf[NB - 1]);
-  }
+  if (row1 <= a.topk) ring(std::integral_constant<int, kFp4Only>{});
+  else if (row0 >= a.topk) ring(std::integral_constant<int, kWindowOnly>{});
+  else ring(std::integral_constant<int, kMixed>{});
 
   if (a.n_splits == 1) {
     // ---- the whole list was this split's: normalize and write the output
@@ -558,22 +712,14 @@ struct HLoads {
 
 __device__ __forceinline__ void issue_hrow(const AttnArgs& a, const int* rslot, int rel, int abs_row, int n_rel,
                                            int c32, const uint8_t* win_row0, HLoads& L) {
-  const int s = rel < n_rel ? rslot[rel] : kRowAbsent;
+  const int s = row_at(rslot, rel, n_rel);
   L.s = s;
-  const uint8_t* p0 = a.kv_pool;
-  const uint8_t* p1 = a.kv_pool;
-  if (s >= 0) {
-    const uint8_t* page = a.kv_pool + (int64_t)(s >> 6) * kPageBytes;
-    p0 = page + (s & 63) * kEntryCodes + 16 * c32;
-    p1 = page + kPage * kEntryCodes + (s & 63) * kEntryScales + 16 * (c32 >> 3);
-  } else if (s == kRowWindow) {
-    p0 = win_row0 + (int64_t)(abs_row - a.topk) * kD + 32 * c32;
-    p1 = p0 + 16;
-  }
-  L.lo = gld16(p0);
-  L.hi = gld16(p1);
+  const RowPtrs rp = row_ptrs(a, s, win_row0, abs_row, 16 * c32, 16 * (c32 >> 3), 32 * c32);
+  L.lo = gld16(rp.p0);
+  L.hi = gld16(rp.p1);
 }
 
+template <int KP>
 __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) half_t tile[2][kSub * kTileRowHalves];  // double-buffered
   __shared__ __attribute__((aligned(16))) half_t pmat[64 * kPStride];            // P [head][row]
@@ -614,7 +760,7 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
 
   // ---- resolve the split's rows once (all index loads, then all page loads)
   {
-    constexpr int kPer = (kMaxRows + kSub + kHThreads - 1) / kHThreads;  // 5
+    constexpr int kPer = KP;
     int jj[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -630,18 +776,9 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = (int)threadIdx.x + k * kHThreads;
-      const int row = row0 + r;
-      int sl = kRowAbsent;
-      if (row < row1) {
-        if (row < a.topk) {
-          const int j = jj[k];
-          if (j >= 0 && j < n && pp[k] >= 0 && pp[k] < a.n_pages) sl = (int)((int64_t)pp[k] * kPage + (j & 63));
-        } else {
-          sl = kRowWindow;
-        }
-      }
-      if (r < n_rel) rslot[r] = sl;
+      if (r < n_rel) rslot[r] = row_slot(a, row0 + r, row1, n, jj[k], pp[k]);
     }
+    resolve_rest(a, idx_row, b, n, row0, row1, kPer * kHThreads, kHThreads, n_rel, rslot);
   }
   // each head's largest |q| over this wave's 256 channels (bf16 bits in the high half)
   {
@@ -964,6 +1101,11 @@ struct CombineArgs {
 // formed (one wave, in registers) while those are in flight.
 constexpr int kMaxSplits = 24;
 constexpr int kLoadRing = 3;  // sub-chunks whose row loads are in flight together
+constexpr int kStraightSubs = 5;  // splits of at most this many sub-chunks: the loop unrolled whole
+constexpr int kStraightBufs = 4;  // with this many load buffers
+// Rows per thread that cover a whole list (the longest split)
+constexpr int kResolveMax = (kMaxRows + kAttnThreads - 1) / kAttnThreads;  // 9
+constexpr int kHResolveMax = (kMaxRows + kHThreads - 1) / kHThreads;       // 5
 
 template <int MAXS>
 __global__ __launch_bounds__(128) void attn_combine_kernel(CombineArgs a) {
@@ -1038,38 +1180,38 @@ bool all_heads(int H, int BT) { return H == 64 && BT >= 8; }
 
 // Rows per split (a multiple of 32) and the number of splits of one (b, t)'s
 // [top-k | window] row list: about kTargetWorkgroups workgroups in all.
-void split_plan(int BT, int H, int topk, int* n_splits, int* split_rows) {
+void split_plan(int BT, int H, int topk, int* n_splits, int* split_rows, int* split_base, int* split_extra) {
+  const int rows = topk + CSA2_SWA;
+  const int subs = (rows + csa2::kSub - 1) / csa2::kSub;
   if (all_heads(H, BT)) {
-    const int rows = topk + CSA2_SWA;
-    const int max_splits = std::min((rows + csa2::kSub - 1) / csa2::kSub, csa2::kMaxSplits);
+    const int max_splits = std::min(subs, csa2::kMaxSplits);
     int ns = std::max(1, std::min((csa2::kTargetWorkgroups + BT - 1) / BT, max_splits));
     int per = (rows + ns - 1) / ns;
     per = (per + csa2::kSub - 1) / csa2::kSub * csa2::kSub;
     *split_rows = per;
     *n_splits = (rows + per - 1) / per;
+    *split_base = per / csa2::kSub;
+    *split_extra = 0;
     return;
   }
-  const int rows = topk + CSA2_SWA;
-  const int max_splits = (rows + csa2::kSub - 1) / csa2::kSub;
   const int units = BT * (H / 16);
-  // a large batch takes two splits per list (two workgroups per compute unit,
-  // so that one's waits hide behind the other's work)
+  // as many splits as fit the target in one round of workgroups (a second,
+  // partly filled round would make its workgroups share compute units); a
+  // large batch takes two workgroups per compute unit, so that one's waits
+  // hide behind the other's work
   const int target = units >= csa2::kTargetWorkgroups / 2 ? 2 * csa2::kTargetWorkgroups : csa2::kTargetWorkgroups;
-  int ns = (target + units - 1) / units;
-  ns = std::max(1, std::min(ns, max_splits));
-  // whole sub-chunks per split, rounded down (so at least ns splits), then
-  // no more than kMaxSplits splits
-  int per = std::max(csa2::kSub, rows / ns / csa2::kSub * csa2::kSub);
-  const int min_per = (rows + csa2::kMaxSplits - 1) / csa2::kMaxSplits;
-  if (per < min_per) per = (min_per + csa2::kSub - 1) / csa2::kSub * csa2::kSub;
-  *split_rows = per;
-  *n_splits = (rows + per - 1) / per;
+  const int ns = std::max(1, std::min(target / units, std::min(subs, csa2::kMaxSplits)));
+  // the sub-chunks shared out as evenly as whole sub-chunks allow
+  *n_splits = ns;
+  *split_base = subs / ns;
+  *split_extra = subs % ns;
+  *split_rows = (*split_base + (*split_extra > 0 ? 1 : 0)) * csa2::kSub;
 }
 }  // namespace
 
 extern "C" size_t csa2_attn_ws_bytes(int32_t B, int32_t T, int32_t H, int32_t topk) {
-  int ns, per;
-  split_plan(B * T, H, topk, &ns, &per);
+  int ns, per, base, extra;
+  split_plan(B * T, H, topk, &ns, &per, &base, &extra);
   if (ns == 1) return 256;  // no partials
   const size_t units = (size_t)B * T * (H / 16) * ns;
   return align256(units * 16 * csa2::kD * 4) + align256(units * 32 * 4);
@@ -1109,7 +1251,7 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   aa.T = T;
   aa.H = H;
   aa.BT = B * T;
-  split_plan(B * T, H, topk, &aa.n_splits, &aa.split_rows);
+  split_plan(B * T, H, topk, &aa.n_splits, &aa.split_rows, &aa.split_base, &aa.split_extra);
   const size_t units = (size_t)B * T * (H / 16) * aa.n_splits;
   if (aa.n_splits > 1) {
     aa.part_o = reinterpret_cast<float*>(ws);
@@ -1119,13 +1261,30 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
     aa.out_lse = out_lse;
   }
   const int n_units = aa.n_splits * B * T;
+  // rows each thread resolves up front: enough for the split's rows
   if (all_heads(H, B * T)) {
-    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel, dim3(n_units),
-                dim3(csa2::kHThreads), (hipStream_t)stream, aa);
+    const int kp = (aa.split_rows + csa2::kHThreads - 1) / csa2::kHThreads;
+    if (kp <= 1)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel<1>, dim3(n_units), dim3(csa2::kHThreads),
+                  (hipStream_t)stream, aa);
+    else if (kp <= 2)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel<2>, dim3(n_units), dim3(csa2::kHThreads),
+                  (hipStream_t)stream, aa);
+    else
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_heads_kernel<csa2::kHResolveMax>, dim3(n_units),
+                  dim3(csa2::kHThreads), (hipStream_t)stream, aa);
   } else {
     const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
-    CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, csa2::attn_split_kernel<csa2::kLoadRing>, dim3(grid),
-                dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
+    const int kp = (aa.split_rows + csa2::kAttnThreads - 1) / csa2::kAttnThreads;
+    if (aa.split_rows <= csa2::kStraightSubs * csa2::kSub)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kStraightBufs, 1, csa2::kStraightSubs>),
+                  dim3(grid), dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
+    else if (kp <= 3)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, 3, 0>), dim3(grid),
+                  dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
+    else
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, csa2::kResolveMax, 0>),
+                  dim3(grid), dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
   }
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   if (aa.n_splits == 1) return CSA2_OK;

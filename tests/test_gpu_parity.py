@@ -766,7 +766,8 @@ def test_attention_8k_b1(oracle):
 # holding both top-k and window rows
 @pytest.mark.parametrize("H,T,k,frac", [(16, 1, 256, 1.0), (32, 2, 512, 0.7), (64, 1, 2048, 0.5),
                                         (64, 2, 2048, 1.0), (16, 4, 8, 1.0), (64, 1, 100, 0.0),
-                                        (64, 3, 2048, 0.5), (64, 4, 100, 0.0), (64, 3, 2047, 1.0)])
+                                        (64, 3, 2048, 0.5), (64, 4, 100, 0.0), (64, 3, 2047, 1.0),
+                                        (32, 32, 2048, 0.8)])
 def test_attention_random_index_sets(oracle, H, T, k, frac):
     say(f"attention random sets H={H} T={T} k={k} valid={frac}")
     n = [5000, 300, 9999]
