@@ -138,6 +138,15 @@ struct SubLoads {
   int s[2];  // the rows' slots (or kRowAbsent / kRowWindow)
 };
 
+// The values of a batch of loads, all in flight together, are taken here
+// (an empty asm that reads them): the loads cannot move into a later
+// branch, and the wait for the first of them is a wait for them all.
+template <int N>
+__device__ __forceinline__ void resolve_fence(const int (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" ::"v"(v[k]));
+}
+
 // Cache slot of list row `row` of a (b, t) (rows past row1 are absent):
 // j is its top-k index and pg the page-table word of j's page (both unused
 // for a window row).
@@ -295,13 +304,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       const int row = row0 + (int)threadIdx.x + k * kAttnThreads;
       jj[k] = idx_row[max(0, min(row, a.topk - 1))];
     }
-    // (unconditional, clamped: a load inside a branch would be waited for there)
+    // (unconditional, clamped; each batch of loads is taken whole before the
+    // next goes out: left to itself the compiler sinks them into the
+    // per-row branch below, one row's two round trips after another's)
+    resolve_fence(jj);
     int pp[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int lp = max(0, min(jj[k] >> 6, a.max_pages - 1));
       pp[k] = a.page_table[(int64_t)b * a.max_pages + lp];
     }
+    resolve_fence(pp);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = (int)threadIdx.x + k * kAttnThreads;
@@ -767,12 +780,14 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
       const int row = row0 + (int)threadIdx.x + k * kHThreads;
       jj[k] = idx_row[max(0, min(row, a.topk - 1))];
     }
+    resolve_fence(jj);  // (each batch taken whole, as in the head-tile kernel)
     int pp[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int lp = max(0, min(jj[k] >> 6, a.max_pages - 1));
       pp[k] = a.page_table[(int64_t)b * a.max_pages + lp];
     }
+    resolve_fence(pp);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int r = (int)threadIdx.x + k * kHThreads;
