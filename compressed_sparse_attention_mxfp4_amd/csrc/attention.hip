@@ -240,20 +240,31 @@ __device__ __forceinline__ void issue_sub(const AttnArgs& a, const SubSlots& ss,
 // KP: rows of the list each thread resolves (KP * 256 >= the split's rows)
 // MAXS > 0: every split has at most MAXS sub-chunks, and the sub-chunk loop
 // is unrolled whole (no loop-carried load buffers, whose copies into the
-// loop's registers would wait for the loads): sub-chunk sc uses buffer
-// sc % NB.  MAXS = 0: the sub-chunks go through a ring of NB load buffers.
-template <int NB, int KP, int MAXS>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t kr[4][kSub * kRowHalves];
-  __shared__ __attribute__((aligned(16))) v4f ssum[2][4][2][64];  // double-buffered by sub-chunk
-  __shared__ __attribute__((aligned(16))) float alph[4][16];       // per wave: rescale factor per head
-  __shared__ __attribute__((aligned(16))) float qmax[4][16];       // per wave: max |q| per head
+// loop's registers would wait for the loads).  MAXS = 0: the sub-chunks go
+// through a ring of NB load buffers.
+// GR (with MAXS > 0): groups of 4 waves in the workgroup; group gi takes
+// the split's sub-chunks gi, gi + GR, ... with its own online softmax, and
+// the groups' results are merged at the end.  Two groups put two waves on
+// each SIMD, so that one's waits (LDS round trips, the softmax's dependent
+// steps) hide behind the other's work.  A group's j-th sub-chunk uses load
+// buffer j % NB.
+template <int NB, int KP, int MAXS, int GR>
+__global__ __launch_bounds__(kAttnThreads * GR, GR == 1 ? 2 : 1) void attn_split_kernel(AttnArgs a) {
+  static_assert(GR == 1 || MAXS > 0, "groups only with the unrolled loop");
+  constexpr int kThreads = kAttnThreads * GR;
+  __shared__ __attribute__((aligned(16))) half_t kr[GR][4][kSub * kRowHalves];
+  __shared__ __attribute__((aligned(16))) v4f ssum[GR][2][4][2][64];  // double-buffered by sub-chunk
+  __shared__ __attribute__((aligned(16))) float alph[GR][4][16];       // per wave: rescale factor per head
+  __shared__ __attribute__((aligned(16))) float qmax[4][16];           // per wave: max |q| per head
+  __shared__ __attribute__((aligned(16))) float gml[2][16];            // group 1's final m, l per head
+  __shared__ __attribute__((aligned(16))) float gfac[4][2][16];        // group 0 wave: merge factors per head
   __shared__ __attribute__((aligned(16))) int rslot[kMaxRows + kSub];
   // STRAIGHT: each row's two load bases (FP4 entry: its codes and its scale
   // bytes; window row: its bytes and 16 bytes on; absent: the pool's first
   // bytes), so that a lane's load addresses cost one add each
   constexpr bool STRAIGHT = MAXS > 0;
-  constexpr int kRB = STRAIGHT ? MAXS * kSub : 1;
+  constexpr int JG = STRAIGHT ? (MAXS + GR - 1) / GR : 1;  // sub-chunks of a group, at most
+  constexpr int kRB = STRAIGHT ? JG * GR * kSub : 1;
   __shared__ __attribute__((aligned(16))) uint64_t rbase[kRB][2];
 
   // XCD-aware order: workgroup id % 8 picks the XCD (and its L2).  The NHT
@@ -270,7 +281,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   const int bt = unit / a.n_splits;
   const int b = bt / a.T, t = bt % a.T;
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = (threadIdx.x >> 6) & 3;               // in its group
+  const int grp = GR == 1 ? 0 : (int)(threadIdx.x >> 8);  // wave group
   const int g = lane >> 4, col = lane & 15;
   int n = a.n_entries[b];
   n = min(n, a.max_pages * kPage);
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     int jj[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const int row = row0 + (int)threadIdx.x + k * kAttnThreads;
+      const int row = row0 + (int)threadIdx.x + k * kThreads;
       jj[k] = idx_row[max(0, min(row, a.topk - 1))];
     }
     // (unconditional, clamped; each batch of loads is taken whole before the
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     resolve_fence(pp);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const int r = (int)threadIdx.x + k * kAttnThreads;
+      const int r = (int)threadIdx.x + k * kThreads;
       const int sl = row_slot(a, row0 + r, row1, n, jj[k], pp[k]);
       if (r < n_rel) rslot[r] = sl;
       if (STRAIGHT && r < kRB) {
@@ -326,7 +338,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
         *reinterpret_cast<v4u*>(&rbase[r][0]) = __builtin_bit_cast(v4u, RowPtrs{rp.p0, rp.p1});
       }
     }
-    resolve_rest(a, idx_row, b, n, row0, row1, kPer * kAttnThreads, kAttnThreads, n_rel, rslot);
+    resolve_rest(a, idx_row, b, n, row0, row1, kPer * kThreads, kThreads, n_rel, rslot);
   }
 
   // ---- Q slice as the B operand of S^T = K.Q^T: lane (g, col) holds head
@@ -350,7 +362,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = max(mx, max((qraw[s][e] << 16) & 0x7FFF0000u, qraw[s][e] & 0x7FFF0000u));
     const float m4 = rows4_max(__uint_as_float(mx));
-    if (lane < 16) qmax[wave][lane] = m4;
+    if (grp == 0 && lane < 16) qmax[wave][lane] = m4;
     __syncthreads();  // also publishes rslot
   }
   // the query in fp16 (after the first row loads are out)
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   // sub-chunk, the wave's channels 32g .. 32g + 31 (16-byte chunks 4g ..
   // 4g + 3 of the wave's tile), straight into the A operand of S^T = K.Q^T,
   // and stores them into the tile for the transposed P.V reads
-  half_t* my_kr = kr[wave];
+  half_t* my_kr = kr[grp][wave];
   uint32_t st_addr[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
       v4f sacc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int d = 0; d < 4; ++d) sacc = mfma16(kA[rt][d], qb[d], sacc);
-      ssum[sc & 1][wave][rt][lane] = sacc;
+      ssum[grp][(sc / GR) & 1][wave][rt][lane] = sacc;
     }
     // one barrier per sub-chunk: the next sub-chunk writes the other buffer,
     // and this buffer is rewritten only after the next sub-chunk's barrier;
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) part[w4][rt] = ssum[sc & 1][w4][rt][lane];
+      for (int rt = 0; rt < 2; ++rt) part[w4][rt] = ssum[grp][(sc / GR) & 1][w4][rt][lane];
     // fixed order: ((w0 + w1) + w2) + w3
     v4f st[2];
 #pragma unroll
@@ -540,9 +552,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
     // every wave of the workgroup takes the same decision)
     // lane (g, col) has head col's factor; output rows are heads 4g..4g+3
     if (__ballot(grow && m_run != -__builtin_inff()) != 0) {
-      if (lane < 16) alph[wave][lane] = alpha;
+      if (lane < 16) alph[grp][wave][lane] = alpha;
       wave_lds_order();
-      const v4f al = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+      const v4f al = *reinterpret_cast<const v4f*>(&alph[grp][wave][4 * g]);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -606,38 +618,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
         for (int rt = 0; rt < 2; ++rt) rb[rt] = *reinterpret_cast<const v4u*>(&rbase[sc * kSub + 16 * rt + col][0]);
       }
     };
-    // the first NB sub-chunks' row loads (everything they need read from LDS
-    // together first), then the query's conversion
+    // the group's first NB sub-chunks' row loads (everything they need read
+    // from LDS together first), then the query's conversion
     {
       v4u rb[NB][2];
       SubSlots ss[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        ss[i] = read_sub(rslot, i * kSub, n_rel, col);
-        read_bases(i, rb[i]);
+        ss[i] = read_sub(rslot, (GR * i + grp) * kSub, n_rel, col);
+        read_bases(GR * i + grp, rb[i]);
       }
       // (in sub-chunk order: the wait counter retires loads in issue order,
       // so each sub-chunk then waits only for its own rows)
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        issue_from(i, ss[i], rb[i], buf[i]);
+        issue_from(GR * i + grp, ss[i], rb[i], buf[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     q_convert();
     if constexpr (STRAIGHT) {
+      // every group runs the same number of rounds (one barrier each); a
+      // group without a sub-chunk in the last round takes its barrier alone
+      const int n_rounds = (n_sub + GR - 1) / GR;
 #pragma unroll
-      for (int sc = 0; sc < MAXS; ++sc) {
-        if (sc < n_sub) {
-          if (sc + NB < MAXS) {
-            // sub-chunk sc + NB refills this buffer after the processing
-            v4u rb[2];
-            const SubSlots ns = read_sub(rslot, (sc + NB) * kSub, n_rel, col);
-            read_bases(sc + NB, rb);
-            process(sc, buf[sc % NB], mode_tag);
-            issue_from(sc + NB, ns, rb, buf[sc % NB]);
+      for (int j = 0; j < JG; ++j) {
+        if (j < n_rounds) {
+          const int sc = GR * j + grp;
+          if (sc < n_sub) {
+            if (j + NB < JG) {
+              // the group's sub-chunk NB later refills this buffer after
+              // the processing
+              const int nx = GR * (j + NB) + grp;
+              v4u rb[2];
+              const SubSlots ns = read_sub(rslot, nx * kSub, n_rel, col);
+              read_bases(nx, rb);
+              process(sc, buf[j % NB], mode_tag);
+              issue_from(nx, ns, rb, buf[j % NB]);
+            } else {
+              process(sc, buf[j % NB], mode_tag);
+            }
           } else {
-            process(sc, buf[sc % NB], mode_tag);
+            lds_barrier();  // (the one its sub-chunk would have taken)
           }
         }
       }
@@ -660,12 +682,51 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(AttnArgs a)
   else if (row0 >= a.topk) ring(std::integral_constant<int, kWindowOnly>{});
   else ring(std::integral_constant<int, kMixed>{});
 
+  if constexpr (GR == 2) {
+    // ---- the groups' results merged: group 1 leaves its output
+    // accumulators in LDS (wave w in its own tile, which only it used) and
+    // its running (m, l) per head; group 0 rescales both to the larger
+    // reference (a group with no row yet has m = -inf and contributes 0)
+    if (grp == 1) {
+      float* ob = reinterpret_cast<float*>(my_kr);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[(4 * c + i) * 64 + lane] = o_acc[c][i];
+      if (wave == 0 && lane < 16) {
+        gml[0][lane] = m_run;
+        gml[1][lane] = l_run;
+      }
+    }
+    lds_barrier();
+    if (grp == 1) return;
+    const float m1 = gml[0][col], l1 = gml[1][col];
+    const float m = fmaxf(m_run, m1);
+    const float f0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float f1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+    l_run = l_run * f0 + l1 * f1;
+    m_run = m;
+    // lane (g, col) has head col's factors; its output rows are heads 4g..4g+3
+    if (lane < 16) {
+      gfac[wave][0][lane] = f0;
+      gfac[wave][1][lane] = f1;
+    }
+    wave_lds_order();
+    const v4f a0 = *reinterpret_cast<const v4f*>(&gfac[wave][0][4 * g]);
+    const v4f a1 = *reinterpret_cast<const v4f*>(&gfac[wave][1][4 * g]);
+    const float* ob1 = reinterpret_cast<const float*>(kr[1][wave]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o_acc[c][i] = o_acc[c][i] * a0[i] + ob1[(4 * c + i) * 64 + lane] * a1[i];
+  }
+
   if (a.n_splits == 1) {
     // ---- the whole list was this split's: normalize and write the output
     // (heads 4g+i of lane (g, col) need their sums: lanes 0..15 hold l, m)
-    if (lane < 16) alph[wave][lane] = 1.0f / l_run;
+    if (lane < 16) alph[grp][wave][lane] = 1.0f / l_run;
     wave_lds_order();
-    const v4f inv = *reinterpret_cast<const v4f*>(&alph[wave][4 * g]);
+    const v4f inv = *reinterpret_cast<const v4f*>(&alph[grp][wave][4 * g]);
     float* orow = a.out + ((int64_t)bt * a.H + ht * 16) * kD;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -1118,6 +1179,7 @@ constexpr int kMaxSplits = 24;
 constexpr int kLoadRing = 3;  // sub-chunks whose row loads are in flight together
 constexpr int kStraightSubs = 5;  // splits of at most this many sub-chunks: the loop unrolled whole
 constexpr int kStraightBufs = 4;  // with this many load buffers
+constexpr int kPairBufs = 3;      // two wave groups: load buffers of each (its whole share)
 // Rows per thread that cover a whole list (the longest split)
 constexpr int kResolveMax = (kMaxRows + kAttnThreads - 1) / kAttnThreads;  // 9
 constexpr int kHResolveMax = (kMaxRows + kHThreads - 1) / kHThreads;       // 5
@@ -1291,14 +1353,20 @@ extern "C" int csa2_sparse_attn(const uint16_t* q, float sm_scale, const uint8_t
   } else {
     const int grid = 8 * (H / 16) * ((n_units + 7) / 8);
     const int kp = (aa.split_rows + csa2::kAttnThreads - 1) / csa2::kAttnThreads;
-    if (aa.split_rows <= csa2::kStraightSubs * csa2::kSub)
-      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kStraightBufs, 1, csa2::kStraightSubs>),
+    // two wave groups per workgroup when the splits have two sub-chunks or
+    // more and one round of workgroups holds the grid (one per compute unit)
+    if (aa.split_rows <= csa2::kStraightSubs * csa2::kSub && aa.split_rows >= 2 * csa2::kSub &&
+        grid <= csa2::kTargetWorkgroups)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kPairBufs, 1, csa2::kStraightSubs, 2>),
+                  dim3(grid), dim3(2 * csa2::kAttnThreads), (hipStream_t)stream, aa);
+    else if (aa.split_rows <= csa2::kStraightSubs * csa2::kSub)
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kStraightBufs, 1, csa2::kStraightSubs, 1>),
                   dim3(grid), dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
     else if (kp <= 3)
-      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, 3, 0>), dim3(grid),
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, 3, 0, 1>), dim3(grid),
                   dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
     else
-      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, csa2::kResolveMax, 0>),
+      CSA2_LAUNCH(CSA2_K_ATTN_SPLIT, (csa2::attn_split_kernel<csa2::kLoadRing, csa2::kResolveMax, 0, 1>),
                   dim3(grid), dim3(csa2::kAttnThreads), (hipStream_t)stream, aa);
   }
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
