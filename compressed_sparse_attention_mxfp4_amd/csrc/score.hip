@@ -528,17 +528,20 @@ __device__ int fine_crossing(const uint32_t* h, uint32_t x) {
   return top - k;
 }
 
-// Exclusive prefix sum over the workgroup in thread order; every thread
-// also gets the total.  Uses scan_tot[kWaves] (free again on return).
-__device__ int block_excl_scan512(int v, int* scan_tot, int* total) {
+// Exclusive prefix sum over one group of four waves (waves 4 gr .. 4 gr + 3)
+// in thread order; every thread also gets its group's total.  Both groups
+// call it together (its two barriers are the workgroup's).  Uses
+// scan_tot[kWaves] (free again on return).
+__device__ int group_excl_scan256(int v, int* scan_tot, int* total) {
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int g0 = wave & ~3, wg = wave & 3;
   const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) scan_tot[wave] = x;
   lds_barrier();
-  const int wt = (int)wave_incl_scan(lane < kWaves ? (uint32_t)scan_tot[lane] : 0u);
-  const int before = wave > 0 ? __builtin_amdgcn_readlane(wt, wave - 1) : 0;
-  *total = __builtin_amdgcn_readlane(wt, kWaves - 1);
+  const int wt = (int)wave_incl_scan(lane < 4 ? (uint32_t)scan_tot[g0 + lane] : 0u);
+  const int before = wg > 0 ? __builtin_amdgcn_readlane(wt, wg - 1) : 0;
+  *total = __builtin_amdgcn_readlane(wt, 3);
   lds_barrier();
   return before + x - v;
 }
@@ -549,9 +552,12 @@ __device__ int block_excl_scan512(int v, int* scan_tot, int* total) {
 // the fine bin (22 key bits) holding the part's m-th largest key, where m is
 // one and a half times the part's expected share of the list's top K plus
 // 16 (all keys when that is the whole part).  Keys and block maxima are
-// read back from the workspace, where this workgroup has just written them,
-// 8 consecutive positions per thread and round (4,096 per round); a part of
-// one round is read once.
+// read back from the workspace, where this workgroup has just written them.
+// The (token, list) pairs go two at a time, one to each half of the
+// workgroup (waves 0-3 and 4-7), in rounds of 16 consecutive positions per
+// thread (4,096 per half and round; a part of one round is read once); both
+// halves run the same steps and barriers, with the work masked off where a
+// half has nothing to do, so the two pairs' dependent steps overlap.
 template <bool POOL>
 __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, int Ts, int Tg, int seg, int nseg,
                                int c0, int c1,
@@ -599,67 +605,88 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
   }
   lds_barrier();
 
-  for (int p = 0; p < n_pairs; ++p) {
-    SegPlan pl = plan[p];
+  // ---- 2. the pairs, two at a time
+  constexpr int kGT = kScoreThreads / 2;  // threads of a half
+  constexpr int kPer = 16;                // positions per thread and round
+  const int grp = wave >> 2;
+  const int gt = tid & (kGT - 1);
+  uint32_t* gfine = fine[grp];
+  for (int r = 0; r < (n_pairs + 1) / 2; ++r) {
+    const int p = 2 * r + grp;
+    const bool mine = p < n_pairs;
+    const bool two = 2 * r + 1 < n_pairs;
+    const SegPlan pl0 = plan[2 * r];
+    const SegPlan pl1 = plan[two ? 2 * r + 1 : 2 * r];
+    SegPlan pl = grp ? pl1 : pl0;
+    // rounds, and whether a fine pass runs: the same in both halves
+    const int len = max(pl0.p1 - pl0.p0, two ? pl1.p1 - pl1.p0 : 0);
+    const int n_rr = (len + kPer * kGT - 1) / (kPer * kGT);
+    const bool fine_any = pl0.coarse >= 0 || (two && pl1.coarse >= 0);
+    const bool fine_mine = mine && pl.coarse >= 0;
     const float* src = pl.list == 0 ? a.out_s + pl.bt * list_stride_s : a.out_bm + pl.bt * bm_stride(a.max_n);
-    // keys of positions q0 .. q0 + 7 (0 past the part); rows start 16-byte
-    // aligned and p0 is a multiple of 8
-    auto load8 = [&](int q0, uint32_t (&k)[8]) {
-      if (q0 + 8 <= pl.p1) {
+    // keys of positions q0 .. q0 + 15 (0 past the part, and in a half with
+    // no pair); rows start 16-byte aligned and p0 is a multiple of 8
+    auto load16 = [&](int q0, uint32_t (&k)[kPer]) __attribute__((always_inline)) {
+      if (mine && q0 + kPer <= pl.p1) {
         const v4u* v = reinterpret_cast<const v4u*>(src + q0);
-        const v4u x0 = v[0], x1 = v[1];
+        v4u x[kPer / 4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k[e] = score_key(__uint_as_float(x0[e]));
-          k[4 + e] = score_key(__uint_as_float(x1[e]));
-        }
+        for (int i = 0; i < kPer / 4; ++i) x[i] = v[i];
+#pragma unroll
+        for (int i = 0; i < kPer / 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) k[4 * i + e] = score_key(__uint_as_float(x[i][e]));
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k[e] = q0 + e < pl.p1 ? score_key(src[q0 + e]) : 0u;
+        for (int e = 0; e < kPer; ++e) k[e] = (mine && q0 + e < pl.p1) ? score_key(src[q0 + e]) : 0u;
       }
     };
-    const bool one = pl.p1 - pl.p0 <= 8 * kScoreThreads;
-    uint32_t keys[8];
-    if (pl.coarse >= 0) {
-      // ---- 2. fine histogram (next 12 bits) of the keys in the crossing
+    const bool one = n_rr == 1;
+    uint32_t keys[kPer];
+    if (fine_any) {
+      // ---- fine histogram (next 12 bits) of the keys in the crossing
       // coarse bin, and its crossing: the threshold
+      if (fine_mine) {
 #pragma unroll
-      for (int i = 0; i < kFineBins / kScoreThreads; ++i) fine[p][tid + i * kScoreThreads] = 0u;
-      lds_barrier();
-      for (int base = pl.p0; base < pl.p1; base += 8 * kScoreThreads) {
-        load8(base + 8 * tid, keys);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (keys[e] != 0u && (int)(keys[e] >> 22) == pl.coarse)
-            atomicAdd(&fine[p][(keys[e] >> 10) & (kFineBins - 1)], 1u);
+        for (int i = 0; i < kFineBins / kGT; ++i) gfine[gt + i * kGT] = 0u;
       }
       lds_barrier();
-      if (wave == 0) {
-        const int c2 = fine_crossing(fine[p], (uint32_t)pl.rem);
+      for (int rr = 0; rr < n_rr; ++rr) {
+        load16(pl.p0 + rr * kPer * kGT + kPer * gt, keys);
+        if (fine_mine) {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e)
+            if (keys[e] != 0u && (int)(keys[e] >> 22) == pl.coarse)
+              atomicAdd(&gfine[(keys[e] >> 10) & (kFineBins - 1)], 1u);
+        }
+      }
+      lds_barrier();
+      if (fine_mine && (wave & 3) == 0) {
+        const int c2 = fine_crossing(gfine, (uint32_t)pl.rem);
         if (lane == 0) plan[p].thr = ((uint32_t)pl.coarse << 22) | ((uint32_t)c2 << 10);
       }
       lds_barrier();
-      pl.thr = plan[p].thr;
+      if (mine) pl.thr = plan[p].thr;
     } else if (one) {
-      load8(pl.p0 + 8 * tid, keys);
+      load16(pl.p0 + kPer * gt, keys);
     }
 
     // ---- 3. compaction: kept keys in list order
     SegHeader* hdr = a.seg_hdr + (pl.bt * 2 + pl.list) * a.max_segs + seg;
     Cand* cand = a.seg_cand + (pl.bt * 2 + pl.list) * a.seg_region + seg_off_at(a.seg_k, seg);
     int written = 0;
-    for (int base = pl.p0; base < pl.p1; base += 8 * kScoreThreads) {
-      const int q0 = base + 8 * tid;
-      if (!one) load8(q0, keys);
+    for (int rr = 0; rr < n_rr; ++rr) {
+      const int q0 = pl.p0 + rr * kPer * kGT + kPer * gt;
+      if (!one) load16(q0, keys);
       uint32_t keep = 0u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) keep |= (keys[e] != 0u && keys[e] >= pl.thr ? 1u : 0u) << e;
+      for (int e = 0; e < kPer; ++e) keep |= (keys[e] != 0u && keys[e] >= pl.thr ? 1u : 0u) << e;
       const int cnt = __builtin_popcount(keep);
       int tot;
-      const int before = block_excl_scan512(cnt, scan_tot, &tot);
+      const int before = group_excl_scan256(cnt, scan_tot, &tot);
       int o = written + before;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kPer; ++e) {
         if ((keep >> e) & 1u) {
           if (o < cap) cand[o] = Cand{keys[e], q0 + e};
           ++o;
@@ -667,7 +694,7 @@ __device__ void write_segments(const ScoreArgs& a, const RowCtx& rc, int slot, i
       }
       written += tot;
     }
-    if (tid == 0) {
+    if (mine && gt == 0) {
       uint32_t flags = 0u;
       if (written < pl.n_valid) flags |= kSegDropped;
       if (written > cap) flags |= kSegOverflow;
