@@ -784,9 +784,8 @@ struct HLoads {
   int s;
 };
 
-__device__ __forceinline__ void issue_hrow(const AttnArgs& a, const int* rslot, int rel, int abs_row, int n_rel,
-                                           int c32, const uint8_t* win_row0, HLoads& L) {
-  const int s = row_at(rslot, rel, n_rel);
+__device__ __forceinline__ void issue_hrow_s(const AttnArgs& a, int s, int abs_row, int c32, const uint8_t* win_row0,
+                                             HLoads& L) {
   L.s = s;
   const RowPtrs rp = row_ptrs(a, s, win_row0, abs_row, 16 * c32, 16 * (c32 >> 3), 32 * c32);
   L.lo = gld16(rp.p0);
@@ -878,10 +877,14 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   // pool's first bytes), so that every path reaches the loops with the same
   // loads in flight and the waits on them count exactly
   const int sc_pro = kh == 1 ? 0 : n_sub + 4;
-  auto issue_sub = [&](int sc, HLoads (&L)[2]) __attribute__((always_inline)) {
-    issue_hrow(a, rslot, sc * kSub + drow, row0 + sc * kSub + drow, n_rel, c32, win_row0, L[0]);
-    issue_hrow(a, rslot, sc * kSub + drow, row0 + sc * kSub + drow, n_rel, c32 + 8, win_row0, L[1]);
+  // (sub_slot: the slot of this lane's row of sub-chunk sc, read from LDS
+  // ahead of the loads it addresses)
+  auto sub_slot = [&](int sc) __attribute__((always_inline)) { return row_at(rslot, sc * kSub + drow, n_rel); };
+  auto issue_sub_s = [&](int sc, int s, HLoads (&L)[2]) __attribute__((always_inline)) {
+    issue_hrow_s(a, s, row0 + sc * kSub + drow, c32, win_row0, L[0]);
+    issue_hrow_s(a, s, row0 + sc * kSub + drow, c32 + 8, win_row0, L[1]);
   };
+  auto issue_sub = [&](int sc, HLoads (&L)[2]) __attribute__((always_inline)) { issue_sub_s(sc, sub_slot(sc), L); };
   issue_sub(sc_pro, buf[0]);
   issue_sub(sc_pro + 1, buf[1]);
 
@@ -1011,6 +1014,9 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
   auto process = [&](auto kh_c, int sc, HLoads (&slot)[2]) __attribute__((always_inline)) {
     constexpr bool KH1 = decltype(kh_c)::value;
     const uint32_t tb = (uint32_t)(sc & 1) * kBufBytes;
+    // (kh = 1: the slot of sub-chunk sc + 3's row, read now, long before its
+    // loads go out after the dequant)
+    const int s_next = KH1 ? sub_slot(sc + 3) : 0;
     // ---- Q.K role: partial logits of rows 16 rt + 4 g + i, head 16 ht + col,
     // over this wave's channel half
     v4f sacc[2];
@@ -1074,7 +1080,7 @@ __global__ __launch_bounds__(kHThreads) void attn_heads_kernel(AttnArgs a) {
       // 1); past the last sub-chunk the rows are absent (zeros into a
       // buffer no wave reads again, loads of the pool's first bytes)
       dequant(sc + 1, slot);
-      issue_sub(sc + 3, slot);
+      issue_sub_s(sc + 3, s_next, slot);
     }
     lds_barrier();  // 2: P, the rescale factors and the next tile
     // ---- P.V role: rescale, then O[heads][64 w + 16 ct ..] += P . V
