@@ -135,8 +135,9 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint
 // The K-th largest key tau comes from radix levels over v = key - (smallest
 // key), the first over the top 12 bits that vary among the keys; then every
 // key above tau and the first keys equal to tau, up to K, are written as
-// out[rank] = val(position, payload) (LDS), rank = place in ascending
-// position order.
+// out[rank] = val(position, payload), rank = place in ascending position
+// order: into LDS (out), or with GOUT straight to global memory (gout; the
+// stores need no barrier and no copy pass after them).
 // The keys may be part of a larger list whose top K is wanted: with more
 // than K keys, tau must be at least min_tau; with K or fewer, `complete`
 // must hold.  Otherwise nothing is emitted and the result is -1.  Returns
@@ -148,9 +149,10 @@ struct KeyStats {
   uint32_t kmin, kmax;
 };
 
-template <int EMAX, bool PAY, typename Val>
+template <int EMAX, bool PAY, bool GOUT = false, typename Val>
 __device__ __forceinline__ int lds_topk(const uint32_t* keys, const uint32_t* pay, int n, int K, uint32_t min_tau,
-                                        bool complete, KeyStats ks, SelShared& sh, uint32_t* out, Val val) {
+                                        bool complete, KeyStats ks, SelShared& sh, uint32_t* out, Val val,
+                                        int32_t* gout = nullptr) {
   static_assert(EMAX % 8 == 0, "chunks of 8");
   constexpr int NC = EMAX / 8;
   const int tid = (int)threadIdx.x;
@@ -334,7 +336,11 @@ __device__ __forceinline__ int lds_topk(const uint32_t* keys, const uint32_t* pa
     each([&](int r) {
       const bool eq = k[r] != 0u && k[r] == tau;
       const bool take = (k[r] > tau || (eq && eq_seen < need_eq)) && rank < K;
-      *(take ? out + rank : sh.dummy + lane) = val(i0 + r, pv[PAY ? r : 0]);
+      if (GOUT) {
+        if (take) gout[rank] = (int32_t)val(i0 + r, pv[PAY ? r : 0]);
+      } else {
+        *(take ? out + rank : sh.dummy + lane) = val(i0 + r, pv[PAY ? r : 0]);
+      }
       rank += take ? 1 : 0;
       eq_seen += eq ? 1 : 0;
     });
@@ -377,11 +383,12 @@ __device__ __forceinline__ void seg_issue(const SelectArgs& a, int64_t bt, int l
 
 // Top K of a (row, list) from its segments (seg_issue): returns kSegBad when
 // a segment reports an out-of-range MXFP4 scale; else, with `use`, the
-// number selected (out[rank] = val(list position), LDS), or kSegFail when
-// the segments cannot give the exact top K (or `use` is false).
+// number selected (gout[rank] = val(list position), global memory; nothing
+// is written otherwise), or kSegFail when the segments cannot give the
+// exact top K (or `use` is false).
 template <typename Val>
 __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int list, int K, bool use,
-                                          const SegCands& L, SelShared& sh, uint32_t* out, Val val) {
+                                          const SegCands& L, SelShared& sh, int32_t* gout, Val val) {
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -485,8 +492,8 @@ __device__ __forceinline__ int seg_finish(const SelectArgs& a, int64_t bt, int l
     }
   }
   lds_barrier();
-  const int got = lds_topk<kSegE, true>(sh.stage, sh.stage + kPosOff, tot, K, thr_max, complete, ks, sh, out,
-                                        [&](int, uint32_t pos) { return val(pos); });
+  const int got = lds_topk<kSegE, true, true>(sh.stage, sh.stage + kPosOff, tot, K, thr_max, complete, ks, sh,
+                                              nullptr, [&](int, uint32_t pos) { return val(pos); }, gout);
   return got < 0 ? kSegFail : got;
 }
 
@@ -636,25 +643,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     for (int i = tid; i < P; i += kSelThreads) sh.pool_blk[i] = -1;
   }
   // (the LDS writes above are ordered before the emission by the selection's barriers)
-  // the top-k goes to the stage's first slots (rank order; the keys being
-  // ranked are in registers by then), then out to memory in one coalesced pass
+  // the segments' selection goes straight to the output (rank order); the
+  // whole-list fallback ranks into LDS (the top-k into the stage's first
+  // slots, the keys being ranked are in registers by then), then out to
+  // memory in one coalesced pass
   uint32_t* topk_buf = sh.stage;
-  uint32_t* const sel_out = pool_list ? reinterpret_cast<uint32_t*>(sh.pool_blk) : topk_buf;
-  int got = seg_finish(a, row, list, K, a.mode != 1, L, sh, sel_out, [&](uint32_t pos) {
+  int32_t* const gout = pool_list ? a.out_pool + (int64_t)row * P : out;
+  int got = seg_finish(a, row, list, K, a.mode != 1, L, sh, gout, [&](uint32_t pos) {
     return (FULL || pool_list) ? pos : (uint32_t)(sh.pool_blk[pos >> 3] * kBlock + (pos & 7));
   });
-  if (got == kSegFail && a.mode != 2) {
-    // the whole lists (the top-k's fallback recomputes the pool)
-    lds_barrier();
-    if (FULL) pool_n = pool_whole(a, row, nb, sh);
-    got = pool_list ? pool_n : pool_topk<FULL>(a, row, n, pool_n, sh, topk_buf);
-  }
-  lds_barrier();
-  if (pool_list) {
-    for (int i = tid; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = got < 0 ? got : sh.pool_blk[i];
-    if (tid == 0) a.out_pool_n[row] = got;
+  if (got >= 0) {
+    for (int i = got + tid; i < K; i += kSelThreads) gout[i] = -1;
+    if (pool_list && tid == 0) a.out_pool_n[row] = got;
   } else {
-    for (int i = tid; i < a.topk; i += kSelThreads) out[i] = i < got ? (int32_t)topk_buf[i] : (got < 0 ? got : -1);
+    if (got == kSegFail && a.mode != 2) {
+      // the whole lists (the top-k's fallback recomputes the pool)
+      lds_barrier();
+      if (FULL) pool_n = pool_whole(a, row, nb, sh);
+      got = pool_list ? pool_n : pool_topk<FULL>(a, row, n, pool_n, sh, topk_buf);
+    }
+    lds_barrier();
+    if (pool_list) {
+      for (int i = tid; i < P; i += kSelThreads) a.out_pool[(int64_t)row * P + i] = got < 0 ? got : sh.pool_blk[i];
+      if (tid == 0) a.out_pool_n[row] = got;
+    } else {
+      for (int i = tid; i < a.topk; i += kSelThreads) out[i] = i < got ? (int32_t)topk_buf[i] : (got < 0 ? got : -1);
+    }
   }
   if (FULL && !wr_one) {
     for (int64_t t = wr_t0; t < wr_items; t += wr_stride) {
