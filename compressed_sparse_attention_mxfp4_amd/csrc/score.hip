@@ -1132,12 +1132,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     cur_ok = POOL || next_pg >= 0;
     float gmax = 0.0f;
     float s_mine = 0.0f;
-#pragma unroll
-    for (int st = 0; st < kSub; ++st) {
-      // ---- the sub-tile's keys as f16 (exact for every E4M3 code), in the
-      // channel order of the query slices
-      __builtin_amdgcn_sched_barrier(0);
-      v8h kf[4];
+    // ---- a sub-tile's keys as f16 (exact for every E4M3 code), in the
+    // channel order of the query slices
+    auto convert = [&](int st, v8h (&kf)[4]) __attribute__((always_inline)) {
       if (MX) {
         mxbad |= mx_scale_bad(cur.k[st][1]);
         // MXFP4: E2M1 codes times the group's power-of-two scale, exact in
@@ -1170,48 +1167,86 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
             kf[slice][e + 3] = hi2[1];
           }
       }
-      // the same sub-tile of the next chunk streams into the freed registers
-      // (after the conversions have read them)
-      __builtin_amdgcn_sched_barrier(0);
-      load_sub<POOL, MX>(a, rc, next, next_pg, st, g, col, cur.k[st]);
-      __builtin_amdgcn_sched_barrier(0);
-      // the 8 MFMAs of each row tile, then the sub-tile's Gram matrix
-      v4f sl4[kRT], sm4[kRT];
+    };
+    // fl(2^9 d) = fl(S_l + 2^7 S_m) (both sums exact, one rounding), then
+    // fl(w_h * max(d_h, +0)) and the row tile's pairwise sum
+    auto weigh = [&](const v4f& cl, const v4f& cm, const v4f& wv) __attribute__((always_inline)) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r = __builtin_fmaf(128.0f, cm[i], cl[i]);
+        p[i] = wv[i] * (r > 0.0f ? r : 0.0f);
+      }
+      return (p[0] + p[1]) + (p[2] + p[3]);
+    };
+    const v4f z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    v8h kf[4];
+    __builtin_amdgcn_sched_barrier(0);
+    convert(0, kf);
+    // the same sub-tile of the next chunk streams into the freed registers
+    // (after the conversions have read them)
+    __builtin_amdgcn_sched_barrier(0);
+    load_sub<POOL, MX>(a, rc, next, next_pg, 0, g, col, cur.k[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // software pipeline over (sub-tile, row tile) steps: each step's 8 MFMAs
+    // go out between the VALU work that weighs the previous step's sums, so
+    // the wave's VALU work fills the matrix unit's busy cycles
+    v4f pl = z4, pm = z4, gram_prev = z4;
+    float q4[kRT];
+#pragma unroll
+    for (int st = 0; st < kSub; ++st) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-        v4f cl = z, cm = z;
+        v4f cl = z4, cm = z4;
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
           cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[rt][sl], kf[sl], cl, 0, 0, 0);
           cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(qm[rt][sl], kf[sl], cm, 0, 0, 0);
         }
-        sl4[rt] = cl;
-        sm4[rt] = cm;
+        if (st > 0 || rt > 0) {
+          const int prt = rt == 0 ? kRT - 1 : rt - 1;
+          q4[prt] = weigh(pl, pm, wreg[prt]);
+          if (rt == 0) {
+            s_mine = keep_subtile(s_mine, head_sum4(q4), st - 1, lane);
+            gmax = fmaxf(gmax, fmaxf(fmaxf(gram_prev[0], gram_prev[1]), fmaxf(gram_prev[2], gram_prev[3])));
+          }
+        }
+        // order: one MFMA (mask 0x008), two VALU (mask 0x002), eight times
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pl = cl;
+        pm = cm;
       }
       // K K^T over the 128 channels: its diagonal holds sum_c k_c^2 of each
       // entry, and no other element exceeds the largest diagonal one
       // (Cauchy-Schwarz), so the maximum over all outputs is the largest
       // sum of squares of the sub-tile
-      v4f gram = {0.0f, 0.0f, 0.0f, 0.0f};
+      v4f gram = z4;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], kf[sl], gram, 0, 0, 0);
-      float q4[kRT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        const v4f wv = wreg[rt];
-        float p[4];
+      gram_prev = gram;
+      if (st + 1 < kSub) {
+        v8h kn[4];
+        convert(st + 1, kn);  // beside the Gram MFMAs, four VALU after each
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // fl(2^9 d) = fl(S_l + 2^7 S_m): both sums exact, one rounding
-          const float r = __builtin_fmaf(128.0f, sm4[rt][i], sl4[rt][i]);
-          p[i] = wv[i] * (r > 0.0f ? r : 0.0f);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
-        q4[rt] = (p[0] + p[1]) + (p[2] + p[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_sub<POOL, MX>(a, rc, next, next_pg, st + 1, g, col, cur.k[st + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = kn[i];
       }
-      gmax = fmaxf(gmax, fmaxf(fmaxf(gram[0], gram[1]), fmaxf(gram[2], gram[3])));
-      s_mine = keep_subtile(s_mine, head_sum4(q4), st, lane);
     }
+    q4[kRT - 1] = weigh(pl, pm, wreg[kRT - 1]);
+    s_mine = keep_subtile(s_mine, head_sum4(q4), kSub - 1, lane);
+    gmax = fmaxf(gmax, fmaxf(fmaxf(gram_prev[0], gram_prev[1]), fmaxf(gram_prev[2], gram_prev[3])));
     // every entry of the chunk has sum_c k_c^2 < 500, hence (Cauchy-Schwarz
     // over 128 channels) sum_c |k_c| < sqrt(128 * 500) < 253: the fast path
     // is exact, since every partial sum of ql * k or qm * k (|ql|, |qm| <=
