@@ -210,6 +210,25 @@ def time_steps(torch, ev, K, run_step):
     return ms, wall / K
 
 
+def time_chained(torch, ev, K, chain, per, single):
+    """Average ms per step over K steps replayed as graphs of `per` consecutive steps
+    (chain()), the remainder as single-step graphs (single(i)); one event pair around all."""
+    whole = ev.create(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.rt.hipEventRecord(whole[0], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    for _ in range(K // per):
+        chain()
+    for i in range(K % per):
+        single(i)
+    ev.rt.hipEventRecord(whole[1], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev.elapsed_ms(whole[0], whole[1]) / K
+    ev.destroy(whole)
+    return ms, wall / K
+
+
 def counters_driver(args):
     """Launch sequence for rocprofv3 counter runs: a plain 256 MiB device copy
     (calibrates FETCH_SIZE / WRITE_SIZE), then 3 times each: the Full indexer
@@ -470,6 +489,20 @@ def bench_layer(args):
         for i in range(args.warmup):
             graphs[i % args.copies].replay()
         torch.cuda.synchronize()
+        # the same steps captured `copies` at a time (cache copies 0 .. copies - 1 in turn), as a
+        # decode forward captures its consecutive layers in one graph: the gap the GPU leaves
+        # between two graph launches is paid once per `copies` steps
+        chain = capture(torch, 1, lambda _c, s: [step(c, s) for c in range(args.copies)])[0]
+        step(args.copies - 1, stream)
+        torch.cuda.synchronize()
+        ref_last = out_topk.clone(), out.clone()
+        chain.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_topk, ref_last[0]) and torch.equal(out, ref_last[1]), \
+            "chained graph replay differs from the eager step"
+        for _ in range(max(1, args.warmup // args.copies)):
+            chain.replay()
+        torch.cuda.synchronize()
 
     def run_step(i):
         if graphs is not None:
@@ -477,13 +510,19 @@ def bench_layer(args):
         else:
             step(i, stream)
 
-    ms_per_step, wall = time_steps(torch, ev, K, run_step)
+    ms_single, wall_single = time_steps(torch, ev, K, run_step)
+    if graphs is not None:
+        ms_per_step, wall = time_chained(torch, ev, K, chain.replay, args.copies, lambda i: graphs[i].replay())
+    else:
+        ms_per_step, wall = ms_single, wall_single
     value = 1000.0 / ms_per_step
     nbytes = algorithmic_bytes(wl, 68 if mx else 128)
     scan_gbs = nbytes["scan"] / (kern_us["score_full"] * 1e-6) / 1e9
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    log(f"{K} steps ({'eager' if graphs is None else 'graph replay'}): {ms_per_step * 1000:.1f} us/step "
-        f"(wall {wall * 1e6:.1f} us/step); kernels us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
+    log(f"{K} steps ({'eager' if graphs is None else f'graph replay, {args.copies} steps per graph'}): "
+        f"{ms_per_step * 1000:.1f} us/step (wall {wall * 1e6:.1f} us/step); "
+        + ("" if graphs is None else f"one step per graph {ms_single * 1000:.1f} us/step; ")
+        + "kernels us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": K,
@@ -494,7 +533,9 @@ def bench_layer(args):
                    "indexer_heads": wl.HI, "heads": H, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
                    "indexer_key_format": args.kidx_format, "cache_copies_rotated": args.copies,
                    "score_path": args.score_path,
-                   "launch": "eager" if graphs is None else "hip_graph_replay"},
+                   "launch": "eager" if graphs is None else "hip_graph_replay",
+                   "steps_per_graph": None if graphs is None else args.copies},
+        "ms_per_step_one_step_per_graph": None if graphs is None else round(ms_single, 5),
         "hbm_tb_s": round(step_gbs / 1000.0, 3),
         "hbm_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": nbytes["step"],
