@@ -377,6 +377,23 @@ __device__ __forceinline__ float head_sum4(const float (&q4)[kRT]) {
   return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;
 }
 
+// Levels 5 and 6 of the head sum for a chunk's four sub-tiles at once.
+// Lane (g, col) holds s16[st], the sum of heads 16 g .. 16 g + 15 of entry
+// 16 st + col.  Swapping odd rows of one register with even rows of another
+// (lane groups g, g ^ 1) pairs the quarters as Q0 + Q1 and Q2 + Q3 of two
+// sub-tiles per register; swapping the upper half of one register with the
+// lower half of the other (g, g ^ 2) adds those pairs, and sub-tile st's
+// total lands in lane group g = st: lane e holds the sum of entry e.  Then
+// + 0 (no -0).  The tree is the one head_sum4 follows.
+__device__ __forceinline__ float chunk_head_sum(const float (&s16)[4]) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s16[0]), __float_as_uint(s16[1]), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s16[2]), __float_as_uint(s16[3]), false, false);
+  const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float B = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+  return (__uint_as_float(c[0]) + __uint_as_float(c[1])) + 0.0f;
+}
+
 // Lane e = 16 g + col keeps the sum of entry e: sub-tile g's sum (every
 // lane (g', col) holds the sum of entry 16 st + col of sub-tile st).
 __device__ __forceinline__ float keep_subtile(float mine, float sum, int st, int lane) {
@@ -1193,6 +1210,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     // the wave's VALU work fills the matrix unit's busy cycles
     v4f pl = z4, pm = z4, gram_prev = z4;
     float q4[kRT];
+    // Full mode: per sub-tile this lane's quarter of the head sum, summed
+    // across the lane groups once per chunk; Reindex mode sums each
+    // sub-tile on its own (no registers to spare for the four quarters)
+    float s16[kSub];
+    static_assert(kSub == 4, "one sub-tile per lane group");
 #pragma unroll
     for (int st = 0; st < kSub; ++st) {
 #pragma unroll
@@ -1207,7 +1229,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
           const int prt = rt == 0 ? kRT - 1 : rt - 1;
           q4[prt] = weigh(pl, pm, wreg[prt]);
           if (rt == 0) {
-            s_mine = keep_subtile(s_mine, head_sum4(q4), st - 1, lane);
+            if (POOL)
+              s_mine = keep_subtile(s_mine, head_sum4(q4), st - 1, lane);
+            else
+              s16[st - 1] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
             gmax = fmaxf(gmax, fmaxf(fmaxf(gram_prev[0], gram_prev[1]), fmaxf(gram_prev[2], gram_prev[3])));
           }
         }
@@ -1245,7 +1270,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       }
     }
     q4[kRT - 1] = weigh(pl, pm, wreg[kRT - 1]);
-    s_mine = keep_subtile(s_mine, head_sum4(q4), kSub - 1, lane);
+    if (POOL) {
+      s_mine = keep_subtile(s_mine, head_sum4(q4), kSub - 1, lane);
+    } else {
+      s16[kSub - 1] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+      s_mine = chunk_head_sum(s16);
+    }
     gmax = fmaxf(gmax, fmaxf(fmaxf(gram_prev[0], gram_prev[1]), fmaxf(gram_prev[2], gram_prev[3])));
     // every entry of the chunk has sum_c k_c^2 < 500, hence (Cauchy-Schwarz
     // over 128 channels) sum_c |k_c| < sqrt(128 * 500) < 253: the fast path
