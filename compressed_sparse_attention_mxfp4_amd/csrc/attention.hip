@@ -1255,7 +1255,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // 64 heads with B*T >= 8 take the all-heads kernel (one workgroup per (b,
 // t, split)); fewer heads or rows the head-tile kernel (one per (b, t, head
 // tile, split)).
-// (At B*T = 4, 1M context, the head-tile kernel's 272 workgroups finish the
+// (At B*T = 4, 1M context, the head-tile kernel's 272 workgroups (now one
+// round of 256) finished the
 // replayed layer step ~4.5 us sooner than the all-heads kernel's 92; from
 // B*T = 8 on the all-heads kernel is faster: 62 against 67 us per 128K Full
 // layer at B = 8, 56 against 90 us per layer at B*T = 64.)
