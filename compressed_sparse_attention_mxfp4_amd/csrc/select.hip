@@ -18,9 +18,11 @@
 // threshold, hence below tau).  Otherwise the selection falls back to the
 // whole lists.
 //
-// A workgroup is 256 threads, one wave per SIMD: most of the selection's
-// steps cost a fixed number of instructions per wave (reductions, address
-// arithmetic), so more waves per SIMD would only make each step longer.
+// A workgroup is 512 threads, two waves per SIMD.  Each step is a chain of
+// dependent instructions over the keys a thread owns (stage writes, radix
+// digits, ranks), so halving the keys per thread shortens every step, and
+// the second wave on each SIMD fills the first one's latencies; 1,024
+// threads measured no faster (the block-wide steps and barriers grow).
 // The keys being ranked sit in LDS, thread t owning a contiguous range.
 #include <algorithm>
 
@@ -30,7 +32,7 @@
 
 namespace csa2 {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kDigit = 12;
 constexpr int kBins = 1 << kDigit;         // radix digits: 64 bins per lane of one wave
@@ -38,7 +40,7 @@ constexpr int kStage = 32768;              // LDS key slots: a whole list of blo
 constexpr int kPosOff = kStage / 2;        // segment path: candidate positions from here
 // Segment path: at most 64 candidates per thread, 16,384 per row and list
 // (the ranking's reads then end inside the key half)
-constexpr int kSegE = 64;
+constexpr int kSegE = 32;
 constexpr int kCandCap = kSegE * kSelThreads;
 static_assert(kCandCap <= kPosOff, "key reads inside the key half");
 constexpr int kSegFail = CSA2_ROW_UNRANKED;  // the segments cannot give the exact result
@@ -127,10 +129,10 @@ __device__ __forceinline__ int wave_crossing(const uint32_t* h, uint32_t x, uint
 
 // Top K of the keys keys[0 .. n) (LDS, list order, key 0 = empty), order
 // (key desc, position asc).  Thread t owns positions E t .. E t + E - 1,
-// E = ceil(n / 256) rounded up to 8 (at most EMAX), and reads them into
+// E = ceil(n / 512) rounded up to 8 (at most EMAX), and reads them into
 // registers at once (with PAY, also the payload words pay[E t ..]), so every
 // later step works on registers, in chunks of 8 (only the E / 8 chunks in
-// use are processed); the reads end below 256 E, which the callers keep
+// use are processed); the reads end below 512 E, which the callers keep
 // inside their arrays.
 // The K-th largest key tau comes from radix levels over v = key - (smallest
 // key), the first over the top 12 bits that vary among the keys; then every
@@ -351,9 +353,9 @@ __device__ __forceinline__ int lds_topk(const uint32_t* keys, const uint32_t* pa
 // Candidates of one (row, list), loaded ahead of the headers that say how
 // many there are, for the usual segment count W (segs_guess): thread t
 // covers segment t / tps, slots (t % tps) + tps r (r < kSegR), with tps =
-// 256 / W threads per segment; thread t also reads header t (t < max_segs)
+// 512 / W threads per segment; thread t also reads header t (t < max_segs)
 // and every thread the row's segment count.
-constexpr int kSegR = 32;
+constexpr int kSegR = 16;
 struct SegCands {
   v2u c[kSegR];
   SegHeader h;    // header t
@@ -535,7 +537,7 @@ __device__ __forceinline__ int pool_whole(const SelectArgs& a, int row, int nb, 
 }
 
 // Top-k over the pool's positions (list position p = 8 * slot + e): thread t
-// gathers slots t + 256 q with 16-byte loads into the stage.  Full mode:
+// gathers slots t + 512 q with 16-byte loads into the stage.  Full mode:
 // the entries of the pool's blocks from the entry scores; Reindex mode: the
 // pool-order scores.
 template <bool FULL>
@@ -548,7 +550,7 @@ __device__ __forceinline__ int pool_topk(const SelectArgs& a, int row, int n, in
   const float* srow = FULL ? a.s + (int64_t)row * s_stride(a.max_n) : a.s + (int64_t)row * P * kBlock;
   const uint32_t row_bytes = FULL ? (uint32_t)s_stride(a.max_n) * 4u : (uint32_t)P * kBlock * 4u;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, row_bytes, kBufferFlags);
-  constexpr int kSlots = CSA2_MAX_POOL_BLOCKS / kSelThreads;  // 8
+  constexpr int kSlots = CSA2_MAX_POOL_BLOCKS / kSelThreads;  // 4
   v4u g[kSlots][2];
   int blk[kSlots];
 #pragma unroll
