@@ -489,18 +489,19 @@ def bench_layer(args):
         for i in range(args.warmup):
             graphs[i % args.copies].replay()
         torch.cuda.synchronize()
-        # the same steps captured `copies` at a time (cache copies 0 .. copies - 1 in turn), as a
-        # decode forward captures its consecutive layers in one graph: the gap the GPU leaves
-        # between two graph launches is paid once per `copies` steps
-        chain = capture(torch, 1, lambda _c, s: [step(c, s) for c in range(args.copies)])[0]
-        step(args.copies - 1, stream)
+        # the same steps captured `steps_per_graph` at a time (step j on cache copy j mod copies),
+        # as a decode forward captures its consecutive layers in one graph: the gap the GPU leaves
+        # between two graph launches is paid once per graph
+        spg = args.steps_per_graph
+        chain = capture(torch, 1, lambda _c, s: [step(c, s) for c in range(spg)])[0]
+        step(spg - 1, stream)
         torch.cuda.synchronize()
         ref_last = out_topk.clone(), out.clone()
         chain.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_topk, ref_last[0]) and torch.equal(out, ref_last[1]), \
             "chained graph replay differs from the eager step"
-        for _ in range(max(1, args.warmup // args.copies)):
+        for _ in range(max(1, args.warmup // spg)):
             chain.replay()
         torch.cuda.synchronize()
 
@@ -512,14 +513,15 @@ def bench_layer(args):
 
     ms_single, wall_single = time_steps(torch, ev, K, run_step)
     if graphs is not None:
-        ms_per_step, wall = time_chained(torch, ev, K, chain.replay, args.copies, lambda i: graphs[i].replay())
+        ms_per_step, wall = time_chained(torch, ev, K, chain.replay, spg,
+                                         lambda i: graphs[i % args.copies].replay())
     else:
         ms_per_step, wall = ms_single, wall_single
     value = 1000.0 / ms_per_step
     nbytes = algorithmic_bytes(wl, 68 if mx else 128)
     scan_gbs = nbytes["scan"] / (kern_us["score_full"] * 1e-6) / 1e9
     step_gbs = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    log(f"{K} steps ({'eager' if graphs is None else f'graph replay, {args.copies} steps per graph'}): "
+    log(f"{K} steps ({'eager' if graphs is None else f'graph replay, {args.steps_per_graph} steps per graph'}): "
         f"{ms_per_step * 1000:.1f} us/step (wall {wall * 1e6:.1f} us/step); "
         + ("" if graphs is None else f"one step per graph {ms_single * 1000:.1f} us/step; ")
         + "kernels us: " + ", ".join(f"{k}={v:.1f}" for k, v in kern_us.items()))
@@ -534,7 +536,7 @@ def bench_layer(args):
                    "indexer_key_format": args.kidx_format, "cache_copies_rotated": args.copies,
                    "score_path": args.score_path,
                    "launch": "eager" if graphs is None else "hip_graph_replay",
-                   "steps_per_graph": None if graphs is None else args.copies},
+                   "steps_per_graph": None if graphs is None else args.steps_per_graph},
         "ms_per_step_one_step_per_graph": None if graphs is None else round(ms_single, 5),
         "hbm_tb_s": round(step_gbs / 1000.0, 3),
         "hbm_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -913,6 +915,8 @@ def main():
                     choices=["full_1m_b4", "full_8k_b1", "group_128k_b8", "schedule_20l_b32", "cache_write_1m",
                              "prefill_256t_1m"])
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (> 512 MB touched)")
+    ap.add_argument("--steps-per-graph", type=int, default=8,
+                    help="consecutive layer steps per replayed graph (cache copy = step mod copies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kidx-format", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="indexer-key format: E4M3 (128 B per entry) or the pages' MXFP4 (68 B per entry, "
